@@ -1,0 +1,403 @@
+/*
+ * HGA reference oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU implementation of what the Hierarchical Global
+ * Attention hot path computes.  Only tests/, the smoke check and the CPU
+ * baseline leg of the benchmark may load it.  It shares no code, header,
+ * table or helper with the GPU library; the two meet only through the seeded
+ * inputs that synth/ produces.
+ *
+ * Source of every definition: "Technische Samenvatting: Hierarchical Global
+ * Attention (HGA)" (gist.science summary of the HGA paper), section
+ * "Kernmechanisme":
+ *   item 1  fixed-size chunks (C tokens), each split into groups;
+ *   item 2  level-1 routing of the current query against chunk key summaries,
+ *           level-2 routing against the group key summaries of the chosen
+ *           chunks, and the always-visible current / sink / local chunks;
+ *   item 3  RoPE-aware summaries: high-frequency pairs are rotated per token
+ *           and then averaged, low-frequency pairs are averaged in raw key
+ *           space and then rotated to the chunk's representative position;
+ *   item 4  exact softmax attention over the original token K/V of the
+ *           selected set (no summary enters the output).
+ * Where the page leaves a step open, this file takes the plainest reading:
+ *   - RoPE pairs are (x_j, x_{j+d/2}) with omega_j = theta^(-2j/d);
+ *   - pair j is high-frequency iff its wavelength 2*pi/omega_j is below a
+ *     configured threshold (the chunk size), the same split for chunk and
+ *     group summaries;
+ *   - a span's representative position is its midpoint a + (n-1)/2;
+ *   - group summaries use the same mixed rule over the group's own span;
+ *   - routing is per (sequence, KV head) with the query pooled as the mean of
+ *     the rotated queries of that KV head's query heads (and query tokens);
+ *   - level 2 keeps a single global top-k over all groups of the chosen
+ *     chunks; candidates are the complete chunks strictly between the sink
+ *     and local windows; ties order by (score descending, id ascending);
+ *   - pool keys are stored rotated and rounded once (bf16 RNE, or fp32).
+ *
+ * Parity pins: every function here is checked in tests/test_oracle_pins.py
+ * against closed forms, library routines or brute force.  No function is
+ * "parity unpinned".
+ *
+ * All arithmetic is IEEE fp64 in the order written; loops are plain.  The
+ * only library primitives are libm (pow, sin, cos, exp, log, frexp, ldexp,
+ * nearbyint) and qsort.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+  int d;              /* head dim, even */
+  int hq;             /* query heads */
+  int hkv;            /* key/value heads; hq % hkv == 0 */
+  int C;              /* chunk size in tokens */
+  int G;              /* groups per chunk; C % G == 0 */
+  int n_sink;         /* always-visible leading chunks */
+  int n_local;        /* always-visible chunks just before the current one */
+  int topk_c;         /* level-1 chunk budget */
+  int topk_g;         /* level-2 group budget */
+  double theta;       /* RoPE base */
+  double hf_wavelength; /* pair j is high-frequency iff 2*pi/omega_j < this */
+  int pool_bf16;      /* 1: pool keys stored as bf16 (RNE); 0: as fp32 (RNE) */
+} ora_cfg;
+
+/* ---------------------------------------------------------------- RoPE
+ * Pairs are (x_j, x_{j+d/2}) for j < d/2 (half-split convention).  Pair j
+ * turns at angular frequency omega_j = theta^(-2j/d); at position p it is
+ * rotated by the angle p*omega_j:  (a, b) -> (a cos - b sin, a sin + b cos).
+ */
+double ora_omega(const ora_cfg* c, int j) {
+  return pow(c->theta, -2.0 * (double)j / (double)c->d);
+}
+
+int ora_is_hf(const ora_cfg* c, int j) {
+  double wavelength = 2.0 * M_PI / ora_omega(c, j);
+  return wavelength < c->hf_wavelength;
+}
+
+/* Rotate vector x (length d) to position pos (pos may be fractional). */
+void ora_rope(const ora_cfg* c, const double* x, double pos, double* out) {
+  int h = c->d / 2;
+  for (int j = 0; j < h; ++j) {
+    double ang = pos * ora_omega(c, j);
+    double cs = cos(ang), sn = sin(ang);
+    double a = x[j], b = x[j + h];
+    out[j] = a * cs - b * sn;
+    out[j + h] = a * sn + b * cs;
+  }
+}
+
+/* --------------------------------------------------------- summaries
+ * Summary of the span of n tokens starting at position a (raw, pre-RoPE keys
+ * kraw[n][d]).  Representative position r = a + (n-1)/2 (the span midpoint).
+ *   HF pair j: mean over the span of the per-token rotated pair.
+ *   LF pair j: the mean raw pair, rotated to r.
+ */
+void ora_span_summary(const ora_cfg* c, const double* kraw, long a, int n, double* out) {
+  int d = c->d, h = d / 2;
+  double r = (double)a + 0.5 * (double)(n - 1);
+  for (int j = 0; j < h; ++j) {
+    double w = ora_omega(c, j);
+    double sa = 0.0, sb = 0.0;
+    if (ora_is_hf(c, j)) {
+      for (int i = 0; i < n; ++i) {
+        double ang = (double)(a + i) * w;
+        double ka = kraw[(long)i * d + j], kb = kraw[(long)i * d + j + h];
+        sa += ka * cos(ang) - kb * sin(ang);
+        sb += ka * sin(ang) + kb * cos(ang);
+      }
+      out[j] = sa / n;
+      out[j + h] = sb / n;
+    } else {
+      for (int i = 0; i < n; ++i) {
+        sa += kraw[(long)i * d + j];
+        sb += kraw[(long)i * d + j + h];
+      }
+      sa /= n;
+      sb /= n;
+      out[j] = sa * cos(r * w) - sb * sin(r * w);
+      out[j + h] = sa * sin(r * w) + sb * cos(r * w);
+    }
+  }
+}
+
+/* Summaries of every complete chunk and group of one (sequence, KV head):
+ * kraw[T][d] -> chunk_sum[T/C][d], group_sum[(T/C)*G][d]. */
+void ora_summaries(const ora_cfg* c, const double* kraw, long T, double* chunk_sum, double* group_sum) {
+  int d = c->d, g = c->C / c->G;
+  long nch = T / c->C;
+  for (long ch = 0; ch < nch; ++ch) {
+    long a = ch * c->C;
+    ora_span_summary(c, kraw + a * d, a, c->C, chunk_sum + ch * d);
+    for (int i = 0; i < c->G; ++i) {
+      long ga = a + (long)i * g;
+      ora_span_summary(c, kraw + ga * d, ga, g, group_sum + (ch * c->G + i) * d);
+    }
+  }
+}
+
+/* -------------------------------------------------------------- pool
+ * Round-to-nearest-even of an fp64 value to bf16 (8 significant bits, fp32
+ * exponent range), done directly from fp64 so there is no double rounding. */
+double ora_round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  double m = frexp(x, &e);        /* x = m * 2^e, 0.5 <= |m| < 1 */
+  int q = e - 8;                  /* weight of the last kept bit */
+  if (q < -133) q = -133;         /* bf16 subnormal quantum is 2^-133 */
+  double s = ldexp(x, -q);
+  return ldexp(nearbyint(s), q);  /* default rounding mode: ties to even */
+}
+
+void ora_round_bf16_vec(const double* x, long n, double* out) {
+  for (long i = 0; i < n; ++i) out[i] = ora_round_bf16(x[i]);
+}
+
+/* Rotated pool keys for tokens pos0..pos0+n-1: round(RoPE(k, p)). */
+void ora_pool(const ora_cfg* c, const double* kraw, long pos0, long n, double* kpool) {
+  int d = c->d;
+  for (long i = 0; i < n; ++i) {
+    ora_rope(c, kraw + i * d, (double)(pos0 + i), kpool + i * d);
+    for (int e = 0; e < d; ++e) {
+      double v = kpool[i * d + e];
+      kpool[i * d + e] = c->pool_bf16 ? ora_round_bf16(v) : (double)(float)v;
+    }
+  }
+}
+
+/* ------------------------------------------------ windows, candidates
+ * For the current chunk ct:
+ *   sink chunks   [0, min(n_sink, ct))
+ *   local chunks  [max(0, ct - n_local), ct)
+ *   candidates    n_sink <= ch < ct - n_local (complete chunks only).
+ * Returns the number of window chunks written to win (ascending, no
+ * duplicates) and sets *cand_lo, *cand_hi to the candidate range. */
+int ora_windows(const ora_cfg* c, long ct, long* win, long* cand_lo, long* cand_hi) {
+  int n = 0;
+  for (long ch = 0; ch < ct; ++ch) {
+    int in_sink = ch < c->n_sink;
+    int in_local = ch >= ct - c->n_local;
+    if (in_sink || in_local) win[n++] = ch;
+  }
+  *cand_lo = c->n_sink;
+  *cand_hi = ct - c->n_local;
+  if (*cand_hi < *cand_lo) *cand_hi = *cand_lo;
+  return n;
+}
+
+/* ------------------------------------------------------ selection */
+typedef struct {
+  double s;
+  long id;
+} ora_item;
+
+static int by_score_desc_id_asc(const void* x, const void* y) {
+  const ora_item* a = (const ora_item*)x;
+  const ora_item* b = (const ora_item*)y;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->id > b->id) - (a->id < b->id);
+}
+
+static int by_id(const void* x, const void* y) {
+  long a = *(const long*)x, b = *(const long*)y;
+  return (a > b) - (a < b);
+}
+
+static double dot(const double* x, const double* y, int d) {
+  double s = 0.0;
+  for (int i = 0; i < d; ++i) s += x[i] * y[i];
+  return s;
+}
+
+/* Pooled routing query of one KV head: mean over its hg query heads and lq
+ * query tokens (positions pos0..pos0+lq-1) of RoPE(q, position).
+ * q is [hg][lq][d], raw (pre-RoPE). */
+void ora_pooled_query(const ora_cfg* c, const double* q, int hg, int lq, long pos0, double* qbar) {
+  int d = c->d;
+  double* tmp = (double*)malloc(sizeof(double) * d);
+  for (int e = 0; e < d; ++e) qbar[e] = 0.0;
+  for (int h = 0; h < hg; ++h)
+    for (int t = 0; t < lq; ++t) {
+      ora_rope(c, q + ((long)h * lq + t) * d, (double)(pos0 + t), tmp);
+      for (int e = 0; e < d; ++e) qbar[e] += tmp[e];
+    }
+  for (int e = 0; e < d; ++e) qbar[e] /= (double)(hg * lq);
+  free(tmp);
+}
+
+/* Two-level selection for one (sequence, KV head).
+ *   q           [hg][lq][d] raw query of the KV head's query heads
+ *   pos0, lq    query tokens pos0..pos0+lq-1, all inside chunk ct
+ *   chunk_sum   [>= ct][d], group_sum [>= ct*G][d]
+ * Writes the ascending list of selected group ids (window chunks expanded to
+ * all their groups, the current chunk's groups up to the last query token,
+ * and the routed groups) and returns its length, or -1 if max_sel is too
+ * small.  margins[0], margins[1] receive the level-1 and level-2 score gaps
+ * between the last kept and first dropped item (INFINITY when nothing is
+ * dropped).  cand_scores (optional) receives the level-1 scores of the
+ * candidate chunks in chunk order. */
+int ora_select(const ora_cfg* c, const double* q, int lq, long pos0, const double* chunk_sum,
+               const double* group_sum, int* sel_groups, int max_sel, double* margins,
+               double* cand_scores) {
+  int d = c->d, G = c->G, g = c->C / c->G, hg = c->hq / c->hkv;
+  long ct = pos0 / c->C;
+  long last = pos0 + lq - 1;
+  double inv_sqrt_d = 1.0 / sqrt((double)d);
+
+  double* qbar = (double*)malloc(sizeof(double) * d);
+  ora_pooled_query(c, q, hg, lq, pos0, qbar);
+
+  long* win = (long*)malloc(sizeof(long) * (ct + 1));
+  long lo, hi;
+  int nwin = ora_windows(c, ct, win, &lo, &hi);
+  long ncand = hi - lo;
+
+  /* level 1 */
+  ora_item* l1 = (ora_item*)malloc(sizeof(ora_item) * (ncand > 0 ? ncand : 1));
+  for (long i = 0; i < ncand; ++i) {
+    l1[i].id = lo + i;
+    l1[i].s = dot(qbar, chunk_sum + (lo + i) * d, d) * inv_sqrt_d;
+    if (cand_scores) cand_scores[i] = l1[i].s;
+  }
+  qsort(l1, ncand, sizeof(ora_item), by_score_desc_id_asc);
+  long k1 = c->topk_c < ncand ? c->topk_c : ncand;
+  margins[0] = (k1 < ncand) ? l1[k1 - 1].s - l1[k1].s : INFINITY;
+  if (k1 == 0) margins[0] = INFINITY;
+
+  /* level 2: global top-k over all groups of the chosen chunks */
+  long n2 = k1 * G;
+  ora_item* l2 = (ora_item*)malloc(sizeof(ora_item) * (n2 > 0 ? n2 : 1));
+  for (long i = 0; i < k1; ++i)
+    for (int j = 0; j < G; ++j) {
+      long gid = l1[i].id * G + j;
+      l2[i * G + j].id = gid;
+      l2[i * G + j].s = dot(qbar, group_sum + gid * d, d) * inv_sqrt_d;
+    }
+  qsort(l2, n2, sizeof(ora_item), by_score_desc_id_asc);
+  long k2 = c->topk_g < n2 ? c->topk_g : n2;
+  margins[1] = (k2 < n2) ? l2[k2 - 1].s - l2[k2].s : INFINITY;
+  if (k2 == 0) margins[1] = INFINITY;
+
+  /* union with the windows, then sort ascending */
+  long cap = (long)nwin * G + (last / g - ct * G + 1) + k2;
+  long* ids = (long*)malloc(sizeof(long) * cap);
+  long n = 0;
+  for (int w = 0; w < nwin; ++w)
+    for (int j = 0; j < G; ++j) ids[n++] = win[w] * G + j;
+  for (long gid = ct * G; gid <= last / g; ++gid) ids[n++] = gid;
+  for (long i = 0; i < k2; ++i) ids[n++] = l2[i].id;
+  qsort(ids, n, sizeof(long), by_id);
+
+  int ret = (n <= max_sel) ? (int)n : -1;
+  if (ret >= 0)
+    for (long i = 0; i < n; ++i) sel_groups[i] = (int)ids[i];
+
+  free(ids);
+  free(l2);
+  free(l1);
+  free(win);
+  free(qbar);
+  return ret;
+}
+
+/* ------------------------------------------------- exact attention
+ * For each query head of one KV head and each query token tau
+ * (pos0..pos0+lq-1): softmax over the selected tokens p <= tau of
+ * RoPE(q, tau) . kpool[p] / sqrt(d), applied to vpool.
+ *   q [hg][lq][d] raw; kpool/vpool [T][d] for this KV head;
+ *   out [hg][lq][d]; lse [hg][lq] (optional) = log sum exp of the logits. */
+void ora_attend(const ora_cfg* c, const double* q, int lq, long pos0, const double* kpool,
+                const double* vpool, const int* sel_groups, int n_sel, double* out, double* lse) {
+  int d = c->d, g = c->C / c->G, hg = c->hq / c->hkv;
+  double inv_sqrt_d = 1.0 / sqrt((double)d);
+  long ntok = (long)n_sel * g;
+  double* qr = (double*)malloc(sizeof(double) * d);
+  double* lg = (double*)malloc(sizeof(double) * (ntok > 0 ? ntok : 1));
+  for (int h = 0; h < hg; ++h)
+    for (int t = 0; t < lq; ++t) {
+      long tau = pos0 + t;
+      ora_rope(c, q + ((long)h * lq + t) * d, (double)tau, qr);
+      double m = -INFINITY;
+      for (long i = 0; i < ntok; ++i) {
+        long p = (long)sel_groups[i / g] * g + i % g;
+        lg[i] = (p <= tau) ? dot(qr, kpool + p * d, d) * inv_sqrt_d : -INFINITY;
+        if (lg[i] > m) m = lg[i];
+      }
+      double den = 0.0;
+      double* o = out + ((long)h * lq + t) * d;
+      for (int e = 0; e < d; ++e) o[e] = 0.0;
+      for (long i = 0; i < ntok; ++i) {
+        if (lg[i] == -INFINITY) continue;
+        long p = (long)sel_groups[i / g] * g + i % g;
+        double w = exp(lg[i] - m);
+        den += w;
+        for (int e = 0; e < d; ++e) o[e] += w * vpool[p * d + e];
+      }
+      for (int e = 0; e < d; ++e) o[e] /= den;
+      if (lse) lse[(long)h * lq + t] = m + log(den);
+    }
+  free(lg);
+  free(qr);
+}
+
+/* Exact merge of two attention results over disjoint token sets, each given
+ * as (normalised output, log-sum-exp).  n rows of d values. */
+void ora_merge(int d, long n, const double* oa, const double* la, const double* ob,
+               const double* lb, double* out, double* lse) {
+  for (long r = 0; r < n; ++r) {
+    double m = la[r] > lb[r] ? la[r] : lb[r];
+    double wa = exp(la[r] - m), wb = exp(lb[r] - m);
+    for (int e = 0; e < d; ++e) out[r * d + e] = (wa * oa[r * d + e] + wb * ob[r * d + e]) / (wa + wb);
+    if (lse) lse[r] = m + log(wa + wb);
+  }
+}
+
+/* Gather: copy the selected groups' token rows of one (sequence, KV head)
+ * pool [T][d] into a compact working set [n_sel*g][d].  Values are copied,
+ * never computed. */
+void ora_gather(const ora_cfg* c, const double* pool, const int* sel_groups, int n_sel, double* ws) {
+  int d = c->d, g = c->C / c->G;
+  for (int s = 0; s < n_sel; ++s)
+    memcpy(ws + (long)s * g * d, pool + (long)sel_groups[s] * g * d, sizeof(double) * g * d);
+}
+
+/* ------------------------------------------------ batched driver (timing)
+ * One decode/prefill step over nunits independent (sequence, KV head)
+ * units: selection then attention, one unit per OpenMP thread.  Per-unit
+ * arrays are laid out back to back:
+ *   q [nunits][hg][lq][d], pos0 [nunits], chunk_sum [nunits][nch][d],
+ *   group_sum [nunits][nch*G][d], kpool/vpool [nunits][T][d],
+ *   sel [nunits][max_sel], nsel [nunits], out [nunits][hg][lq][d]. */
+int ora_step(const ora_cfg* c, int nunits, const double* q, int lq, const long* pos0,
+             const double* chunk_sum, const double* group_sum, long nch, const double* kpool,
+             const double* vpool, long T, int* sel, int* nsel, int max_sel, double* out) {
+  int d = c->d, hg = c->hq / c->hkv, bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : bad)
+  for (int u = 0; u < nunits; ++u) {
+    double margins[2];
+    const double* qu = q + (long)u * hg * lq * d;
+    int n = ora_select(c, qu, lq, pos0[u], chunk_sum + (long)u * nch * d,
+                       group_sum + (long)u * nch * c->G * d, sel + (long)u * max_sel, max_sel,
+                       margins, NULL);
+    nsel[u] = n;
+    if (n < 0) {
+      bad += 1;
+      continue;
+    }
+    ora_attend(c, qu, lq, pos0[u], kpool + (long)u * T * d, vpool + (long)u * T * d,
+               sel + (long)u * max_sel, n, out + (long)u * hg * lq * d, NULL);
+  }
+  return bad;
+}
+
+int ora_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
