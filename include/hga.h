@@ -1,0 +1,199 @@
+/*
+ * hga.h -- C ABI of the MI355X (gfx950) Hierarchical Global Attention hot path.
+ *
+ * HGA replaces dense causal attention of a pretrained GQA model without new
+ * weights: the projected Q/K/V go in, the attention output comes out (HGA
+ * technical summary, gist.science, sections "Methodologie" and
+ * "Belangrijkste Bijdragen", item 1).  Inside, each query routes in two
+ * levels over RoPE-aware key summaries, and then attends exactly over the
+ * token K/V of the selected set ("Kernmechanisme", items 1-4).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, C-contiguous, in the layouts written next
+ *     to each argument.  Pointers are device pointers unless stated.
+ *   - The caller owns all memory.  No entry point allocates or frees memory;
+ *     scratch space comes from the caller's workspace `ws` (see
+ *     hga_workspace_bytes).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously.  No entry point synchronises.
+ *   - Arguments are checked on the host before anything is launched.  On any
+ *     error the call returns a status other than HGA_OK and launches nothing.
+ *     A HIP launch failure returns HGA_ERR_HIP.
+ *   - Query positions live in device memory (q_pos0), so that a captured
+ *     graph can be replayed for successive positions.  The kernels check
+ *     them; a unit whose position is invalid gets n_sel = -1 from hga_route
+ *     and NaN outputs from hga_attend.
+ *   - Supported shapes: head_dim 64 or 128; chunk_size 64 with 4 groups of
+ *     16 tokens; n_q_heads / n_kv_heads in {1, 2, 4, 8}.  Other shapes
+ *     return HGA_ERR_UNSUPPORTED (there is no slow fallback path).
+ *   - A workspace serves one stream at a time.  Two calls that may run
+ *     concurrently need two workspaces.
+ *   - No global mutable state; the library is safe to call from several host
+ *     threads on different streams.
+ */
+#ifndef HGA_H_
+#define HGA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum */
+  HGA_ERR_UNSUPPORTED = 2,      /* valid config outside the supported shapes */
+  HGA_ERR_WORKSPACE_TOO_SMALL = 3,
+  HGA_ERR_OUT_OF_RANGE = 4,     /* positions beyond a capacity, max_sel too small */
+  HGA_ERR_HIP = 5               /* a HIP runtime call or launch failed */
+} hga_status;
+
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+
+/* Where hga_attend reads K/V for a selected group. */
+typedef enum {
+  HGA_SRC_POOL = 0,        /* group id gid occupies rows gid*16 .. of a [cap][d] pool */
+  HGA_SRC_WORKING_SET = 1  /* list slot s occupies rows s*16 .. of a [max_sel*16][d] set */
+} hga_src_layout;
+
+/* Which part of the selected list a call covers (the pinned-host tier
+ * attends the resident window groups and the transferred routed groups in two
+ * calls, then merges them with hga_merge_partials). */
+typedef enum {
+  HGA_PART_ALL = 0,
+  HGA_PART_WINDOWS = 1,    /* sink, local and current-chunk groups */
+  HGA_PART_ROUTED = 2      /* groups chosen by the two-level routing */
+} hga_part;
+
+typedef struct {
+  int32_t head_dim;        /* d */
+  int32_t n_q_heads;       /* Hq */
+  int32_t n_kv_heads;      /* Hkv; query head h reads KV head h / (Hq/Hkv) */
+  int32_t chunk_size;      /* C: tokens per chunk */
+  int32_t groups_per_chunk;/* G: contiguous groups of C/G tokens */
+  int32_t n_sink_chunks;   /* leading chunks that are always visible */
+  int32_t n_local_chunks;  /* chunks just before the current one, always visible */
+  int32_t topk_chunks;     /* level-1 budget k_c */
+  int32_t topk_groups;     /* level-2 budget k_g (global over the k_c*G groups) */
+  double rope_theta;       /* RoPE base: omega_j = theta^(-2j/d), pairs (j, j+d/2) */
+  double hf_wavelength;    /* pair j is high-frequency iff 2*pi/omega_j < this */
+  int32_t qkv_dtype;       /* hga_dtype of q, k, v and of the K/V pool */
+} hga_config;
+
+/* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
+ * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
+ * theta <= 1), HGA_ERR_UNSUPPORTED for valid shapes this build does not
+ * implement. */
+hga_status hga_validate(const hga_config* cfg);
+
+/* Worst-case length of a selected-group list for queries of up to max_lq
+ * tokens: (n_sink + n_local + 1) * G + topk_groups. */
+hga_status hga_max_selected(const hga_config* cfg, int32_t max_lq, int32_t* max_sel);
+
+/* Bytes of device workspace needed by hga_route and hga_attend for batch B,
+ * contexts up to max_ctx tokens and up to max_lq query tokens per call.  The
+ * workspace must be zero-filled once before its first use (hga_workspace_reset
+ * does that, as does allocating it zeroed); every call leaves it ready for the
+ * next one. */
+hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx, int32_t max_lq,
+                               size_t* bytes);
+
+/* Zero-fills a workspace with a kernel (no hipMemset node, so it may be
+ * captured in a graph). */
+hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream);
+
+/* Pool append and RoPE-aware summaries ("Kernmechanisme" item 3).
+ *   k_raw  [B][Hkv][n_tok][d] raw (pre-RoPE) projected keys of positions
+ *          pos0 .. pos0+n_tok-1, qkv_dtype
+ *   v_new  [B][Hkv][n_tok][d] values of those positions (may be NULL when
+ *          k_pool is NULL)
+ *   k_pool, v_pool  [B][Hkv][pool_cap][d] qkv_dtype.  If non-NULL, row p of
+ *          k_pool receives RoPE(k_raw, p) rounded once to qkv_dtype
+ *          (round-to-nearest-even), and row p of v_pool receives v unchanged.
+ *          NULL skips the append.
+ *   chunk_sum [B][Hkv][max_chunks][d] fp32, group_sum [B][Hkv][max_chunks*G][d]
+ *          fp32.  For every chunk that lies entirely inside the range, its
+ *          chunk summary and its G group summaries are written: for pair j,
+ *          high-frequency pairs take the mean of the per-token rotated pair,
+ *          low-frequency pairs take the mean raw pair rotated to the span's
+ *          midpoint a + (n-1)/2.  NULL (both) skips the summaries.
+ * A decode step that completes a chunk passes that chunk's 64 raw keys (the
+ * rows already in the pool are rewritten with identical values).
+ * Errors: HGA_ERR_OUT_OF_RANGE if pos0 + n_tok > pool_cap or a completed
+ * chunk index >= max_chunks. */
+hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_raw,
+                               const void* v_new, int32_t pos0, int32_t n_tok, void* k_pool,
+                               void* v_pool, int32_t pool_cap, float* chunk_sum,
+                               float* group_sum, int32_t max_chunks, void* stream);
+
+/* Two-level routing ("Kernmechanisme" item 2) for each (sequence b, KV head).
+ *   q_raw   [B][Hq][lq][d] raw queries of positions q_pos0[b] .. +lq-1, which
+ *           must lie in one chunk c_t (device q_pos0 [B] int32)
+ *   The routing query is the mean over the KV head's query heads and query
+ *   tokens of RoPE(q, position).  Level 1 scores the candidate chunks
+ *   n_sink <= c < c_t - n_local as qbar . chunk_sum[c] / sqrt(d) and keeps
+ *   the top_k_c by (score desc, id asc); level 2 scores the G groups of each
+ *   kept chunk the same way and keeps the global top k_g.  Summaries of all
+ *   candidate chunks must have been built.
+ *   sel_groups [B][Hkv][max_sel] int32 receives, in ascending order, the
+ *           sink groups, the routed groups, the local groups and the current
+ *           chunk's groups up to the last query token; n_sel [B][Hkv] their
+ *           count (-1 for an invalid position).
+ *   chunk_scores_opt [B][Hkv][max_chunks] fp64 (nullable): level-1 score of
+ *           every candidate chunk, at its chunk index.
+ * Errors: HGA_ERR_OUT_OF_RANGE if max_sel < hga_max_selected(). */
+hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                     const int32_t* q_pos0, const float* chunk_sum, const float* group_sum,
+                     int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel, int32_t max_sel,
+                     double* chunk_scores_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* Gather of the selected token K/V into a compact working set.
+ *   k_pool, v_pool [B][Hkv][pool_cap][d]: device memory, or pinned host memory
+ *           (pool_is_host = 1, read directly over PCIe).
+ *   k_ws, v_ws [B][Hkv][max_sel*16][d]: list slot s of unit (b, h) receives
+ *           the 16 rows of group sel_groups[b][h][s].  Bit-exact copy.
+ *   part    HGA_PART_ALL copies every slot; HGA_PART_ROUTED only the routed
+ *           slots; HGA_PART_WINDOWS only the window slots (q_pos0 tells them
+ *           apart; it may be NULL for HGA_PART_ALL).
+ * Errors: HGA_ERR_INVALID_ARGUMENT if pool_is_host is set and the pool is
+ * not pinned host memory. */
+hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, const void* v_pool,
+                      int32_t pool_cap, int32_t pool_is_host, const int32_t* sel_groups,
+                      const int32_t* n_sel, int32_t max_sel, const int32_t* q_pos0, int32_t part,
+                      void* k_ws, void* v_ws, void* stream);
+
+/* Exact attention over the selected set ("Kernmechanisme" item 4): for query
+ * head h (KV head h / (Hq/Hkv)) and query token tau,
+ *   out = sum_p softmax_p(RoPE(q, tau) . K[p] / sqrt(d)) V[p]
+ * over the tokens p <= tau of the selected groups (restricted to `part`).
+ *   k_src, v_src  the rotated pool (HGA_SRC_POOL, src_cap rows per unit) or
+ *           a working set from hga_gather (HGA_SRC_WORKING_SET, max_sel*16 rows)
+ *   out     [B][Hq][lq][d] fp32
+ *   lse_opt [B][Hq][lq] fp32 natural-log sum of exp of the logits (nullable);
+ *           with hga_merge_partials it joins results over disjoint parts.
+ * Decode (lq < 16) runs a VALU wavefront-reduction kernel; lq >= 16 runs the
+ * MFMA chunked-prefill kernel. */
+hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                      const int32_t* q_pos0, const void* k_src, const void* v_src,
+                      int32_t src_layout, int32_t src_cap, const int32_t* sel_groups,
+                      const int32_t* n_sel, int32_t max_sel, int32_t part, float* out,
+                      float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* Exact merge of two attention results over disjoint token sets:
+ * out = (e^{lse_a} out_a + e^{lse_b} out_b) / (e^{lse_a} + e^{lse_b}),
+ * lse_out = log(e^{lse_a} + e^{lse_b}) (lse_out nullable).  Rows are
+ * [B][Hq][lq], each of d fp32 values.  out may alias out_a or out_b. */
+hga_status hga_merge_partials(const hga_config* cfg, int32_t B, int32_t lq, const float* out_a,
+                              const float* lse_a, const float* out_b, const float* lse_b,
+                              float* out, float* lse_out, void* stream);
+
+const char* hga_status_string(hga_status s);
+int32_t hga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H_ */

@@ -1,0 +1,247 @@
+// C ABI of the HGA hot path: host-side validation, workspace layout and
+// launches.  Every check runs before anything is enqueued; no entry point
+// allocates, frees or synchronises.
+#include <math.h>
+
+#include "hga_internal.h"
+
+using namespace hga;
+
+namespace {
+
+constexpr int kMaxLqDecode = 15;
+constexpr int kMaxUnitsRoute = 1 << 17;
+constexpr size_t kMaxRouteLds = 60 * 1024;
+
+hga_status check_cfg(const hga_config* c) {
+  if (!c) return HGA_ERR_INVALID_ARGUMENT;
+  if (c->head_dim <= 0 || c->head_dim % 2 != 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->n_q_heads % c->n_kv_heads != 0 || c->chunk_size <= 0 || c->groups_per_chunk <= 0 ||
+      c->chunk_size % c->groups_per_chunk != 0 || c->n_sink_chunks < 0 || c->n_local_chunks < 0 ||
+      c->topk_chunks < 0 || c->topk_groups < 0 || !(c->rope_theta > 1.0) ||
+      !(c->hf_wavelength >= 0.0) || (c->qkv_dtype != HGA_F32 && c->qkv_dtype != HGA_BF16))
+    return HGA_ERR_INVALID_ARGUMENT;
+  const int hg = c->n_q_heads / c->n_kv_heads;
+  if ((c->head_dim != 64 && c->head_dim != 128) || c->chunk_size != kChunk ||
+      c->groups_per_chunk != kGroups || (hg != 1 && hg != 2 && hg != 4 && hg != 8))
+    return HGA_ERR_UNSUPPORTED;
+  return HGA_OK;
+}
+
+KCfg make_kcfg(const hga_config* c) {
+  KCfg k{};
+  k.d = c->head_dim;
+  k.hq = c->n_q_heads;
+  k.hkv = c->n_kv_heads;
+  k.hg = c->n_q_heads / c->n_kv_heads;
+  k.n_sink = c->n_sink_chunks;
+  k.n_local = c->n_local_chunks;
+  k.topk_c = c->topk_chunks;
+  k.topk_g = c->topk_groups;
+  k.dtype = c->qkv_dtype;
+  k.inv_sqrt_d = 1.0 / sqrt((double)c->head_dim);
+  k.qscale_log2 = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
+  k.hf_mask = 0;
+  for (int j = 0; j < c->head_dim / 2; ++j) {
+    k.omega[j] = pow(c->rope_theta, -2.0 * (double)j / (double)c->head_dim);
+    if (2.0 * M_PI / k.omega[j] < c->hf_wavelength) k.hf_mask |= 1ull << j;
+  }
+  return k;
+}
+
+int max_selected(const hga_config* c) {
+  return (c->n_sink_chunks + c->n_local_chunks + 1) * c->groups_per_chunk + c->topk_groups;
+}
+
+hga_status hip_status(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_HIP; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+hga_status hga_validate(const hga_config* cfg) { return check_cfg(cfg); }
+
+hga_status hga_max_selected(const hga_config* cfg, int32_t max_lq, int32_t* out) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (!out || max_lq <= 0 || max_lq > kChunk) return HGA_ERR_INVALID_ARGUMENT;
+  *out = max_selected(cfg);
+  return HGA_OK;
+}
+
+hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx, int32_t max_lq,
+                               size_t* bytes) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (!bytes || B <= 0 || max_ctx <= 0 || max_lq <= 0 || max_lq > kChunk)
+    return HGA_ERR_INVALID_ARGUMENT;
+  const KCfg k = make_kcfg(cfg);
+  const int max_chunks = (max_ctx + kChunk - 1) / kChunk;
+  const size_t r = route_ws_bytes(k, B, max_chunks);
+  const size_t a = attend_ws_bytes(k, B, max_lq, max_selected(cfg));
+  *bytes = kCounterBytes + round_up(r > a ? r : a, 256);
+  return HGA_OK;
+}
+
+hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return HGA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_raw,
+                               const void* v_new, int32_t pos0, int32_t n_tok, void* k_pool,
+                               void* v_pool, int32_t pool_cap, float* chunk_sum,
+                               float* group_sum, int32_t max_chunks, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !k_raw || pos0 < 0 || n_tok <= 0) return HGA_ERR_INVALID_ARGUMENT;
+  const bool append = k_pool || v_pool;
+  const bool summ = chunk_sum || group_sum;
+  if (append && (!k_pool || !v_pool || !v_new || pool_cap <= 0)) return HGA_ERR_INVALID_ARGUMENT;
+  if (summ && (!chunk_sum || !group_sum || max_chunks <= 0)) return HGA_ERR_INVALID_ARGUMENT;
+  const int64_t end = (int64_t)pos0 + n_tok;
+  if (end > INT32_MAX) return HGA_ERR_OUT_OF_RANGE;
+  if (append && end > pool_cap) return HGA_ERR_OUT_OF_RANGE;
+  if (summ) {
+    const int64_t last_complete = end / kChunk - 1;  // highest chunk that can complete here
+    if (last_complete >= max_chunks) return HGA_ERR_OUT_OF_RANGE;
+  }
+  if (!append && !summ) return HGA_OK;
+  const KCfg k = make_kcfg(cfg);
+  return hip_status(launch_build(k, B, k_raw, v_new, pos0, n_tok, append ? k_pool : nullptr,
+                                 append ? v_pool : nullptr, pool_cap, summ ? chunk_sum : nullptr,
+                                 summ ? group_sum : nullptr, max_chunks, (hipStream_t)stream));
+}
+
+hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                     const int32_t* q_pos0, const float* chunk_sum, const float* group_sum,
+                     int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel, int32_t max_sel,
+                     double* chunk_scores_opt, void* ws, size_t ws_bytes, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !chunk_sum || !group_sum ||
+      max_chunks <= 0 || !sel_groups || !n_sel || !ws)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
+  if ((int64_t)B * cfg->n_kv_heads > kMaxUnitsRoute) return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+  const int n2 = k.topk_c * kGroups;
+  const size_t lds = (size_t)(max_cand > n2 ? max_cand : n2) * (sizeof(double) + 2 * sizeof(int) + 1);
+  if (lds > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
+  if (ws_bytes < kCounterBytes + route_ws_bytes(k, B, max_chunks))
+    return HGA_ERR_WORKSPACE_TOO_SMALL;
+  RouteLaunch r;
+  r.q = q_raw;
+  r.q_pos0 = q_pos0;
+  r.chunk_sum = chunk_sum;
+  r.group_sum = group_sum;
+  r.sel = sel_groups;
+  r.n_sel = n_sel;
+  r.chunk_scores = chunk_scores_opt;
+  r.counters = static_cast<unsigned*>(ws) + kRouteCounterBase;
+  r.scores = reinterpret_cast<double*>(static_cast<char*>(ws) + kCounterBytes);
+  r.B = B;
+  r.lq = lq;
+  r.max_chunks = max_chunks;
+  r.max_sel = max_sel;
+  return hip_status(launch_route(k, r, (hipStream_t)stream));
+}
+
+hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, const void* v_pool,
+                      int32_t pool_cap, int32_t pool_is_host, const int32_t* sel_groups,
+                      const int32_t* n_sel, int32_t max_sel, const int32_t* q_pos0, int32_t part,
+                      void* k_ws, void* v_ws, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !k_pool || !v_pool || pool_cap <= 0 || !sel_groups || !n_sel || max_sel <= 0 ||
+      !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
+      (part != HGA_PART_ALL && !q_pos0))
+    return HGA_ERR_INVALID_ARGUMENT;
+  const void* kp = k_pool;
+  const void* vp = v_pool;
+  if (pool_is_host) {
+    const void* src[2] = {k_pool, v_pool};
+    const void* dev[2] = {nullptr, nullptr};
+    for (int i = 0; i < 2; ++i) {
+      hipPointerAttribute_t at;
+      if (hipPointerGetAttributes(&at, src[i]) != hipSuccess) {
+        (void)hipGetLastError();
+        return HGA_ERR_INVALID_ARGUMENT;
+      }
+      if (at.type != hipMemoryTypeHost || !at.devicePointer) return HGA_ERR_INVALID_ARGUMENT;
+      dev[i] = at.devicePointer;
+    }
+    kp = dev[0];
+    vp = dev[1];
+  }
+  const KCfg k = make_kcfg(cfg);
+  return hip_status(launch_gather(k, B, kp, vp, pool_cap, sel_groups, n_sel, max_sel, q_pos0, part,
+                                  k_ws, v_ws, (hipStream_t)stream));
+}
+
+hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                      const int32_t* q_pos0, const void* k_src, const void* v_src,
+                      int32_t src_layout, int32_t src_cap, const int32_t* sel_groups,
+                      const int32_t* n_sel, int32_t max_sel, int32_t part, float* out,
+                      float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_src || !v_src ||
+      (src_layout != HGA_SRC_POOL && src_layout != HGA_SRC_WORKING_SET) || !sel_groups ||
+      !n_sel || max_sel <= 0 || part < HGA_PART_ALL || part > HGA_PART_ROUTED || !out || !ws)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (src_layout == HGA_SRC_POOL && src_cap <= 0) return HGA_ERR_INVALID_ARGUMENT;
+  if (lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnitsRoute) return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  if (ws_bytes < kCounterBytes + attend_ws_bytes(k, B, lq, max_sel))
+    return HGA_ERR_WORKSPACE_TOO_SMALL;
+  AttendLaunch a;
+  a.q = q_raw;
+  a.q_pos0 = q_pos0;
+  a.k = k_src;
+  a.v = v_src;
+  a.sel = sel_groups;
+  a.n_sel = n_sel;
+  a.out = out;
+  a.lse = lse_opt;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  a.counters = static_cast<unsigned*>(ws) + kAttendCounterBase;
+  a.B = B;
+  a.lq = lq;
+  a.src_layout = src_layout;
+  a.src_cap = src_layout == HGA_SRC_POOL ? src_cap : max_sel * kGroupTokens;
+  a.max_sel = max_sel;
+  a.part_sel = part;
+  return hip_status(launch_attend(k, a, (hipStream_t)stream));
+}
+
+hga_status hga_merge_partials(const hga_config* cfg, int32_t B, int32_t lq, const float* out_a,
+                              const float* lse_a, const float* out_b, const float* lse_b,
+                              float* out, float* lse_out, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || lq <= 0 || !out_a || !lse_a || !out_b || !lse_b || !out)
+    return HGA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_merge(B, cfg->n_q_heads, lq, cfg->head_dim, out_a, lse_a, out_b, lse_b,
+                                 out, lse_out, (hipStream_t)stream));
+}
+
+const char* hga_status_string(hga_status s) {
+  switch (s) {
+    case HGA_OK: return "ok";
+    case HGA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HGA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HGA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HGA_ERR_OUT_OF_RANGE: return "position or size out of range";
+    case HGA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t hga_version(void) { return 1; }
+
+}  // extern "C"

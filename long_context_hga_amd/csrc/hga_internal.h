@@ -1,0 +1,75 @@
+// Host-side declarations shared by the HGA translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "hga_device.h"
+
+namespace hga {
+
+hipError_t launch_build(const KCfg& cfg, int B, const void* k_raw, const void* v_new, int pos0,
+                        int n_tok, void* k_pool, void* v_pool, int pool_cap, float* chunk_sum,
+                        float* group_sum, int max_chunks, hipStream_t st);
+
+struct RouteLaunch {
+  const void* q;
+  const int* q_pos0;
+  const float* chunk_sum;
+  const float* group_sum;
+  int* sel;
+  int* n_sel;
+  double* chunk_scores;
+  double* scores;       // workspace [B*Hkv][max_cand]
+  unsigned* counters;   // workspace [B*Hkv]
+  int B, lq, max_chunks, max_sel;
+};
+hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st);
+size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks);
+
+struct AttendLaunch {
+  const void* q;
+  const int* q_pos0;
+  const void* k;
+  const void* v;
+  const int* sel;
+  const int* n_sel;
+  float* out;
+  float* lse;
+  float* part;          // workspace partials
+  unsigned* counters;   // workspace [B*Hkv*lq]
+  int B, lq, src_layout, src_cap, max_sel, part_sel;
+};
+hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
+size_t attend_ws_bytes(const KCfg& cfg, int B, int lq, int max_sel);
+
+hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
+                         int pool_cap, const int* sel, const int* n_sel, int max_sel,
+                         const int* q_pos0, int part, void* k_ws, void* v_ws, hipStream_t st);
+
+hipError_t launch_merge(int B, int hq, int lq, int d, const float* oa, const float* la,
+                        const float* ob, const float* lb, float* out, float* lse, hipStream_t st);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Position of list slots by part: the selected list of a unit is ordered
+// sink groups | routed groups | local groups | current-chunk groups.
+struct ListParts {
+  int n_head;    // sink groups
+  int n_routed;  // routed groups
+  int n_tail;    // local + current groups
+};
+__device__ __host__ inline ListParts list_parts(int n_sel, int pos_last, int lq_first_pos,
+                                                int n_sink, int n_local) {
+  const int ct = lq_first_pos / kChunk;
+  const Windows w = windows_of(ct, n_sink, n_local);
+  ListParts lp;
+  lp.n_head = w.sink_end * kGroups;
+  const int cur = pos_last / kGroupTokens - ct * kGroups + 1;
+  lp.n_tail = (ct - w.local_begin) * kGroups + cur;
+  lp.n_routed = n_sel - lp.n_head - lp.n_tail;
+  return lp;
+}
+
+}  // namespace hga

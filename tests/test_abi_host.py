@@ -1,0 +1,121 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol
+include/hga.h declares, and validation rejects bad arguments before any
+launch (so none of these calls needs a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_hga_amd as hga
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "hga.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:hga_status|const char\*|int32_t)\s+(hga_\w+)\(", src,
+                                 re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = hga.lib()
+    names = declared_symbols()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(hga.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert hga.hga_version() == 1
+    for s in range(6):
+        assert hga.hga_status_string(s)
+
+
+def cfg(**over):
+    return hga.config_from(synth.CONFIGS["decode64k"], **over)
+
+
+def test_validate():
+    assert hga.hga_validate(cfg()) == hga.HGA_OK
+    assert hga.hga_validate(hga.config_from(synth.CONFIGS["tiny"])) == hga.HGA_OK
+    bad = [dict(head_dim=127), dict(n_q_heads=30), dict(groups_per_chunk=3), dict(rope_theta=1.0),
+           dict(topk_chunks=-1), dict(hf_wavelength=float("nan")), dict(qkv_dtype=7)]
+    for b in bad:
+        assert hga.hga_validate(cfg(**b)) == hga.HGA_ERR_INVALID_ARGUMENT, b
+    unsup = [dict(head_dim=96), dict(chunk_size=128), dict(groups_per_chunk=8),
+             dict(n_q_heads=64, n_kv_heads=4)]
+    for u in unsup:
+        assert hga.hga_validate(cfg(**u)) == hga.HGA_ERR_UNSUPPORTED, u
+    assert hga.lib().hga_validate(None) == hga.HGA_ERR_INVALID_ARGUMENT
+
+
+def test_sizes():
+    c = cfg()
+    assert hga.hga_max_selected(c, 1) == (1 + 4 + 1) * 4 + 104
+    n = hga.hga_workspace_bytes(c, 8, 65536, 1)
+    assert n >= (1 << 20) + 8 * 4 * 1023 * 8
+    with pytest.raises(hga.HgaError):
+        hga.hga_workspace_bytes(c, 0, 65536, 1)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def test_build_summaries_rejects():
+    c = ctypes.byref(cfg())
+    L = hga.lib()
+    f = L.hga_build_summaries
+    ok = (c, 1, FAKE, FAKE, 0, 64, FAKE, FAKE, 64, FAKE, FAKE, 1, None)
+    assert f(*ok[:2], None, *ok[3:]) == hga.HGA_ERR_INVALID_ARGUMENT
+    assert f(c, 1, FAKE, FAKE, 0, 65, FAKE, FAKE, 64, FAKE, FAKE, 1, None) == hga.HGA_ERR_OUT_OF_RANGE
+    assert f(c, 1, FAKE, FAKE, 0, 128, FAKE, FAKE, 128, FAKE, FAKE, 1, None) == hga.HGA_ERR_OUT_OF_RANGE
+    assert f(c, 1, FAKE, FAKE, 0, 64, FAKE, None, 64, FAKE, FAKE, 1, None) == hga.HGA_ERR_INVALID_ARGUMENT
+    assert f(c, 1, FAKE, FAKE, -1, 64, FAKE, FAKE, 64, FAKE, FAKE, 1, None) == hga.HGA_ERR_INVALID_ARGUMENT
+    assert f(c, 1, FAKE, FAKE, 0, 64, None, None, 0, None, None, 0, None) == hga.HGA_OK  # no-op
+
+
+def test_route_rejects():
+    c = ctypes.byref(cfg())
+    f = hga.lib().hga_route
+    args = [c, 8, FAKE, 1, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, 128, None, FAKE, 1 << 30, None]
+    a = list(args); a[10] = 127
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    a = list(args); a[13] = 1000
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[2] = None
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[3] = 65
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[7] = 100000
+    assert f(*a) == hga.HGA_ERR_UNSUPPORTED  # candidate table beyond the LDS budget
+
+
+def test_attend_rejects():
+    c = ctypes.byref(cfg())
+    f = hga.lib().hga_attend
+    args = [c, 8, FAKE, 1, FAKE, FAKE, FAKE, 0, 65536, FAKE, FAKE, 128, 0, FAKE, None, FAKE,
+            1 << 30, None]
+    a = list(args); a[7] = 5
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[12] = 3
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[16] = 4096
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[8] = 0
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[13] = None
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+
+
+def test_gather_and_merge_reject():
+    c = ctypes.byref(cfg())
+    g = hga.lib().hga_gather
+    assert g(c, 8, FAKE, FAKE, 65536, 0, FAKE, FAKE, 128, None, 2, FAKE, FAKE, None) == \
+        hga.HGA_ERR_INVALID_ARGUMENT  # part needs positions
+    assert g(c, 8, None, FAKE, 65536, 0, FAKE, FAKE, 128, None, 0, FAKE, FAKE, None) == \
+        hga.HGA_ERR_INVALID_ARGUMENT
+    m = hga.lib().hga_merge_partials
+    assert m(c, 8, 1, FAKE, None, FAKE, FAKE, FAKE, None, None) == hga.HGA_ERR_INVALID_ARGUMENT

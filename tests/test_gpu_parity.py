@@ -1,0 +1,359 @@
+"""GPU parity of the HIP hot path against the fp64 oracle (through the C ABI).
+
+Comparison rules: see tests/oracle_ref.py.  Workloads come from synth with
+their seeds; reduced sizes keep the oracle within seconds while spanning
+several tiles, splits and a ragged tail; the full 64K x 8 decode workload is
+checked on sampled units plus properties of every unit.
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+from oracle_ref import (ATOL_OUT, UnitCache, check_pool_keys, check_selection, check_summaries,
+                        max_abs, q_unit)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import long_context_hga_amd as hga  # noqa: E402
+import gpu_harness as gh  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def ora_cfg(inp, **over):
+    p = dict(inp.params)
+    p.update(over)
+    return oracle.cfg_from(p)
+
+
+def f64_pool(t, bf16):
+    a = t.cpu().numpy()
+    if bf16:
+        return synth.bf16_to_f32(a.view(np.uint16)).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ------------------------------------------------------------ summaries
+@pytest.mark.parametrize("name,B,T", [("tiny", None, None), ("decode4k", None, None),
+                                      ("decode64k", 2, 8192)])
+def test_build_summaries_parity(name, B, T):
+    say(f"[summaries] {name} B={B} T={T}")
+    inp = synth.generate(name, batch=B, context=T)
+    st = gh.build_state(inp)
+    torch.cuda.synchronize()
+    cfg = ora_cfg(inp)
+    bf16 = inp.is_bf16
+    kp = f64_pool(st.k_pool, bf16)
+    vp = st.v_pool.cpu().numpy()
+    cs = st.chunk_sum.cpu().numpy()
+    gs = st.group_sum.cpu().numpy()
+    uc = UnitCache(inp, cfg)
+    for b in range(inp.k.shape[0]):
+        for h in range(inp.k.shape[1]):
+            ocs, ogs, okp, _ = uc.get(b, h)
+            check_pool_keys(kp[b, h], okp, bf16)
+            np.testing.assert_array_equal(vp[b, h].view(inp.v.dtype), inp.v[b, h])
+            check_summaries(cs[b, h], ocs)
+            check_summaries(gs[b, h], ogs)
+
+
+def test_build_summaries_incremental_append():
+    """Token-by-token append plus per-chunk refresh equals the bulk build."""
+    inp = synth.generate("decode4k", context=1024)
+    bulk = gh.build_state(inp)
+    st = gh.build_state(inp)
+    st.k_pool.zero_()
+    st.v_pool.zero_()
+    st.chunk_sum.zero_()
+    st.group_sum.zero_()
+    T = 1024
+    for p0 in range(0, T, 64):
+        for p in range(p0, p0 + 63):  # single-token appends
+            hga.hga_build_summaries(st.cfg, 1, st.k_raw[:, :, p:p + 1].contiguous(),
+                                    st.v_raw[:, :, p:p + 1].contiguous(), p, 1, st.k_pool,
+                                    st.v_pool, T, st.chunk_sum, st.group_sum, st.max_chunks)
+        # the token that completes the chunk comes with the chunk's raw keys
+        hga.hga_build_summaries(st.cfg, 1, st.k_raw[:, :, p0:p0 + 64].contiguous(),
+                                st.v_raw[:, :, p0:p0 + 64].contiguous(), p0, 64, st.k_pool,
+                                st.v_pool, T, st.chunk_sum, st.group_sum, st.max_chunks)
+    torch.cuda.synchronize()
+    assert torch.equal(st.k_pool, bulk.k_pool)
+    assert torch.equal(st.v_pool, bulk.v_pool)
+    assert torch.equal(st.chunk_sum, bulk.chunk_sum)
+    assert torch.equal(st.group_sum, bulk.group_sum)
+
+
+# ------------------------------------------------------ route + attend
+def run_decode_case(inp, st, positions, tok_of_pos=None, cfg_over=None):
+    """Route + attend at each position (lq=1) for every unit; compare."""
+    cfg = ora_cfg(inp, **(cfg_over or {}))
+    uc = UnitCache(inp, cfg)
+    B, hkv = inp.k.shape[0], inp.k.shape[1]
+    hg = cfg.hq // cfg.hkv
+    n_pinned = n_units = 0
+    worst = 0.0
+    for i, pos in enumerate(positions):
+        tok = i if tok_of_pos is None else tok_of_pos(i)
+        q = gh.query_slice(st, tok)
+        pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+        s = gh.alloc_step(st, 1)
+        gh.route(st, q, 1, pos_t, s)
+        gh.attend(st, q, 1, pos_t, s)
+        torch.cuda.synchronize()
+        sel = s.sel.cpu().numpy()
+        nsel = s.n_sel.cpu().numpy()
+        out = s.out.cpu().numpy()
+        lse = s.lse.cpu().numpy()
+        scores = s.scores.cpu().numpy()
+        for b in range(B):
+            for h in range(hkv):
+                cs, gs, kp, v = uc.get(b, h)
+                qu = q_unit(inp, cfg, b, h, tok, 1)
+                osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
+                g = sel[b, h, :nsel[b, h]]
+                n_units += 1
+                n_pinned += check_selection(cfg, g, osel, margins, oscores, pos, 1)
+                lo = cfg.n_sink
+                if oscores.size and pos // 64 - cfg.n_local > lo:
+                    np.testing.assert_allclose(scores[b, h, lo:lo + oscores.size], oscores,
+                                               rtol=0, atol=1e-7)
+                o_ref, l_ref = oracle.attend(cfg, qu, pos, kp, v, g)
+                err = max_abs(out[b, h * hg:(h + 1) * hg, 0], o_ref[:, 0])
+                worst = max(worst, err)
+                assert err <= ATOL_OUT, (pos, b, h, err)
+                assert max_abs(lse[b, h * hg:(h + 1) * hg, 0], l_ref[:, 0]) <= 1e-3
+    return n_pinned, n_units, worst
+
+
+def test_tiny_decode_last_8_positions():
+    inp = synth.generate("tiny")
+    st = gh.build_state(inp, max_lq=1)
+    positions = list(range(1016, 1024))
+    pinned, units, worst = run_decode_case(inp, st, positions)
+    say(f"[tiny] pinned {pinned}/{units} worst {worst:.2e}")
+    assert pinned == units
+
+
+def test_decode4k():
+    inp = synth.generate("decode4k")
+    st = gh.build_state(inp)
+    pinned, units, worst = run_decode_case(inp, st, [4095])
+    say(f"[decode4k] pinned {pinned}/{units} worst {worst:.2e}")
+
+
+@pytest.mark.parametrize("pos", [0, 1, 15, 16, 63, 64, 100, 319, 320, 321, 383, 384, 1000, 2047,
+                                 4094])
+def test_decode_edge_positions(pos):
+    """Small t (windows only / overlapping windows), partial groups, chunk
+    boundaries, a ragged number of selected groups."""
+    inp = synth.generate("decode4k")
+    st = gh.build_state(inp)
+    run_decode_case(inp, st, [pos], tok_of_pos=lambda i: 0)
+
+
+def test_decode64k_reduced_batch2():
+    inp = synth.generate("decode64k", batch=2, context=8192)
+    st = gh.build_state(inp)
+    pinned, units, worst = run_decode_case(inp, st, [8191, 8190, 7000, 4160],
+                                           tok_of_pos=lambda i: 0)
+    say(f"[decode64k B2 T8192] pinned {pinned}/{units} worst {worst:.2e}")
+
+
+def test_select_all_equals_dense():
+    """Budgets above the candidate counts: the output is dense causal attention."""
+    # t = 2047: candidates are chunks 1..26, so 26 chunks / 104 groups is all of them
+    over = dict(topk_chunks=26, topk_groups=104)
+    inp = synth.generate("decode4k", context=2048)
+    st = gh.build_state(inp, cfg_over=over)
+    cfg = ora_cfg(inp, **over)
+    t = 2047
+    q = gh.query_slice(st, 0)
+    pos_t = torch.full((1,), t, dtype=torch.int32, device="cuda")
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, pos_t, s)
+    gh.attend(st, q, 1, pos_t, s)
+    torch.cuda.synchronize()
+    uc = UnitCache(inp, cfg)
+    for h in range(4):
+        n = int(s.n_sel[0, h])
+        assert list(s.sel[0, h, :n].cpu().numpy()) == list(range(t // 16 + 1))
+        _, _, kp, v = uc.get(0, h)
+        o_ref, _ = oracle.attend(cfg, q_unit(inp, cfg, 0, h, 0, 1), t, kp, v, np.arange(t // 16 + 1))
+        assert max_abs(s.out[0, h * 8:(h + 1) * 8, 0].cpu().numpy(), o_ref[:, 0]) <= ATOL_OUT
+
+
+def test_invalid_position_is_loud():
+    inp = synth.generate("decode4k")
+    st = gh.build_state(inp)
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    for bad in (-1, 4096 * 4):
+        pos_t = torch.full((1,), bad, dtype=torch.int32, device="cuda")
+        gh.route(st, q, 1, pos_t, s)
+        gh.attend(st, q, 1, pos_t, s)
+        torch.cuda.synchronize()
+        assert (s.n_sel == -1).all()
+        assert torch.isnan(s.out).all()
+
+
+def test_parts_merge_and_working_set():
+    """windows + routed parts merged == all; gather is a bit-exact copy;
+    attention over the working set equals attention over the pool."""
+    inp = synth.generate("decode64k", batch=2, context=8192)
+    st = gh.build_state(inp)
+    q = gh.query_slice(st, 0)
+    pos_t = st.pos0
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, pos_t, s)
+    gh.attend(st, q, 1, pos_t, s)
+    out_all = s.out.clone()
+    lse_all = s.lse.clone()
+    oa, la = torch.empty_like(s.out), torch.empty_like(s.lse)
+    ob, lb = torch.empty_like(s.out), torch.empty_like(s.lse)
+    gh.attend(st, q, 1, pos_t, s, part=hga.HGA_PART_WINDOWS, out=oa, lse=la)
+    gh.attend(st, q, 1, pos_t, s, part=hga.HGA_PART_ROUTED, out=ob, lse=lb)
+    om, lm = torch.empty_like(oa), torch.empty_like(la)
+    hga.hga_merge_partials(st.cfg, st.B, 1, oa, la, ob, lb, om, lm)
+    torch.cuda.synchronize()
+    assert (om - out_all).abs().max().item() <= 1e-5
+    assert (lm - lse_all).abs().max().item() <= 1e-5
+
+    B, hkv, d = st.B, 4, 128
+    kw = torch.zeros((B, hkv, st.max_sel * 16, d), dtype=torch.int16, device="cuda")
+    vw = torch.zeros_like(kw)
+    hga.hga_gather(st.cfg, B, st.k_pool, st.v_pool, st.T, 0, s.sel, s.n_sel, st.max_sel, pos_t,
+                   hga.HGA_PART_ALL, kw, vw)
+    ow = torch.empty_like(s.out)
+    lw = torch.empty_like(s.lse)
+    gh.attend(st, q, 1, pos_t, s, k_src=kw, v_src=vw, layout=hga.HGA_SRC_WORKING_SET, out=ow,
+              lse=lw)
+    torch.cuda.synchronize()
+    sel = s.sel.cpu().numpy()
+    nsel = s.n_sel.cpu().numpy()
+    kp = st.k_pool.cpu().numpy()
+    kwn = kw.cpu().numpy()
+    for b in range(B):
+        for h in range(hkv):
+            g = sel[b, h, :nsel[b, h]]
+            want = kp[b, h].reshape(-1, 16, d)[g].reshape(-1, d)
+            np.testing.assert_array_equal(kwn[b, h, :len(g) * 16], want)
+    assert torch.equal(ow, out_all)
+    # routed-only gather leaves window slots untouched
+    kr = torch.zeros_like(kw)
+    vr = torch.zeros_like(vw)
+    hga.hga_gather(st.cfg, B, st.k_pool, st.v_pool, st.T, 0, s.sel, s.n_sel, st.max_sel, pos_t,
+                   hga.HGA_PART_ROUTED, kr, vr)
+    torch.cuda.synchronize()
+    krn = kr.cpu().numpy()
+    for b in range(B):
+        for h in range(hkv):
+            n_head = 4
+            n_routed = nsel[b, h] - n_head - 4 * 4 - 4
+            sl = slice(n_head * 16, (n_head + n_routed) * 16)
+            np.testing.assert_array_equal(krn[b, h, sl], kwn[b, h, sl])
+            assert not krn[b, h, :n_head * 16].any()
+
+
+def test_host_pool_gather_matches_device():
+    inp = synth.generate("decode64k", batch=1, context=4096)
+    st = gh.build_state(inp)
+    sth = gh.build_state(inp, pool_on_host=True)
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    kw = torch.zeros((1, 4, st.max_sel * 16, 128), dtype=torch.int16, device="cuda")
+    vw = torch.zeros_like(kw)
+    kh = torch.zeros_like(kw)
+    vh = torch.zeros_like(kw)
+    hga.hga_gather(st.cfg, 1, st.k_pool, st.v_pool, st.T, 0, s.sel, s.n_sel, st.max_sel, st.pos0,
+                   hga.HGA_PART_ALL, kw, vw)
+    hga.hga_gather(st.cfg, 1, sth.k_pool, sth.v_pool, st.T, 1, s.sel, s.n_sel, st.max_sel, st.pos0,
+                   hga.HGA_PART_ALL, kh, vh)
+    torch.cuda.synchronize()
+    assert torch.equal(kw, kh) and torch.equal(vw, vh)
+
+
+def test_determinism_bitwise():
+    inp = synth.generate("decode64k", batch=2, context=8192)
+    st = gh.build_state(inp)
+    q = gh.query_slice(st, 0)
+    res = []
+    for _ in range(3):
+        s = gh.alloc_step(st, 1)
+        gh.route(st, q, 1, st.pos0, s)
+        gh.attend(st, q, 1, st.pos0, s)
+        torch.cuda.synchronize()
+        res.append((s.sel.clone(), s.out.clone(), s.lse.clone()))
+    for r in res[1:]:
+        assert torch.equal(r[0], res[0][0]) and torch.equal(r[1], res[0][1])
+        assert torch.equal(r[2], res[0][2])
+
+
+def test_prefill32k_route_and_needles():
+    """Pooled 64-token query routing at 32K; all 16 planted needle chunks are
+    kept at level 1."""
+    inp = synth.generate("prefill32k")
+    st = gh.build_state(inp)
+    cfg = ora_cfg(inp)
+    s = gh.alloc_step(st, 64)
+    gh.route(st, st.q, 64, st.pos0, s)
+    torch.cuda.synchronize()
+    uc = UnitCache(inp, cfg)
+    pos = int(inp.pos0[0])
+    for h in range(4):
+        cs, gs, _, _ = uc.get(0, h, need_pool=False)
+        qu = q_unit(inp, cfg, 0, h, 0, 64)
+        osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
+        n = int(s.n_sel[0, h])
+        g = s.sel[0, h, :n].cpu().numpy()
+        check_selection(cfg, g, osel, margins, oscores, pos, 64)
+        chunks = set(int(x) // 4 for x in g)
+        assert set(int(c) for c in inp.needle_chunks[0]) <= chunks
+
+
+@pytest.mark.slow
+def test_decode64k_full_sampled():
+    """The benchmarked workload at full size: every unit's list is
+    well-formed; two sampled units match the oracle end to end."""
+    say("[decode64k full] generating")
+    inp = synth.generate("decode64k")
+    st = gh.build_state(inp)
+    cfg = ora_cfg(inp)
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    gh.attend(st, q, 1, st.pos0, s)
+    torch.cuda.synchronize()
+    say("[decode64k full] gpu done")
+    nsel = s.n_sel.cpu().numpy()
+    sel = s.sel.cpu().numpy()
+    assert (nsel == 128).all()
+    for b in range(8):
+        for h in range(4):
+            g = sel[b, h, :128]
+            assert (np.diff(g) > 0).all()
+            assert set(range(4)) <= set(g) and set(range(1019 * 4, 1024 * 4)) <= set(g)
+    assert np.isfinite(s.out.cpu().numpy()).all()
+    uc = UnitCache(inp, cfg)
+    out = s.out.cpu().numpy()
+    kp_all = st.k_pool
+    for b, h in [(0, 0), (7, 3)]:
+        cs, gs, kp, v = uc.get(b, h)
+        check_pool_keys(f64_pool(kp_all[b, h], True), kp, True)
+        check_summaries(st.chunk_sum[b, h].cpu().numpy(), cs)
+        check_summaries(st.group_sum[b, h].cpu().numpy(), gs)
+        qu = q_unit(inp, cfg, b, h, 0, 1)
+        osel, margins, oscores = oracle.select(cfg, qu, 65535, cs, gs)
+        check_selection(cfg, sel[b, h], osel, margins, oscores, 65535, 1)
+        o_ref, _ = oracle.attend(cfg, qu, 65535, kp, v, sel[b, h])
+        assert max_abs(out[b, h * 8:(h + 1) * 8, 0], o_ref[:, 0]) <= ATOL_OUT
