@@ -1,29 +1,33 @@
 """Benchmark of the HGA decode hot path on one MI355X.
 
-Workload (default): one decode step of a GQA attention layer (32 query / 4 KV
-heads, head_dim 128, bf16, RoPE theta 1e6) at 65536 tokens of context, batch
-8 independent sequences, query at position 65535.  C = 64 tokens per chunk in
+Workload: one decode step of a GQA attention layer (32 query / 4 KV heads,
+head_dim 128, bf16, RoPE theta 1e6) at 65536 tokens of context, batch 8
+independent sequences, query at position 65535.  C = 64 tokens per chunk in
 4 groups of 16; 1 sink + 4 local chunks, top-52 chunks then top-104 groups,
 so 2048 of 65536 keys (3.125 %) are attended per (sequence, KV head).
 
 One step = the whole path for the new token of every sequence:
-  1. hga_build_summaries: the token at 65535 completes chunk 1023, so the
-     chunk's 64 raw keys are rotated into the pool and its chunk and group
-     summaries are written;
-  2. hga_route: pooled query, level-1 scores of 1018 candidate chunks,
-     top-52, level-2 scores of 208 groups, top-104, window merge;
-  3. hga_attend: exact softmax attention over the 128 selected groups with
-     the gather fused into the loads.
+  1. hga_build_summaries (side stream): the new token at 65535 is rotated
+     into the pool; it completes chunk 1023, whose chunk and group summaries
+     are then built from the chunk's 64 raw keys;
+  2. hga_route (concurrently): pooled query, level-1 scores of 1018
+     candidate chunks, top-52, level-2 scores of 208 groups, top-104, window
+     merge;
+  3. hga_attend (after both): exact softmax attention over the 128 selected
+     groups with the gather fused into the loads, then the split merge.
 Inputs are resident in HBM before timing.  The state (pool, summaries,
 queries) is replicated R times at distinct addresses and the steps cycle
 through the replicas, so the timed traffic comes from HBM and not from the
-256 MB last-level cache.
+256 MB last-level cache.  The timed region replays a HIP graph holding R
+consecutive steps.
 
 Prints one JSON line.  ``value`` = decoded query tokens per second per layer
-(B tokens per step).  ``roofline`` covers the dominant kernel (hga_attend):
-algorithmic bytes per launch / its mean launch duration measured with HIP
-events on the launch stream.  ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample (the same step, repeated for ~10 s) on this host's cores.
+(B tokens per step).  ``roofline`` covers the dominant kernel (hga_attend's
+split kernel plus its merge): algorithmic bytes per launch / its mean launch
+duration, measured with HIP events on the launch stream while a spin kernel
+keeps the queue filled ahead (so host launch latency does not enter).
+``cpu_baseline`` times the fp64 CPU oracle doing the same step, repeated for
+about 10 s, on this host's cores.
 """
 from __future__ import annotations
 
@@ -41,7 +45,7 @@ HBM_PEAK_GBS = 8000.0
 
 
 def algorithmic_bytes(p, B):
-    """Bytes the method must move per step (per launch) at the decode workload."""
+    """Bytes the method must move per step at the decode workload."""
     d, hkv, hq = p["head_dim"], p["n_kv_heads"], p["n_q_heads"]
     g = p["chunk_size"] // p["groups_per_chunk"]
     max_sel = (p["n_sink_chunks"] + p["n_local_chunks"] + 1) * p["groups_per_chunk"] + p["topk_groups"]
@@ -53,13 +57,14 @@ def algorithmic_bytes(p, B):
     idx = hkv * max_sel * 4
     attend = B * (kv + q + o + idx)
     route = B * (n_cand * d * 4 * hkv + p["topk_chunks"] * p["groups_per_chunk"] * d * 4 * hkv + q + idx)
-    refresh = B * hkv * p["chunk_size"] * d * 2 * 4 + B * hkv * (1 + p["groups_per_chunk"]) * d * 4
+    # new token: raw K, V in, rotated K, V out; refresh: 64 raw keys in, 1 + G rows out
+    refresh = B * hkv * (4 * d * 2 + p["chunk_size"] * d * 2 + (1 + p["groups_per_chunk"]) * d * 4)
     return dict(attend=attend, route=route, refresh=refresh, total=attend + route + refresh)
 
 
 def cpu_baseline(inp, cfg_params, min_seconds=10.0):
-    """The fp64 C oracle doing the same step (chunk refresh + route + attend for
-    every sequence of the batch), repeated for about min_seconds."""
+    """The fp64 C oracle doing the same step (append + chunk refresh + route +
+    attend for every sequence of the batch), repeated for about min_seconds."""
     import numpy as np
     import oracle
     cfg = oracle.cfg_from(cfg_params)
@@ -92,8 +97,8 @@ def cpu_baseline(inp, cfg_params, min_seconds=10.0):
     t_start = time.perf_counter()
     while len(times) < 5 or time.perf_counter() - t_start < min_seconds:
         t0 = time.perf_counter()
-        for u in range(U):  # refresh of the chunk the new token completes
-            kp[u, c0:c0 + 64] = oracle.pool(cfg, kraw[u], c0)
+        for u in range(U):  # append of the new token, refresh of the chunk it completes
+            kp[u, pos] = oracle.pool(cfg, kraw[u][pos - c0:pos - c0 + 1], pos)[0]
             cs[u, c0 // 64] = oracle.span_summary(cfg, kraw[u], c0)
             for i in range(4):
                 gs[u, c0 // 16 + i] = oracle.span_summary(cfg, kraw[u][16 * i:16 * i + 16], c0 + 16 * i)
@@ -101,9 +106,9 @@ def cpu_baseline(inp, cfg_params, min_seconds=10.0):
         times.append(time.perf_counter() - t0)
     med = float(np.median(times))
     return {"value": B / med, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"the full step: all {B} sequences x {hkv} KV heads, chunk refresh + route + "
-                      f"attend of one decode token at position {pos} (context {T}); fp64 C oracle, "
-                      f"OpenMP over the {U} units; median of {len(times)} runs "
+            "sample": f"the full step: all {B} sequences x {hkv} KV heads, append + chunk refresh + "
+                      f"route + attend of one decode token at position {pos} (context {T}); fp64 C "
+                      f"oracle, OpenMP over the {U} units; median of {len(times)} runs "
                       f"({med * 1e3:.1f} ms each, {time.perf_counter() - t_start:.1f} s total)"}
 
 
@@ -128,11 +133,9 @@ def main():
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    name = "decode64k"
+    torch.cuda.set_device(0)
     t_gen = time.time()
-    inp = synth.generate(name)
+    inp = synth.generate("decode64k")
     p = inp.params
     B, T = p["batch"], p["context"]
     st = gh.build_state(inp)
@@ -142,9 +145,11 @@ def main():
     pos = int(inp.pos0[0])
     c0 = (pos // 64) * 64
     q = gh.query_slice(st, 0)
-    # raw K/V of the chunk that the new token completes (kept by the caller)
+    # raw K/V of the new token, and raw keys of the chunk it completes (kept by
+    # the caller until the chunk's summaries are built)
+    kt = st.k_raw[:, :, pos:pos + 1].contiguous()
+    vt = st.v_raw[:, :, pos:pos + 1].contiguous()
     kc = st.k_raw[:, :, c0:c0 + 64].contiguous()
-    vc = st.v_raw[:, :, c0:c0 + 64].contiguous()
     R = max(1, args.replicas)
     reps = []
     for r in range(R):
@@ -153,48 +158,84 @@ def main():
             v_pool=st.v_pool if r == 0 else st.v_pool.clone(),
             chunk_sum=st.chunk_sum if r == 0 else st.chunk_sum.clone(),
             group_sum=st.group_sum if r == 0 else st.group_sum.clone(),
-            q=q if r == 0 else q.clone(), kc=kc if r == 0 else kc.clone(),
-            vc=vc if r == 0 else vc.clone(), ws=torch.zeros_like(st.ws),
-            s=gh.alloc_step(st, 1)))
+            q=q if r == 0 else q.clone(), kt=kt if r == 0 else kt.clone(),
+            vt=vt if r == 0 else vt.clone(), kc=kc if r == 0 else kc.clone(),
+            ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, 1)))
     del st.k_raw, st.v_raw
     torch.cuda.synchronize()
     cfg = st.cfg
-    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
 
     def step(r, ev=None):
+        # The new token's pool append and the refresh of the chunk it
+        # completes run on a side stream, concurrently with routing (which
+        # reads neither); attention waits for them.  stream=None: the binding
+        # enqueues on torch's current stream (the capture stream inside
+        # torch.cuda.graph).
         x = reps[r]
-        hga.hga_build_summaries(cfg, B, x["kc"], x["vc"], c0, 64, x["k_pool"], x["v_pool"], T,
-                                x["chunk_sum"], x["group_sum"], st.max_chunks, stream)
+        cur = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        with torch.cuda.stream(side):
+            side.wait_event(fork)
+            hga.hga_build_summaries(cfg, B, x["kt"], x["vt"], pos, 1, x["k_pool"], x["v_pool"], T,
+                                    None, None, st.max_chunks)
+            hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
+                                    x["group_sum"], st.max_chunks)
+            join = torch.cuda.Event()
+            join.record(side)
         s = x["s"]
+        if ev is not None:
+            ev[0].record()
         hga.hga_route(cfg, B, x["q"], 1, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
-                      s.sel, s.n_sel, st.max_sel, None, x["ws"], stream)
+                      s.sel, s.n_sel, st.max_sel, None, x["ws"])
         if ev is not None:
-            ev[0].record(stream)
+            ev[1].record()
+        cur.wait_event(join)
+        if ev is not None:
+            ev[2].record()
         hga.hga_attend(cfg, B, x["q"], 1, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
-                       s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"], stream)
+                       s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
         if ev is not None:
-            ev[1].record(stream)
+            ev[3].record()
 
-    for i in range(args.warmup):
+    for i in range(max(args.warmup, R)):
         step(i % R)
     torch.cuda.synchronize()
-    # whole-step timing
+    eager_out = [x["s"].out.clone() for x in reps]
+
+    # whole-step throughput: one HIP graph holds R consecutive steps (one per
+    # replica); the timed region replays it
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(r)
+    for _ in range(max(1, args.warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, args.steps // R)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i % R)
-    t1.record(stream)
+    t0.record()
+    for _ in range(n_rep):
+        g.replay()
+    t1.record()
     torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-    # per-launch duration of the dominant kernel, events on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    steps_timed = n_rep * R
+    ms_step = t0.elapsed_time(t1) / steps_timed
+    for r, x in enumerate(reps):  # graph replays reproduce the eager results
+        assert torch.equal(x["s"].out, eager_out[r]), "graph replay differs from eager run"
+
+    # per-launch kernel durations: events on the launch stream around each
+    # call, with the queue filled ahead (a spin kernel holds the GPU while
+    # the host enqueues) so host launch latency does not enter the figures
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda._sleep(int(2e8))
     for i in range(args.steps):
         step(i % R, evs[i])
     torch.cuda.synchronize()
-    attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attend_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     s0 = reps[0]["s"]
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 
@@ -205,7 +246,7 @@ def main():
         "value": B / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps_timed,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
@@ -217,12 +258,14 @@ def main():
                                "batch 8 decode at t=65535, C=64 (4x16), 1 sink + 4 local chunks, "
                                "top-52 chunks, top-104 groups (2048 keys, 3.125%), pool in HBM",
                    "batch": B, "context": T, "replicas": R,
+                   "timing": "HIP graph of R steps, replayed",
                    "step_bytes_algorithmic": ab["total"],
                    "step_GBps_algorithmic": ab["total"] / (ms_step * 1e-3) / 1e9},
-        "roofline": {"kernel": "hga_attend (attend_decode_kernel)", "bound": "hbm",
+        "roofline": {"kernel": "hga_attend (split + merge kernels)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": ab["attend"], "launch_ms": attend_ms},
+                     "bytes_per_launch": ab["attend"], "launch_ms": attend_ms,
+                     "route_launch_ms": route_ms, "route_bytes_per_launch": ab["route"]},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

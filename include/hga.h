@@ -94,14 +94,15 @@ hga_status hga_max_selected(const hga_config* cfg, int32_t max_lq, int32_t* max_
 
 /* Bytes of device workspace needed by hga_route and hga_attend for batch B,
  * contexts up to max_ctx tokens and up to max_lq query tokens per call.  The
- * workspace must be zero-filled once before its first use (hga_workspace_reset
- * does that, as does allocating it zeroed); every call leaves it ready for the
- * next one. */
+ * workspace carries nothing from one call to the next (route keeps its
+ * scores there between its two kernels, attend its per-split partials), so
+ * it needs no initialisation; one workspace may serve route and attend on
+ * the same stream. */
 hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx, int32_t max_lq,
                                size_t* bytes);
 
-/* Zero-fills a workspace with a kernel (no hipMemset node, so it may be
- * captured in a graph). */
+/* Zero-fills a buffer (e.g. a workspace) with a kernel; no hipMemset node, so
+ * it may be captured in a graph. */
 hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 
 /* Pool append and RoPE-aware summaries ("Kernmechanisme" item 3).

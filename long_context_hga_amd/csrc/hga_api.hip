@@ -10,7 +10,8 @@ using namespace hga;
 namespace {
 
 constexpr int kMaxLqDecode = 15;
-constexpr int kMaxUnitsRoute = 1 << 17;
+constexpr int kMaxListDecode = 256;  // 32 splits of 8 groups
+constexpr int kMaxUnits = 1 << 20;
 constexpr size_t kMaxRouteLds = 60 * 1024;
 
 hga_status check_cfg(const hga_config* c) {
@@ -81,7 +82,7 @@ hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx
   const int max_chunks = (max_ctx + kChunk - 1) / kChunk;
   const size_t r = route_ws_bytes(k, B, max_chunks);
   const size_t a = attend_ws_bytes(k, B, max_lq, max_selected(cfg));
-  *bytes = kCounterBytes + round_up(r > a ? r : a, 256);
+  *bytes = round_up(r > a ? r : a, 256);
   return HGA_OK;
 }
 
@@ -125,14 +126,11 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
       max_chunks <= 0 || !sel_groups || !n_sel || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
-  if ((int64_t)B * cfg->n_kv_heads > kMaxUnitsRoute) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads > kMaxUnits) return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
-  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
-  const int n2 = k.topk_c * kGroups;
-  const size_t lds = (size_t)(max_cand > n2 ? max_cand : n2) * (sizeof(double) + 2 * sizeof(int) + 1);
-  if (lds > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
-  if (ws_bytes < kCounterBytes + route_ws_bytes(k, B, max_chunks))
-    return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
+  const size_t need = route_ws_bytes(k, B, max_chunks);
+  if (ws_bytes < need) return HGA_ERR_WORKSPACE_TOO_SMALL;
   RouteLaunch r;
   r.q = q_raw;
   r.q_pos0 = q_pos0;
@@ -141,8 +139,9 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
   r.sel = sel_groups;
   r.n_sel = n_sel;
   r.chunk_scores = chunk_scores_opt;
-  r.counters = static_cast<unsigned*>(ws) + kRouteCounterBase;
-  r.scores = reinterpret_cast<double*>(static_cast<char*>(ws) + kCounterBytes);
+  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+  r.scores = static_cast<double*>(ws);
+  r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
   r.B = B;
   r.lq = lq;
   r.max_chunks = max_chunks;
@@ -195,10 +194,10 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
     return HGA_ERR_INVALID_ARGUMENT;
   if (src_layout == HGA_SRC_POOL && src_cap <= 0) return HGA_ERR_INVALID_ARGUMENT;
   if (lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnitsRoute) return HGA_ERR_UNSUPPORTED;
+  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits) return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
-  if (ws_bytes < kCounterBytes + attend_ws_bytes(k, B, lq, max_sel))
-    return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < attend_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   AttendLaunch a;
   a.q = q_raw;
   a.q_pos0 = q_pos0;
@@ -208,8 +207,7 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   a.n_sel = n_sel;
   a.out = out;
   a.lse = lse_opt;
-  a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
-  a.counters = static_cast<unsigned*>(ws) + kAttendCounterBase;
+  a.part = static_cast<float*>(ws);
   a.B = B;
   a.lq = lq;
   a.src_layout = src_layout;

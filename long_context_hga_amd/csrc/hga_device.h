@@ -12,11 +12,6 @@ constexpr int kMaxPairs = 64;       // head_dim <= 128
 constexpr int kGroupTokens = 16;    // tokens per group (C = 64, G = 4)
 constexpr int kChunk = 64;
 constexpr int kGroups = 4;
-// Workspace: a fixed counter area (one 32-bit arrival counter per unit and
-// kernel), then data.  Counters return to zero at the end of every call.
-constexpr size_t kCounterBytes = size_t(1) << 20;
-constexpr int kRouteCounterBase = 0;
-constexpr int kAttendCounterBase = 1 << 17;
 
 // Everything a kernel needs to know about the configuration, passed by value.
 struct KCfg {
@@ -75,27 +70,27 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double x, int m) {
-  return __shfl_xor(x, m, 64);
+// The same controls on an fp64 value (each 32-bit half moved by DPP).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xffffffffu), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+// Sum over 8 consecutive lanes (fp64); every lane of the group gets it.
+__device__ __forceinline__ double group8_sum_d(double x) {
+  x += dpp_d<kDppXor1>(x);
+  x += dpp_d<kDppXor2>(x);
+  x += dpp_d<kDppHalfMirror>(x);
+  return x;
 }
 
-// Arrival counter of a "last workgroup finishes the job" pattern.  Every
-// thread's global writes are released at agent scope before the count; the
-// workgroup that brings the count to `total` resets it to zero and acquires
-// the others' writes.  Returns true in every thread of that last workgroup.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total, int* lds_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (prev + 1 == total);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *lds_flag = last;
-  }
-  __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
+// Keeps the compiler from consuming a loaded value before this point: the
+// empty asm takes the registers as in/out operands, so uses (and the wait for
+// the load) cannot be hoisted above it.  It emits no instruction.
+__device__ __forceinline__ void hold(float4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
 // The visible windows of a query chunk ct: sink chunks [0, sink_end),

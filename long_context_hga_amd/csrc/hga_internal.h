@@ -22,11 +22,12 @@ struct RouteLaunch {
   int* n_sel;
   double* chunk_scores;
   double* scores;       // workspace [B*Hkv][max_cand]
-  unsigned* counters;   // workspace [B*Hkv]
+  double* qbar;         // workspace [B*Hkv][d]
   int B, lq, max_chunks, max_sel;
 };
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st);
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks);
+size_t route_select_lds(const KCfg& cfg, int max_chunks);
 
 struct AttendLaunch {
   const void* q;
@@ -38,7 +39,6 @@ struct AttendLaunch {
   float* out;
   float* lse;
   float* part;          // workspace partials
-  unsigned* counters;   // workspace [B*Hkv*lq]
   int B, lq, src_layout, src_cap, max_sel, part_sel;
 };
 hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);

@@ -8,11 +8,12 @@
 // stored already rotated and rounded once to the pool dtype.
 //
 // One workgroup per (chunk overlapping the range, KV head, sequence).  256
-// threads = P pairs x S token slices (P = d/2).  Each thread rotates its pair
-// for the tokens of its slice in fp64 (fp64 vector math runs at the fp32
-// non-packed rate on gfx950, and this kernel is off the decode critical path),
-// writes the rounded pool rows and keeps fp64 slice sums.  Slices are then
-// combined through LDS into the group and chunk summaries (fp32 stores).
+// threads = P pairs x S token slices (P = d/2).  Each thread loads its pair
+// for all tokens of its slice at once, then rotates them in fp64 (fp64 vector
+// math runs at the fp32 non-packed rate on gfx950), stepping the angle by one
+// fp64 rotation per token from a single sincos, writes the rounded pool rows
+// and keeps fp64 slice sums.  Slices are then combined through LDS into the
+// group and chunk summaries (fp32 stores).
 #include "hga_internal.h"
 
 namespace hga {
@@ -54,42 +55,65 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   T* kp = static_cast<T*>(a.k_pool) + (size_t)unit * a.pool_cap * D;
   T* vp = static_cast<T*>(a.v_pool) + (size_t)unit * a.pool_cap * D;
 
-  double sa = 0.0, sb = 0.0;
+  // every load of this thread first (TS tokens of pair j), unconditionally
+  // from a clamped in-range row so that they are all in flight together;
+  // rows outside [lo, hi) are loaded but not used
+  T xa[TS], xb[TS], ya[TS], yb[TS];
+  const T* vsrc = a.k_pool ? vr : kr;
+#pragma unroll
   for (int i = 0; i < TS; ++i) {
-    const int p = c0 + s * TS + i;
-    if (p < lo || p >= hi) continue;
-    const size_t row = (size_t)(p - lo) * D;
-    double ka, kb;
-    if constexpr (BF16) {
-      ka = bf16_to_f(kr[row + j]);
-      kb = bf16_to_f(kr[row + j + P]);
-    } else {
-      ka = kr[row + j];
-      kb = kr[row + j + P];
-    }
-    double cs, sn;
-    rope_cs((double)p, w, &cs, &sn);
-    const double ra = ka * cs - kb * sn;
-    const double rb = ka * sn + kb * cs;
-    if (a.k_pool) {
-      const size_t prow = (size_t)p * D;
+    int r = c0 + s * TS + i - lo;
+    r = r < 0 ? 0 : (r >= a.n_tok ? a.n_tok - 1 : r);
+    const size_t row = (size_t)r * D;
+    xa[i] = kr[row + j];
+    xb[i] = kr[row + j + P];
+    ya[i] = vsrc[row + j];
+    yb[i] = vsrc[row + j + P];
+  }
+  // angles of consecutive positions by rotation: (cos, sin)(p w) from
+  // (cos, sin)(p0 w) and (cos, sin)(w) in fp64 (error ~1e-16 per step)
+  const int p_first = c0 + s * TS;
+  double cs, sn, cd, sd;
+  rope_cs((double)p_first, w, &cs, &sn);
+  sincos(w, &sd, &cd);
+  double sa = 0.0, sb = 0.0;
+#pragma unroll
+  for (int i = 0; i < TS; ++i) {
+    const int p = p_first + i;
+    if (p >= lo && p < hi) {
+      double ka, kb;
       if constexpr (BF16) {
-        kp[prow + j] = f64_to_bf16_rne(ra);
-        kp[prow + j + P] = f64_to_bf16_rne(rb);
+        ka = bf16_to_f(xa[i]);
+        kb = bf16_to_f(xb[i]);
       } else {
-        kp[prow + j] = (float)ra;
-        kp[prow + j + P] = (float)rb;
+        ka = xa[i];
+        kb = xb[i];
       }
-      vp[prow + j] = vr[row + j];
-      vp[prow + j + P] = vr[row + j + P];
+      const double ra = ka * cs - kb * sn;
+      const double rb = ka * sn + kb * cs;
+      if (a.k_pool) {
+        const size_t prow = (size_t)p * D;
+        if constexpr (BF16) {
+          kp[prow + j] = f64_to_bf16_rne(ra);
+          kp[prow + j + P] = f64_to_bf16_rne(rb);
+        } else {
+          kp[prow + j] = (float)ra;
+          kp[prow + j + P] = (float)rb;
+        }
+        vp[prow + j] = ya[i];
+        vp[prow + j + P] = yb[i];
+      }
+      if (hf) {
+        sa += ra;
+        sb += rb;
+      } else {
+        sa += ka;
+        sb += kb;
+      }
     }
-    if (hf) {
-      sa += ra;
-      sb += rb;
-    } else {
-      sa += ka;
-      sb += kb;
-    }
+    const double c2 = cs * cd - sn * sd;
+    sn = sn * cd + cs * sd;
+    cs = c2;
   }
   if (!complete || !a.chunk_sum) return;  // uniform across the workgroup
 

@@ -6,7 +6,11 @@ Comparison rules (written here once, used by every GPU test):
     than 1e-6 (both sides rotate in fp64; only an fp64 value within ~1e-16
     of a rounding midpoint can round differently).
   * pool values: bit-exact copy.
-  * summaries: fp32 results within 1 fp32 ulp of the fp64 oracle.
+  * summaries: fp32 results within 1 fp32 ulp of the fp64 oracle, plus an
+    absolute 2e-10: at positions up to 65535 the fp64 angle p*omega itself
+    carries up to ~1.5e-11 rad of rounding, and the two sides may round it
+    differently (per-token product vs. fp64 angle stepping); on a span mean
+    of keys of size ~4 that is < 1e-10, far below the 1e-6 score margin.
   * selections: where the oracle's level-1 and level-2 score gaps at the
     cut both exceed 1e-6, the GPU list equals the oracle list exactly.
     Otherwise the unit is reported "unpinned": the windows must be present,
@@ -89,7 +93,7 @@ def check_pool_keys(gpu_vals: np.ndarray, ora_vals: np.ndarray, bf16: bool):
 
 
 def check_summaries(gpu: np.ndarray, ora: np.ndarray):
-    tol = np.abs(ora) * 2.0 ** -23 + 1e-30
+    tol = np.abs(ora) * 2.0 ** -23 + 2e-10
     bad = np.abs(gpu.astype(np.float64) - ora) > tol
     assert not bad.any(), (np.argwhere(bad)[:5], gpu[bad][:5], ora[bad][:5])
 
