@@ -6,15 +6,16 @@ independent sequences, query at position 65535.  C = 64 tokens per chunk in
 4 groups of 16; 1 sink + 4 local chunks, top-52 chunks then top-104 groups,
 so 2048 of 65536 keys (3.125 %) are attended per (sequence, KV head).
 
-One step = the whole path for the new token of every sequence:
-  1. hga_build_summaries (side stream): the new token at 65535 is rotated
-     into the pool; it completes chunk 1023, whose chunk and group summaries
-     are then built from the chunk's 64 raw keys;
-  2. hga_route (concurrently): pooled query, level-1 scores of 1018
-     candidate chunks, top-52, level-2 scores of 208 groups, top-104, window
-     merge;
-  3. hga_attend (after both): exact softmax attention over the 128 selected
-     groups with the gather fused into the loads, then the split merge.
+One step = the whole path for the new token of every sequence, on one
+stream:
+  1. hga_build_summaries: the new token at 65535 is rotated into the pool;
+  2. hga_route: pooled query, level-1 scores of 1018 candidate chunks,
+     top-52, level-2 scores of 208 groups, top-104, window merge;
+  3. hga_attend: exact softmax attention over the 128 selected groups with
+     the gather fused into the loads, then the split merge;
+  4. hga_build_summaries: the token completed chunk 1023, whose chunk and
+     group summaries are built from the chunk's 64 raw keys (read by routing
+     from the next step on).
 Inputs are resident in HBM before timing.  The state (pool, summaries,
 queries) is replicated R times at distinct addresses and the steps cycle
 through the replicas, so the timed traffic comes from HBM and not from the
@@ -164,40 +165,28 @@ def main():
     del st.k_raw, st.v_raw
     torch.cuda.synchronize()
     cfg = st.cfg
-    side = torch.cuda.Stream()
 
     def step(r, ev=None):
-        # The new token's pool append and the refresh of the chunk it
-        # completes run on a side stream, concurrently with routing (which
-        # reads neither); attention waits for them.  stream=None: the binding
-        # enqueues on torch's current stream (the capture stream inside
-        # torch.cuda.graph).
+        # One stream: the new token's pool append, routing, attention, then
+        # the summaries of the chunk the token completed (needed from the
+        # next step on).  stream=None: the binding enqueues on torch's current
+        # stream (the capture stream inside torch.cuda.graph).
         x = reps[r]
-        cur = torch.cuda.current_stream()
-        fork = torch.cuda.Event()
-        fork.record(cur)
-        with torch.cuda.stream(side):
-            side.wait_event(fork)
-            hga.hga_build_summaries(cfg, B, x["kt"], x["vt"], pos, 1, x["k_pool"], x["v_pool"], T,
-                                    None, None, st.max_chunks)
-            hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
-                                    x["group_sum"], st.max_chunks)
-            join = torch.cuda.Event()
-            join.record(side)
         s = x["s"]
+        hga.hga_build_summaries(cfg, B, x["kt"], x["vt"], pos, 1, x["k_pool"], x["v_pool"], T,
+                                None, None, st.max_chunks)
         if ev is not None:
             ev[0].record()
         hga.hga_route(cfg, B, x["q"], 1, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
                       s.sel, s.n_sel, st.max_sel, None, x["ws"])
         if ev is not None:
             ev[1].record()
-        cur.wait_event(join)
-        if ev is not None:
-            ev[2].record()
         hga.hga_attend(cfg, B, x["q"], 1, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
                        s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
+        hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
+                                x["group_sum"], st.max_chunks)
 
     for i in range(max(args.warmup, R)):
         step(i % R)
@@ -229,13 +218,13 @@ def main():
     # per-launch kernel durations: events on the launch stream around each
     # call, with the queue filled ahead (a spin kernel holds the GPU while
     # the host enqueues) so host launch latency does not enter the figures
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda._sleep(int(2e8))
     for i in range(args.steps):
         step(i % R, evs[i])
     torch.cuda.synchronize()
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attend_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    attend_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     s0 = reps[0]["s"]
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 

@@ -469,12 +469,28 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs args) {
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / a.lq, tq = blockIdx.x % a.lq;
   const int b = unit / c.hkv, h = unit % c.hkv;
-  const int pos0 = a.q_pos0[b];
-  const int n_sel = a.n_sel[unit];
   const size_t orow0 = ((size_t)(b * c.hq + h * HG) * a.lq + tq) * D;  // head hh: + hh*lq*D
   const int i0 = 4 * tid;  // first output of this thread
   const int hh = i0 / D, e = i0 % D;
   const bool mine = i0 < HG * D;
+  // every split's (m, l, 4 o values) of this thread's head is read before the
+  // list length is known (splits that did not run are read but not used)
+  const int ic = mine ? i0 : 0;
+  const int hc = mine ? hh : 0;
+  const float* pbase = a.part + (size_t)(unit * a.lq + tq) * args.n_splits * part_floats<D, HG>();
+  float pm[kMaxSplits], pl[kMaxSplits];
+  float4 po[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    if (sp < args.n_splits) {  // uniform
+      const float* pp = pbase + (size_t)sp * part_floats<D, HG>();
+      pm[sp] = pp[hc];
+      pl[sp] = pp[HG + hc];
+      po[sp] = *reinterpret_cast<const float4*>(pp + part_head<HG>() + ic);
+    }
+  }
+  const int pos0 = a.q_pos0[b];
+  const int n_sel = a.n_sel[unit];
 
   bool bad = n_sel < 0 || n_sel > a.max_sel || pos0 < 0 || (pos0 % kChunk) + a.lq > kChunk;
   ListParts lp{0, 0, 0};
@@ -493,18 +509,6 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs args) {
   if (!mine) return;
   const int n_part = part_count(a.part_sel, lp, n_sel);
   const int n_act = (n_part + kSplitGroups - 1) / kSplitGroups;
-  const float* pbase = a.part + (size_t)(unit * a.lq + tq) * args.n_splits * part_floats<D, HG>();
-  float pm[kMaxSplits], pl[kMaxSplits];
-  float4 po[kMaxSplits];
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
-    if (sp < args.n_splits) {  // uniform
-      const float* pp = pbase + (size_t)(sp < n_act ? sp : 0) * part_floats<D, HG>();
-      pm[sp] = pp[hh];
-      pl[sp] = pp[HG + hh];
-      po[sp] = *reinterpret_cast<const float4*>(pp + part_head<HG>() + i0);
-    }
-  }
   float M = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)

@@ -78,6 +78,55 @@ __device__ __forceinline__ double dpp_d(double x) {
   const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row_shr:1,2,4,8
+// within each 16-lane row (zero fill), then row_bcast:15 / row_bcast:31
+// carry the row totals into the later rows.
+template <int CTRL, int ROWS, bool ZERO>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, ZERO);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xF, true>(v);
+  v += dpp_i<0x112, 0xF, true>(v);
+  v += dpp_i<0x114, 0xF, true>(v);
+  v += dpp_i<0x118, 0xF, true>(v);
+  v += dpp_i<0x142, 0xA, false>(v);
+  v += dpp_i<0x143, 0xC, false>(v);
+  return v;
+}
+
+// fp64 max / min over the wave: DPP inside 16-lane rows, then
+// v_permlane16_swap / v_permlane32_swap across rows (each swap returns the
+// lane's own value and its partner's, in some order).
+template <bool MAX>
+__device__ __forceinline__ double wave_ext_d(double x) {
+  auto op = [](double a, double b) { return MAX ? fmax(a, b) : fmin(a, b); };
+  x = op(x, dpp_d<kDppXor1>(x));
+  x = op(x, dpp_d<kDppXor2>(x));
+  x = op(x, dpp_d<kDppHalfMirror>(x));
+  x = op(x, dpp_d<kDppMirror>(x));
+  {
+    const unsigned long long u = __double_as_longlong(x);
+    auto lo = __builtin_amdgcn_permlane16_swap((unsigned)u, (unsigned)u, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+    x = op(__longlong_as_double(((unsigned long long)hi[0] << 32) | lo[0]),
+           __longlong_as_double(((unsigned long long)hi[1] << 32) | lo[1]));
+  }
+  {
+    const unsigned long long u = __double_as_longlong(x);
+    auto lo = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+    auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(u >> 32), (unsigned)(u >> 32), false, false);
+    x = op(__longlong_as_double(((unsigned long long)hi[0] << 32) | lo[0]),
+           __longlong_as_double(((unsigned long long)hi[1] << 32) | lo[1]));
+  }
+  return x;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0));
+}
+
 // Sum over 8 consecutive lanes (fp64); every lane of the group gets it.
 __device__ __forceinline__ double group8_sum_d(double x) {
   x += dpp_d<kDppXor1>(x);

@@ -17,12 +17,12 @@
 //    loads in flight at once), level-2 top-k, and the ascending group list.
 //    The kernel boundary makes the first launch's scores visible to the
 //    second with plain loads.
-// Top-k: a 256-bin histogram between the min and max score finds the bin
-// holding the k-th largest score; every score in a higher bin is kept, and
-// the boundary bin is resolved exactly by rank counting with the order
-// (score descending, id ascending).  Scores stay fp64 throughout, so the
-// kept set equals the fp64 reference wherever its score gap exceeds the
-// error of the fp32-stored summaries.
+// Top-k (one wave, no barriers): a 256-bin histogram between the min and
+// max score finds the bin holding the k-th largest score; every score in a
+// higher bin is kept, and the boundary bin is resolved exactly by rank
+// counting with the order (score descending, id ascending).  Scores stay
+// fp64 throughout, so the kept set equals the fp64 reference wherever its
+// score gap exceeds the error of the fp32-stored summaries.
 #include "hga_internal.h"
 
 namespace hga {
@@ -36,122 +36,157 @@ struct RouteArgs {
   int max_cand;
 };
 
-__device__ __forceinline__ double wave_max_d(double x) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmax(x, __shfl_xor(x, m, 64));
-  return x;
-}
-__device__ __forceinline__ double wave_min_d(double x) {
-  for (int m = 32; m >= 1; m >>= 1) x = fmin(x, __shfl_xor(x, m, 64));
-  return x;
-}
-
-struct SelShared {
-  double red[8];
-  int hist[256];
-  int scan[8];
-  int bstar, need, bcount;
+// Top-k by one wave, no barriers: the k best of s[0..n) (LDS, fp64; order
+// score descending, index ascending) are written ascending by index to out
+// (LDS); returns min(k, n).  hist (256 ints), bl and win (n ints each) are
+// LDS scratch.  A 256-bin histogram between the min and max score finds the
+// bin holding the k-th largest score; every score in a higher bin is kept,
+// and the boundary bin is resolved exactly by rank counting.  Counts use a
+// DPP scan and ballot / mbcnt.
+//   n <= 1024: scores stay in registers (element i in slot i / 64 of lane
+//   i % 64); longer lists stream from LDS in the same passes.
+struct TopkScratch {
+  int* hist;  // 256
+  int* bl;    // boundary members, by index
+  int* win;   // 1 if the boundary member at that list position is kept
 };
 
-// Flags the k best of s[0..n) (score desc, index asc).  All 256 threads.
-__device__ void topk_flags(const double* s, int n, int k, unsigned char* flag, int* blist,
-                           SelShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (k >= n || k <= 0) {
-    for (int i = tid; i < n; i += 256) flag[i] = k > 0;
-    __syncthreads();
-    return;
-  }
-  double mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < n; i += 256) {
-    mn = fmin(mn, s[i]);
-    mx = fmax(mx, s[i]);
-  }
-  mn = wave_min_d(mn);
-  mx = wave_max_d(mx);
-  if (lane == 0) {
-    sh.red[wave] = mn;
-    sh.red[4 + wave] = mx;
-  }
-  sh.hist[tid] = 0;
-  if (tid == 0) sh.bcount = 0;
-  __syncthreads();
-  mn = fmin(fmin(sh.red[0], sh.red[1]), fmin(sh.red[2], sh.red[3]));
-  mx = fmax(fmax(sh.red[4], sh.red[5]), fmax(sh.red[6], sh.red[7]));
-  const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
-  auto bin = [&](double x) {
-    double f = (x - mn) * scale;
-    int b = f >= 0.0 ? (int)f : 0;  // monotone in x; NaN -> 0
-    return b > 255 ? 255 : b;
-  };
-  for (int i = tid; i < n; i += 256) atomicAdd(&sh.hist[bin(s[i])], 1);
-  __syncthreads();
-  if (wave == 0) {
-    const int h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
-    const int h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
-    const int local = h0 + h1 + h2 + h3;
-    int suf = local;  // count in bins >= 4*lane
-    for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
-    const int above = suf - local;
-    if (above < k && k <= suf) {
-      const int c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1;
-      int bs, ab;
-      if (c3 >= k) { bs = 4 * lane + 3; ab = above; }
-      else if (c2 >= k) { bs = 4 * lane + 2; ab = c3; }
-      else if (c1 >= k) { bs = 4 * lane + 1; ab = c2; }
-      else { bs = 4 * lane; ab = c1; }
-      sh.bstar = bs;
-      sh.need = k - ab;
-    }
-  }
-  __syncthreads();
-  const int bs = sh.bstar, need = sh.need;
-  for (int i = tid; i < n; i += 256) {
-    const int bi = bin(s[i]);
-    flag[i] = bi > bs;
-    if (bi == bs) blist[atomicAdd(&sh.bcount, 1)] = i;
-  }
-  __syncthreads();
-  const int m = sh.bcount;
-  for (int t = tid; t < m; t += 256) {
-    const int i = blist[t];
+__device__ __forceinline__ int topk_bin(double x, double mn, double scale) {
+  const double f = (x - mn) * scale;
+  const int b = f >= 0.0 ? (int)f : 0;  // monotone in x; NaN -> 0
+  return b > 255 ? 255 : b;
+}
+
+// Boundary bin and how many of its members are kept, from the histogram.
+__device__ __forceinline__ void topk_cut(const int* hist, int k, int* bs, int* need) {
+  const int lane = threadIdx.x & 63;
+  const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+            h3 = hist[4 * lane + 3];
+  const int local = h0 + h1 + h2 + h3;
+  const int pre = wave_incl_scan(local);
+  const int total = __builtin_amdgcn_readlane(pre, 63);
+  const int suf = total - pre + local;  // scores in bins >= 4*lane
+  const int above = suf - local;
+  int bs_l, ab_l;
+  const int c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1;
+  if (c3 >= k) { bs_l = 4 * lane + 3; ab_l = above; }
+  else if (c2 >= k) { bs_l = 4 * lane + 2; ab_l = c3; }
+  else if (c1 >= k) { bs_l = 4 * lane + 1; ab_l = c2; }
+  else { bs_l = 4 * lane; ab_l = c1; }
+  const int src = __ffsll((long long)__ballot(above < k && k <= suf)) - 1;
+  *bs = __builtin_amdgcn_readlane(bs_l, src);
+  *need = k - __builtin_amdgcn_readlane(ab_l, src);
+}
+
+// Ranks the nb boundary members; win[t] = 1 for the `need` best.
+__device__ __forceinline__ void topk_rank(const double* s, int nb, int need, const int* bl, int* win) {
+  const int lane = threadIdx.x & 63;
+  for (int t = lane; t < nb; t += 64) {
+    const int i = bl[t];
     const double si = s[i];
     int r = 0;
-    for (int u = 0; u < m; ++u) {
-      const int jx = blist[u];
+    for (int u = 0; u < nb; ++u) {
+      const int jx = bl[u];
       const double sj = s[jx];
       r += (sj > si) || (sj == si && jx < i);
     }
-    if (r < need) flag[i] = 1;
+    win[t] = r < need;
   }
-  __syncthreads();
 }
 
-// Ordered compaction: out[rank] = i for every flagged i, ascending.  Returns
-// the count (in every thread).
-__device__ int compact_ordered(const unsigned char* flag, int n, int* out, SelShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + 255) / 256;
-  const int b0 = tid * per, b1 = min(n, b0 + per);
-  int cnt = 0;
-  for (int i = b0; i < b1; ++i) cnt += flag[i];
-  int inc = cnt;  // inclusive wave scan
-  for (int off = 1; off < 64; off <<= 1) {
-    int o = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += o;
+__device__ int wave_topk(const double* s, int n, int k, int* out, const TopkScratch& sc) {
+  constexpr int SL = 16;
+  const int lane = threadIdx.x & 63;
+  if (k <= 0) return 0;
+  if (k >= n) {
+    for (int i = lane; i < n; i += 64) out[i] = i;
+    return n;
   }
-  if (lane == 63) sh.scan[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += sh.scan[w];
-  const int total = sh.scan[0] + sh.scan[1] + sh.scan[2] + sh.scan[3];
-  int pos = base + inc - cnt;
-  for (int i = b0; i < b1; ++i)
-    if (flag[i]) out[pos++] = i;
-  __syncthreads();
-  return total;
+  for (int j = 0; j < 4; ++j) sc.hist[4 * lane + j] = 0;
+  int cnt = 0;
+  if (n <= 64 * SL) {
+    double x[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const int i = 64 * j + lane;
+      x[j] = s[i < n ? i : n - 1];
+    }
+    double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const bool v = 64 * j + lane < n;
+      mn = fmin(mn, v ? x[j] : INFINITY);
+      mx = fmax(mx, v ? x[j] : -INFINITY);
+    }
+    mn = wave_ext_d<false>(mn);
+    mx = wave_ext_d<true>(mx);
+    const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+    int bins[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) bins[j] = 64 * j + lane < n ? topk_bin(x[j], mn, scale) : -1;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < SL; ++j)
+      if (bins[j] >= 0) atomicAdd(&sc.hist[bins[j]], 1);
+    __builtin_amdgcn_wave_barrier();
+    int bs, need;
+    topk_cut(sc.hist, k, &bs, &need);
+    int nb = 0, bpos[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const unsigned long long m = __ballot(bins[j] == bs);
+      bpos[j] = nb + lanes_below(m);
+      if (bins[j] == bs) sc.bl[bpos[j]] = 64 * j + lane;
+      nb += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    topk_rank(s, nb, need, sc.bl, sc.win);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const bool keep = bins[j] > bs || (bins[j] == bs && sc.win[bpos[j]]);
+      const unsigned long long m = __ballot(keep);
+      if (keep) out[cnt + lanes_below(m)] = 64 * j + lane;
+      cnt += __popcll(m);
+    }
+  } else {
+    double mn = INFINITY, mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) {
+      mn = fmin(mn, s[i]);
+      mx = fmax(mx, s[i]);
+    }
+    mn = wave_ext_d<false>(mn);
+    mx = wave_ext_d<true>(mx);
+    const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < n; i += 64) atomicAdd(&sc.hist[topk_bin(s[i], mn, scale)], 1);
+    __builtin_amdgcn_wave_barrier();
+    int bs, need;
+    topk_cut(sc.hist, k, &bs, &need);
+    int nb = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const bool e = i < n && topk_bin(s[i], mn, scale) == bs;
+      const unsigned long long m = __ballot(e);
+      if (e) sc.bl[nb + lanes_below(m)] = i;
+      nb += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    topk_rank(s, nb, need, sc.bl, sc.win);
+    __builtin_amdgcn_wave_barrier();
+    int seen = 0;  // boundary members met so far, in index order
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int bi = i < n ? topk_bin(s[i], mn, scale) : -1;
+      const unsigned long long mb = __ballot(bi == bs);
+      const bool keep = bi > bs || (bi == bs && sc.win[seen + lanes_below(mb)]);
+      seen += __popcll(mb);
+      const unsigned long long m = __ballot(keep);
+      if (keep) out[cnt + lanes_below(m)] = i;
+      cnt += __popcll(m);
+    }
+  }
+  return cnt;
 }
 
 // Position and candidate range of a unit; false if the query position is
@@ -307,14 +342,35 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int RPP = 256 / kLanesPerRow;  // rows per pass of the workgroup
   constexpr int U = 8;                     // passes in flight
-  __shared__ SelShared sh;
+  __shared__ int hist[256];
+  __shared__ int kk[2];
   extern __shared__ double dyn[];
 
   const KCfg& c = a.cfg;
   const RouteLaunch& r = a.r;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
   const int unit = b * c.hkv + h;
+
+  // every load that does not depend on the position goes out first: this
+  // lane's qbar slice (for level 2) and the level-1 scores (clamped to the
+  // table; entries past the candidates are dropped below)
+  const int sub = lane % kLanesPerRow;
+  double qv[NV][4];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+  const double* scores = r.scores + (size_t)unit * a.max_cand;
+  constexpr int SPT = 4;  // scores per thread in flight
+  double v4[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int i = u * 256 + tid;
+    v4[u] = scores[i < a.max_cand ? i : a.max_cand - 1];
+  }
+
   int pos0;
   Windows w;
   if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) {
@@ -326,39 +382,30 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 
   const int n2max = c.topk_c * kGroups;
   const int nmax = a.max_cand > n2max ? a.max_cand : n2max;
+  // LDS: scores | boundary list | boundary winners | level-1 list | level-2 list
   double* s_lds = dyn;
-  int* blist = reinterpret_cast<int*>(s_lds + nmax);
-  int* sel1 = blist + nmax;
-  unsigned char* flag = reinterpret_cast<unsigned char*>(sel1 + nmax);
+  int* bl = reinterpret_cast<int*>(s_lds + nmax);
+  int* win = bl + nmax;
+  int* sel = win + nmax;
+  int* sel2 = sel + nmax;
+  const TopkScratch tks{hist, bl, win};
 
-  // qbar slice of this lane (for level 2) and the level-1 scores: all loads
-  // first
-  const int sub = lane % kLanesPerRow;
-  double qv[NV][4];
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
-  const double* scores = r.scores + (size_t)unit * a.max_cand;
-  for (int i0 = 0; i0 < n_cand; i0 += 4 * 256) {
-    double v4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256 + tid;
-      v4[u] = scores[i < n_cand ? i : n_cand - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256 + tid;
-      if (i < n_cand) s_lds[i] = v4[u];
-    }
+  for (int u = 0; u < SPT; ++u) {
+    const int i = u * 256 + tid;
+    if (i < n_cand) s_lds[i] = v4[u];
+  }
+  for (int i = SPT * 256 + tid; i < n_cand; i += 256) s_lds[i] = scores[i];
+  __syncthreads();
+  // level 1 (one wave): kept candidate indices, ascending, into sel
+  if (wave == 0) {
+    const int k1 = wave_topk(s_lds, n_cand, c.topk_c, sel, tks);
+    if (lane == 0) kk[0] = k1;
   }
   __syncthreads();
-  topk_flags(s_lds, n_cand, c.topk_c, flag, blist, sh);
-  const int k1 = compact_ordered(flag, n_cand, sel1, sh);  // candidate indices, ascending
+  const int k1 = kk[0];
 
-  // level 2: the G groups of each kept chunk
+  // level 2 (all waves): the G groups of each kept chunk
   const int n2 = k1 * kGroups;
   const int rsub = tid / kLanesPerRow;
   for (int base = 0; base < n2; base += RPP * U) {
@@ -367,7 +414,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     for (int u = 0; u < U; ++u) {
       int i = base + u * RPP + rsub;
       i = i < n2 ? i : n2 - 1;  // clamped: every load issues, extras ignored
-      const int gid = (w.cand_lo + sel1[i / kGroups]) * kGroups + i % kGroups;
+      const int gid = (w.cand_lo + sel[i / kGroups]) * kGroups + i % kGroups;
       const float4* rowp = reinterpret_cast<const float4*>(
           r.group_sum + ((size_t)unit * r.max_chunks * kGroups + gid) * D);
 #pragma unroll
@@ -389,8 +436,13 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  topk_flags(s_lds, n2, c.topk_g, flag, blist, sh);
-  const int k2 = compact_ordered(flag, n2, blist, sh);  // level-2 indices, ascending = gid order
+  // level 2 selection (one wave): kept group indices, ascending = gid order
+  if (wave == 0) {
+    const int k2 = wave_topk(s_lds, n2, c.topk_g, sel2, tks);
+    if (lane == 0) kk[1] = k2;
+  }
+  __syncthreads();
+  const int k2 = kk[1];
 
   // the list: sink | routed | local | current
   const int last = pos0 + r.lq - 1;
@@ -404,8 +456,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     if (i < n_head) {
       gid = i;
     } else if (i < n_head + k2) {
-      const int x = blist[i - n_head];
-      gid = (w.cand_lo + sel1[x / kGroups]) * kGroups + x % kGroups;
+      const int x = sel2[i - n_head];
+      gid = (w.cand_lo + sel[x / kGroups]) * kGroups + x % kGroups;
     } else {
       gid = w.local_begin * kGroups + (i - n_head - k2);
     }
@@ -425,7 +477,8 @@ size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks) {
 size_t route_select_lds(const KCfg& cfg, int max_chunks) {
   const int max_cand = max_cand_of(cfg, max_chunks);
   const int n2 = cfg.topk_c * kGroups;
-  return (size_t)(max_cand > n2 ? max_cand : n2) * (sizeof(double) + 2 * sizeof(int) + 1);
+  const size_t nmax = (size_t)(max_cand > n2 ? max_cand : n2);
+  return nmax * (sizeof(double) + 3 * sizeof(int)) + (size_t)n2 * sizeof(int);
 }
 
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st) {

@@ -357,3 +357,27 @@ def test_decode64k_full_sampled():
         check_selection(cfg, sel[b, h], osel, margins, oscores, 65535, 1)
         o_ref, _ = oracle.attend(cfg, qu, 65535, kp, v, sel[b, h])
         assert max_abs(out[b, h * 8:(h + 1) * 8, 0], o_ref[:, 0]) <= ATOL_OUT
+
+
+def test_decode_128k_long_candidate_list():
+    """131072 tokens: 2042 candidate chunks, beyond the register-resident
+    top-k (1024), so the streaming selection runs; two units vs the oracle."""
+    inp = synth.generate("decode64k", batch=1, context=131072)
+    st = gh.build_state(inp)
+    cfg = ora_cfg(inp)
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    gh.attend(st, q, 1, st.pos0, s)
+    torch.cuda.synchronize()
+    pos = int(inp.pos0[0])
+    uc = UnitCache(inp, cfg)
+    for h in (0, 3):
+        cs, gs, kp, v = uc.get(0, h)
+        qu = q_unit(inp, cfg, 0, h, 0, 1)
+        osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
+        n = int(s.n_sel[0, h])
+        g = s.sel[0, h, :n].cpu().numpy()
+        check_selection(cfg, g, osel, margins, oscores, pos, 1)
+        o_ref, _ = oracle.attend(cfg, qu, pos, kp, v, g)
+        assert max_abs(s.out[0, h * 8:(h + 1) * 8, 0].cpu().numpy(), o_ref[:, 0]) <= ATOL_OUT
