@@ -44,6 +44,16 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM traffic of the attention entry point (its split kernel plus its merge
+# kernel), from two rocprofv3 --pmc passes over this bench (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, summed over the two kernels) and scaled by
+# what the same counters read for a plain device copy of known size
+# (bench.py --calibrate-copy).  Valid only for the kernel source it was taken
+# on: if hga_attend.hip has changed since, traffic is reported as null.
+ATTEND_TRAFFIC = dict(
+    source_sha256="541f63edf4d3ed7724168182173ec6062a6694e3ee75c39d6b5962dd6257ba01",
+    fetch_kib=16820.61 + 1108.02, write_kib=2080.0 + 129.0, fetch_scale=2.0, write_scale=1.0)
+
 
 def algorithmic_bytes(p, B):
     """Bytes the method must move per step at the decode workload."""
@@ -61,6 +71,34 @@ def algorithmic_bytes(p, B):
     # new token: raw K, V in, rotated K, V out; refresh: 64 raw keys in, 1 + G rows out
     refresh = B * hkv * (4 * d * 2 + p["chunk_size"] * d * 2 + (1 + p["groups_per_chunk"]) * d * 4)
     return dict(attend=attend, route=route, refresh=refresh, total=attend + route + refresh)
+
+
+def attend_source_sha():
+    import hashlib
+    path = os.path.join(ROOT, "long_context_hga_amd", "csrc", "hga_attend.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def attend_traffic():
+    """HBM bytes per hga_attend call from the stored counter figures, or None."""
+    t = ATTEND_TRAFFIC
+    if t is None or t["source_sha256"] != attend_source_sha():
+        return None
+    return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
+
+
+def calibrate_copy(n_bytes=512 << 20, reps=4):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE
+    and WRITE_SIZE counters: each dispatch reads and writes n_bytes."""
+    import torch
+    src = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": n_bytes,
+                      "bytes_written_per_dispatch": n_bytes, "dispatches": reps}), flush=True)
 
 
 def cpu_baseline(inp, cfg_params, min_seconds=10.0):
@@ -120,11 +158,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
               "per-GPU and this build has no multi-GPU leg", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
@@ -252,7 +296,7 @@ def main():
                    "step_GBps_algorithmic": ab["total"] / (ms_step * 1e-3) / 1e9},
         "roofline": {"kernel": "hga_attend (split + merge kernels)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": attend_traffic(),
                      "bytes_per_launch": ab["attend"], "launch_ms": attend_ms,
                      "route_launch_ms": route_ms, "route_bytes_per_launch": ab["route"]},
     }
