@@ -174,8 +174,14 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
  *   out     [B][Hq][lq][d] fp32
  *   lse_opt [B][Hq][lq] fp32 natural-log sum of exp of the logits (nullable);
  *           with hga_merge_partials it joins results over disjoint parts.
- * Decode (lq < 16) runs a VALU wavefront-reduction kernel; lq >= 16 runs the
- * MFMA chunked-prefill kernel. */
+ * Decode (lq < 16) runs a VALU wavefront-reduction kernel; 16 <= lq <= 64
+ * (the query tokens of one chunk; the page's "Experimentele Resultaten" report a fused
+ * prefill speed-up) runs the MFMA chunked-prefill kernel, which needs head_dim 128 and
+ * bf16 (else HGA_ERR_UNSUPPORTED).  Query tokens must lie in one chunk:
+ * (q_pos0 % chunk_size) + lq <= chunk_size, checked on the device (NaN
+ * outputs otherwise).  Pool rows after the last query token are never read
+ * into the result, whatever they hold.
+ * Errors: HGA_ERR_UNSUPPORTED for max_sel > 256. */
 hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
                       const int32_t* q_pos0, const void* k_src, const void* v_src,
                       int32_t src_layout, int32_t src_cap, const int32_t* sel_groups,

@@ -193,7 +193,11 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
       !n_sel || max_sel <= 0 || part < HGA_PART_ALL || part > HGA_PART_ROUTED || !out || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
   if (src_layout == HGA_SRC_POOL && src_cap <= 0) return HGA_ERR_INVALID_ARGUMENT;
-  if (lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;
+  // 16..64 query tokens run the MFMA prefill kernel: head_dim 128, bf16 (it
+  // takes K/V as bf16 operands unrounded; an fp32 pool would need a
+  // three-product split)
+  if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
+    return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits) return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);

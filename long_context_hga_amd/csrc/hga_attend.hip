@@ -23,30 +23,18 @@
 //   Other shapes: every lane all-reduces the Hg dots over its row.
 //   The running maximum is updated once per group (4 tokens per lane) and
 //   the accumulators are rescaled only when it moved.  The split's state
-//   merges through LDS into one partial (m, l, o) per head; the last split
-//   of a (sequence, KV head, query token) to finish merges all partials
-//   exactly (log-sum-exp) and writes fp32 output.
+//   merges through LDS into one partial (m, l, o) per head; a second kernel
+//   merges the partials of all splits of a (sequence, KV head, query token)
+//   exactly (log-sum-exp) and writes fp32 output.  Token rows after the
+//   query position are masked, and their V (possibly never written) is
+//   replaced by zeros before it meets a zero probability.
 // The query rotation uses an fp64 angle and sincos (one per pair, shared
 // through LDS), so the result does not depend on position magnitude.
-#include "hga_internal.h"
+#include "hga_attend_common.h"
 
 namespace hga {
 
-constexpr int kSplitGroups = 8;   // selected groups per workgroup
 constexpr int kWaveGroups = 2;    // groups per wave
-constexpr int kMaxSplits = 32;    // splits per (unit, query token): max_sel <= 256
-
-struct AttendArgs {
-  KCfg cfg;
-  AttendLaunch a;
-  int n_splits;
-};
-
-// Partial of one split: m[HG], l[HG], padding to a 16-byte boundary, o[HG][D].
-template <int HG>
-__host__ __device__ constexpr int part_head() { return (2 * HG + 3) / 4 * 4; }
-template <int D, int HG>
-__host__ __device__ constexpr int part_floats() { return part_head<HG>() + HG * D; }
 
 template <int D, int HG>
 struct AttendShared {
@@ -90,18 +78,6 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* f) {
   }
 }
 
-// Virtual group index v of a part -> slot of the unit's selected list.
-__device__ __forceinline__ int part_slot(int part, const ListParts& lp, int v) {
-  if (part == HGA_PART_ROUTED) return lp.n_head + v;
-  if (part == HGA_PART_WINDOWS) return v < lp.n_head ? v : v + lp.n_routed;
-  return v;
-}
-__device__ __forceinline__ int part_count(int part, const ListParts& lp, int n_sel) {
-  if (part == HGA_PART_ROUTED) return lp.n_routed;
-  if (part == HGA_PART_WINDOWS) return lp.n_head + lp.n_tail;
-  return n_sel;
-}
-
 // Reduce-scatter layout (d = 128, Hg = 8): register slot k of a lane whose
 // column index within its 8-lane half-row is i holds head i ^ kSlotMask[k].
 constexpr int kSlotMask[8] = {0, 1, 2, 3, 7, 6, 5, 4};
@@ -119,20 +95,6 @@ __device__ __forceinline__ void gather8(float x, float* p) {
   p[5] = dpp_f<kDppXor1>(p[4]);
   p[6] = dpp_f<kDppXor2>(p[4]);
   p[7] = dpp_f<kDppXor3>(p[4]);
-}
-
-// Sum / max over the 4 token rows of a wave (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float rows_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float rows_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 template <int D, int HG, bool BF16>
@@ -304,6 +266,10 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
           float p8[8], vf[8];
           gather8(pw, p8);
           unpack8<BF16>(vraw[gi * STEPS + st], vf);
+          if (gpos[gi] + st * RPS + row > tau) {  // a row not yet written may hold NaN
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vf[i] = 0.f;
+          }
 #pragma unroll
           for (int k = 0; k < 8; ++k)
 #pragma unroll
@@ -390,6 +356,10 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
         for (int st = 0; st < STEPS; ++st) {
           float vf[8];
           unpack8<BF16>(vraw[gi * STEPS + st], vf);
+          if (gpos[gi] + st * RPS + row > tau) {  // a row not yet written may hold NaN
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vf[i] = 0.f;
+          }
 #pragma unroll
           for (int hh = 0; hh < HG; ++hh) {
             const float mref = m[hh] == -INFINITY ? 0.f : m[hh];
@@ -553,6 +523,22 @@ static void launch_dh(const AttendArgs& x, dim3 grid, hipStream_t st) {
 }
 
 template <int D>
+static void launch_combine_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
+  switch (x.cfg.hg) {
+    case 1: hipLaunchKernelGGL((attend_combine_kernel<D, 1>), grid, dim3(256), 0, st, x); break;
+    case 2: hipLaunchKernelGGL((attend_combine_kernel<D, 2>), grid, dim3(256), 0, st, x); break;
+    case 4: hipLaunchKernelGGL((attend_combine_kernel<D, 4>), grid, dim3(256), 0, st, x); break;
+    default: hipLaunchKernelGGL((attend_combine_kernel<D, 8>), grid, dim3(256), 0, st, x); break;
+  }
+}
+
+static void launch_combine(const AttendArgs& x, hipStream_t st) {
+  const dim3 grid(x.a.B * x.cfg.hkv * x.a.lq);
+  if (x.cfg.d == 128) launch_combine_d<128>(x, grid, st);
+  else launch_combine_d<64>(x, grid, st);
+}
+
+template <int D>
 static void launch_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
   switch (x.cfg.hg) {
     case 1: launch_dh<D, 1>(x, grid, st); break;
@@ -567,6 +553,11 @@ hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st)
   x.cfg = cfg;
   x.a = a;
   x.n_splits = (a.max_sel + kSplitGroups - 1) / kSplitGroups;
+  if (a.lq >= kPrefillMinLq) {
+    launch_prefill(x, st);
+    launch_combine(x, st);
+    return hipGetLastError();
+  }
   dim3 grid(x.n_splits, cfg.hkv, a.B * a.lq);
   if (cfg.d == 128) launch_d<128>(x, grid, st);
   else launch_d<64>(x, grid, st);

@@ -1,0 +1,56 @@
+// Declarations shared by the decode and the chunked-prefill attention
+// kernels: split geometry, the per-split partial layout that the merge kernel
+// reads, list-part helpers and cross-row reductions.
+#pragma once
+
+#include "hga_internal.h"
+
+namespace hga {
+
+constexpr int kSplitGroups = 8;   // selected groups per workgroup
+constexpr int kMaxSplits = 32;    // splits per (unit, query token): max_sel <= 256
+constexpr int kPrefillMinLq = 16; // query tokens from which the MFMA prefill kernel runs
+
+struct AttendArgs {
+  KCfg cfg;
+  AttendLaunch a;
+  int n_splits;
+};
+
+// Partial of one split: m[HG], l[HG], padding to a 16-byte boundary, o[HG][D].
+template <int HG>
+__host__ __device__ constexpr int part_head() { return (2 * HG + 3) / 4 * 4; }
+template <int D, int HG>
+__host__ __device__ constexpr int part_floats() { return part_head<HG>() + HG * D; }
+
+// Virtual group index v of a part -> slot of the unit's selected list.
+__device__ __forceinline__ int part_slot(int part, const ListParts& lp, int v) {
+  if (part == HGA_PART_ROUTED) return lp.n_head + v;
+  if (part == HGA_PART_WINDOWS) return v < lp.n_head ? v : v + lp.n_routed;
+  return v;
+}
+__device__ __forceinline__ int part_count(int part, const ListParts& lp, int n_sel) {
+  if (part == HGA_PART_ROUTED) return lp.n_routed;
+  if (part == HGA_PART_WINDOWS) return lp.n_head + lp.n_tail;
+  return n_sel;
+}
+
+// Sum / max over the 4 token rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Chunked-prefill split kernel (MFMA); the merge kernel of hga_attend.hip
+// combines its partials.
+void launch_prefill(const AttendArgs& x, hipStream_t st);
+
+}  // namespace hga

@@ -108,6 +108,12 @@ def test_attend_rejects():
     assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
     a = list(args); a[13] = None
     assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[3] = 65  # more query tokens than a chunk
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    # 16..64 query tokens (MFMA prefill) need head_dim 128 and bf16
+    for over in (dict(qkv_dtype=hga.HGA_F32), dict(head_dim=64)):
+        a = list(args); a[0] = ctypes.byref(cfg(**over)); a[3] = 32
+        assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
 
 
 def test_gather_and_merge_reject():
