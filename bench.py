@@ -29,6 +29,11 @@ duration, measured with HIP events on the launch stream while a spin kernel
 keeps the queue filled ahead (so host launch latency does not enter).
 ``cpu_baseline`` times the fp64 CPU oracle doing the same step, repeated for
 about 10 s, on this host's cores.
+
+``--workload prefill32k`` runs the chunked-prefill leg instead: one 64-token
+query chunk at 32K context (append + summaries of the chunk, routing with the
+pooled query, MFMA attention), reported as query tokens/s with the attention
+call's achieved TFLOP/s against the bf16 dense MFMA peak.
 """
 from __future__ import annotations
 
@@ -157,6 +162,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--workload", default="decode64k", choices=["decode64k", "prefill32k"],
+                    help="decode64k (default): the batch-8 64K decode step; prefill32k: one "
+                         "64-token query chunk at 32K context (MFMA attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
@@ -165,11 +173,16 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
               "per-GPU and this build has no multi-GPU leg", file=sys.stderr)
         sys.exit(2)
-
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.workload == "prefill32k":
+        run_prefill32k(args)
+    else:
+        run_decode64k(args)
 
+
+def run_decode64k(args):
     import numpy as np
     import torch
 
@@ -304,6 +317,203 @@ def main():
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, p)
     print(json.dumps(out), flush=True)
+
+
+def prefill_algorithmic(p):
+    """Algorithmic flops and bytes of attending one query chunk (lq = C
+    tokens of chunk c_q) over its selected set, per the method: QK^T and PV
+    over the visible keys (all window and routed keys; current-chunk keys
+    up to each token)."""
+    d, hq, hkv = p["head_dim"], p["n_q_heads"], p["n_kv_heads"]
+    C, G = p["chunk_size"], p["groups_per_chunk"]
+    g = C // G
+    n_sel = (p["n_sink_chunks"] + p["n_local_chunks"] + 1) * G + p["topk_groups"]
+    prior = (n_sel - G) * g              # keys before the query chunk
+    visits = C * prior + C * (C + 1) // 2  # (query, key) pairs per head
+    flops = hq * visits * d * 2 * 2
+    kv = hkv * n_sel * g * d * 2 * 2
+    q = hq * C * d * 2
+    o = hq * C * d * 4
+    return dict(flops=flops, attend_bytes=kv + q + o + hkv * n_sel * 4, n_sel=n_sel)
+
+
+def cpu_baseline_prefill(inp, cfg_params, min_seconds=10.0):
+    """The fp64 C oracle doing the prefill step: the query chunk's pool append
+    and summaries, then routing and attention of its 64 tokens, for every KV
+    head, repeated for about min_seconds."""
+    import numpy as np
+    import oracle
+    cfg = oracle.cfg_from(cfg_params)
+    p = cfg_params
+    d, hkv = p["head_dim"], p["n_kv_heads"]
+    hg = p["n_q_heads"] // hkv
+    B, T, lq = inp.k.shape[0], inp.k.shape[2], inp.q.shape[2]
+    pos = int(inp.pos0[0])
+    U = B * hkv
+    cs = np.zeros((U, T // 64, d))
+    gs = np.zeros((U, T // 16, d))
+    kp = np.zeros((U, T, d))
+    vp = np.zeros((U, T, d))
+    kraw = []
+    for b in range(B):
+        for h in range(hkv):
+            u = b * hkv + h
+            kr = inp.f64(inp.k[b, h])
+            a, g = oracle.summaries(cfg, kr[:pos])
+            cs[u, :a.shape[0]] = a
+            gs[u, :g.shape[0]] = g
+            kp[u, :pos] = oracle.pool(cfg, kr[:pos], 0)
+            vp[u] = inp.f64(inp.v[b, h])
+            kraw.append(kr[pos:pos + lq].copy())
+    q = np.stack([inp.f64(inp.q[b, h * hg:(h + 1) * hg]) for b in range(B) for h in range(hkv)])
+    max_sel = (p["n_sink_chunks"] + p["n_local_chunks"] + 1) * 4 + p["topk_groups"]
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 5 or time.perf_counter() - t_start < min_seconds:
+        t0 = time.perf_counter()
+        for u in range(U):
+            kp[u, pos:pos + lq] = oracle.pool(cfg, kraw[u], pos)
+            cs[u, pos // 64] = oracle.span_summary(cfg, kraw[u], pos)
+            for i in range(4):
+                gs[u, pos // 16 + i] = oracle.span_summary(cfg, kraw[u][16 * i:16 * i + 16], pos + 16 * i)
+        oracle.step(cfg, q, np.full(U, pos), cs, gs, kp, vp, max_sel)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": B * lq / med, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the full prefill step: {hkv} KV heads, append + summaries of the {lq}-token "
+                      f"query chunk at {pos}, route + attend of its {lq} tokens (context {T}); "
+                      f"fp64 C oracle, OpenMP over the {U} units; median of {len(times)} runs "
+                      f"({med * 1e3:.1f} ms each, {time.perf_counter() - t_start:.1f} s total)"}
+
+
+def run_prefill32k(args):
+    import numpy as np
+    import torch
+
+    import gpu_harness as gh
+    import long_context_hga_amd as hga
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    inp = synth.generate("prefill32k")
+    p = inp.params
+    B, T = p["batch"], p["context"]
+    pos = int(inp.pos0[0])
+    lq = inp.q.shape[2]
+    st = gh.build_state(inp)
+    torch.cuda.synchronize()
+    kc = st.k_raw[:, :, pos:pos + lq].contiguous()
+    vc = st.v_raw[:, :, pos:pos + lq].contiguous()
+    R = max(1, args.replicas)
+    reps = []
+    for r in range(R):
+        reps.append(dict(
+            k_pool=st.k_pool if r == 0 else st.k_pool.clone(),
+            v_pool=st.v_pool if r == 0 else st.v_pool.clone(),
+            chunk_sum=st.chunk_sum if r == 0 else st.chunk_sum.clone(),
+            group_sum=st.group_sum if r == 0 else st.group_sum.clone(),
+            q=st.q if r == 0 else st.q.clone(), kc=kc if r == 0 else kc.clone(),
+            vc=vc if r == 0 else vc.clone(), ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, lq)))
+    del st.k_raw, st.v_raw
+    torch.cuda.synchronize()
+    cfg = st.cfg
+
+    def step(r, ev=None):
+        # the query chunk's K/V enter the pool (and its summaries are built),
+        # then its 64 tokens are routed (pooled query) and attended
+        x = reps[r]
+        s = x["s"]
+        hga.hga_build_summaries(cfg, B, x["kc"], x["vc"], pos, lq, x["k_pool"], x["v_pool"], T,
+                                x["chunk_sum"], x["group_sum"], st.max_chunks)
+        if ev is not None:
+            ev[0].record()
+        hga.hga_route(cfg, B, x["q"], lq, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
+                      s.sel, s.n_sel, st.max_sel, None, x["ws"])
+        if ev is not None:
+            ev[1].record()
+        hga.hga_attend(cfg, B, x["q"], lq, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
+                       s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
+        if ev is not None:
+            ev[2].record()
+
+    ms_step, steps_timed = time_graph(step, R, args)
+    route_ms, attend_ms = time_launches(step, R, args)
+    s0 = reps[0]["s"]
+    assert torch.isfinite(s0.out).all().item()
+    alg = prefill_algorithmic(p)
+    achieved = alg["flops"] / (attend_ms * 1e-3) / 1e12
+    out = {
+        "metric": "routed-attention query tokens/s per layer, chunked prefill at 32K ctx; "
+                  "MFMA utilisation",
+        "value": B * lq / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps_timed,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, pre-RoPE, 16 planted needle chunks)",
+        "config": {"workload": "prefill32k: GQA 32q/4kv heads, d=128, bf16, theta 1e6, ctx 32768, "
+                               "query chunk 511 (64 tokens at 32704..32767), 1 sink + 4 local "
+                               "chunks, top-20 chunks, top-40 groups (1024 keys, 3.125%)",
+                   "batch": B, "context": T, "query_tokens": lq, "replicas": R,
+                   "timing": "HIP graph of R steps, replayed"},
+        "roofline": {"kernel": "hga_attend (MFMA prefill split + merge kernels)", "bound": "mfma",
+                     "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": achieved / 2500.0, "traffic": None,
+                     "flops_per_launch": alg["flops"], "launch_ms": attend_ms,
+                     "hbm_bytes_per_launch": alg["attend_bytes"],
+                     "route_launch_ms": route_ms},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_prefill(inp, p)
+    print(json.dumps(out), flush=True)
+
+
+def time_graph(step, R, args):
+    """Mean step time (ms) over graph replays of R consecutive steps."""
+    import torch
+    for i in range(max(args.warmup, R)):
+        step(i % R)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(r)
+    for _ in range(max(1, args.warmup // R)):
+        g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, args.steps // R)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(n_rep):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (n_rep * R), n_rep * R
+
+
+def time_launches(step, R, args):
+    """Mean durations (ms) of the route and attend calls: events on the launch
+    stream around each call, with the queue filled ahead by a spin kernel so
+    host launch latency does not enter."""
+    import numpy as np
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda._sleep(int(2e8))
+    for i in range(args.steps):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attend_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    return route_ms, attend_ms
 
 
 if __name__ == "__main__":
