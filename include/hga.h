@@ -92,7 +92,8 @@ hga_status hga_validate(const hga_config* cfg);
  * tokens: (n_sink + n_local + 1) * G + topk_groups. */
 hga_status hga_max_selected(const hga_config* cfg, int32_t max_lq, int32_t* max_sel);
 
-/* Bytes of device workspace needed by hga_route and hga_attend for batch B,
+/* Bytes of device workspace needed by hga_route, hga_attend and
+ * hga_attend_tiered for batch B,
  * contexts up to max_ctx tokens and up to max_lq query tokens per call.  The
  * workspace carries nothing from one call to the next (route keeps its
  * scores there between its two kernels, attend its per-split partials), so
@@ -110,8 +111,9 @@ hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream);
  *          pos0 .. pos0+n_tok-1, qkv_dtype
  *   v_new  [B][Hkv][n_tok][d] values of those positions (may be NULL when
  *          k_pool is NULL)
- *   k_pool, v_pool  [B][Hkv][pool_cap][d] qkv_dtype.  If non-NULL, row p of
- *          k_pool receives RoPE(k_raw, p) rounded once to qkv_dtype
+ *   k_pool, v_pool  [B][Hkv][pool_cap][d] qkv_dtype, device memory or pinned
+ *          host memory (written over PCIe).  If non-NULL, row p of k_pool
+ *          receives RoPE(k_raw, p) rounded once to qkv_dtype
  *          (round-to-nearest-even), and row p of v_pool receives v unchanged.
  *          NULL skips the append.
  *   chunk_sum [B][Hkv][max_chunks][d] fp32, group_sum [B][Hkv][max_chunks*G][d]
@@ -187,6 +189,37 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
                       int32_t src_layout, int32_t src_cap, const int32_t* sel_groups,
                       const int32_t* n_sel, int32_t max_sel, int32_t part, float* out,
                       float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-tier attention (page section "Geheugenarchitectuur": summaries and the
+ * always-visible windows are hot in device memory, the full token K/V history
+ * is cold in host RAM).  For the list written by hga_route:
+ *   stream_b: the routed groups are copied from the pinned host pool over PCIe
+ *             into the working set (hga_gather, HGA_PART_ROUTED) and attended
+ *             there (hga_attend, HGA_PART_ROUTED, HGA_SRC_WORKING_SET);
+ *   stream_a: meanwhile the window groups are attended from the device pool
+ *             (HGA_PART_WINDOWS, HGA_SRC_POOL); then stream_a waits for
+ *             stream_b and merges the two parts exactly (log-sum-exp).
+ * The result equals hga_attend over the whole list (up to fp32 rounding of
+ * the merge).  Stream b starts after the work already queued on stream a;
+ * when the call returns, out / lse_opt are complete in stream a's order.
+ *   k_hot, v_hot   [B][Hkv][hot_cap][d] device pool; only the rows of the
+ *                  window groups (sink, local, current chunk up to the last
+ *                  query token) are read
+ *   k_cold, v_cold [B][Hkv][cold_cap][d] pinned host memory (the full pool)
+ *   k_ws, v_ws     [B][Hkv][max_sel*16][d] device working set (routed slots
+ *                  are overwritten)
+ *   out, lse_opt   as hga_attend
+ *   ws             hga_workspace_bytes() of workspace (this call needs room
+ *                  for two attention partial sets and two part results)
+ * The call creates and releases two HIP events (no memory).
+ * Errors: as hga_attend; HGA_ERR_INVALID_ARGUMENT if the cold pool is not
+ * pinned host memory. */
+hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                             const int32_t* q_pos0, const void* k_hot, const void* v_hot,
+                             int32_t hot_cap, const void* k_cold, const void* v_cold,
+                             int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
+                             int32_t max_sel, void* k_ws, void* v_ws, float* out, float* lse_opt,
+                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b);
 
 /* Exact merge of two attention results over disjoint token sets:
  * out = (e^{lse_a} out_a + e^{lse_b} out_b) / (e^{lse_a} + e^{lse_b}),

@@ -31,8 +31,8 @@ HGA_PART_WINDOWS = 1
 HGA_PART_ROUTED = 2
 
 EXPORTED = ("hga_validate", "hga_max_selected", "hga_workspace_bytes", "hga_workspace_reset",
-            "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_merge_partials",
-            "hga_status_string", "hga_version")
+            "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_attend_tiered",
+            "hga_merge_partials", "hga_status_string", "hga_version")
 
 
 class HgaError(RuntimeError):
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "hga_gather": [_C, _I, _P, _P, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P],
             "hga_attend": [_C, _I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P,
                            ctypes.c_size_t, _P],
+            "hga_attend_tiered": [_C, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P,
+                                  _P, _P, _P, ctypes.c_size_t, _P, _P],
             "hga_merge_partials": [_C, _I, _I, _P, _P, _P, _P, _P, _P, _P],
         }
         for name, args in sig.items():
@@ -199,6 +201,22 @@ def hga_attend(cfg, B, q_raw, lq, q_pos0, k_src, v_src, src_layout, src_cap, sel
                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                             _stream(stream)),
            "hga_attend")
+
+
+def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, v_cold, cold_cap,
+                      sel_groups, n_sel, max_sel, k_ws, v_ws, out, lse_opt, ws, stream_a=None,
+                      stream_b=None):
+    """Windows from the device pool on stream_a, routed groups copied from the
+    pinned host pool and attended on stream_b, merged on stream_a.  stream_a
+    defaults to the current stream; stream_b must be another stream."""
+    if stream_b is None:
+        raise ValueError("hga_attend_tiered needs a second stream (stream_b)")
+    _check(lib().hga_attend_tiered(_cfg(cfg), B, _ptr(q_raw), lq, _ptr(q_pos0), _ptr(k_hot),
+                                   _ptr(v_hot), hot_cap, _ptr(k_cold), _ptr(v_cold), cold_cap,
+                                   _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(k_ws), _ptr(v_ws),
+                                   _ptr(out), _ptr(lse_opt), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream_a), _stream(stream_b)),
+           "hga_attend_tiered")
 
 
 def hga_merge_partials(cfg, B, lq, out_a, lse_a, out_b, lse_b, out, lse_out=None, stream=None):

@@ -58,6 +58,35 @@ hga_status hip_status(hipError_t e) { return e == hipSuccess ? HGA_OK : HGA_ERR_
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Device address of pinned host memory (hipHostMalloc / pinned allocations);
+// false if p is not pinned host memory.
+bool pinned_device_ptr(const void* p, const void** dev) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type != hipMemoryTypeHost || !at.devicePointer) return false;
+  *dev = at.devicePointer;
+  return true;
+}
+
+// Workspace of hga_attend_tiered: the partials of its two attention calls
+// and their two (out, lse) results.
+struct TieredWs {
+  size_t part_bytes, res_floats;
+};
+TieredWs tiered_ws(const KCfg& k, int B, int lq, int max_sel) {
+  TieredWs t;
+  t.part_bytes = round_up(attend_ws_bytes(k, B, lq, max_sel), 256);
+  t.res_floats = round_up((size_t)B * k.hq * lq * (k.d + 1), 64);
+  return t;
+}
+size_t tiered_ws_bytes(const KCfg& k, int B, int lq, int max_sel) {
+  const TieredWs t = tiered_ws(k, B, lq, max_sel);
+  return 2 * t.part_bytes + 2 * t.res_floats * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,7 +110,7 @@ hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx
   const KCfg k = make_kcfg(cfg);
   const int max_chunks = (max_ctx + kChunk - 1) / kChunk;
   const size_t r = route_ws_bytes(k, B, max_chunks);
-  const size_t a = attend_ws_bytes(k, B, max_lq, max_selected(cfg));
+  const size_t a = tiered_ws_bytes(k, B, max_lq, max_selected(cfg));  // >= hga_attend's
   *bytes = round_up(r > a ? r : a, 256);
   return HGA_OK;
 }
@@ -111,6 +140,12 @@ hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_r
   }
   if (!append && !summ) return HGA_OK;
   const KCfg k = make_kcfg(cfg);
+  if (append) {  // a pinned host pool is written through its device mapping
+    const void* kd = nullptr;
+    const void* vd = nullptr;
+    if (pinned_device_ptr(k_pool, &kd)) k_pool = const_cast<void*>(kd);
+    if (pinned_device_ptr(v_pool, &vd)) v_pool = const_cast<void*>(vd);
+  }
   return hip_status(launch_build(k, B, k_raw, v_new, pos0, n_tok, append ? k_pool : nullptr,
                                  append ? v_pool : nullptr, pool_cap, summ ? chunk_sum : nullptr,
                                  summ ? group_sum : nullptr, max_chunks, (hipStream_t)stream));
@@ -161,21 +196,8 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
     return HGA_ERR_INVALID_ARGUMENT;
   const void* kp = k_pool;
   const void* vp = v_pool;
-  if (pool_is_host) {
-    const void* src[2] = {k_pool, v_pool};
-    const void* dev[2] = {nullptr, nullptr};
-    for (int i = 0; i < 2; ++i) {
-      hipPointerAttribute_t at;
-      if (hipPointerGetAttributes(&at, src[i]) != hipSuccess) {
-        (void)hipGetLastError();
-        return HGA_ERR_INVALID_ARGUMENT;
-      }
-      if (at.type != hipMemoryTypeHost || !at.devicePointer) return HGA_ERR_INVALID_ARGUMENT;
-      dev[i] = at.devicePointer;
-    }
-    kp = dev[0];
-    vp = dev[1];
-  }
+  if (pool_is_host && (!pinned_device_ptr(k_pool, &kp) || !pinned_device_ptr(v_pool, &vp)))
+    return HGA_ERR_INVALID_ARGUMENT;
   const KCfg k = make_kcfg(cfg);
   return hip_status(launch_gather(k, B, kp, vp, pool_cap, sel_groups, n_sel, max_sel, q_pos0, part,
                                   k_ws, v_ws, (hipStream_t)stream));
@@ -219,6 +241,94 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   a.max_sel = max_sel;
   a.part_sel = part;
   return hip_status(launch_attend(k, a, (hipStream_t)stream));
+}
+
+hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                             const int32_t* q_pos0, const void* k_hot, const void* v_hot,
+                             int32_t hot_cap, const void* k_cold, const void* v_cold,
+                             int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
+                             int32_t max_sel, void* k_ws, void* v_ws, float* out, float* lse_opt,
+                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
+      hot_cap <= 0 || !k_cold || !v_cold || cold_cap <= 0 || !sel_groups || !n_sel ||
+      max_sel <= 0 || !k_ws || !v_ws || !out || !ws)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
+    return HGA_ERR_UNSUPPORTED;
+  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits) return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  if (ws_bytes < tiered_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  const void* kc = nullptr;
+  const void* vc = nullptr;
+  if (!pinned_device_ptr(k_cold, &kc) || !pinned_device_ptr(v_cold, &vc))
+    return HGA_ERR_INVALID_ARGUMENT;
+  const TieredWs t = tiered_ws(k, B, lq, max_sel);
+  char* w = static_cast<char*>(ws);
+  float* part_a = reinterpret_cast<float*>(w);
+  float* part_b = reinterpret_cast<float*>(w + t.part_bytes);
+  float* res = reinterpret_cast<float*>(w + 2 * t.part_bytes);
+  const size_t n_out = (size_t)B * k.hq * lq * k.d;
+  float* oa = res;
+  float* la = oa + n_out;
+  float* ob = res + t.res_floats;
+  float* lb = ob + n_out;
+  hipStream_t sa = static_cast<hipStream_t>(stream_a);
+  hipStream_t sb = static_cast<hipStream_t>(stream_b);
+
+  AttendLaunch a;
+  a.q = q_raw;
+  a.q_pos0 = q_pos0;
+  a.sel = sel_groups;
+  a.n_sel = n_sel;
+  a.B = B;
+  a.lq = lq;
+  a.max_sel = max_sel;
+  AttendLaunch ah = a, ac = a;
+  ah.k = k_hot;
+  ah.v = v_hot;
+  ah.src_layout = HGA_SRC_POOL;
+  ah.src_cap = hot_cap;
+  ah.part_sel = HGA_PART_WINDOWS;
+  ah.out = oa;
+  ah.lse = la;
+  ah.part = part_a;
+  ac.k = k_ws;
+  ac.v = v_ws;
+  ac.src_layout = HGA_SRC_WORKING_SET;
+  ac.src_cap = max_sel * kGroupTokens;
+  ac.part_sel = HGA_PART_ROUTED;
+  ac.out = ob;
+  ac.lse = lb;
+  ac.part = part_b;
+
+  // fork: stream b starts after everything already queued on stream a (the
+  // list written by hga_route); join: the merge on stream a waits for b
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return HGA_ERR_HIP;
+  if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipEventDestroy(fork);
+    return HGA_ERR_HIP;
+  }
+  // The window attention is queued right behind the fork, ahead of the
+  // transfer, so its workgroups take their CUs while the copy kernel (whose
+  // waves mostly wait on PCIe) fills the rest.
+  hipError_t e = hipEventRecord(fork, sa);
+  if (e == hipSuccess) e = launch_attend(k, ah, sa);
+  if (e == hipSuccess) e = hipStreamWaitEvent(sb, fork, 0);
+  if (e == hipSuccess)
+    e = launch_gather(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0, HGA_PART_ROUTED,
+                      k_ws, v_ws, sb);
+  if (e == hipSuccess) e = launch_attend(k, ac, sb);
+  if (e == hipSuccess) e = hipEventRecord(join, sb);
+  if (e == hipSuccess) e = hipStreamWaitEvent(sa, join, 0);
+  if (e == hipSuccess) e = launch_merge(B, k.hq, lq, k.d, oa, la, ob, lb, out, lse_opt, sa);
+  // the events are released once the work that references them completes
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  return hip_status(e);
 }
 
 hga_status hga_merge_partials(const hga_config* cfg, int32_t B, int32_t lq, const float* out_a,

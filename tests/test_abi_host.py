@@ -116,6 +116,28 @@ def test_attend_rejects():
         assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
 
 
+def test_attend_tiered_rejects():
+    c = ctypes.byref(cfg())
+    f = hga.lib().hga_attend_tiered
+    args = [c, 4, FAKE, 1, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, 65536, FAKE, FAKE, 128, FAKE, FAKE,
+            FAKE, None, FAKE, 1 << 30, None, None]
+    a = list(args); a[8] = None  # no cold pool
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[14] = None  # no working set
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[19] = 4096
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[13] = 300
+    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
+    a = list(args); a[0] = ctypes.byref(cfg(qkv_dtype=hga.HGA_F32)); a[3] = 32
+    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
+    # hga_workspace_bytes covers the tiered call: with that size the call gets
+    # past the workspace check and rejects the cold pool, which is not pinned
+    n = hga.hga_workspace_bytes(cfg(), 4, 65536, 1)
+    a = list(args); a[19] = n
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+
+
 def test_gather_and_merge_reject():
     c = ctypes.byref(cfg())
     g = hga.lib().hga_gather
