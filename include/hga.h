@@ -106,16 +106,18 @@ hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx
  * it may be captured in a graph. */
 hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream);
 
-/* Pool append and RoPE-aware summaries ("Kernmechanisme" item 3).
+/* Pool append and RoPE-aware summaries ("Kernmechanisme" items 3 and 4).
  *   k_raw  [B][Hkv][n_tok][d] raw (pre-RoPE) projected keys of positions
  *          pos0 .. pos0+n_tok-1, qkv_dtype
  *   v_new  [B][Hkv][n_tok][d] values of those positions (may be NULL when
  *          k_pool is NULL)
- *   k_pool, v_pool  [B][Hkv][pool_cap][d] qkv_dtype, device memory or pinned
- *          host memory (written over PCIe).  If non-NULL, row p of k_pool
- *          receives RoPE(k_raw, p) rounded once to qkv_dtype
- *          (round-to-nearest-even), and row p of v_pool receives v unchanged.
- *          NULL skips the append.
+ *   k_pool  [B][Hkv][pool_cap][d] qkv_dtype: row p receives RoPE(k_raw, p)
+ *          rounded once to qkv_dtype (round-to-nearest-even).
+ *   v_pool  [B][Hkv][pool_cap/16][d][16] qkv_dtype: each 16-token group is
+ *          stored transposed, so token p, dim e sits at
+ *          [(p/16)*d + e]*16 + p%16 of its unit; values unchanged.
+ *          Both pools: device memory or pinned host memory (written over
+ *          PCIe); pool_cap a multiple of 16.  NULL (both) skips the append.
  *   chunk_sum [B][Hkv][max_chunks][d] fp32, group_sum [B][Hkv][max_chunks*G][d]
  *          fp32.  For every chunk that lies entirely inside the range, its
  *          chunk summary and its G group summaries are written: for pair j,
@@ -153,10 +155,12 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
                      double* chunk_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
 /* Gather of the selected token K/V into a compact working set.
- *   k_pool, v_pool [B][Hkv][pool_cap][d]: device memory, or pinned host memory
- *           (pool_is_host = 1, read directly over PCIe).
- *   k_ws, v_ws [B][Hkv][max_sel*16][d]: list slot s of unit (b, h) receives
- *           the 16 rows of group sel_groups[b][h][s].  Bit-exact copy.
+ *   k_pool, v_pool as written by hga_build_summaries (pool_cap a multiple of
+ *           16): device memory, or pinned host memory (pool_is_host = 1, read
+ *           directly over PCIe).
+ *   k_ws, v_ws [B][Hkv][max_sel*16][d] elements: list slot s of unit (b, h)
+ *           receives the 16*d block of group sel_groups[b][h][s] (K rows;
+ *           V in the pool's transposed group layout).  Bit-exact copy.
  *   part    HGA_PART_ALL copies every slot; HGA_PART_ROUTED only the routed
  *           slots; HGA_PART_WINDOWS only the window slots (q_pos0 tells them
  *           apart; it may be NULL for HGA_PART_ALL).
@@ -171,15 +175,17 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
  * head h (KV head h / (Hq/Hkv)) and query token tau,
  *   out = sum_p softmax_p(RoPE(q, tau) . K[p] / sqrt(d)) V[p]
  * over the tokens p <= tau of the selected groups (restricted to `part`).
- *   k_src, v_src  the rotated pool (HGA_SRC_POOL, src_cap rows per unit) or
- *           a working set from hga_gather (HGA_SRC_WORKING_SET, max_sel*16 rows)
+ *   k_src, v_src  the pool written by hga_build_summaries (HGA_SRC_POOL,
+ *           src_cap tokens per unit, a multiple of 16) or a working set from
+ *           hga_gather (HGA_SRC_WORKING_SET, max_sel*16 tokens)
  *   out     [B][Hq][lq][d] fp32
  *   lse_opt [B][Hq][lq] fp32 natural-log sum of exp of the logits (nullable);
  *           with hga_merge_partials it joins results over disjoint parts.
- * Decode (lq < 16) runs a VALU wavefront-reduction kernel; 16 <= lq <= 64
- * (the query tokens of one chunk; the page's "Experimentele Resultaten" report a fused
- * prefill speed-up) runs the MFMA chunked-prefill kernel, which needs head_dim 128 and
- * bf16 (else HGA_ERR_UNSUPPORTED).  Query tokens must lie in one chunk:
+ * Both shapes contract on the matrix cores: decode (lq < 16) takes the Hg
+ * query heads of a KV head as the columns of one MFMA block; 16 <= lq <= 64
+ * (the query tokens of one chunk; the page's "Experimentele Resultaten"
+ * report a fused prefill speed-up) runs the chunked-prefill kernel, which
+ * needs head_dim 128 and bf16 (else HGA_ERR_UNSUPPORTED).  Query tokens must lie in one chunk:
  * (q_pos0 % chunk_size) + lq <= chunk_size, checked on the device (NaN
  * outputs otherwise).  Pool rows after the last query token are never read
  * into the result, whatever they hold.

@@ -129,7 +129,8 @@ hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_r
   if (B <= 0 || !k_raw || pos0 < 0 || n_tok <= 0) return HGA_ERR_INVALID_ARGUMENT;
   const bool append = k_pool || v_pool;
   const bool summ = chunk_sum || group_sum;
-  if (append && (!k_pool || !v_pool || !v_new || pool_cap <= 0)) return HGA_ERR_INVALID_ARGUMENT;
+  if (append && (!k_pool || !v_pool || !v_new || pool_cap <= 0 || pool_cap % kGroupTokens != 0))
+    return HGA_ERR_INVALID_ARGUMENT;
   if (summ && (!chunk_sum || !group_sum || max_chunks <= 0)) return HGA_ERR_INVALID_ARGUMENT;
   const int64_t end = (int64_t)pos0 + n_tok;
   if (end > INT32_MAX) return HGA_ERR_OUT_OF_RANGE;
@@ -190,7 +191,8 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
                       void* k_ws, void* v_ws, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (B <= 0 || !k_pool || !v_pool || pool_cap <= 0 || !sel_groups || !n_sel || max_sel <= 0 ||
+  if (B <= 0 || !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 ||
+      !sel_groups || !n_sel || max_sel <= 0 ||
       !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
       (part != HGA_PART_ALL && !q_pos0))
     return HGA_ERR_INVALID_ARGUMENT;
@@ -214,7 +216,8 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
       (src_layout != HGA_SRC_POOL && src_layout != HGA_SRC_WORKING_SET) || !sel_groups ||
       !n_sel || max_sel <= 0 || part < HGA_PART_ALL || part > HGA_PART_ROUTED || !out || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
-  if (src_layout == HGA_SRC_POOL && src_cap <= 0) return HGA_ERR_INVALID_ARGUMENT;
+  if (src_layout == HGA_SRC_POOL && (src_cap <= 0 || src_cap % kGroupTokens != 0))
+    return HGA_ERR_INVALID_ARGUMENT;
   // 16..64 query tokens run the MFMA prefill kernel: head_dim 128, bf16 (it
   // takes K/V as bf16 operands unrounded; an fp32 pool would need a
   // three-product split)
@@ -252,7 +255,8 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
   if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
-      hot_cap <= 0 || !k_cold || !v_cold || cold_cap <= 0 || !sel_groups || !n_sel ||
+      hot_cap <= 0 || hot_cap % kGroupTokens != 0 || !k_cold || !v_cold || cold_cap <= 0 ||
+      cold_cap % kGroupTokens != 0 || !sel_groups || !n_sel ||
       max_sel <= 0 || !k_ws || !v_ws || !out || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))

@@ -49,8 +49,21 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Chunked-prefill split kernel (MFMA); the merge kernel of hga_attend.hip
-// combines its partials.
-void launch_prefill(const AttendArgs& x, hipStream_t st);
+// Matrix-core operand types (v_mfma_f32_16x16x32_bf16).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The bf16 elements of x whose bit in keep (bit i = element i) is clear
+// become +0.
+__device__ __forceinline__ uint4 keep_bf16(uint4 x, uint32_t keep) {
+  auto m = [&](int i) {
+    return ((keep >> (2 * i)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * i + 1)) & 1u ? 0xFFFF0000u : 0u);
+  };
+  return make_uint4(x.x & m(0), x.y & m(1), x.z & m(2), x.w & m(3));
+}
+
+// Split kernels; the merge kernel of hga_attend.hip combines their partials.
+void launch_decode(const AttendArgs& x, hipStream_t st);   // 1..15 query tokens
+void launch_prefill(const AttendArgs& x, hipStream_t st);  // 16..64 query tokens
 
 }  // namespace hga

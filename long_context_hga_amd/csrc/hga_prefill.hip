@@ -28,7 +28,8 @@
 // the products carry about 2^-17 relative error before fp32 accumulation.
 //
 // LDS (64 KiB): the split's K rows, 16-byte chunks XOR-swizzled by key, and
-// V^T rows of 128 keys, 8-byte units XOR-swizzled by dim, so neither the
+// V^T rows of 128 keys (copied from the pool's transposed group blocks),
+// 8-byte units XOR-swizzled by dim, so neither the
 // staging writes nor the operand reads conflict on banks.  The query needs no
 // staging: each lane's QK^T operand holds both halves of its RoPE pairs.
 //
@@ -38,9 +39,6 @@
 #include "hga_attend_common.h"
 
 namespace hga {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSplitKeys = kSplitGroups * kGroupTokens;    // 128 keys per split
 
@@ -125,24 +123,18 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
   // ---- every K/V load of the split, issued before any is used (clamped
   // addresses for missing groups; their rows are masked or zeroed below)
   //   K: iteration it loads group it, thread = (row tid/16, chunk tid%16)
-  //   V: iteration it loads groups 2it (threads < 128) and 2it+1, thread =
-  //      (key pair (tid%128)%8, chunk (tid%128)/8): rows 2*pair and 2*pair+1
+  //   V: iteration it loads group it's V^T block ([D][16], as the pool stores
+  //      it), thread = (dim tid/2, tokens 8*(tid%2) .. +7)
   uint4 kraw[kSplitGroups];
 #pragma unroll
   for (int it = 0; it < kSplitGroups; ++it)
     kraw[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + gbase[it] +
                                                (size_t)(tid / CH) * D + (tid % CH) * 8);
-  const bool upper = tid >= 128;
-  const int vpg = (tid & 127) & 7, vch = (tid & 127) >> 3;
-  uint4 vraw[kSplitGroups / 2][2];
+  uint4 vraw[kSplitGroups];
 #pragma unroll
-  for (int it = 0; it < kSplitGroups / 2; ++it) {
-    const size_t vb = upper ? gbase[2 * it + 1] : gbase[2 * it];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      vraw[it][e] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + vb +
-                                                    (size_t)(2 * vpg + e) * D + vch * 8);
-  }
+  for (int it = 0; it < kSplitGroups; ++it)
+    vraw[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + gbase[it] +
+                                               (size_t)(tid >> 1) * kGroupTokens + 8 * (tid & 1));
 
   // ---- rotated, pre-scaled query of the lane's row at tau = pos0 + row:
   // the angle tau * omega_j is formed in fp64 as a fraction of a turn and
@@ -195,27 +187,17 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
     *reinterpret_cast<uint4*>(ks + key * D + (ch ^ (key % CH)) * 8) = kraw[it];
   }
   {
+    const int dim = tid >> 1, hf = tid & 1;
 #pragma unroll
-    for (int it = 0; it < kSplitGroups / 2; ++it) {
-      const int gp = upper ? gpos[2 * it + 1] : gpos[2 * it];
-      const int vp = (2 * it + (upper ? 1 : 0)) * (kGroupTokens / 2) + vpg;  // pair index in the split
-      const int p_first = gp + 2 * vpg;
-      const bool ok0 = gp >= 0 && p_first <= pos_last;
-      const bool ok1 = gp >= 0 && p_first + 1 <= pos_last;
-      const int ch = vch;
-      uint4 e0 = vraw[it][0], e1 = vraw[it][1];
-      if (!ok0) e0 = make_uint4(0u, 0u, 0u, 0u);
-      if (!ok1) e1 = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t w0[4] = {e0.x, e0.y, e0.z, e0.w};
-      const uint32_t w1[4] = {e1.x, e1.y, e1.z, e1.w};
+    for (int it = 0; it < kSplitGroups; ++it) {
+      const int gp = gpos[it];
+      uint32_t keep = 0u;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = (i & 1) ? (w0[i >> 1] >> 16) : (w0[i >> 1] & 0xFFFFu);
-        const uint32_t hi = (i & 1) ? (w1[i >> 1] & 0xFFFF0000u) : (w1[i >> 1] << 16);
-        const int r = ch * 8 + i;
-        const int unit8 = (vp >> 1) ^ (r & 31);
-        *reinterpret_cast<uint32_t*>(vt + r * kSplitKeys + unit8 * 4 + (vp & 1) * 2) = lo | hi;
-      }
+      for (int i = 0; i < 8; ++i) keep |= (gp >= 0 && gp + 8 * hf + i <= pos_last) ? (1u << i) : 0u;
+      const uint4 x = keep_bf16(vraw[it], keep);
+      const int u0 = 4 * it + 2 * hf;  // 8-byte unit of key 16*it + 8*hf
+      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + ((u0 ^ (dim & 31)) * 4)) = make_uint2(x.x, x.y);
+      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + (((u0 + 1) ^ (dim & 31)) * 4)) = make_uint2(x.z, x.w);
     }
   }
   __syncthreads();

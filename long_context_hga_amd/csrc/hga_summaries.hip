@@ -5,7 +5,9 @@
 // are rotated per token and then averaged, low-frequency pairs are averaged
 // raw and then rotated to the span's representative position (taken as the
 // midpoint a + (n-1)/2).  Item 4: the pool keeps the exact token keys, here
-// stored already rotated and rounded once to the pool dtype.
+// stored already rotated and rounded once to the pool dtype, and the exact
+// values, stored per 16-token group as a transposed [d][16] block (the layout
+// in which the attention kernels feed V to the matrix cores).
 //
 // One workgroup per (chunk overlapping the range, KV head, sequence).  256
 // threads = P pairs x S token slices (P = d/2).  Each thread loads its pair
@@ -100,8 +102,10 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
           kp[prow + j] = (float)ra;
           kp[prow + j + P] = (float)rb;
         }
-        vp[prow + j] = ya[i];
-        vp[prow + j + P] = yb[i];
+        // V: each 16-token group is stored transposed, a [D][16] block
+        const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
+        vp[vcol + (size_t)j * kGroupTokens] = ya[i];
+        vp[vcol + (size_t)(j + P) * kGroupTokens] = yb[i];
       }
       if (hf) {
         sa += ra;

@@ -123,6 +123,19 @@ def attend(st: State, q: torch.Tensor, lq: int, pos0: torch.Tensor, s: Step,
                    st.ws)
 
 
+def v_token_view(v_pool: torch.Tensor) -> torch.Tensor:
+    """View [B][H][T/16][16][d] of a V pool, whose 16-token groups are stored
+    transposed ([d][16] blocks): element [b, h, g, t, e] is token 16g+t, dim e."""
+    B, H, T, d = v_pool.shape
+    return v_pool.view(B, H, T // 16, d, 16).transpose(3, 4)
+
+
+def v_rows(v_pool: torch.Tensor) -> np.ndarray:
+    """A V pool as token rows [B][H][T][d] (host copy)."""
+    B, H, T, d = v_pool.shape
+    return v_token_view(v_pool).cpu().numpy().reshape(B, H, T, d)
+
+
 def query_slice(st: State, i: int) -> torch.Tensor:
     """Query token i of every head as its own lq=1 query [B][Hq][1][d]."""
     return st.q[:, :, i:i + 1, :].contiguous()

@@ -54,7 +54,7 @@ def test_build_summaries_parity(name, B, T):
     cfg = ora_cfg(inp)
     bf16 = inp.is_bf16
     kp = f64_pool(st.k_pool, bf16)
-    vp = st.v_pool.cpu().numpy()
+    vp = gh.v_rows(st.v_pool)
     cs = st.chunk_sum.cpu().numpy()
     gs = st.group_sum.cpu().numpy()
     uc = UnitCache(inp, cfg)

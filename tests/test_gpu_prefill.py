@@ -157,7 +157,10 @@ def test_unwritten_rows_after_the_query_are_ignored():
     pos, lq = 30 * 64 + 3, 20
     nan_bits = torch.tensor([0x7FC0], dtype=torch.int32).to(torch.int16).item()
     st.k_pool[:, :, pos + lq:] = nan_bits
-    st.v_pool[:, :, pos + lq:] = nan_bits
+    vt = gh.v_token_view(st.v_pool)  # V groups are stored transposed
+    p1 = pos + lq
+    vt[:, :, p1 // 16, p1 % 16:] = nan_bits
+    vt[:, :, p1 // 16 + 1:] = nan_bits
     run_prefill(inp, st, pos, lq, check_sel=False, uc=uc)
     # decode: token 5 of the query chunk at position pos + 7
     p1 = pos + 7
@@ -203,3 +206,14 @@ def test_prefill_determinism_bitwise():
         res.append((s.out.clone(), s.lse.clone()))
     for r in res[1:]:
         assert torch.equal(r[0], res[0][0]) and torch.equal(r[1], res[0][1])
+
+
+@pytest.mark.parametrize("chunk,off,lq", [(63, 62, 2), (40, 5, 3), (33, 57, 7), (20, 0, 15),
+                                          (0, 1, 15), (2, 49, 15)])
+def test_multi_token_decode(chunk, off, lq):
+    """2..15 query tokens of one chunk (several 16-row column blocks of
+    (head, token) rows on the decode kernel) against the oracle."""
+    inp = synth.generate("prefill32k", batch=2, context=4096)
+    st = gh.build_state(inp)
+    say(f"[multi-token decode] pos {chunk * 64 + off} lq {lq}")
+    run_prefill(inp, st, chunk * 64 + off, lq)

@@ -78,7 +78,7 @@ def test_tiered_reads_only_window_rows_of_the_device_pool():
     nan_bits = torch.tensor([0x7FC0], dtype=torch.int32).to(torch.int16).item()
     lo, hi = 64 * 1, 64 * (ct - 4)  # between the sink chunk and the local window
     st.k_pool[:, :, lo:hi] = nan_bits
-    st.v_pool[:, :, lo:hi] = nan_bits
+    gh.v_token_view(st.v_pool)[:, :, lo // 16:hi // 16] = nan_bits
     kw = torch.zeros((1, 4, st.max_sel * 16, 128), dtype=st.k_pool.dtype, device="cuda")
     vw = torch.zeros_like(kw)
     out = torch.full_like(out0, float("nan"))
