@@ -6,16 +6,15 @@ independent sequences, query at position 65535.  C = 64 tokens per chunk in
 4 groups of 16; 1 sink + 4 local chunks, top-52 chunks then top-104 groups,
 so 2048 of 65536 keys (3.125 %) are attended per (sequence, KV head).
 
-One step = the whole path for the new token of every sequence, on one
-stream:
-  1. hga_build_summaries: the new token at 65535 is rotated into the pool;
-  2. hga_route: pooled query, level-1 scores of 1018 candidate chunks,
-     top-52, level-2 scores of 208 groups, top-104, window merge;
-  3. hga_attend: exact softmax attention over the 128 selected groups with
-     the gather fused into the loads, then the split merge;
-  4. hga_build_summaries: the token completed chunk 1023, whose chunk and
-     group summaries are built from the chunk's 64 raw keys (read by routing
-     from the next step on).
+One step = the whole path for the new token of every sequence, one
+hga_decode_step call on one stream (four launches):
+  - the new token at 65535 is rotated into the pool, its raw key joins the
+    chunk staging rows, and chunk 1023, which it completes, gets its chunk
+    and group summaries (read by routing from the next step on);
+  - routing: pooled query, level-1 scores of 1018 candidate chunks, top-52,
+    level-2 scores of 208 groups, top-104, window merge;
+  - exact softmax attention over the 128 selected groups with the gather
+    fused into the loads, then the split merge.
 Inputs are resident in HBM before timing.  The state (pool, summaries,
 queries) is replicated R times at distinct addresses and the steps cycle
 through the replicas, so the timed traffic comes from HBM and not from the
@@ -24,9 +23,11 @@ consecutive steps.
 
 Prints one JSON line.  ``value`` = decoded query tokens per second per layer
 (B tokens per step).  ``roofline`` covers the dominant kernel (hga_attend's
-split kernel plus its merge): algorithmic bytes per launch / its mean launch
-duration, measured with HIP events on the launch stream while a spin kernel
-keeps the queue filled ahead (so host launch latency does not enter).
+split kernel plus its merge, the same kernels as the step's attention):
+algorithmic bytes per launch / its mean launch duration, measured with HIP
+events around hga_attend calls on the launch stream (the step run through the
+separate entry points) while a spin kernel keeps the queue filled ahead (so
+host launch latency does not enter).
 ``cpu_baseline`` times the fp64 CPU oracle doing the same step, repeated for
 about 10 s, on this host's cores.
 
@@ -207,8 +208,9 @@ def run_decode64k(args):
     pos = int(inp.pos0[0])
     c0 = (pos // 64) * 64
     q = gh.query_slice(st, 0)
-    # raw K/V of the new token, and raw keys of the chunk it completes (kept by
-    # the caller until the chunk's summaries are built)
+    # raw K/V of the new token; raw keys of the chunk it completes (the
+    # staging rows of the fused step, and the chunk input of the separate
+    # summary call)
     kt = st.k_raw[:, :, pos:pos + 1].contiguous()
     vt = st.v_raw[:, :, pos:pos + 1].contiguous()
     kc = st.k_raw[:, :, c0:c0 + 64].contiguous()
@@ -222,30 +224,37 @@ def run_decode64k(args):
             group_sum=st.group_sum if r == 0 else st.group_sum.clone(),
             q=q if r == 0 else q.clone(), kt=kt if r == 0 else kt.clone(),
             vt=vt if r == 0 else vt.clone(), kc=kc if r == 0 else kc.clone(),
-            ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, 1)))
+            stage=kc.clone(), ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, 1)))
     del st.k_raw, st.v_raw
     torch.cuda.synchronize()
     cfg = st.cfg
 
-    def step(r, ev=None):
-        # One stream: the new token's pool append, routing, attention, then
-        # the summaries of the chunk the token completed (needed from the
-        # next step on).  stream=None: the binding enqueues on torch's current
-        # stream (the capture stream inside torch.cuda.graph).
+    def step(r):
+        # The fused decode step (four launches): level-1 scores; selection
+        # with the token's pool append and the completed chunk's summaries
+        # in extra workgroups; attention; split merge.  stream=None: the
+        # binding enqueues on torch's current stream (the capture stream
+        # inside torch.cuda.graph).
+        x = reps[r]
+        s = x["s"]
+        hga.hga_decode_step(cfg, B, x["q"], x["kt"], x["vt"], st.pos0, x["k_pool"], x["v_pool"], T,
+                            x["stage"], x["chunk_sum"], x["group_sum"], st.max_chunks, s.sel,
+                            s.n_sel, st.max_sel, s.out, s.lse, x["ws"])
+
+    def step_parts(r, ev):
+        # The same step through the separate entry points, with events around
+        # the route and attend calls (per-call durations).
         x = reps[r]
         s = x["s"]
         hga.hga_build_summaries(cfg, B, x["kt"], x["vt"], pos, 1, x["k_pool"], x["v_pool"], T,
                                 None, None, st.max_chunks)
-        if ev is not None:
-            ev[0].record()
+        ev[0].record()
         hga.hga_route(cfg, B, x["q"], 1, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
                       s.sel, s.n_sel, st.max_sel, None, x["ws"])
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         hga.hga_attend(cfg, B, x["q"], 1, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
                        s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
-        if ev is not None:
-            ev[2].record()
+        ev[2].record()
         hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
                                 x["group_sum"], st.max_chunks)
 
@@ -282,10 +291,12 @@ def run_decode64k(args):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda._sleep(int(2e8))
     for i in range(args.steps):
-        step(i % R, evs[i])
+        step_parts(i % R, evs[i])
     torch.cuda.synchronize()
     route_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     attend_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    for r, x in enumerate(reps):  # the separate calls give the fused step's bits
+        assert torch.equal(x["s"].out, eager_out[r]), "separate calls differ from the fused step"
     s0 = reps[0]["s"]
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 

@@ -145,7 +145,8 @@ hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_r
  *   sel_groups [B][Hkv][max_sel] int32 receives, in ascending order, the
  *           sink groups, the routed groups, the local groups and the current
  *           chunk's groups up to the last query token; n_sel [B][Hkv] their
- *           count (-1 for an invalid position).
+ *           count (-1 for an invalid position: negative, tokens spanning two
+ *           chunks, or a query chunk at or beyond max_chunks).
  *   chunk_scores_opt [B][Hkv][max_chunks] fp64 (nullable): level-1 score of
  *           every candidate chunk, at its chunk index.
  * Errors: HGA_ERR_OUT_OF_RANGE if max_sel < hga_max_selected(). */
@@ -195,6 +196,36 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
                       int32_t src_layout, int32_t src_cap, const int32_t* sel_groups,
                       const int32_t* n_sel, int32_t max_sel, int32_t part, float* out,
                       float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* One fused decode step: for each sequence b, the query token at position
+ * q_pos0[b] (device) is appended, routed and attended, in four launches
+ * instead of the six of the separate calls:
+ *   1. level-1 scores of every candidate chunk (as hga_route);
+ *   2. level-1 / level-2 selection and the list (as hga_route), and, in extra
+ *      workgroups of the same launch, the token work: its rotated key and its
+ *      value into the pool (bit-identical to hga_build_summaries with
+ *      n_tok = 1), its raw key into the chunk staging rows, and, when the
+ *      token is the last of its chunk, that chunk's summaries (as
+ *      hga_build_summaries over the chunk).  The current chunk is never a
+ *      routing candidate, so this work and the routing do not interact;
+ *   3. attention over the list, 4. the split merge (as hga_attend).
+ *   q_raw       [B][Hq][1][d] raw query
+ *   k_new, v_new [B][Hkv][d] raw key and value of the token at q_pos0[b]
+ *   k_stage     [B][Hkv][chunk_size][d] qkv_dtype, caller-owned and kept
+ *               across steps: row p % chunk_size holds the raw key of position
+ *               p of the current chunk.  Before the first step of a chunk the
+ *               caller (or the previous steps) must have written the rows of
+ *               the chunk's earlier positions.
+ *   other arguments as hga_build_summaries, hga_route and hga_attend; the
+ *   workspace is shared by the route and attend phases.
+ * A position outside the pool gives n_sel = -1 and NaN outputs and writes
+ * nothing.  Errors: as hga_route and hga_attend. */
+hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, const void* k_new,
+                           const void* v_new, const int32_t* q_pos0, void* k_pool, void* v_pool,
+                           int32_t pool_cap, void* k_stage, float* chunk_sum, float* group_sum,
+                           int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
+                           int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Host-tier attention (page section "Geheugenarchitectuur": summaries and the
  * always-visible windows are hot in device memory, the full token K/V history

@@ -13,6 +13,15 @@ constexpr int kMaxLqDecode = 15;
 constexpr int kMaxListDecode = 256;  // 32 splits of 8 groups
 constexpr int kMaxUnits = 1 << 20;
 constexpr size_t kMaxRouteLds = 60 * 1024;
+constexpr int64_t kMaxGridZ = 65535;
+
+// Third grid dimension of the attention split kernels: B * (16-row column
+// blocks of Hg*lq query rows) for decode, B for prefill.
+int64_t grid_z_of(const hga_config* c, int B, int lq) {
+  if (lq >= 16) return B;
+  const int rows = c->n_q_heads / c->n_kv_heads * lq;
+  return (int64_t)B * ((rows + 15) / 16);
+}
 
 hga_status check_cfg(const hga_config* c) {
   if (!c) return HGA_ERR_INVALID_ARGUMENT;
@@ -224,7 +233,8 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
+    return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (ws_bytes < attend_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   AttendLaunch a;
@@ -246,6 +256,75 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   return hip_status(launch_attend(k, a, (hipStream_t)stream));
 }
 
+hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, const void* k_new,
+                           const void* v_new, const int32_t* q_pos0, void* k_pool, void* v_pool,
+                           int32_t pool_cap, void* k_stage, float* chunk_sum, float* group_sum,
+                           int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
+                           int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !q_raw || !k_new || !v_new || !q_pos0 || !k_pool || !v_pool || pool_cap <= 0 ||
+      pool_cap % kGroupTokens != 0 || !k_stage || !chunk_sum || !group_sum || max_chunks <= 0 ||
+      !sel_groups || !n_sel || !out || !ws)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
+  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads > kMaxUnits || grid_z_of(cfg, B, 1) > kMaxGridZ)
+    return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
+  const size_t need_r = route_ws_bytes(k, B, max_chunks);
+  const size_t need_a = attend_ws_bytes(k, B, 1, max_sel);
+  if (ws_bytes < need_r || ws_bytes < need_a) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  RouteLaunch r;
+  r.q = q_raw;
+  r.q_pos0 = q_pos0;
+  r.chunk_sum = chunk_sum;
+  r.group_sum = group_sum;
+  r.sel = sel_groups;
+  r.n_sel = n_sel;
+  r.chunk_scores = nullptr;
+  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+  r.scores = static_cast<double*>(ws);
+  r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
+  r.B = B;
+  r.lq = 1;
+  r.max_chunks = max_chunks;
+  r.max_sel = max_sel;
+  StepFront f;
+  f.k_new = k_new;
+  f.v_new = v_new;
+  f.k_stage = k_stage;
+  f.k_pool = k_pool;
+  f.v_pool = v_pool;
+  f.pool_cap = pool_cap;
+  f.chunk_sum = chunk_sum;
+  f.group_sum = group_sum;
+  hipError_t e = launch_route(k, r, st, &f);
+  if (e != hipSuccess) return HGA_ERR_HIP;
+
+  AttendLaunch a;
+  a.q = q_raw;
+  a.q_pos0 = q_pos0;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.sel = sel_groups;
+  a.n_sel = n_sel;
+  a.out = out;
+  a.lse = lse_opt;
+  a.part = static_cast<float*>(ws);
+  a.B = B;
+  a.lq = 1;
+  a.src_layout = HGA_SRC_POOL;
+  a.src_cap = pool_cap;
+  a.max_sel = max_sel;
+  a.part_sel = HGA_PART_ALL;
+  return hip_status(launch_attend(k, a, st));
+}
+
 hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
                              const int32_t* q_pos0, const void* k_hot, const void* v_hot,
                              int32_t hot_cap, const void* k_cold, const void* v_cold,
@@ -262,7 +341,8 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
+    return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (ws_bytes < tiered_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   const void* kc = nullptr;

@@ -1,0 +1,156 @@
+// Device body of the pool append and the RoPE-aware chunk/group summaries,
+// shared by hga_build_summaries and the fused decode step.
+//
+// HGA technical summary (gist.science), "Kernmechanisme" item 3: summaries
+// come from the projected keys with no new layers; high-frequency RoPE pairs
+// are rotated per token and then averaged, low-frequency pairs are averaged
+// raw and then rotated to the span's representative position (taken as the
+// midpoint a + (n-1)/2).
+//
+// 256 threads = P pairs x S token slices (P = d/2).  Each thread loads its
+// pair for all tokens of its slice at once, rotates them in fp64, stepping the
+// angle by one fp64 rotation per token from a single sincos, writes the
+// rounded pool rows and keeps fp64 slice sums; the slices combine through LDS
+// into the group and chunk summaries (fp32 stores).
+#pragma once
+
+#include "hga_internal.h"
+
+namespace hga {
+
+// The work of one chunk (start c0) for the tokens [lo, hi) of a unit:
+// rotated keys and values of those tokens into the pool (kp, vp: the unit's
+// pool bases, NULL = no append), and, if the chunk lies entirely inside
+// [lo, hi), its chunk summary (cs_row) and G group summaries (gs_rows, G
+// consecutive rows); NULL = no summaries.  krow(p) / vrow(p) return the raw
+// key / value row of position p in [lo, hi).  part: LDS scratch of S*P*2
+// doubles.  Called by all 256 threads of a workgroup with uniform arguments.
+template <int D, bool BF16, class KRow, class VRow>
+__device__ __forceinline__ void build_span(
+    const KCfg& cfg, int c0, int lo, int hi, KRow krow, VRow vrow,
+    typename std::conditional<BF16, uint16_t, float>::type* kp,
+    typename std::conditional<BF16, uint16_t, float>::type* vp, float* cs_row, float* gs_rows,
+    double* part_lds) {
+  constexpr int P = D / 2;               // pairs
+  constexpr int S = 256 / P;             // token slices
+  constexpr int TS = kChunk / S;         // tokens per slice
+  constexpr int SPG = kGroupTokens / TS; // slices per group
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  double (*part)[P][2] = reinterpret_cast<double (*)[P][2]>(part_lds);
+
+  const int tid = threadIdx.x;
+  const int j = tid % P, s = tid / P;
+  const bool complete = c0 >= lo && c0 + kChunk <= hi;
+  const bool hf = (cfg.hf_mask >> j) & 1ull;
+  const double w = cfg.omega[j];
+
+  // every load of this thread first (TS tokens of pair j), unconditionally
+  // from a clamped in-range row so that they are all in flight together;
+  // rows outside [lo, hi) are loaded but not used
+  T xa[TS], xb[TS], ya[TS], yb[TS];
+#pragma unroll
+  for (int i = 0; i < TS; ++i) {
+    int p = c0 + s * TS + i;
+    p = p < lo ? lo : (p >= hi ? hi - 1 : p);
+    const T* kr = krow(p);
+    const T* vr = kp ? vrow(p) : kr;
+    xa[i] = kr[j];
+    xb[i] = kr[j + P];
+    ya[i] = vr[j];
+    yb[i] = vr[j + P];
+  }
+  // angles of consecutive positions by rotation: (cos, sin)(p w) from
+  // (cos, sin)(p0 w) and (cos, sin)(w) in fp64 (error ~1e-16 per step)
+  const int p_first = c0 + s * TS;
+  double cs, sn, cd, sd;
+  rope_cs((double)p_first, w, &cs, &sn);
+  sincos(w, &sd, &cd);
+  double sa = 0.0, sb = 0.0;
+#pragma unroll
+  for (int i = 0; i < TS; ++i) {
+    const int p = p_first + i;
+    if (p >= lo && p < hi) {
+      double ka, kb;
+      if constexpr (BF16) {
+        ka = bf16_to_f(xa[i]);
+        kb = bf16_to_f(xb[i]);
+      } else {
+        ka = xa[i];
+        kb = xb[i];
+      }
+      const double ra = ka * cs - kb * sn;
+      const double rb = ka * sn + kb * cs;
+      if (kp) {
+        const size_t prow = (size_t)p * D;
+        if constexpr (BF16) {
+          kp[prow + j] = f64_to_bf16_rne(ra);
+          kp[prow + j + P] = f64_to_bf16_rne(rb);
+        } else {
+          kp[prow + j] = (float)ra;
+          kp[prow + j + P] = (float)rb;
+        }
+        // V: each 16-token group is stored transposed, a [D][16] block
+        const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
+        vp[vcol + (size_t)j * kGroupTokens] = ya[i];
+        vp[vcol + (size_t)(j + P) * kGroupTokens] = yb[i];
+      }
+      if (hf) {
+        sa += ra;
+        sb += rb;
+      } else {
+        sa += ka;
+        sb += kb;
+      }
+    }
+    const double c2 = cs * cd - sn * sd;
+    sn = sn * cd + cs * sd;
+    cs = c2;
+  }
+  if (!complete || !cs_row) return;  // uniform across the workgroup
+
+  part[s][j][0] = sa;
+  part[s][j][1] = sb;
+  __syncthreads();
+
+  // group gi = s (s < G): sum its slices
+  if (s < kGroups) {
+    double ga = 0.0, gb = 0.0;
+    for (int q = 0; q < SPG; ++q) {
+      ga += part[s * SPG + q][j][0];
+      gb += part[s * SPG + q][j][1];
+    }
+    ga /= kGroupTokens;
+    gb /= kGroupTokens;
+    if (!hf) {
+      double cs, sn;
+      rope_cs((double)(c0 + s * kGroupTokens) + 0.5 * (kGroupTokens - 1), w, &cs, &sn);
+      const double ra = ga * cs - gb * sn, rb = ga * sn + gb * cs;
+      ga = ra;
+      gb = rb;
+    }
+    float* gs = gs_rows + (size_t)s * D;
+    gs[j] = (float)ga;
+    gs[j + P] = (float)gb;
+  }
+  if (s == 0) {
+    double ca = 0.0, cb = 0.0;
+    for (int q = 0; q < S; ++q) {
+      ca += part[q][j][0];
+      cb += part[q][j][1];
+    }
+    ca /= kChunk;
+    cb /= kChunk;
+    if (!hf) {
+      double cs, sn;
+      rope_cs((double)c0 + 0.5 * (kChunk - 1), w, &cs, &sn);
+      const double ra = ca * cs - cb * sn, rb = ca * sn + cb * cs;
+      ca = ra;
+      cb = rb;
+    }
+    cs_row[j] = (float)ca;
+    cs_row[j + P] = (float)cb;
+  }
+}
+
+
+}  // namespace hga

@@ -25,7 +25,21 @@ struct RouteLaunch {
   double* qbar;         // workspace [B*Hkv][d]
   int B, lq, max_chunks, max_sel;
 };
-hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st);
+// The token work of a fused decode step, run by extra workgroups of the
+// selection launch: the new token's pool append, its raw key into the chunk
+// staging rows, and the summaries of the chunk it completes.
+struct StepFront {
+  const void* k_new;  // [B][Hkv][d] raw key of the new token (position q_pos0[b])
+  const void* v_new;  // [B][Hkv][d]
+  void* k_stage;      // [B][Hkv][C][d] raw keys of the current chunk
+  void* k_pool;
+  void* v_pool;
+  int pool_cap;
+  float* chunk_sum;   // written for a completed chunk
+  float* group_sum;
+};
+hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
+                        const StepFront* front = nullptr);
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks);
 size_t route_select_lds(const KCfg& cfg, int max_chunks);
 

@@ -23,7 +23,7 @@
 // counting with the order (score descending, id ascending).  Scores stay
 // fp64 throughout, so the kept set equals the fp64 reference wherever its
 // score gap exceeds the error of the fp32-stored summaries.
-#include "hga_internal.h"
+#include "hga_build_dev.h"
 
 namespace hga {
 
@@ -34,6 +34,7 @@ struct RouteArgs {
   KCfg cfg;
   RouteLaunch r;
   int max_cand;
+  StepFront f;  // used by the workgroups with blockIdx.z == 1 of route_select
 };
 
 // Top-k by one wave, no barriers: the k best of s[0..n) (LDS, fp64; order
@@ -190,13 +191,13 @@ __device__ int wave_topk(const double* s, int n, int k, int* out, const TopkScra
 }
 
 // Position and candidate range of a unit; false if the query position is
-// unusable (negative, query tokens spanning two chunks, or candidates whose
-// summaries lie beyond the table).
+// unusable (negative, query tokens spanning two chunks, or a query chunk
+// beyond the summary table).
 __device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch& r, int max_cand,
                                                int b, int* pos0, Windows* w) {
   *pos0 = r.q_pos0[b];
   *w = windows_of(*pos0 / kChunk, c.n_sink, c.n_local);
-  return *pos0 >= 0 && (*pos0 % kChunk) + r.lq <= kChunk && w->cand_hi <= r.max_chunks &&
+  return *pos0 >= 0 && (*pos0 % kChunk) + r.lq <= kChunk && *pos0 / kChunk < r.max_chunks &&
          w->cand_hi - w->cand_lo <= max_cand;
 }
 
@@ -337,7 +338,41 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   }
 }
 
-template <int D>
+// Token work of a fused decode step for unit (h, b), on one workgroup: the
+// raw key goes to its staging row, the rotated key and the value to the pool
+// (the same arithmetic as hga_build_summaries with one token), and when the
+// token is the last of its chunk the chunk's summaries are built from the
+// staging rows plus the new key.  Neither is read by this step's routing: the
+// current chunk is never a candidate.
+template <int D, bool BF16>
+__device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  const KCfg& c = a.cfg;
+  const StepFront& f = a.f;
+  const int unit = b * c.hkv + h;
+  const int pos = a.r.q_pos0[b];
+  if (pos < 0 || pos >= f.pool_cap) return;  // route_select reports the position
+  const int c0 = pos / kChunk * kChunk;
+  const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * D;
+  const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * D;
+  T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
+  T* kp = static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
+  T* vp = static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
+  for (int i = threadIdx.x; i < D; i += 256) stage[(size_t)(pos - c0) * D + i] = kn[i];
+  build_span<D, BF16>(c, c0, pos, pos + 1, [&](int) { return kn; }, [&](int) { return vn; }, kp, vp,
+                      nullptr, nullptr, lds);
+  const int chunk = pos / kChunk;
+  if (pos - c0 == kChunk - 1 && chunk < a.r.max_chunks) {  // uniform
+    float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
+    float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
+    build_span<D, BF16>(
+        c, c0, c0, c0 + kChunk,
+        [&](int p) { return p == pos ? kn : stage + (size_t)(p - c0) * D; },
+        [&](int) { return kn; }, static_cast<T*>(nullptr), static_cast<T*>(nullptr), cs, gs, lds);
+  }
+}
+
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int RPP = 256 / kLanesPerRow;  // rows per pass of the workgroup
@@ -350,6 +385,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
+  if (blockIdx.z == 1) {  // a fused decode step's token work
+    step_front<D, BF16>(a, h, b, dyn);
+    return;
+  }
   const int unit = b * c.hkv + h;
 
   // every load that does not depend on the position goes out first: this
@@ -481,24 +520,36 @@ size_t route_select_lds(const KCfg& cfg, int max_chunks) {
   return nmax * (sizeof(double) + 3 * sizeof(int)) + (size_t)n2 * sizeof(int);
 }
 
-hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st) {
-  RouteArgs a;
+hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
+                        const StepFront* front) {
+  RouteArgs a{};
   a.cfg = cfg;
   a.r = r;
   a.max_cand = max_cand_of(cfg, r.max_chunks);
+  if (front) a.f = *front;
   const int n_tiles = (a.max_cand + kTile - 1) / kTile;
-  const size_t lds = route_select_lds(cfg, r.max_chunks);
+  size_t lds = route_select_lds(cfg, r.max_chunks);
+  const size_t front_lds = (size_t)256 * 2 * sizeof(double);  // build_span scratch: S*P*2 doubles
+  if (front && lds < front_lds) lds = front_lds;
   dim3 grid(n_tiles, cfg.hkv, r.B);
-  dim3 sgrid(cfg.hkv, r.B);
+  dim3 sgrid(cfg.hkv, r.B, front ? 2 : 1);
   const bool bf = cfg.dtype == HGA_BF16;
   if (cfg.d == 128) {
-    if (bf) hipLaunchKernelGGL((route_tiles_kernel<128, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((route_tiles_kernel<128, false>), grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((route_select_kernel<128>), sgrid, dim3(256), lds, st, a);
+    if (bf) {
+      hipLaunchKernelGGL((route_tiles_kernel<128, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
+    } else {
+      hipLaunchKernelGGL((route_tiles_kernel<128, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
+    }
   } else {
-    if (bf) hipLaunchKernelGGL((route_tiles_kernel<64, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((route_tiles_kernel<64, false>), grid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((route_select_kernel<64>), sgrid, dim3(256), lds, st, a);
+    if (bf) {
+      hipLaunchKernelGGL((route_tiles_kernel<64, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
+    } else {
+      hipLaunchKernelGGL((route_tiles_kernel<64, false>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
+    }
   }
   return hipGetLastError();
 }
