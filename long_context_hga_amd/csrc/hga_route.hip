@@ -17,10 +17,11 @@
 //    loads in flight at once), level-2 top-k, and the ascending group list.
 //    The kernel boundary makes the first launch's scores visible to the
 //    second with plain loads.
-// Top-k (one wave, no barriers): a 256-bin histogram between the min and
-// max score finds the bin holding the k-th largest score; every score in a
-// higher bin is kept, and the boundary bin is resolved exactly by rank
-// counting with the order (score descending, id ascending).  Scores stay
+// Top-k (the whole workgroup for up to 1024 scores, one wave streaming from
+// LDS beyond): a 256-bin histogram between the min and max score finds the
+// bin holding the k-th largest score; every score in a higher bin is kept,
+// and the boundary bin is resolved exactly by rank counting with the order
+// (score descending, id ascending).  Scores stay
 // fp64 throughout, so the kept set equals the fp64 reference wherever its
 // score gap exceeds the error of the fp32-stored summaries.
 #include "hga_build_dev.h"
@@ -188,6 +189,112 @@ __device__ int wave_topk(const double* s, int n, int k, int* out, const TopkScra
     }
   }
   return cnt;
+}
+
+// Top-k by a whole 256-thread workgroup (n <= 1024, all threads call it with
+// the same arguments): the k best of s[0..n) (LDS, fp64; order score
+// descending, index ascending) are written ascending by index to out (LDS);
+// returns min(k, n) in every thread.  Thread t owns elements 4t..4t+3, so
+// the kept indices come out in order from one exclusive scan of per-thread
+// counts.  Same histogram / cut / boundary-rank steps as wave_topk, with a
+// quarter of the elements per lane.  Scratch: hist (256 ints), bl (n ints),
+// red (8 doubles), ints (8 ints).
+struct BlockTopkScratch {
+  int* hist;
+  int* bl;
+  double* red;
+  int* ints;
+};
+
+__device__ int block_topk(const double* s, int n, int k, int* out, const BlockTopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (k <= 0) return 0;
+  if (k >= n) {
+    for (int i = tid; i < n; i += 256) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  sc.hist[tid] = 0;
+  double x[4];
+  bool v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    v[e] = i < n;
+    x[e] = s[v[e] ? i : n - 1];
+  }
+  double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    mn = fmin(mn, v[e] ? x[e] : INFINITY);
+    mx = fmax(mx, v[e] ? x[e] : -INFINITY);
+  }
+  mn = wave_ext_d<false>(mn);
+  mx = wave_ext_d<true>(mx);
+  if (lane == 0) {
+    sc.red[wave] = mn;
+    sc.red[4 + wave] = mx;
+  }
+  __syncthreads();
+  mn = fmin(fmin(sc.red[0], sc.red[1]), fmin(sc.red[2], sc.red[3]));
+  mx = fmax(fmax(sc.red[4], sc.red[5]), fmax(sc.red[6], sc.red[7]));
+  const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+  int bin[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bin[e] = v[e] ? topk_bin(x[e], mn, scale) : -1;
+    if (bin[e] >= 0) atomicAdd(&sc.hist[bin[e]], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int bs, need;
+    topk_cut(sc.hist, k, &bs, &need);
+    if (lane == 0) {
+      sc.ints[0] = bs;
+      sc.ints[1] = need;
+      sc.ints[2] = 0;  // boundary members collected
+    }
+  }
+  __syncthreads();
+  const int bs = sc.ints[0], need = sc.ints[1];
+  const int nb = sc.hist[bs];
+  int keep = 0;  // bit e: element 4t+e kept
+#pragma unroll
+  for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs ? 1 : 0) << e;
+  if (nb == need) {  // the whole boundary bin is kept
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (bin[e] == bs ? 1 : 0) << e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (bin[e] == bs) sc.bl[atomicAdd(&sc.ints[2], 1)] = 4 * tid + e;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (bin[e] == bs) {
+        const int i = 4 * tid + e;
+        int r = 0;
+        for (int u = 0; u < nb; ++u) {
+          const int j = sc.bl[u];
+          const double sj = s[j];
+          r += (sj > x[e]) || (sj == x[e] && j < i);
+        }
+        keep |= (r < need ? 1 : 0) << e;
+      }
+    }
+  }
+  // kept indices in ascending order: exclusive scan of per-thread counts
+  const int cnt = __popc(keep);
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) sc.ints[4 + wave] = incl;
+  __syncthreads();
+  int off = incl - cnt;
+  for (int w = 0; w < wave; ++w) off += sc.ints[4 + w];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (keep & (1 << e)) out[off++] = 4 * tid + e;
+  __syncthreads();
+  return k;
 }
 
 // Position and candidate range of a unit; false if the query position is
@@ -379,6 +486,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   constexpr int U = 8;                     // passes in flight
   __shared__ int hist[256];
   __shared__ int kk[2];
+  __shared__ double red[8];
+  __shared__ int ints[8];
   extern __shared__ double dyn[];
 
   const KCfg& c = a.cfg;
@@ -428,6 +537,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   int* sel = win + nmax;
   int* sel2 = sel + nmax;
   const TopkScratch tks{hist, bl, win};
+  const BlockTopkScratch bts{hist, bl, red, ints};
 
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
@@ -436,13 +546,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   }
   for (int i = SPT * 256 + tid; i < n_cand; i += 256) s_lds[i] = scores[i];
   __syncthreads();
-  // level 1 (one wave): kept candidate indices, ascending, into sel
-  if (wave == 0) {
-    const int k1 = wave_topk(s_lds, n_cand, c.topk_c, sel, tks);
-    if (lane == 0) kk[0] = k1;
+  // level 1: kept candidate indices, ascending, into sel
+  int k1;
+  if (n_cand <= 1024) {
+    k1 = block_topk(s_lds, n_cand, c.topk_c, sel, bts);
+  } else {  // long candidate lists: one wave streams them from LDS
+    if (wave == 0) {
+      const int k = wave_topk(s_lds, n_cand, c.topk_c, sel, tks);
+      if (lane == 0) kk[0] = k;
+    }
+    __syncthreads();
+    k1 = kk[0];
   }
-  __syncthreads();
-  const int k1 = kk[0];
 
   // level 2 (all waves): the G groups of each kept chunk
   const int n2 = k1 * kGroups;
@@ -475,13 +590,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  // level 2 selection (one wave): kept group indices, ascending = gid order
-  if (wave == 0) {
-    const int k2 = wave_topk(s_lds, n2, c.topk_g, sel2, tks);
-    if (lane == 0) kk[1] = k2;
+  // level 2 selection: kept group indices, ascending = gid order
+  int k2;
+  if (n2 <= 1024) {
+    k2 = block_topk(s_lds, n2, c.topk_g, sel2, bts);
+  } else {
+    if (wave == 0) {
+      const int k = wave_topk(s_lds, n2, c.topk_g, sel2, tks);
+      if (lane == 0) kk[1] = k;
+    }
+    __syncthreads();
+    k2 = kk[1];
   }
-  __syncthreads();
-  const int k2 = kk[1];
 
   // the list: sink | routed | local | current
   const int last = pos0 + r.lq - 1;
