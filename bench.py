@@ -55,10 +55,11 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE; KiB per dispatch, summed over the two kernels) and scaled by
 # what the same counters read for a plain device copy of known size
 # (bench.py --calibrate-copy).  Valid only for the kernel source it was taken
-# on: if hga_attend.hip has changed since, traffic is reported as null.
+# on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
+# reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="541f63edf4d3ed7724168182173ec6062a6694e3ee75c39d6b5962dd6257ba01",
-    fetch_kib=16820.61 + 1108.02, write_kib=2080.0 + 129.0, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="eab72420f4d5ec6c70da3f96824a9dcae3f705c7eef8638255bc273854022456",
+    fetch_kib=16748.46 + 1467.05, write_kib=2080.01 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):
@@ -80,10 +81,13 @@ def algorithmic_bytes(p, B):
 
 
 def attend_source_sha():
+    """sha256 of the decode attention sources (split kernel + merge kernel)."""
     import hashlib
-    path = os.path.join(ROOT, "long_context_hga_amd", "csrc", "hga_attend.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in ("hga_attend.hip", "hga_decode.hip"):
+        with open(os.path.join(ROOT, "long_context_hga_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def attend_traffic():
