@@ -110,14 +110,18 @@ def _quant(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def generate(name: str, batch: Optional[int] = None, context: Optional[int] = None,
-             seeds: Optional[List[int]] = None) -> Inputs:
+             seeds: Optional[List[int]] = None, overrides: Optional[dict] = None) -> Inputs:
     """Draw the inputs of workload ``name``.
 
     ``batch`` / ``context`` override the workload's sizes (smaller parity
     cases); the seed of sequence b stays 1000*index + b unless ``seeds``
     gives them explicitly.  With a shorter context the query moves to the
-    end of it (the same offset from the end as in the full workload)."""
+    end of it (the same offset from the end as in the full workload).
+    ``overrides`` replaces other entries of the workload (head counts,
+    head_dim, dtype, budgets, lq) for shape-coverage cases."""
     p = dict(CONFIGS[name])
+    if overrides:
+        p.update(overrides)
     B = p["batch"] if batch is None else int(batch)
     T = p["context"] if context is None else int(context)
     if context is not None:
