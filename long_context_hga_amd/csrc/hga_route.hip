@@ -364,34 +364,64 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   }
 
   // ---- pooled routing query (fp64): thread (j, slice) rotates pair j of
-  // every query head of this KV head for the query tokens of its slice
+  // every query head of this KV head for the query tokens of its slice,
+  // t = sl, sl+S, ...  The head sum of a token is rotated once; the angle of
+  // the next token of the slice follows by one fp64 rotation by S*omega_j
+  // (error ~1e-16 per step); later tokens (prefill) are loaded in batches of
+  // 4 with all their loads in flight.
   {
     double qa = 0.0, qb = 0.0;
-    for (int t = sl; t < lq; t += S) {
-      if (t != sl) {  // later query tokens (prefill): load them here
+    double cs, sn, cd = 1.0, sd = 0.0;
+    rope_cs((double)(pos0 + sl), wj, &cs, &sn);
+    if (lq > S) sincos((double)S * wj, &sd, &cd);
+    auto head_sum = [&](const T* ha, const T* hb, double* x, double* y) {
+      double sx = 0.0, sy = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        if (hh < c.hg) {
+          if constexpr (BF16) {
+            sx += bf16_to_f(ha[hh]);
+            sy += bf16_to_f(hb[hh]);
+          } else {
+            sx += ha[hh];
+            sy += hb[hh];
+          }
+        }
+      }
+      *x = sx;
+      *y = sy;
+    };
+    auto rotate_add = [&](double x, double y) {
+      qa += x * cs - y * sn;
+      qb += x * sn + y * cs;
+      const double c2 = cs * cd - sn * sd;
+      sn = sn * cd + cs * sd;
+      cs = c2;
+    };
+    if (sl < lq) {
+      double x, y;
+      head_sum(xa, xb, &x, &y);
+      rotate_add(x, y);
+    }
+    for (int t0 = sl + S; t0 < lq; t0 += 4 * S) {  // prefill: later tokens
+      T ya[4][8], yb[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + u * S < lq ? t0 + u * S : lq - 1;
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh) {
           const int hc = hh < c.hg ? hh : c.hg - 1;
           const size_t row = ((size_t)(b * c.hq + h * c.hg + hc) * lq + t) * D;
-          xa[hh] = q[row + j];
-          xb[hh] = q[row + j + P];
+          ya[u][hh] = q[row + j];
+          yb[u][hh] = q[row + j + P];
         }
       }
-      double cs, sn;
-      rope_cs((double)(pos0 + t), wj, &cs, &sn);
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) {
-        if (hh < c.hg) {
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + u * S < lq) {
           double x, y;
-          if constexpr (BF16) {
-            x = bf16_to_f(xa[hh]);
-            y = bf16_to_f(xb[hh]);
-          } else {
-            x = xa[hh];
-            y = xb[hh];
-          }
-          qa += x * cs - y * sn;
-          qb += x * sn + y * cs;
+          head_sum(ya[u], yb[u], &x, &y);
+          rotate_add(x, y);
         }
       }
     }
