@@ -80,20 +80,15 @@ bool pinned_device_ptr(const void* p, const void** dev) {
   return true;
 }
 
-// Workspace of hga_attend_tiered: the partials of its two attention calls
-// and their two (out, lse) results.
-struct TieredWs {
-  size_t part_bytes, res_floats;
-};
-TieredWs tiered_ws(const KCfg& k, int B, int lq, int max_sel) {
-  TieredWs t;
-  t.part_bytes = round_up(attend_ws_bytes(k, B, lq, max_sel), 256);
-  t.res_floats = round_up((size_t)B * k.hq * lq * (k.d + 1), 64);
-  return t;
+// Partial records per (unit, query token) of hga_attend_tiered: the window
+// part's splits, then the routed part's.
+int tiered_rec_splits(const hga_config* c) {
+  const int w = (c->n_sink_chunks + c->n_local_chunks + 1) * c->groups_per_chunk;
+  return (w + 7) / 8 + (c->topk_groups + 7) / 8;
 }
-size_t tiered_ws_bytes(const KCfg& k, int B, int lq, int max_sel) {
-  const TieredWs t = tiered_ws(k, B, lq, max_sel);
-  return 2 * t.part_bytes + 2 * t.res_floats * sizeof(float);
+size_t tiered_ws_bytes(const hga_config* c, const KCfg& k, int B, int lq) {
+  const int pf = ((2 * k.hg + 3) / 4 * 4) + k.hg * k.d;
+  return (size_t)B * k.hkv * lq * tiered_rec_splits(c) * pf * sizeof(float);
 }
 
 }  // namespace
@@ -119,7 +114,9 @@ hga_status hga_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_ctx
   const KCfg k = make_kcfg(cfg);
   const int max_chunks = (max_ctx + kChunk - 1) / kChunk;
   const size_t r = route_ws_bytes(k, B, max_chunks);
-  const size_t a = tiered_ws_bytes(k, B, max_lq, max_selected(cfg));  // >= hga_attend's
+  size_t a = attend_ws_bytes(k, B, max_lq, max_selected(cfg));
+  const size_t t = tiered_ws_bytes(cfg, k, B, max_lq);
+  a = a > t ? a : t;
   *bytes = round_up(r > a ? r : a, 256);
   return HGA_OK;
 }
@@ -205,6 +202,7 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
       !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
       (part != HGA_PART_ALL && !q_pos0))
     return HGA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_sel * cfg->n_kv_heads * B > INT32_MAX) return HGA_ERR_UNSUPPORTED;
   const void* kp = k_pool;
   const void* vp = v_pool;
   if (pool_is_host && (!pinned_device_ptr(k_pool, &kp) || !pinned_device_ptr(v_pool, &vp)))
@@ -253,6 +251,8 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   a.src_cap = src_layout == HGA_SRC_POOL ? src_cap : max_sel * kGroupTokens;
   a.max_sel = max_sel;
   a.part_sel = part;
+  a.two_part = 0;
+  a.rec_splits = 0;
   return hip_status(launch_attend(k, a, (hipStream_t)stream));
 }
 
@@ -322,6 +322,8 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
   a.src_cap = pool_cap;
   a.max_sel = max_sel;
   a.part_sel = HGA_PART_ALL;
+  a.two_part = 0;
+  a.rec_splits = 0;
   return hip_status(launch_attend(k, a, st));
 }
 
@@ -340,75 +342,67 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_INVALID_ARGUMENT;
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
-  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  if (max_sel > kMaxListDecode || tiered_rec_splits(cfg) > kMaxListDecode / 8)
+    return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
-  if (ws_bytes < tiered_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < tiered_ws_bytes(cfg, k, B, lq)) return HGA_ERR_WORKSPACE_TOO_SMALL;
   const void* kc = nullptr;
   const void* vc = nullptr;
   if (!pinned_device_ptr(k_cold, &kc) || !pinned_device_ptr(v_cold, &vc))
     return HGA_ERR_INVALID_ARGUMENT;
-  const TieredWs t = tiered_ws(k, B, lq, max_sel);
-  char* w = static_cast<char*>(ws);
-  float* part_a = reinterpret_cast<float*>(w);
-  float* part_b = reinterpret_cast<float*>(w + t.part_bytes);
-  float* res = reinterpret_cast<float*>(w + 2 * t.part_bytes);
-  const size_t n_out = (size_t)B * k.hq * lq * k.d;
-  float* oa = res;
-  float* la = oa + n_out;
-  float* ob = res + t.res_floats;
-  float* lb = ob + n_out;
   hipStream_t sa = static_cast<hipStream_t>(stream_a);
   hipStream_t sb = static_cast<hipStream_t>(stream_b);
 
+  // one partial buffer: the window part's splits, then the routed part's;
+  // one merge over both
   AttendLaunch a;
   a.q = q_raw;
   a.q_pos0 = q_pos0;
   a.sel = sel_groups;
   a.n_sel = n_sel;
+  a.out = out;
+  a.lse = lse_opt;
+  a.part = static_cast<float*>(ws);
   a.B = B;
   a.lq = lq;
   a.max_sel = max_sel;
+  a.two_part = 1;
+  a.rec_splits = tiered_rec_splits(cfg);
   AttendLaunch ah = a, ac = a;
   ah.k = k_hot;
   ah.v = v_hot;
   ah.src_layout = HGA_SRC_POOL;
   ah.src_cap = hot_cap;
   ah.part_sel = HGA_PART_WINDOWS;
-  ah.out = oa;
-  ah.lse = la;
-  ah.part = part_a;
   ac.k = k_ws;
   ac.v = v_ws;
   ac.src_layout = HGA_SRC_WORKING_SET;
   ac.src_cap = max_sel * kGroupTokens;
   ac.part_sel = HGA_PART_ROUTED;
-  ac.out = ob;
-  ac.lse = lb;
-  ac.part = part_b;
 
   // fork: stream b starts after everything already queued on stream a (the
-  // list written by hga_route); join: the merge on stream a waits for b
+  // list written by hga_route); join: the merge on stream a waits for b.  The
+  // window part is queued right behind the fork, ahead of the transfer, so
+  // its workgroups take their CUs before the copy kernel's waves (which
+  // mostly wait on PCIe) fill the rest.
   hipEvent_t fork = nullptr, join = nullptr;
   if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return HGA_ERR_HIP;
   if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
     (void)hipEventDestroy(fork);
     return HGA_ERR_HIP;
   }
-  // The window attention is queued right behind the fork, ahead of the
-  // transfer, so its workgroups take their CUs while the copy kernel (whose
-  // waves mostly wait on PCIe) fills the rest.
   hipError_t e = hipEventRecord(fork, sa);
-  if (e == hipSuccess) e = launch_attend(k, ah, sa);
+  if (e == hipSuccess) e = launch_attend_split(k, ah, sa);
   if (e == hipSuccess) e = hipStreamWaitEvent(sb, fork, 0);
   if (e == hipSuccess)
     e = launch_gather(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0, HGA_PART_ROUTED,
                       k_ws, v_ws, sb);
-  if (e == hipSuccess) e = launch_attend(k, ac, sb);
+  if (e == hipSuccess) e = launch_attend_split(k, ac, sb);
   if (e == hipSuccess) e = hipEventRecord(join, sb);
   if (e == hipSuccess) e = hipStreamWaitEvent(sa, join, 0);
-  if (e == hipSuccess) e = launch_merge(B, k.hq, lq, k.d, oa, la, ob, lb, out, lse_opt, sa);
+  if (e == hipSuccess) e = launch_attend_merge(k, a, sa);
   // the events are released once the work that references them completes
   (void)hipEventDestroy(fork);
   (void)hipEventDestroy(join);

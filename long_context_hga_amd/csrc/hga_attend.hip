@@ -51,7 +51,9 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
   ListParts lp{0, 0, 0};
   if (!bad) {
     lp = list_parts(n_sel, pos0 + a.lq - 1, pos0, c.n_sink, c.n_local);
-    bad = lp.n_routed < 0;
+    // a two-part list longer than the record layout holds (not one hga_route
+    // writes) is reported, not truncated
+    bad = lp.n_routed < 0 || records_active(a, lp, n_sel) > args.n_splits;
   }
   const size_t lrow = (size_t)(b * c.hq + h * HG + hh) * a.lq + tq;
   if (bad) {
@@ -61,8 +63,7 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
     if (a.lse && lane == 0) a.lse[lrow] = nan;
     return;
   }
-  const int n_part = part_count(a.part_sel, lp, n_sel);
-  const int n_act = (n_part + kSplitGroups - 1) / kSplitGroups;
+  const int n_act = records_active(a, lp, n_sel);
   float M = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
@@ -112,11 +113,29 @@ static void launch_combine(const AttendArgs& x, hipStream_t st) {
   else launch_combine_d<64>(x, grid, st);
 }
 
-hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st) {
+static AttendArgs attend_args(const KCfg& cfg, const AttendLaunch& a) {
   AttendArgs x;
   x.cfg = cfg;
   x.a = a;
-  x.n_splits = (a.max_sel + kSplitGroups - 1) / kSplitGroups;
+  x.grid_splits = (a.max_sel + kSplitGroups - 1) / kSplitGroups;
+  x.n_splits = a.rec_splits > 0 ? a.rec_splits : x.grid_splits;
+  return x;
+}
+
+hipError_t launch_attend_split(const KCfg& cfg, const AttendLaunch& a, hipStream_t st) {
+  const AttendArgs x = attend_args(cfg, a);
+  if (a.lq >= kPrefillMinLq) launch_prefill(x, st);
+  else launch_decode(x, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_merge(const KCfg& cfg, const AttendLaunch& a, hipStream_t st) {
+  launch_combine(attend_args(cfg, a), st);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st) {
+  const AttendArgs x = attend_args(cfg, a);
   if (a.lq >= kPrefillMinLq) launch_prefill(x, st);
   else launch_decode(x, st);
   launch_combine(x, st);

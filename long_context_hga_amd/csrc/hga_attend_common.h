@@ -14,7 +14,8 @@ constexpr int kPrefillMinLq = 16; // query tokens from which the MFMA prefill ke
 struct AttendArgs {
   KCfg cfg;
   AttendLaunch a;
-  int n_splits;
+  int n_splits;     // partial records per (unit, query token)
+  int grid_splits;  // split workgroups per (unit, column block / head)
 };
 
 // Partial of one split: m[HG], l[HG], padding to a 16-byte boundary, o[HG][D].
@@ -33,6 +34,21 @@ __device__ __forceinline__ int part_count(int part, const ListParts& lp, int n_s
   if (part == HGA_PART_ROUTED) return lp.n_routed;
   if (part == HGA_PART_WINDOWS) return lp.n_head + lp.n_tail;
   return n_sel;
+}
+
+// First partial record of this call's splits, and the number of records the
+// merge kernel combines, for the one-part and the two-part layouts.
+__device__ __forceinline__ int record_base(const AttendLaunch& a, const ListParts& lp) {
+  return (a.two_part && a.part_sel == HGA_PART_ROUTED)
+             ? (lp.n_head + lp.n_tail + kSplitGroups - 1) / kSplitGroups
+             : 0;
+}
+__device__ __forceinline__ int records_active(const AttendLaunch& a, const ListParts& lp,
+                                              int n_sel) {
+  if (a.two_part)
+    return (lp.n_head + lp.n_tail + kSplitGroups - 1) / kSplitGroups +
+           (lp.n_routed + kSplitGroups - 1) / kSplitGroups;
+  return (part_count(a.part_sel, lp, n_sel) + kSplitGroups - 1) / kSplitGroups;
 }
 
 // Sum / max over the 4 token rows of a wave (lanes l, l^16, l^32, l^48).

@@ -317,9 +317,10 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
     constexpr int EPT = D / TPR;         // dims per thread (8 or 4)
     const int r = tid / TPR, e0 = (tid % TPR) * EPT;
     const int gr = cb * kColRows + r;
-    if (gr < n_rows) {
+    const int ri = split + record_base(a, lp);  // < n_splits for lists hga_route can write
+    if (gr < n_rows && ri < args.n_splits) {
       const int tq = gr / HG, hh = gr % HG;
-      float* rec = a.part + ((size_t)(unit * a.lq + tq) * args.n_splits + split) * part_floats<D, HG>();
+      float* rec = a.part + ((size_t)(unit * a.lq + tq) * args.n_splits + ri) * part_floats<D, HG>();
 #pragma unroll
       for (int e = 0; e < EPT; e += 4) {
         float4 acc = *reinterpret_cast<const float4*>(&sh.ob[0][r][e0 + e]);
@@ -361,7 +362,7 @@ static void launch_decode_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
 
 void launch_decode(const AttendArgs& x, hipStream_t st) {
   const int ncb = (x.cfg.hg * x.a.lq + kColRows - 1) / kColRows;
-  const dim3 grid(x.n_splits, x.cfg.hkv, x.a.B * ncb);
+  const dim3 grid(x.grid_splits, x.cfg.hkv, x.a.B * ncb);
   if (x.cfg.d == 128) launch_decode_d<128>(x, grid, st);
   else launch_decode_d<64>(x, grid, st);
 }

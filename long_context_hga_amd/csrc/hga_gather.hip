@@ -5,8 +5,9 @@
 // "Geheugenarchitectuur": only the routed working set moves to accelerator
 // memory; the full token K/V may stay in host RAM.  The gather copies whole
 // 16-token groups (one contiguous 4 KiB row block per group, KV head and
-// tensor at d = 128, bf16), 16 bytes per lane, from device memory or
-// directly from pinned host memory over PCIe.
+// tensor at d = 128, bf16; the same block size for the transposed V
+// groups), 16 bytes per lane, from device memory or directly from pinned host
+// memory over PCIe.
 #include "hga_internal.h"
 
 namespace hga {
@@ -22,31 +23,40 @@ struct GatherArgs {
   int hkv, n_sink, n_local, pool_cap, max_sel, part, row_vecs;  // row_vecs: uint4 per token row
 };
 
-// grid = (max_sel, Hkv, B); one workgroup copies one group of K and of V.
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  const int slot = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int unit = b * a.hkv + h;
-  const int n_sel = a.n_sel[unit];
-  if (n_sel < 0 || slot >= n_sel) return;
-  if (a.part != HGA_PART_ALL) {
-    const int pos0 = a.q_pos0[b];
-    // the list covers query tokens of one chunk; the last listed group holds
-    // the last query token
-    const int last_gid = a.sel[(size_t)unit * a.max_sel + n_sel - 1];
-    const ListParts lp = list_parts(n_sel, last_gid * kGroupTokens, pos0, a.n_sink, a.n_local);
-    const bool routed = slot >= lp.n_head && slot < lp.n_head + lp.n_routed;
-    if ((a.part == HGA_PART_ROUTED) != routed) return;
-  }
-  const int gid = a.sel[(size_t)unit * a.max_sel + slot];
-  if (gid < 0 || (size_t)(gid + 1) * kGroupTokens > (size_t)a.pool_cap) return;
-  const int n = kGroupTokens * a.row_vecs;  // uint4 per group
-  const size_t src = ((size_t)unit * a.pool_cap + (size_t)gid * kGroupTokens) * a.row_vecs;
-  const size_t dst = ((size_t)unit * a.max_sel + slot) * kGroupTokens * a.row_vecs;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const uint4 kv = a.k_pool[src + i];
-    const uint4 vv = a.v_pool[src + i];
-    a.k_ws[dst + i] = kv;
-    a.v_ws[dst + i] = vv;
+// A persistent grid of at most kGatherWgs workgroups walks the (slot, KV
+// head, sequence) items; each item copies one group of K and of V (4 KiB
+// each at d = 128, bf16), 16 bytes per lane.  Reading a pinned host pool,
+// the workgroups spend their time waiting on PCIe, so the grid is kept small
+// enough to leave CUs to work queued on other streams.
+constexpr int kGatherWgs = 256;
+
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a, int n_items) {
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int slot = item % a.max_sel;
+    const int unit = item / a.max_sel;  // b * Hkv + h
+    const int b = unit / a.hkv;
+    const int n_sel = a.n_sel[unit];
+    if (n_sel < 0 || slot >= n_sel) continue;  // uniform over the workgroup
+    if (a.part != HGA_PART_ALL) {
+      const int pos0 = a.q_pos0[b];
+      // the list covers query tokens of one chunk; the last listed group holds
+      // the last query token
+      const int last_gid = a.sel[(size_t)unit * a.max_sel + n_sel - 1];
+      const ListParts lp = list_parts(n_sel, last_gid * kGroupTokens, pos0, a.n_sink, a.n_local);
+      const bool routed = slot >= lp.n_head && slot < lp.n_head + lp.n_routed;
+      if ((a.part == HGA_PART_ROUTED) != routed) continue;
+    }
+    const int gid = a.sel[(size_t)unit * a.max_sel + slot];
+    if (gid < 0 || (size_t)(gid + 1) * kGroupTokens > (size_t)a.pool_cap) continue;
+    const int n = kGroupTokens * a.row_vecs;  // uint4 per group
+    const size_t src = ((size_t)unit * a.pool_cap + (size_t)gid * kGroupTokens) * a.row_vecs;
+    const size_t dst = ((size_t)unit * a.max_sel + slot) * kGroupTokens * a.row_vecs;
+    for (int i = threadIdx.x; i < n; i += 256) {
+      const uint4 kv = a.k_pool[src + i];
+      const uint4 vv = a.v_pool[src + i];
+      a.k_ws[dst + i] = kv;
+      a.v_ws[dst + i] = vv;
+    }
   }
 }
 
@@ -68,7 +78,9 @@ hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void*
   a.max_sel = max_sel;
   a.part = part;
   a.row_vecs = cfg.d * (cfg.dtype == HGA_BF16 ? 2 : 4) / 16;
-  hipLaunchKernelGGL(gather_kernel, dim3(max_sel, cfg.hkv, B), dim3(256), 0, st, a);
+  const int n_items = max_sel * cfg.hkv * B;
+  const int n_wg = n_items < kGatherWgs ? n_items : kGatherWgs;
+  hipLaunchKernelGGL(gather_kernel, dim3(n_wg), dim3(256), 0, st, a, n_items);
   return hipGetLastError();
 }
 

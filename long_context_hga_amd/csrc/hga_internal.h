@@ -54,8 +54,14 @@ struct AttendLaunch {
   float* lse;
   float* part;          // workspace partials
   int B, lq, src_layout, src_cap, max_sel, part_sel;
+  // Two-part record layout (host tier): the window part's splits are records
+  // [0, ceil(n_w/8)), the routed part's follow; rec_splits records per
+  // (unit, query token).  two_part = 0: one part, ceil(max_sel/8) records.
+  int two_part, rec_splits;
 };
 hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
+hipError_t launch_attend_split(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
+hipError_t launch_attend_merge(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
 size_t attend_ws_bytes(const KCfg& cfg, int B, int lq, int max_sel);
 
 hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,

@@ -270,8 +270,9 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
     }
   }
   l = rows_sum(l);
-  if (row < a.lq) {
-    float* rec = a.part + ((size_t)(unit * a.lq + row) * args.n_splits + sp) * part_floats<D, HG>();
+  const int ri = sp + record_base(a, lp);  // < n_splits for lists hga_route can write
+  if (row < a.lq && ri < args.n_splits) {
+    float* rec = a.part + ((size_t)(unit * a.lq + row) * args.n_splits + ri) * part_floats<D, HG>();
     if (qg == 0) {
       rec[hj] = m;
       rec[HG + hj] = l;
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
 }
 
 void launch_prefill(const AttendArgs& x, hipStream_t st) {
-  const dim3 grid(x.n_splits, x.cfg.hq, x.a.B);
+  const dim3 grid(x.grid_splits, x.cfg.hq, x.a.B);
   switch (x.cfg.hg) {
     case 1: hipLaunchKernelGGL((attend_prefill_kernel<128, 1>), grid, dim3(256), 0, st, x); break;
     case 2: hipLaunchKernelGGL((attend_prefill_kernel<128, 2>), grid, dim3(256), 0, st, x); break;
