@@ -68,6 +68,21 @@ __device__ __forceinline__ float rows_max(float x) {
 // Matrix-core operand types (v_mfma_f32_16x16x32_bf16).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one register of two bf16, rounded to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// (a, b) -> bf16 pairs hi, lo with a ~= hi.x + lo.x, b ~= hi.y + lo.y: 16
+// significant bits of each value in two bf16 operands.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
 
 // The bf16 elements of x whose bit in keep (bit i = element i) is clear
 // become +0.

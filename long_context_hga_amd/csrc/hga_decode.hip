@@ -36,20 +36,7 @@
 
 namespace hga {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kColRows = 16;  // query rows per column block
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 h = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// (a, b) -> bf16 pairs hi, lo with a ~= hi.x + lo.x, b ~= hi.y + lo.y
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = pack_bf16x2(a, b);
-  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
-}
 
 // 8 fp32 values (two uint4) -> bf16x8 hi and lo operands
 __device__ __forceinline__ void split8(const uint4& x0, const uint4& x1, bf16x8& hi, bf16x8& lo) {

@@ -17,7 +17,7 @@
 //   S^T = K Q^T   A = 16 keys x 32 dims of K (LDS, bf16 as stored in the
 //                 pool), B = the rotated query (bf16 hi + lo parts, two
 //                 products), C = 16 keys x 16 query rows: each lane holds 4
-//                 keys of one query row, so the row statistics of the online
+//                 keys of one query row, so the row statistics of the
 //                 softmax reduce over the 4 lanes of a column (permlane swaps)
 //   O^T += V^T P^T  A = 16 dims x 32 keys of V (LDS, stored transposed),
 //                 B = the probabilities of the lane's own S^T entries (bf16 hi
@@ -28,12 +28,20 @@
 // the products carry about 2^-17 relative error before fp32 accumulation.
 //
 // LDS (64 KiB): the split's K rows, 16-byte chunks XOR-swizzled by key, and
-// V^T rows of 128 keys (copied from the pool's transposed group blocks),
-// 8-byte units XOR-swizzled by dim, so neither the
-// staging writes nor the operand reads conflict on banks.  The query needs no
-// staging: each lane's QK^T operand holds both halves of its RoPE pairs.
+// V^T rows of 128 keys (copied from the pool's transposed group blocks).  A
+// V^T row keeps each 32-key tile in the order of the S^T entries: chunk qg of
+// the tile holds keys 4qg + 0..3 and 16 + 4qg + 0..3, so one 16-byte read is
+// a lane's whole A operand of O^T; chunks are XOR-swizzled by dim.  Neither
+// the staging writes nor the operand reads conflict on banks.  The query
+// needs no staging: each lane's QK^T operand holds both halves of its RoPE
+// pairs.
 //
-// The result of each split is a partial (running max m in log2 units, sum l,
+// Softmax in two passes over registers: a split has 128 keys, so a lane's 32
+// scores stay in registers; the row maximum is taken once, then the
+// probabilities, then O^T.  The partial carries that maximum (no online
+// rescaling inside a split).
+//
+// The result of each split is a partial (max m in log2 units, sum l,
 // unnormalised o) per query token in the decode kernel's layout; the merge
 // kernel of the decode path combines the splits exactly.
 #include "hga_attend_common.h"
@@ -42,19 +50,8 @@ namespace hga {
 
 constexpr int kSplitKeys = kSplitGroups * kGroupTokens;    // 128 keys per split
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// x -> (hi, lo) bf16 bit patterns with x ~= hi + lo.
-__device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
-  hi = bf16_rne_bits(x);
-  lo = bf16_rne_bits(x - __uint_as_float(hi << 16));
-}
-
 template <int D, int HG>
-__global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_prefill_kernel(AttendArgs args) {
   static_assert(D == 128, "staging maps assume 16 chunks of 16 bytes per key row");
   constexpr int KS = D / 32;              // k-steps of the QK^T contraction
   constexpr int NB = D / 16;              // 16-dim blocks of the output
@@ -150,25 +147,21 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
       const uint32_t wx[4] = {qraw[half].x, qraw[half].y, qraw[half].z, qraw[half].w};
       const uint32_t wy[4] = {qraw[half + 2].x, qraw[half + 2].y, qraw[half + 2].z, qraw[half + 2].w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = 32 * half + 8 * qg + i;
-        const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
-        const float fr = (float)(turns - rint(turns));
-        const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
-        const float x = __uint_as_float((i & 1) ? (wx[i >> 1] & 0xFFFF0000u) : (wx[i >> 1] << 16));
-        const float y = __uint_as_float((i & 1) ? (wy[i >> 1] & 0xFFFF0000u) : (wy[i >> 1] << 16));
-        const float rx = (x * cs - y * sn) * c.qscale_log2;
-        const float ry = (x * sn + y * cs) * c.qscale_log2;
-        uint32_t hx, lx, hy, ly;
-        split_hi_lo(rx, hx, lx);
-        split_hi_lo(ry, hy, ly);
-        if (i & 1) {
-          hi[half][i >> 1] |= hx << 16; lo[half][i >> 1] |= lx << 16;
-          hi[half + 2][i >> 1] |= hy << 16; lo[half + 2][i >> 1] |= ly << 16;
-        } else {
-          hi[half][i >> 1] = hx; lo[half][i >> 1] = lx;
-          hi[half + 2][i >> 1] = hy; lo[half + 2][i >> 1] = ly;
+      for (int w = 0; w < 4; ++w) {  // pairs i = 2w, 2w + 1: one packed register each
+        float rx[2], ry[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = 32 * half + 8 * qg + 2 * w + e;
+          const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
+          const float fr = (float)(turns - rint(turns));
+          const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+          const float x = __uint_as_float(e ? (wx[w] & 0xFFFF0000u) : (wx[w] << 16));
+          const float y = __uint_as_float(e ? (wy[w] & 0xFFFF0000u) : (wy[w] << 16));
+          rx[e] = (x * cs - y * sn) * c.qscale_log2;
+          ry[e] = (x * sn + y * cs) * c.qscale_log2;
         }
+        split_pair(rx[0], rx[1], hi[half][w], lo[half][w]);
+        split_pair(ry[0], ry[1], hi[half + 2][w], lo[half + 2][w]);
       }
     }
 #pragma unroll
@@ -178,8 +171,8 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
     }
   }
 
-  // ---- K rows (chunk ch of key at chunk ch ^ (key % CH)) and V^T (the
-  // 8-byte unit u of dim row r at unit u ^ (r % 32)); V of a key that is
+  // ---- K rows (chunk ch of key at chunk ch ^ (key % CH)) and V^T (tile
+  // order as above, chunk c of dim row r at c ^ (r % 16)); V of a key that is
   // missing or lies after the last query token is stored as zero
 #pragma unroll
   for (int it = 0; it < kSplitGroups; ++it) {
@@ -195,79 +188,115 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(AttendArgs args) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) keep |= (gp >= 0 && gp + 8 * hf + i <= pos_last) ? (1u << i) : 0u;
       const uint4 x = keep_bf16(vraw[it], keep);
-      const int u0 = 4 * it + 2 * hf;  // 8-byte unit of key 16*it + 8*hf
-      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + ((u0 ^ (dim & 31)) * 4)) = make_uint2(x.x, x.y);
-      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + (((u0 + 1) ^ (dim & 31)) * 4)) = make_uint2(x.z, x.w);
+      // keys 16*(it%2) + 8hf + 0..7 of tile it/2: column-group qg = 2hf and
+      // 2hf + 1, half it%2 of their chunks
+      const int c0 = 4 * (it >> 1) + 2 * hf, h = 4 * (it & 1);
+      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + ((c0 ^ (dim & 15)) * 8) + h) = make_uint2(x.x, x.y);
+      *reinterpret_cast<uint2*>(vt + dim * kSplitKeys + (((c0 + 1) ^ (dim & 15)) * 8) + h) = make_uint2(x.z, x.w);
     }
   }
   __syncthreads();
   if (wave * 16 >= a.lq) return;  // no query rows in this wave
 
   const int tau = pos0 + row;
-  f32x4 o[NB];
+  constexpr int NT = kSplitGroups / 2;  // tiles of 32 keys (two 16-key blocks)
+  // ---- pass 1: S^T of all 128 keys, kept in registers.  Tile t, block n,
+  // k-step k: A = keys 32t + 16n + 0..15 (this lane: key rl) at dims 32k +
+  // 8qg + 0..7, chunk index swizzled by key % 16 = rl; B = the query (hi and
+  // lo products into one accumulator).
+  // The operand reads of tile t + 1 are issued before the products of tile
+  // t (scheduling barriers keep that order), so LDS latency hides under the
+  // matrix-core work.
+  auto load_k = [&](int t, bf16x8 (&kop)[2][KS]) {
 #pragma unroll
-  for (int n = 0; n < NB; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-  for (int t = 0; t < kSplitGroups / 2; ++t) {
-    const int ga = gpos[2 * t], gb = gpos[2 * t + 1];
-    if (ga < 0 && gb < 0) continue;  // uniform
-    f32x4 s[2];
+      for (int k = 0; k < KS; ++k)
+        kop[n][k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(ks + (32 * t + 16 * n + rl) * D + (((4 * k + qg) ^ rl) * 8)));
+  };
+  f32x4 s[NT][2];
+  bf16x8 kop[2][2][KS];
+  load_k(0, kop[0]);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      s[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = 32 * t + 16 * n + rl;
+  for (int t = 0; t < NT; ++t) {
+    if (t + 1 < NT) load_k(t + 1, kop[(t + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 kop = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(ks + key * D + (((4 * k + qg) ^ (key % CH)) * 8)));
-        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop_hi[k], s[n], 0, 0, 0);
-        s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop_lo[k], s[n], 0, 0, 0);
-      }
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        s[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t & 1][n][k], qop_hi[k], s[t][n], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        s[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t & 1][n][k], qop_lo[k], s[t][n], 0, 0, 0);
     }
-    // this lane: keys 32t + 16n + 4qg + i of query row `row`
-    float sv[8];
-    float tmax = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // V^T operands of tile t: dims 16n + 0..15 (this lane: dim 16n + rl) at
+  // the lane's 8 keys of the tile, one 16-byte chunk of the V^T row
+  auto load_v = [&](int t, bf16x8 (&vop)[NB]) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      vop[n] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(vt + (16 * n + rl) * kSplitKeys + (((4 * t + qg) ^ rl) * 8)));
+  };
+  bf16x8 vop[2][NB];
+  load_v(0, vop[0]);  // in flight during the softmax below
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- masks and the row maximum over the split: this lane holds keys
+  // 32t + 16n + 4qg + i of query row `row`; the 4 lanes of a column hold the
+  // rest of the row.  A key is visible if its group is present and it does
+  // not follow the query token.  With the maximum known before any
+  // probability, no running rescale of o is needed.
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const int gp = n ? gb : ga;
+      const int gp = gpos[2 * t + n];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool vis = gp >= 0 && gp + 4 * qg + i <= tau;
-        sv[4 * n + i] = vis ? s[n][i] : -INFINITY;
-        tmax = fmaxf(tmax, sv[4 * n + i]);
+        s[t][n][i] = vis ? s[t][n][i] : -INFINITY;
+        tmax = fmaxf(tmax, s[t][n][i]);
       }
     }
-    tmax = rows_max(tmax);
-    const float mn = fmaxf(m, tmax);
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float al = exp2f(m - mref);
-    l *= al;
+  const float m = rows_max(tmax);
+  const float mref = m == -INFINITY ? 0.f : m;  // a row with no visible key: p = 0
+  // ---- probabilities as the B operand of O^T = V^T P^T: k-slot 4n + i of
+  // tile t is key 32t + 16n + 4qg + i, split into bf16 hi + lo
+  float l = 0.f;
+  bf16x8 pop_hi[NT], pop_lo[NT];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) o[n] *= al;
-    m = mn;
+  for (int t = 0; t < NT; ++t) {
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = exp2f(sv[2 * k] - mref), p1 = exp2f(sv[2 * k + 1] - mref);
+      const float p0 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1)] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1) + 1] - mref);
       l += p0 + p1;
-      uint32_t h0, l0, h1, l1;
-      split_hi_lo(p0, h0, l0);
-      split_hi_lo(p1, h1, l1);
-      ph[k] = h0 | (h1 << 16);
-      pl[k] = l0 | (l1 << 16);
+      split_pair(p0, p1, ph[k], pl[k]);
     }
-    const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+    pop_hi[t] = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    pop_lo[t] = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+  }
+  // ---- pass 2: O^T += V^T P^T
+  f32x4 o[NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int r = 16 * n + rl;  // dim
-      const uint2 va = *reinterpret_cast<const uint2*>(vt + r * kSplitKeys + (((8 * t + qg) ^ (r & 31)) * 4));
-      const uint2 vb = *reinterpret_cast<const uint2*>(vt + r * kSplitKeys + (((8 * t + 4 + qg) ^ (r & 31)) * 4));
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_hi, o[n], 0, 0, 0);
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop_lo, o[n], 0, 0, 0);
-    }
+  for (int n = 0; n < NB; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + 1 < NT) load_v(t + 1, vop[(t + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_hi[t], o[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_lo[t], o[n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   l = rows_sum(l);
   const int ri = sp + record_base(a, lp);  // < n_splits for lists hga_route can write
