@@ -173,6 +173,9 @@ def main():
                          "64-token query chunk at 32K context (MFMA attention); host64k: "
                          "batch-4 64K decode with the pool in pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="decode sweep over context 4K..64K and batch 8..32 (one JSON line "
+                         "per point) instead of the benchmark line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +186,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.sweep:
+        run_sweep(args)
+        return
     if args.workload == "prefill32k":
         run_prefill32k(args)
     elif args.workload == "host64k":
@@ -192,6 +198,17 @@ def main():
 
 
 def run_decode64k(args):
+    out, inp = measure_decode(args, "decode64k")
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, inp.params)
+    print(json.dumps(out), flush=True)
+
+
+def measure_decode(args, name, batch=None, context=None, overrides=None, replicas=None):
+    """Time the fused decode step of workload ``name`` (optionally resized)
+    as a replayed HIP graph, and the attend / route calls with events.
+    Returns the result line (without cpu_baseline) and the inputs."""
     import numpy as np
     import torch
 
@@ -202,7 +219,7 @@ def run_decode64k(args):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     t_gen = time.time()
-    inp = synth.generate("decode64k")
+    inp = synth.generate(name, batch=batch, context=context, overrides=overrides)
     p = inp.params
     B, T = p["batch"], p["context"]
     st = gh.build_state(inp)
@@ -218,7 +235,7 @@ def run_decode64k(args):
     kt = st.k_raw[:, :, pos:pos + 1].contiguous()
     vt = st.v_raw[:, :, pos:pos + 1].contiguous()
     kc = st.k_raw[:, :, c0:c0 + 64].contiguous()
-    R = max(1, args.replicas)
+    R = max(1, args.replicas if replicas is None else replicas)
     reps = []
     for r in range(R):
         reps.append(dict(
@@ -319,9 +336,13 @@ def run_decode64k(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, pre-RoPE)",
-        "config": {"workload": "decode64k: GQA 32q/4kv heads, d=128, bf16, theta 1e6, ctx 65536, "
-                               "batch 8 decode at t=65535, C=64 (4x16), 1 sink + 4 local chunks, "
-                               "top-52 chunks, top-104 groups (2048 keys, 3.125%), pool in HBM",
+        "config": {"workload": f"{name}: GQA {p['n_q_heads']}q/{p['n_kv_heads']}kv heads, "
+                               f"d={p['head_dim']}, bf16, theta {p['rope_theta']:g}, ctx {T}, "
+                               f"batch {B} decode at t={pos}, C=64 (4x16), "
+                               f"{p['n_sink_chunks']} sink + {p['n_local_chunks']} local chunks, "
+                               f"top-{p['topk_chunks']} chunks, top-{p['topk_groups']} groups "
+                               f"({st.max_sel * 16} keys, {100.0 * st.max_sel * 16 / T:.3g}%), "
+                               "pool in HBM",
                    "batch": B, "context": T, "replicas": R,
                    "timing": "HIP graph of R steps, replayed",
                    "step_bytes_algorithmic": ab["total"],
@@ -332,10 +353,45 @@ def run_decode64k(args):
                      "bytes_per_launch": ab["attend"], "launch_ms": attend_ms,
                      "route_launch_ms": route_ms, "route_bytes_per_launch": ab["route"]},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, p)
-    print(json.dumps(out), flush=True)
+    del reps, st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out, inp
+
+
+# Decode sweep: context 4K..64K and batch 8..32 at 64K.  4K is the 4K decode
+# workload as defined (batch 1, top-8 chunks, top-16 groups); 8K and 16K keep
+# its budget at batch 8 (the windows alone are 384 tokens, above 3.125 % of
+# 8K); 32K and 64K use the 3.125 % budgets of the 32K and 64K workloads.
+SWEEP = [
+    ("decode4k", None, None, None),
+    ("decode64k", 8, 8192, dict(topk_chunks=8, topk_groups=16)),
+    ("decode64k", 8, 16384, dict(topk_chunks=8, topk_groups=16)),
+    ("decode64k", 8, 32768, dict(topk_chunks=20, topk_groups=40)),
+    ("decode64k", 8, 65536, None),
+    ("decode64k", 16, 65536, None),
+    ("decode64k", 32, 65536, None),
+]
+
+
+def run_sweep(args):
+    """One JSON line per sweep point: whole-step tokens/s and the attention
+    call's achieved GB/s against the HBM peak."""
+    for name, batch, context, over in SWEEP:
+        B = batch or 1
+        R = args.replicas if B <= 8 else max(2, args.replicas * 8 // B)
+        print(f"[sweep] {name} batch {batch} context {context} {over or ''} replicas {R}",
+              file=sys.stderr, flush=True)
+        out, _ = measure_decode(args, name, batch=batch, context=context, overrides=over,
+                                replicas=R)
+        c, r = out["config"], out["roofline"]
+        print(json.dumps({"sweep": "decode", "workload": c["workload"], "context": c["context"],
+                          "batch": c["batch"], "tokens_per_s": out["value"],
+                          "ms_per_step": out["ms_per_step"],
+                          "step_GBps_algorithmic": c["step_GBps_algorithmic"],
+                          "attend_ms": r["launch_ms"], "attend_bytes": r["bytes_per_launch"],
+                          "attend_GBps": r["achieved"], "attend_frac_of_8TBps": r["frac"],
+                          "route_ms": r["route_launch_ms"]}), flush=True)
 
 
 def prefill_algorithmic(p):

@@ -199,12 +199,33 @@ __device__ int wave_topk(const double* s, int n, int k, int* out, const TopkScra
 // counts.  Same histogram / cut / boundary-rank steps as wave_topk, with a
 // quarter of the elements per lane.  Scratch: hist (256 ints), bl (n ints),
 // red (8 doubles), ints (8 ints).
+//
+// Every barrier is a round of LDS latency for the whole workgroup, so the
+// range of the scores is not reduced here: the threads that write s call
+// topk_publish before the barrier that publishes s, which also clears the
+// histogram.  The boundary bin is then found by every wave from the same
+// histogram, with no barrier between the count and the cut.
 struct BlockTopkScratch {
   int* hist;
   int* bl;
   double* red;
   int* ints;
 };
+
+// Called by all 256 threads before the barrier that publishes the scores:
+// mn / mx are the min and max of the scores this thread wrote (+inf / -inf if
+// none).
+__device__ __forceinline__ void topk_publish(double mn, double mx, const BlockTopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  mn = wave_ext_d<false>(mn);
+  mx = wave_ext_d<true>(mx);
+  if (lane == 0) {
+    sc.red[wave] = mn;
+    sc.red[4 + wave] = mx;
+  }
+  sc.hist[tid] = 0;
+  if (tid == 0) sc.ints[2] = 0;  // boundary members collected
+}
 
 __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTopkScratch& sc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -214,7 +235,6 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
     __syncthreads();
     return n;
   }
-  sc.hist[tid] = 0;
   double x[4];
   bool v[4];
 #pragma unroll
@@ -223,21 +243,8 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
     v[e] = i < n;
     x[e] = s[v[e] ? i : n - 1];
   }
-  double mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    mn = fmin(mn, v[e] ? x[e] : INFINITY);
-    mx = fmax(mx, v[e] ? x[e] : -INFINITY);
-  }
-  mn = wave_ext_d<false>(mn);
-  mx = wave_ext_d<true>(mx);
-  if (lane == 0) {
-    sc.red[wave] = mn;
-    sc.red[4 + wave] = mx;
-  }
-  __syncthreads();
-  mn = fmin(fmin(sc.red[0], sc.red[1]), fmin(sc.red[2], sc.red[3]));
-  mx = fmax(fmax(sc.red[4], sc.red[5]), fmax(sc.red[6], sc.red[7]));
+  const double mn = fmin(fmin(sc.red[0], sc.red[1]), fmin(sc.red[2], sc.red[3]));
+  const double mx = fmax(fmax(sc.red[4], sc.red[5]), fmax(sc.red[6], sc.red[7]));
   const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
   int bin[4];
 #pragma unroll
@@ -246,17 +253,8 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
     if (bin[e] >= 0) atomicAdd(&sc.hist[bin[e]], 1);
   }
   __syncthreads();
-  if (wave == 0) {
-    int bs, need;
-    topk_cut(sc.hist, k, &bs, &need);
-    if (lane == 0) {
-      sc.ints[0] = bs;
-      sc.ints[1] = need;
-      sc.ints[2] = 0;  // boundary members collected
-    }
-  }
-  __syncthreads();
-  const int bs = sc.ints[0], need = sc.ints[1];
+  int bs, need;
+  topk_cut(sc.hist, k, &bs, &need);  // the same result in every wave
   const int nb = sc.hist[bs];
   int keep = 0;  // bit e: element 4t+e kept
 #pragma unroll
@@ -274,10 +272,16 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
       if (bin[e] == bs) {
         const int i = 4 * tid + e;
         int r = 0;
-        for (int u = 0; u < nb; ++u) {
-          const int j = sc.bl[u];
-          const double sj = s[j];
-          r += (sj > x[e]) || (sj == x[e] && j < i);
+        for (int u = 0; u < nb; u += 4) {  // 4 members per round of LDS reads
+          int j[4];
+          double sj[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) j[q] = sc.bl[u + q < nb ? u + q : nb - 1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sj[q] = s[j[q]];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            r += (u + q < nb) && ((sj[q] > x[e]) || (sj[q] == x[e] && j[q] < i));
         }
         keep |= (r < need ? 1 : 0) << e;
       }
@@ -308,7 +312,9 @@ __device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch&
          w->cand_hi - w->cand_lo <= max_cand;
 }
 
-template <int D, bool BF16>
+// MULTI: more query tokens than token slices S (chunked prefill); a separate
+// instantiation so that the decode form keeps its small register footprint.
+template <int D, bool BF16, bool MULTI>
 __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   constexpr int P = D / 2;
   constexpr int S = 256 / P;                 // query-token slices
@@ -317,7 +323,13 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   constexpr int ITER = (kTile / 4) / RPI;    // row passes per wave
   using T = typename std::conditional<BF16, uint16_t, float>::type;
 
-  __shared__ double qpart[S][P][2];
+  constexpr int JP = P / 2;                  // multi-token path: two adjacent pairs per thread
+  constexpr int S2 = 256 / JP;               // multi-token path: query-token slices
+  constexpr int TPT = kChunk / S2;           // multi-token path: tokens per thread (max)
+  using QT = typename std::conditional<BF16, uint32_t, float2>::type;  // two adjacent dims
+  constexpr int TB = BF16 ? 4 : 2;           // multi-token path: tokens per load batch (64 VGPRs)
+  static_assert(TPT % TB == 0, "token batches");
+  __shared__ double qpart[S2][P][2];
   __shared__ double qbar[D];
 
   const KCfg& c = a.cfg;
@@ -333,15 +345,36 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const int tile0 = blockIdx.x * kTile;
   if (tile0 >= n_cand && blockIdx.x != 0) return;  // tile 0 always stores qbar
 
-  // ---- loads: this thread's raw query pairs (first query token of its
-  // slice) first, then the tile's summary rows.  Rows past the candidates
-  // are read from a clamped in-range row (so every load issues together) and
-  // ignored.
+  // ---- loads: the query first, then the tile's summary rows.  Rows past
+  // the candidates are read from a clamped in-range row (so every load
+  // issues together) and ignored.
+  //   up to S query tokens: thread (j, sl) loads pair j of every query head
+  //   of this KV head for token sl;
+  //   more tokens (prefill): thread (jp, sl2) loads pairs 2jp, 2jp + 1 (two
+  //   adjacent dims of each half) for tokens sl2, sl2 + S2, ..., in batches
+  //   of TB tokens with all their loads in flight (clamped to the last
+  //   token; extras ignored).
+  constexpr bool multi = MULTI;
   const int j = tid % P, sl = tid / P;
+  const int jp = tid % JP, sl2 = tid / JP;
   const T* q = static_cast<const T*>(r.q);
-  const double wj = c.omega[j];
   T xa[8], xb[8];
-  {
+  QT ya[TB][8], yb[TB][8];
+  auto load_batch = [&](int u0) {  // tokens sl2 + (u0 + u) * S2, u < TB
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int tt = sl2 + (u0 + u) * S2;
+      const int t = tt < lq ? tt : lq - 1;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        const int hc = hh < c.hg ? hh : c.hg - 1;
+        const size_t row = ((size_t)(b * c.hq + h * c.hg + hc) * lq + t) * D;
+        ya[u][hh] = *reinterpret_cast<const QT*>(q + row + 2 * jp);
+        yb[u][hh] = *reinterpret_cast<const QT*>(q + row + P + 2 * jp);
+      }
+    }
+  };
+  if constexpr (!multi) {
     const int t0 = sl < lq ? sl : lq - 1;
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
@@ -350,6 +383,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       xa[hh] = q[row + j];
       xb[hh] = q[row + j + P];
     }
+  } else {
+    load_batch(0);
   }
   const int sub = lane % kLanesPerRow, rin = lane / kLanesPerRow;
   float4 buf[ITER][NV];
@@ -363,82 +398,97 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     for (int v = 0; v < NV; ++v) buf[it][v] = rowp[v * kLanesPerRow + sub];
   }
 
-  // ---- pooled routing query (fp64): thread (j, slice) rotates pair j of
-  // every query head of this KV head for the query tokens of its slice,
-  // t = sl, sl+S, ...  The head sum of a token is rotated once; the angle of
-  // the next token of the slice follows by one fp64 rotation by S*omega_j
-  // (error ~1e-16 per step); later tokens (prefill) are loaded in batches of
-  // 4 with all their loads in flight.
+  // ---- pooled routing query (fp64): the query heads of this KV head are
+  // summed per token and dim, the head sum of each token is rotated to the
+  // token's position once, and the rotated sums are added over tokens.  The
+  // angle of a thread's next token follows by one fp64 rotation by the
+  // token stride times omega_j (error ~1e-16 per step).
   {
-    double qa = 0.0, qb = 0.0;
-    double cs, sn, cd = 1.0, sd = 0.0;
-    rope_cs((double)(pos0 + sl), wj, &cs, &sn);
-    if (lq > S) sincos((double)S * wj, &sd, &cd);
-    auto head_sum = [&](const T* ha, const T* hb, double* x, double* y) {
-      double sx = 0.0, sy = 0.0;
+    auto to_d = [](T x) -> double {
+      if constexpr (BF16) return bf16_to_f(x);
+      else return x;
+    };
+    if constexpr (!multi) {
+      if (sl < lq) {
+        double x = 0.0, y = 0.0;
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) {
-        if (hh < c.hg) {
-          if constexpr (BF16) {
-            sx += bf16_to_f(ha[hh]);
-            sy += bf16_to_f(hb[hh]);
-          } else {
-            sx += ha[hh];
-            sy += hb[hh];
+        for (int hh = 0; hh < 8; ++hh)
+          if (hh < c.hg) {
+            x += to_d(xa[hh]);
+            y += to_d(xb[hh]);
+          }
+        double cs, sn;
+        rope_cs((double)(pos0 + sl), c.omega[j], &cs, &sn);
+        qpart[sl][j][0] = x * cs - y * sn;
+        qpart[sl][j][1] = x * sn + y * cs;
+      } else {
+        qpart[sl][j][0] = 0.0;
+        qpart[sl][j][1] = 0.0;
+      }
+    } else {
+      double qa[2] = {0.0, 0.0}, qb[2] = {0.0, 0.0};
+      double cs[2], sn[2], cd[2], sd[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const double wj = c.omega[2 * jp + e];
+        rope_cs((double)(pos0 + sl2), wj, &cs[e], &sn[e]);
+        sincos((double)S2 * wj, &sd[e], &cd[e]);
+      }
+      for (int u0 = 0; u0 < TPT && sl2 + u0 * S2 < lq; u0 += TB) {
+        if (u0 > 0) load_batch(u0);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          if (sl2 + (u0 + u) * S2 < lq) {
+            double x[2] = {0.0, 0.0}, y[2] = {0.0, 0.0};
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh)
+              if (hh < c.hg) {
+                if constexpr (BF16) {
+                  x[0] += bf16_to_f((uint16_t)(ya[u][hh] & 0xFFFFu));
+                  x[1] += bf16_to_f((uint16_t)(ya[u][hh] >> 16));
+                  y[0] += bf16_to_f((uint16_t)(yb[u][hh] & 0xFFFFu));
+                  y[1] += bf16_to_f((uint16_t)(yb[u][hh] >> 16));
+                } else {
+                  x[0] += ya[u][hh].x;
+                  x[1] += ya[u][hh].y;
+                  y[0] += yb[u][hh].x;
+                  y[1] += yb[u][hh].y;
+                }
+              }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              qa[e] += x[e] * cs[e] - y[e] * sn[e];
+              qb[e] += x[e] * sn[e] + y[e] * cs[e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const double c2 = cs[e] * cd[e] - sn[e] * sd[e];
+            sn[e] = sn[e] * cd[e] + cs[e] * sd[e];
+            cs[e] = c2;
           }
         }
       }
-      *x = sx;
-      *y = sy;
-    };
-    auto rotate_add = [&](double x, double y) {
-      qa += x * cs - y * sn;
-      qb += x * sn + y * cs;
-      const double c2 = cs * cd - sn * sd;
-      sn = sn * cd + cs * sd;
-      cs = c2;
-    };
-    if (sl < lq) {
-      double x, y;
-      head_sum(xa, xb, &x, &y);
-      rotate_add(x, y);
-    }
-    for (int t0 = sl + S; t0 < lq; t0 += 4 * S) {  // prefill: later tokens
-      T ya[4][8], yb[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = t0 + u * S < lq ? t0 + u * S : lq - 1;
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-          const int hc = hh < c.hg ? hh : c.hg - 1;
-          const size_t row = ((size_t)(b * c.hq + h * c.hg + hc) * lq + t) * D;
-          ya[u][hh] = q[row + j];
-          yb[u][hh] = q[row + j + P];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (t0 + u * S < lq) {
-          double x, y;
-          head_sum(ya[u], yb[u], &x, &y);
-          rotate_add(x, y);
-        }
+      for (int e = 0; e < 2; ++e) {
+        qpart[sl2][2 * jp + e][0] = qa[e];
+        qpart[sl2][2 * jp + e][1] = qb[e];
       }
     }
-    qpart[sl][j][0] = qa;
-    qpart[sl][j][1] = qb;
     __syncthreads();
-    if (sl == 0) {
-      for (int u = 1; u < S; ++u) {
-        qa += qpart[u][j][0];
-        qb += qpart[u][j][1];
+    if (tid < P) {
+      const int ns = multi ? S2 : S;
+      double sa = 0.0, sb = 0.0;
+      for (int u = 0; u < ns; ++u) {
+        sa += qpart[u][tid][0];
+        sb += qpart[u][tid][1];
       }
       const double inv = 1.0 / (double)(c.hg * lq);
-      qbar[j] = qa * inv;
-      qbar[j + P] = qb * inv;
+      qbar[tid] = sa * inv;
+      qbar[tid + P] = sb * inv;
       if (blockIdx.x == 0) {
-        r.qbar[(size_t)unit * D + j] = qa * inv;
-        r.qbar[(size_t)unit * D + j + P] = qb * inv;
+        r.qbar[(size_t)unit * D + tid] = sa * inv;
+        r.qbar[(size_t)unit * D + tid + P] = sb * inv;
       }
     }
     __syncthreads();
@@ -569,12 +619,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const TopkScratch tks{hist, bl, win};
   const BlockTopkScratch bts{hist, bl, red, ints};
 
+  double mn1 = INFINITY, mx1 = -INFINITY;
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
     const int i = u * 256 + tid;
-    if (i < n_cand) s_lds[i] = v4[u];
+    if (i < n_cand) {
+      s_lds[i] = v4[u];
+      mn1 = fmin(mn1, v4[u]);
+      mx1 = fmax(mx1, v4[u]);
+    }
   }
   for (int i = SPT * 256 + tid; i < n_cand; i += 256) s_lds[i] = scores[i];
+  topk_publish(mn1, mx1, bts);
   __syncthreads();
   // level 1: kept candidate indices, ascending, into sel
   int k1;
@@ -592,6 +648,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   // level 2 (all waves): the G groups of each kept chunk
   const int n2 = k1 * kGroups;
   const int rsub = tid / kLanesPerRow;
+  double mn2 = INFINITY, mx2 = -INFINITY;
   for (int base = 0; base < n2; base += RPP * U) {
     float4 gb[U][NV];
 #pragma unroll
@@ -615,10 +672,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
         d = fma((double)gb[u][v].z, qv[v][2], d);
         d = fma((double)gb[u][v].w, qv[v][3], d);
       }
-      d = group8_sum_d(d);
-      if (sub == 0 && i < n2) s_lds[i] = d * c.inv_sqrt_d;
+      d = group8_sum_d(d) * c.inv_sqrt_d;
+      if (sub == 0 && i < n2) {
+        s_lds[i] = d;
+        mn2 = fmin(mn2, d);
+        mx2 = fmax(mx2, d);
+      }
     }
   }
+  topk_publish(mn2, mx2, bts);
   __syncthreads();
   // level 2 selection: kept group indices, ascending = gid order
   int k2;
@@ -670,6 +732,12 @@ size_t route_select_lds(const KCfg& cfg, int max_chunks) {
   return nmax * (sizeof(double) + 3 * sizeof(int)) + (size_t)n2 * sizeof(int);
 }
 
+template <int D, bool BF16>
+static void launch_tiles(bool multi, dim3 grid, hipStream_t st, const RouteArgs& a) {
+  if (multi) hipLaunchKernelGGL((route_tiles_kernel<D, BF16, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((route_tiles_kernel<D, BF16, false>), grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
                         const StepFront* front) {
   RouteArgs a{};
@@ -684,20 +752,21 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   dim3 grid(n_tiles, cfg.hkv, r.B);
   dim3 sgrid(cfg.hkv, r.B, front ? 2 : 1);
   const bool bf = cfg.dtype == HGA_BF16;
+  const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   if (cfg.d == 128) {
     if (bf) {
-      hipLaunchKernelGGL((route_tiles_kernel<128, true>), grid, dim3(256), 0, st, a);
+      launch_tiles<128, true>(multi, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
     } else {
-      hipLaunchKernelGGL((route_tiles_kernel<128, false>), grid, dim3(256), 0, st, a);
+      launch_tiles<128, false>(multi, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
     }
   } else {
     if (bf) {
-      hipLaunchKernelGGL((route_tiles_kernel<64, true>), grid, dim3(256), 0, st, a);
+      launch_tiles<64, true>(multi, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
     } else {
-      hipLaunchKernelGGL((route_tiles_kernel<64, false>), grid, dim3(256), 0, st, a);
+      launch_tiles<64, false>(multi, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
     }
   }
