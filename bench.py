@@ -33,8 +33,10 @@ about 10 s, on this host's cores.
 
 ``--workload prefill32k`` runs the chunked-prefill leg instead: one 64-token
 query chunk at 32K context (append + summaries of the chunk, routing with the
-pooled query, MFMA attention), reported as query tokens/s with the attention
-call's achieved TFLOP/s against the bf16 dense MFMA peak.
+pooled query, MFMA attention; one hga_prefill_step call), reported as query
+tokens/s with the attention call's achieved TFLOP/s against the bf16 dense
+MFMA peak.  ``--sweep`` prints one line per decode sweep point (context 4K to
+64K, batch 8 to 32 at 64K) instead of the benchmark line.
 """
 from __future__ import annotations
 
@@ -490,31 +492,39 @@ def run_prefill32k(args):
             chunk_sum=st.chunk_sum if r == 0 else st.chunk_sum.clone(),
             group_sum=st.group_sum if r == 0 else st.group_sum.clone(),
             q=st.q if r == 0 else st.q.clone(), kc=kc if r == 0 else kc.clone(),
-            vc=vc if r == 0 else vc.clone(), ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, lq)))
+            vc=vc if r == 0 else vc.clone(), stage=torch.zeros_like(kc),
+            ws=torch.zeros_like(st.ws), s=gh.alloc_step(st, lq)))
     del st.k_raw, st.v_raw
     torch.cuda.synchronize()
     cfg = st.cfg
 
     def step(r, ev=None):
         # the query chunk's K/V enter the pool (and its summaries are built),
-        # then its 64 tokens are routed (pooled query) and attended
+        # then its 64 tokens are routed (pooled query) and attended: one
+        # hga_prefill_step (four launches); with events, the same work through
+        # the separate entry points, timing the route and attend calls
         x = reps[r]
         s = x["s"]
+        if ev is None:
+            hga.hga_prefill_step(cfg, B, x["q"], lq, x["kc"], x["vc"], st.pos0, x["k_pool"],
+                                 x["v_pool"], T, x["stage"], x["chunk_sum"], x["group_sum"],
+                                 st.max_chunks, s.sel, s.n_sel, st.max_sel, s.out, s.lse, x["ws"])
+            return
         hga.hga_build_summaries(cfg, B, x["kc"], x["vc"], pos, lq, x["k_pool"], x["v_pool"], T,
                                 x["chunk_sum"], x["group_sum"], st.max_chunks)
-        if ev is not None:
-            ev[0].record()
+        ev[0].record()
         hga.hga_route(cfg, B, x["q"], lq, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
                       s.sel, s.n_sel, st.max_sel, None, x["ws"])
-        if ev is not None:
-            ev[1].record()
+        ev[1].record()
         hga.hga_attend(cfg, B, x["q"], lq, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
                        s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
-        if ev is not None:
-            ev[2].record()
+        ev[2].record()
 
     ms_step, steps_timed = time_graph(step, R, args)
+    fused_out = [x["s"].out.clone() for x in reps]
     route_ms, attend_ms = time_launches(step, R, args)
+    for r, x in enumerate(reps):  # the separate calls give the fused step's bits
+        assert torch.equal(x["s"].out, fused_out[r]), "separate calls differ from the fused step"
     s0 = reps[0]["s"]
     assert torch.isfinite(s0.out).all().item()
     alg = prefill_algorithmic(p)
@@ -537,7 +547,7 @@ def run_prefill32k(args):
                                "query chunk 511 (64 tokens at 32704..32767), 1 sink + 4 local "
                                "chunks, top-20 chunks, top-40 groups (1024 keys, 3.125%)",
                    "batch": B, "context": T, "query_tokens": lq, "replicas": R,
-                   "timing": "HIP graph of R steps, replayed"},
+                   "timing": "HIP graph of R hga_prefill_step calls, replayed"},
         "roofline": {"kernel": "hga_attend (MFMA prefill split + merge kernels)", "bound": "mfma",
                      "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": achieved / 2500.0, "traffic": None,

@@ -218,14 +218,46 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
  *               the chunk's earlier positions.
  *   other arguments as hga_build_summaries, hga_route and hga_attend; the
  *   workspace is shared by the route and attend phases.
- * A position outside the pool gives n_sel = -1 and NaN outputs and writes
- * nothing.  Errors: as hga_route and hga_attend. */
+ * An unusable position (negative, outside the pool or beyond max_chunks
+ * chunks) gives n_sel = -1 and NaN outputs and writes nothing.  Errors: as
+ * hga_route and hga_attend.  hga_decode_step is hga_prefill_step with lq = 1. */
 hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, const void* k_new,
                            const void* v_new, const int32_t* q_pos0, void* k_pool, void* v_pool,
                            int32_t pool_cap, void* k_stage, float* chunk_sum, float* group_sum,
                            int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
                            int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* One fused chunked-prefill step: for each sequence b, the lq query tokens at
+ * positions q_pos0[b] .. q_pos0[b] + lq - 1, all inside one chunk, are
+ * appended, routed with their pooled query and attended, in the four
+ * launches of hga_decode_step.  This is the per-chunk step of the page's
+ * chunked prefill (HGA technical summary, "Kernmechanisme" items 2-4: the
+ * current chunk's queries route over the chunk summaries and attend the
+ * exact K/V of the selected set; "Experimentele Resultaten" reports the
+ * speed-up of fusing it).
+ *   q_raw        [B][Hq][lq][d] raw queries
+ *   k_new, v_new [B][Hkv][lq][d] raw keys and values of the lq tokens
+ *   k_stage      as hga_decode_step: rows of the chunk's positions before
+ *                q_pos0[b] must hold their raw keys; the call writes the rows
+ *                of its own tokens.  When the last token ends its chunk the
+ *                chunk's summaries are built (from those rows and the new
+ *                keys; in one pass when the step holds the whole chunk).
+ *   other arguments as hga_decode_step; ws sized by hga_workspace_bytes with
+ *   max_lq >= lq.
+ * Results are bit-identical to hga_build_summaries (append of the lq tokens,
+ * then the chunk's summaries if it ends), hga_route and hga_attend with the
+ * same arguments.  lq >= 16 runs the matrix-core prefill attention, which
+ * needs head_dim 128 and bf16 (else HGA_ERR_UNSUPPORTED).
+ * Errors: HGA_ERR_INVALID_ARGUMENT for lq outside 1..chunk_size; otherwise as
+ * hga_decode_step.  Tokens that would cross a chunk end make the position
+ * unusable (n_sel = -1, NaN outputs, nothing written). */
+hga_status hga_prefill_step(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                            const void* k_new, const void* v_new, const int32_t* q_pos0,
+                            void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
+                            float* chunk_sum, float* group_sum, int32_t max_chunks,
+                            int32_t* sel_groups, int32_t* n_sel, int32_t max_sel, float* out,
+                            float* lse_opt, void* ws, size_t ws_bytes, void* stream);
 
 /* Host-tier attention (page section "Geheugenarchitectuur": summaries and the
  * always-visible windows are hot in device memory, the full token K/V history

@@ -32,7 +32,8 @@ HGA_PART_ROUTED = 2
 
 EXPORTED = ("hga_validate", "hga_max_selected", "hga_workspace_bytes", "hga_workspace_reset",
             "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_decode_step",
-            "hga_attend_tiered", "hga_merge_partials", "hga_status_string", "hga_version")
+            "hga_prefill_step", "hga_attend_tiered", "hga_merge_partials", "hga_status_string",
+            "hga_version")
 
 
 class HgaError(RuntimeError):
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
                            ctypes.c_size_t, _P],
             "hga_decode_step": [_C, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P, _I,
                                 _P, _P, _P, ctypes.c_size_t, _P],
+            "hga_prefill_step": [_C, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P,
+                                 _I, _P, _P, _P, ctypes.c_size_t, _P],
             "hga_attend_tiered": [_C, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P,
                                   _P, _P, _P, ctypes.c_size_t, _P, _P],
             "hga_merge_partials": [_C, _I, _I, _P, _P, _P, _P, _P, _P, _P],
@@ -214,6 +217,17 @@ def hga_decode_step(cfg, B, q_raw, k_new, v_new, q_pos0, k_pool, v_pool, pool_ca
                                  _ptr(n_sel), max_sel, _ptr(out), _ptr(lse_opt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "hga_decode_step")
+
+
+def hga_prefill_step(cfg, B, q_raw, lq, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
+                     chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
+                     stream=None):
+    _check(lib().hga_prefill_step(_cfg(cfg), B, _ptr(q_raw), lq, _ptr(k_new), _ptr(v_new),
+                                  _ptr(q_pos0), _ptr(k_pool), _ptr(v_pool), pool_cap,
+                                  _ptr(k_stage), _ptr(chunk_sum), _ptr(group_sum), max_chunks,
+                                  _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(out), _ptr(lse_opt),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "hga_prefill_step")
 
 
 def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, v_cold, cold_cap,

@@ -256,26 +256,30 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   return hip_status(launch_attend(k, a, (hipStream_t)stream));
 }
 
-hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, const void* k_new,
-                           const void* v_new, const int32_t* q_pos0, void* k_pool, void* v_pool,
-                           int32_t pool_cap, void* k_stage, float* chunk_sum, float* group_sum,
-                           int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
-                           int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
-                           void* stream) {
+// The fused step for lq query tokens of one chunk per sequence (decode:
+// lq = 1; chunked prefill: up to a chunk).
+static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                             const void* k_new, const void* v_new, const int32_t* q_pos0,
+                             void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
+                             float* chunk_sum, float* group_sum, int32_t max_chunks,
+                             int32_t* sel_groups, int32_t* n_sel, int32_t max_sel, float* out,
+                             float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (B <= 0 || !q_raw || !k_new || !v_new || !q_pos0 || !k_pool || !v_pool || pool_cap <= 0 ||
-      pool_cap % kGroupTokens != 0 || !k_stage || !chunk_sum || !group_sum || max_chunks <= 0 ||
-      !sel_groups || !n_sel || !out || !ws)
+  if (B <= 0 || lq <= 0 || lq > kChunk || !q_raw || !k_new || !v_new || !q_pos0 || !k_pool ||
+      !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 || !k_stage || !chunk_sum ||
+      !group_sum || max_chunks <= 0 || !sel_groups || !n_sel || !out || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
+  if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
+    return HGA_ERR_UNSUPPORTED;
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads > kMaxUnits || grid_z_of(cfg, B, 1) > kMaxGridZ)
+  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
   const size_t need_r = route_ws_bytes(k, B, max_chunks);
-  const size_t need_a = attend_ws_bytes(k, B, 1, max_sel);
+  const size_t need_a = attend_ws_bytes(k, B, lq, max_sel);
   if (ws_bytes < need_r || ws_bytes < need_a) return HGA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -291,7 +295,7 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
   r.scores = static_cast<double*>(ws);
   r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
   r.B = B;
-  r.lq = 1;
+  r.lq = lq;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
   StepFront f;
@@ -317,7 +321,7 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
   a.lse = lse_opt;
   a.part = static_cast<float*>(ws);
   a.B = B;
-  a.lq = 1;
+  a.lq = lq;
   a.src_layout = HGA_SRC_POOL;
   a.src_cap = pool_cap;
   a.max_sel = max_sel;
@@ -325,6 +329,28 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
   a.two_part = 0;
   a.rec_splits = 0;
   return hip_status(launch_attend(k, a, st));
+}
+
+hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, const void* k_new,
+                           const void* v_new, const int32_t* q_pos0, void* k_pool, void* v_pool,
+                           int32_t pool_cap, void* k_stage, float* chunk_sum, float* group_sum,
+                           int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
+                           int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return fused_step(cfg, B, q_raw, 1, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
+                    chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
+                    ws_bytes, stream);
+}
+
+hga_status hga_prefill_step(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
+                            const void* k_new, const void* v_new, const int32_t* q_pos0,
+                            void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
+                            float* chunk_sum, float* group_sum, int32_t max_chunks,
+                            int32_t* sel_groups, int32_t* n_sel, int32_t max_sel, float* out,
+                            float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+  return fused_step(cfg, B, q_raw, lq, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
+                    chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
+                    ws_bytes, stream);
 }
 
 hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,

@@ -23,14 +23,16 @@ namespace hga {
 // pool bases, NULL = no append), and, if the chunk lies entirely inside
 // [lo, hi), its chunk summary (cs_row) and G group summaries (gs_rows, G
 // consecutive rows); NULL = no summaries.  krow(p) / vrow(p) return the raw
-// key / value row of position p in [lo, hi).  part: LDS scratch of S*P*2
-// doubles.  Called by all 256 threads of a workgroup with uniform arguments.
+// key / value row of position p in [lo, hi).  stage (nullable): the chunk's
+// staging rows, [C][D]; the raw key of each position in [lo, hi) is copied
+// to row p - c0.  part: LDS scratch of S*P*2 doubles.  Called by all 256
+// threads of a workgroup with uniform arguments.
 template <int D, bool BF16, class KRow, class VRow>
 __device__ __forceinline__ void build_span(
     const KCfg& cfg, int c0, int lo, int hi, KRow krow, VRow vrow,
     typename std::conditional<BF16, uint16_t, float>::type* kp,
     typename std::conditional<BF16, uint16_t, float>::type* vp, float* cs_row, float* gs_rows,
-    double* part_lds) {
+    double* part_lds, typename std::conditional<BF16, uint16_t, float>::type* stage = nullptr) {
   constexpr int P = D / 2;               // pairs
   constexpr int S = 256 / P;             // token slices
   constexpr int TS = kChunk / S;         // tokens per slice
@@ -70,6 +72,10 @@ __device__ __forceinline__ void build_span(
   for (int i = 0; i < TS; ++i) {
     const int p = p_first + i;
     if (p >= lo && p < hi) {
+      if (stage) {
+        stage[(size_t)(p - c0) * D + j] = xa[i];
+        stage[(size_t)(p - c0) * D + j + P] = xb[i];
+      }
       double ka, kb;
       if constexpr (BF16) {
         ka = bf16_to_f(xa[i]);

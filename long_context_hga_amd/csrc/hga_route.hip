@@ -525,12 +525,14 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   }
 }
 
-// Token work of a fused decode step for unit (h, b), on one workgroup: the
-// raw key goes to its staging row, the rotated key and the value to the pool
-// (the same arithmetic as hga_build_summaries with one token), and when the
-// token is the last of its chunk the chunk's summaries are built from the
-// staging rows plus the new key.  Neither is read by this step's routing: the
-// current chunk is never a candidate.
+// Token work of a fused step for unit (h, b), on one workgroup: the raw
+// keys of the step's lq tokens go to their staging rows, their rotated keys
+// and values to the pool (the same arithmetic as hga_build_summaries over
+// those tokens), and when the last token ends its chunk the chunk's
+// summaries are built from the staging rows of the earlier positions plus
+// the new keys.  Neither is read by this step's routing: the current chunk
+// is never a candidate.  An unusable position (as route_geometry) writes
+// nothing.
 template <int D, bool BF16>
 __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
@@ -538,23 +540,31 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   const StepFront& f = a.f;
   const int unit = b * c.hkv + h;
   const int pos = a.r.q_pos0[b];
-  if (pos < 0 || pos >= f.pool_cap) return;  // route_select reports the position
+  const int lq = a.r.lq;
+  if (pos < 0 || (pos % kChunk) + lq > kChunk || pos / kChunk >= a.r.max_chunks ||
+      pos + lq > f.pool_cap)
+    return;  // route_select reports the position
   const int c0 = pos / kChunk * kChunk;
-  const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * D;
-  const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * D;
+  const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * lq * D;
+  const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * lq * D;
   T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
   T* kp = static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
   T* vp = static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
-  for (int i = threadIdx.x; i < D; i += 256) stage[(size_t)(pos - c0) * D + i] = kn[i];
-  build_span<D, BF16>(c, c0, pos, pos + 1, [&](int) { return kn; }, [&](int) { return vn; }, kp, vp,
-                      nullptr, nullptr, lds);
+  auto knew = [&](int p) { return kn + (size_t)(p - pos) * D; };
+  auto vnew = [&](int p) { return vn + (size_t)(p - pos) * D; };
   const int chunk = pos / kChunk;
-  if (pos - c0 == kChunk - 1 && chunk < a.r.max_chunks) {  // uniform
-    float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
-    float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
+  float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
+  float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
+  const bool ends = pos + lq - c0 == kChunk;  // uniform
+  if (ends && pos == c0) {  // the whole chunk in this step: one pass
+    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
+    return;
+  }
+  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
+  if (ends) {
     build_span<D, BF16>(
         c, c0, c0, c0 + kChunk,
-        [&](int p) { return p == pos ? kn : stage + (size_t)(p - c0) * D; },
+        [&](int p) { return p >= pos ? knew(p) : stage + (size_t)(p - c0) * D; },
         [&](int) { return kn; }, static_cast<T*>(nullptr), static_cast<T*>(nullptr), cs, gs, lds);
   }
 }

@@ -138,6 +138,34 @@ def test_attend_tiered_rejects():
     assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
 
 
+def test_fused_steps_reject():
+    c = ctypes.byref(cfg())
+    f = hga.lib().hga_prefill_step
+    # cfg, B, q, lq, k_new, v_new, pos, k_pool, v_pool, cap, stage, cs, gs, max_chunks, sel,
+    # n_sel, max_sel, out, lse, ws, ws_bytes, stream
+    args = [c, 8, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, FAKE, 1024, FAKE,
+            FAKE, 128, FAKE, None, FAKE, 1 << 30, None]
+    for lq in (0, 65):
+        a = list(args); a[3] = lq
+        assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT, lq
+    a = list(args); a[10] = None  # no staging rows
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[20] = 4096
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    a = list(args); a[16] = 10  # list shorter than the windows + top-k_g
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    for over in (dict(qkv_dtype=hga.HGA_F32), dict(head_dim=64)):
+        a = list(args); a[0] = ctypes.byref(cfg(**over))
+        assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
+    d = hga.lib().hga_decode_step
+    dargs = [c, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, FAKE, 1024, FAKE, FAKE,
+             128, FAKE, None, FAKE, 1 << 30, None]
+    a = list(dargs); a[9] = None
+    assert d(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(dargs); a[19] = 4096
+    assert d(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_gather_and_merge_reject():
     c = ctypes.byref(cfg())
     g = hga.lib().hga_gather
