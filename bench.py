@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--workload", default="decode64k",
-                    choices=["decode64k", "prefill32k", "host64k"],
+                    choices=["decode64k", "prefill32k", "host64k", "prompt32k"],
                     help="decode64k (default): the batch-8 64K decode step; prefill32k: one "
                          "64-token query chunk at 32K context (MFMA attention); host64k: "
                          "batch-4 64K decode with the pool in pinned host memory")
@@ -193,6 +193,8 @@ def main():
         return
     if args.workload == "prefill32k":
         run_prefill32k(args)
+    elif args.workload == "prompt32k":
+        run_prompt32k(args)
     elif args.workload == "host64k":
         run_host64k(args)
     else:
@@ -559,6 +561,156 @@ def run_prefill32k(args):
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_prefill(inp, p)
     print(json.dumps(out), flush=True)
+
+
+def prompt_flops(n_sel, sel, p):
+    """Algorithmic flops of attending every query chunk of the prompt over its
+    list: QK^T and PV over the visible (query, key) pairs (every key of a
+    group before the chunk; keys up to each token inside it)."""
+    import numpy as np
+    d, hq, hkv = p["head_dim"], p["n_q_heads"], p["n_kv_heads"]
+    C, g = p["chunk_size"], p["chunk_size"] // p["groups_per_chunk"]
+    hg = hq // hkv
+    B, nq = n_sel.shape[0], n_sel.shape[1]
+    pairs = 0
+    for b in range(B):
+        for qc in range(nq):
+            for h in range(hkv):
+                gids = sel[b, qc, h, :n_sel[b, qc, h]]
+                cur = gids[gids // (C // g) == qc]          # groups of the query chunk
+                prior = len(gids) - len(cur)
+                pairs += prior * g * C
+                for gid in cur:                             # key p visible to tau >= p
+                    first = int(gid) * g - qc * C
+                    pairs += sum(C - (first + i) for i in range(g))
+    return int(pairs) * hg * d * 2 * 2
+
+
+def cpu_baseline_prompt(inp, cfg_params, chunks=(508, 509, 510, 511)):
+    """The fp64 C oracle doing the whole-prompt prefill: the pool append and
+    summaries of the whole prompt (timed once), route + attend of a sample of
+    query chunks (all KV heads), scaled to tokens per second of the prompt."""
+    import numpy as np
+    import oracle
+    cfg = oracle.cfg_from(cfg_params)
+    p = cfg_params
+    d, hkv = p["head_dim"], p["n_kv_heads"]
+    hg = p["n_q_heads"] // hkv
+    B, T = inp.k.shape[0], inp.k.shape[2]
+    U = B * hkv
+    t0 = time.perf_counter()
+    cs = np.zeros((U, T // 64, d))
+    gs = np.zeros((U, T // 16, d))
+    kp = np.zeros((U, T, d))
+    vp = np.zeros((U, T, d))
+    for b in range(B):
+        for h in range(hkv):
+            u = b * hkv + h
+            kr = inp.f64(inp.k[b, h])
+            cs[u], gs[u] = oracle.summaries(cfg, kr)
+            kp[u] = oracle.pool(cfg, kr, 0)
+            vp[u] = inp.f64(inp.v[b, h])
+    t_append = time.perf_counter() - t0
+    max_sel = (p["n_sink_chunks"] + p["n_local_chunks"] + 1) * 4 + p["topk_groups"]
+    t0 = time.perf_counter()
+    for qc in chunks:
+        q = np.stack([inp.f64(inp.q[b, h * hg:(h + 1) * hg, qc * 64:(qc + 1) * 64])
+                      for b in range(B) for h in range(hkv)])
+        oracle.step(cfg, q, np.full(U, qc * 64), cs, gs, kp, vp, max_sel)
+    t_chunks = time.perf_counter() - t0
+    per_token = t_append / T + t_chunks / (len(chunks) * 64)
+    return {"value": 1.0 / per_token * B, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"pool append + summaries of the whole {T}-token prompt ({t_append:.1f} s, "
+                      f"{hkv} KV heads) plus route + attend of query chunks "
+                      f"{chunks[0]}..{chunks[-1]} (full budget, {t_chunks:.1f} s), scaled per "
+                      f"token; fp64 C oracle, OpenMP over the {U} units"}
+
+
+def run_prompt32k(args):
+    """Whole-prompt chunked prefill of a 32K prompt: one hga_prefill_prompt call
+    appends the prompt (pool + summaries), routes its 512 query chunks and
+    attends them on the matrix cores."""
+    import numpy as np
+    import torch
+
+    import gpu_harness as gh
+    import long_context_hga_amd as hga
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    inp = synth.generate("prompt32k")
+    p = inp.params
+    B, T = p["batch"], p["context"]
+    nq = T // 64
+    st = gh.build_state(inp, max_lq=64)
+    cfg, hkv = st.cfg, p["n_kv_heads"]
+    kp, vp = torch.zeros_like(st.k_pool), torch.zeros_like(st.v_pool)
+    cs, gs = torch.zeros_like(st.chunk_sum), torch.zeros_like(st.group_sum)
+    sel = torch.zeros((B, nq, hkv, st.max_sel), dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros((B, nq, hkv), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, p["n_q_heads"], T, p["head_dim"]), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, p["n_q_heads"], T), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(hga.hga_prompt_workspace_bytes(cfg, B, T, st.max_chunks), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(phases):
+        hga.hga_prefill_prompt(cfg, B, T, st.q, st.k_raw, st.v_raw, kp, vp, T, cs, gs,
+                               st.max_chunks, sel, n_sel, st.max_sel, out, lse, ws, phases=phases)
+
+    def timed(phases, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        torch.cuda._sleep(int(2e8))  # the queue fills ahead: no host launch latency
+        for e0, e1 in evs:
+            e0.record()
+            call(phases)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    for _ in range(max(3, args.warmup // 4)):
+        call(hga.HGA_PROMPT_ALL)
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 10)
+    ms_prompt = timed(hga.HGA_PROMPT_ALL, n)
+    ms_append = timed(hga.HGA_PROMPT_APPEND, n)
+    ms_route = timed(hga.HGA_PROMPT_ROUTE, n)
+    ms_attend = timed(hga.HGA_PROMPT_ATTEND, n)
+    assert torch.equal(kp, st.k_pool) and torch.isfinite(out).all().item()
+    flops = prompt_flops(n_sel.cpu().numpy(), sel.cpu().numpy(), p)
+    achieved = flops / (ms_attend * 1e-3) / 1e12
+    res = {
+        "metric": "whole-prompt chunked prefill tokens/s per layer at 32K; MFMA utilisation",
+        "value": B * T / (ms_prompt * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": ms_prompt,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, pre-RoPE)",
+        "config": {"workload": "prompt32k: GQA 32q/4kv heads, d=128, bf16, theta 1e6, a "
+                               "32768-token prompt, all 512 query chunks of 64 tokens; 1 sink + 4 "
+                               "local chunks, top-20 chunks, top-40 groups (1024 keys per chunk "
+                               "at full budget)",
+                   "batch": B, "context": T, "query_chunks": nq,
+                   "timing": "events around each hga_prefill_prompt call (one step = one "
+                             "prompt), queue filled ahead",
+                   "phase_ms": {"append": ms_append, "route": ms_route, "attend": ms_attend}},
+        "roofline": {"kernel": "attend_prompt_kernel (the attend phase, one launch)",
+                     "bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": achieved / 2500.0, "traffic": None, "flops_per_launch": flops,
+                     "launch_ms": ms_attend},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_prompt(inp, p)
+    print(json.dumps(res), flush=True)
 
 
 def run_host64k(args):

@@ -67,6 +67,14 @@ typedef enum {
   HGA_PART_ROUTED = 2      /* groups chosen by the two-level routing */
 } hga_part;
 
+/* Phases of hga_prefill_prompt (bit mask). */
+typedef enum {
+  HGA_PROMPT_APPEND = 1,   /* pool rows and chunk/group summaries of the prompt */
+  HGA_PROMPT_ROUTE = 2,    /* selected list of every query chunk */
+  HGA_PROMPT_ATTEND = 4,   /* attention of every query chunk over its list */
+  HGA_PROMPT_ALL = 7
+} hga_prompt_phase;
+
 typedef struct {
   int32_t head_dim;        /* d */
   int32_t n_q_heads;       /* Hq */
@@ -258,6 +266,47 @@ hga_status hga_prefill_step(const hga_config* cfg, int32_t B, const void* q_raw,
                             float* chunk_sum, float* group_sum, int32_t max_chunks,
                             int32_t* sel_groups, int32_t* n_sel, int32_t max_sel, float* out,
                             float* lse_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of hga_prefill_prompt for B prompts of T tokens with summary
+ * tables of max_chunks rows (host only). */
+hga_status hga_prompt_workspace_bytes(const hga_config* cfg, int32_t B, int32_t T,
+                                      int32_t max_chunks, size_t* bytes);
+
+/* Whole-prompt chunked prefill: the prompt's T tokens (T a multiple of
+ * chunk_size) are appended to the pool with their chunk and group summaries,
+ * then every query chunk qc (positions qc*C .. qc*C + C - 1) is routed with
+ * its pooled query over the complete chunks before it and attended over its
+ * selected list, causally inside its own chunk.  This is the chunked prefill
+ * of the page (HGA technical summary, "Kernmechanisme" items 2-4), whose
+ * "Experimentele Resultaten" report the speed-up of fusing it: since a query
+ * chunk reads only earlier chunks and its own, all query chunks of a prompt
+ * are routed by one launch pair and attended by one launch.
+ *   q_raw        [B][Hq][T][d] raw queries (bf16)
+ *   k_raw, v_raw [B][Hkv][T][d] raw keys and values
+ *   k_pool, v_pool, chunk_sum, group_sum: as hga_build_summaries, written by
+ *                the append phase (pool_cap >= T, max_chunks >= T / C)
+ *   sel_groups   [B][T/C][Hkv][max_sel] list of each query chunk (ascending
+ *                group ids), n_sel [B][T/C][Hkv] its length: written by the
+ *                route phase, as hga_route for that chunk alone
+ *   out          [B][Hq][T][d] fp32, lse_opt [B][Hq][T] (nullable): written by
+ *                the attend phase, as hga_attend for that chunk alone up to
+ *                fp32 rounding (the softmax runs online over tiles of 8
+ *                groups instead of split partials)
+ *   phases       HGA_PROMPT_* mask; a phase reads what the earlier phases (of
+ *                this call or a previous one) wrote
+ *   ws           hga_prompt_workspace_bytes; shared by the phases of one call
+ * Needs head_dim 128 and bf16 (the matrix-core attention): else
+ * HGA_ERR_UNSUPPORTED.  Errors: HGA_ERR_INVALID_ARGUMENT for T not a
+ * multiple of chunk_size, a missing buffer or a bad phase mask;
+ * HGA_ERR_OUT_OF_RANGE for T beyond pool_cap or max_chunks, or max_sel below
+ * hga_max_selected; HGA_ERR_UNSUPPORTED for max_sel > 256;
+ * HGA_ERR_WORKSPACE_TOO_SMALL. */
+hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const void* q_raw,
+                              const void* k_raw, const void* v_raw, void* k_pool, void* v_pool,
+                              int32_t pool_cap, float* chunk_sum, float* group_sum,
+                              int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
+                              int32_t max_sel, float* out, float* lse_opt, int32_t phases,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Host-tier attention (page section "Geheugenarchitectuur": summaries and the
  * always-visible windows are hot in device memory, the full token K/V history

@@ -29,11 +29,15 @@ HGA_SRC_WORKING_SET = 1
 HGA_PART_ALL = 0
 HGA_PART_WINDOWS = 1
 HGA_PART_ROUTED = 2
+HGA_PROMPT_APPEND = 1
+HGA_PROMPT_ROUTE = 2
+HGA_PROMPT_ATTEND = 4
+HGA_PROMPT_ALL = 7
 
 EXPORTED = ("hga_validate", "hga_max_selected", "hga_workspace_bytes", "hga_workspace_reset",
             "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_decode_step",
-            "hga_prefill_step", "hga_attend_tiered", "hga_merge_partials", "hga_status_string",
-            "hga_version")
+            "hga_prefill_step", "hga_prompt_workspace_bytes", "hga_prefill_prompt",
+            "hga_attend_tiered", "hga_merge_partials", "hga_status_string", "hga_version")
 
 
 class HgaError(RuntimeError):
@@ -98,6 +102,9 @@ def lib() -> ctypes.CDLL:
                                 _P, _P, _P, ctypes.c_size_t, _P],
             "hga_prefill_step": [_C, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P,
                                  _I, _P, _P, _P, ctypes.c_size_t, _P],
+            "hga_prompt_workspace_bytes": [_C, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hga_prefill_prompt": [_C, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P,
+                                   _P, _I, _P, ctypes.c_size_t, _P],
             "hga_attend_tiered": [_C, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P,
                                   _P, _P, _P, ctypes.c_size_t, _P, _P],
             "hga_merge_partials": [_C, _I, _I, _P, _P, _P, _P, _P, _P, _P],
@@ -228,6 +235,24 @@ def hga_prefill_step(cfg, B, q_raw, lq, k_new, v_new, q_pos0, k_pool, v_pool, po
                                   _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(out), _ptr(lse_opt),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "hga_prefill_step")
+
+
+def hga_prompt_workspace_bytes(cfg, B: int, T: int, max_chunks: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().hga_prompt_workspace_bytes(_cfg(cfg), B, T, max_chunks, ctypes.byref(out)),
+           "hga_prompt_workspace_bytes")
+    return out.value
+
+
+def hga_prefill_prompt(cfg, B, T, q_raw, k_raw, v_raw, k_pool, v_pool, pool_cap, chunk_sum,
+                       group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
+                       phases=HGA_PROMPT_ALL, stream=None):
+    _check(lib().hga_prefill_prompt(_cfg(cfg), B, T, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw),
+                                    _ptr(k_pool), _ptr(v_pool), pool_cap, _ptr(chunk_sum),
+                                    _ptr(group_sum), max_chunks, _ptr(sel_groups), _ptr(n_sel),
+                                    max_sel, _ptr(out), _ptr(lse_opt), phases, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "hga_prefill_prompt")
 
 
 def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, v_cold, cold_cap,

@@ -186,6 +186,8 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
   r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
   r.B = B;
   r.lq = lq;
+  r.nq = 1;
+  r.q_tokens = lq;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
   return hip_status(launch_route(k, r, (hipStream_t)stream));
@@ -296,6 +298,8 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
   r.B = B;
   r.lq = lq;
+  r.nq = 1;
+  r.q_tokens = lq;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
   StepFront f;
@@ -351,6 +355,101 @@ hga_status hga_prefill_step(const hga_config* cfg, int32_t B, const void* q_raw,
   return fused_step(cfg, B, q_raw, lq, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
                     chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
                     ws_bytes, stream);
+}
+
+// Whole-prompt prefill workspace: routing rows of every (sequence, query
+// chunk, KV head) and the query chunks' first positions.
+static size_t prompt_ws_bytes(const KCfg& k, int B, int T, int max_chunks) {
+  const int nq = T / kChunk;
+  return round_up(route_ws_bytes(k, B * nq, max_chunks), 256) + (size_t)B * nq * sizeof(int32_t);
+}
+
+hga_status hga_prompt_workspace_bytes(const hga_config* cfg, int32_t B, int32_t T,
+                                      int32_t max_chunks, size_t* bytes) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (!bytes || B <= 0 || T <= 0 || T % kChunk != 0 || max_chunks < T / kChunk)
+    return HGA_ERR_INVALID_ARGUMENT;
+  *bytes = round_up(prompt_ws_bytes(make_kcfg(cfg), B, T, max_chunks), 256);
+  return HGA_OK;
+}
+
+hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const void* q_raw,
+                              const void* k_raw, const void* v_raw, void* k_pool, void* v_pool,
+                              int32_t pool_cap, float* chunk_sum, float* group_sum,
+                              int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
+                              int32_t max_sel, float* out, float* lse_opt, int32_t phases,
+                              void* ws, size_t ws_bytes, void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || T <= 0 || T % kChunk != 0 || phases <= 0 || (phases & ~HGA_PROMPT_ALL) ||
+      !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 || !chunk_sum ||
+      !group_sum || max_chunks <= 0 || !sel_groups || !n_sel || !ws)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if ((phases & HGA_PROMPT_APPEND) && (!k_raw || !v_raw)) return HGA_ERR_INVALID_ARGUMENT;
+  if ((phases & (HGA_PROMPT_ROUTE | HGA_PROMPT_ATTEND)) && !q_raw) return HGA_ERR_INVALID_ARGUMENT;
+  if ((phases & HGA_PROMPT_ATTEND) && !out) return HGA_ERR_INVALID_ARGUMENT;
+  if (T > pool_cap || T / kChunk > max_chunks) return HGA_ERR_OUT_OF_RANGE;
+  if (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128) return HGA_ERR_UNSUPPORTED;
+  if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
+  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  const int nq = T / kChunk;
+  const int64_t n_virtual = (int64_t)B * nq;
+  if (n_virtual * cfg->n_kv_heads > kMaxUnits || n_virtual > kMaxGridZ ||
+      n_virtual * cfg->n_q_heads > INT32_MAX / 2)
+    return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
+  if (ws_bytes < prompt_ws_bytes(k, B, T, max_chunks)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (phases & HGA_PROMPT_APPEND) {
+    const hipError_t e = launch_build(k, B, k_raw, v_raw, 0, T, k_pool, v_pool, pool_cap, chunk_sum,
+                                      group_sum, max_chunks, st);
+    if (e != hipSuccess) return HGA_ERR_HIP;
+  }
+  if (phases & HGA_PROMPT_ROUTE) {
+    RouteLaunch r;
+    r.q = q_raw;
+    r.chunk_sum = chunk_sum;
+    r.group_sum = group_sum;
+    r.sel = sel_groups;
+    r.n_sel = n_sel;
+    r.chunk_scores = nullptr;
+    const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+    r.scores = static_cast<double*>(ws);
+    r.qbar = r.scores + (size_t)n_virtual * k.hkv * max_cand;
+    int* pos = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                      round_up(route_ws_bytes(k, (int)n_virtual, max_chunks), 256));
+    r.q_pos0 = pos;
+    r.B = (int)n_virtual;
+    r.lq = kChunk;
+    r.nq = nq;
+    r.q_tokens = T;
+    r.max_chunks = max_chunks;
+    r.max_sel = max_sel;
+    hipError_t e = launch_prompt_positions(pos, (int)n_virtual, nq, st);
+    if (e != hipSuccess) return HGA_ERR_HIP;
+    e = launch_route(k, r, st);
+    if (e != hipSuccess) return HGA_ERR_HIP;
+  }
+  if (phases & HGA_PROMPT_ATTEND) {
+    PromptLaunch p;
+    p.q = q_raw;
+    p.k = k_pool;
+    p.v = v_pool;
+    p.sel = sel_groups;
+    p.n_sel = n_sel;
+    p.out = out;
+    p.lse = lse_opt;
+    p.B = B;
+    p.nq = nq;
+    p.T = T;
+    p.cap = pool_cap;
+    p.max_sel = max_sel;
+    return hip_status(launch_prompt_attend(k, p, st));
+  }
+  return HGA_OK;
 }
 
 hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,

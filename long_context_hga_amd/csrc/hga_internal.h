@@ -24,6 +24,12 @@ struct RouteLaunch {
   double* scores;       // workspace [B*Hkv][max_cand]
   double* qbar;         // workspace [B*Hkv][d]
   int B, lq, max_chunks, max_sel;
+  // B counts virtual sequences: virtual sequence b routes query chunk b % nq
+  // of pool sequence b / nq (nq = 1 outside whole-prompt prefill).  Its lq
+  // query tokens are rows (b % nq) * lq .. of q [B/nq][Hq][q_tokens][d];
+  // positions, lists and workspace rows are per virtual sequence, summaries
+  // per pool sequence.
+  int nq, q_tokens;
 };
 // The token work of a fused decode step, run by extra workgroups of the
 // selection launch: the new token's pool append, its raw key into the chunk
@@ -63,6 +69,21 @@ hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st)
 hipError_t launch_attend_split(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
 hipError_t launch_attend_merge(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
 size_t attend_ws_bytes(const KCfg& cfg, int B, int lq, int max_sel);
+
+// Whole-prompt prefill: attention of every query chunk of the prompt over
+// its selected list (virtual sequence b * nq + qc = chunk qc of sequence b).
+struct PromptLaunch {
+  const void* q;       // [B][Hq][T][d]
+  const void* k;       // pool
+  const void* v;
+  const int* sel;      // [B*nq][Hkv][max_sel]
+  const int* n_sel;    // [B*nq][Hkv]
+  float* out;          // [B][Hq][T][d]
+  float* lse;          // [B][Hq][T] or null
+  int B, nq, T, cap, max_sel;
+};
+hipError_t launch_prompt_positions(int* pos, int n_virtual, int nq, hipStream_t st);
+hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStream_t st);
 
 hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
                          int pool_cap, const int* sel, const int* n_sel, int max_sel,

@@ -1,0 +1,223 @@
+// Matrix-core pieces of the chunked-prefill attention, shared by the split
+// kernel (one query chunk, partials merged afterwards) and the whole-prompt
+// kernel (every query chunk of a prompt, online softmax over the tiles).
+//
+// A tile is 8 selected groups = 128 keys of one KV head, staged in LDS:
+//   ks  [128 keys][D]  bf16 K rows, 16-byte chunk ch of key k at ch ^ (k % 16)
+//   vt  [D][128 keys]  bf16 V^T rows; each 32-key quarter in the key order of
+//                      the S^T entries (chunk qg holds keys 4qg + 0..3 and
+//                      16 + 4qg + 0..3), chunk c of dim row r at c ^ (r % 16)
+// A wave owns 16 query rows; lane (rl, qg) is C-layout column rl (its query
+// row) and row group qg.  Contractions on v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T     A = 16 keys x 32 dims of K, B = the rotated query (bf16
+//                   hi + lo, two products)
+//   O^T += V^T P^T  A = 16 dims x 32 keys of V^T, B = the lane's own
+//                   probabilities (hi + lo) in the key order S^T left them.
+#pragma once
+
+#include "hga_attend_common.h"
+
+namespace hga {
+
+constexpr int kTileGroups = kSplitGroups;                 // groups per tile
+constexpr int kTileKeys = kTileGroups * kGroupTokens;     // 128 keys per tile
+
+// The lane's B operand of S^T = K Q^T is its query row at dims 32k + 8qg +
+// 0..7 (k < 4): both halves of the RoPE pairs j = 8qg + i and 32 + 8qg + i,
+// so the lane rotates its own operand.  qrow: the raw bf16 query row.
+template <int D>
+__device__ __forceinline__ void load_q_raw(const uint16_t* qrow, int qg, uint4 (&qraw)[D / 32]) {
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) qraw[k] = *reinterpret_cast<const uint4*>(qrow + 32 * k + 8 * qg);
+}
+
+// Rotated, pre-scaled query of the lane's row at position tau: the angle
+// tau * omega_j is formed in fp64 as a fraction of a turn and reduced exactly
+// to [-1/2, 1/2]; sin and cos of the reduced turn run in fp32 (v_sin_f32 /
+// v_cos_f32 take turns), within ~1e-6 rad.  The result is split into bf16
+// hi + lo operands.
+template <int D>
+__device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 32], int tau, int qg,
+                                         bf16x8 (&qop_hi)[D / 32], bf16x8 (&qop_lo)[D / 32]) {
+  constexpr int KS = D / 32;
+  const double tau_d = (double)tau;
+  uint32_t hi[KS][4], lo[KS][4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {  // pairs j = 32*half + 8qg + i
+    const uint32_t wx[4] = {qraw[half].x, qraw[half].y, qraw[half].z, qraw[half].w};
+    const uint32_t wy[4] = {qraw[half + 2].x, qraw[half + 2].y, qraw[half + 2].z, qraw[half + 2].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // pairs i = 2w, 2w + 1: one packed register each
+      float rx[2], ry[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = 32 * half + 8 * qg + 2 * w + e;
+        const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
+        const float fr = (float)(turns - rint(turns));
+        const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+        const float x = __uint_as_float(e ? (wx[w] & 0xFFFF0000u) : (wx[w] << 16));
+        const float y = __uint_as_float(e ? (wy[w] & 0xFFFF0000u) : (wy[w] << 16));
+        rx[e] = (x * cs - y * sn) * c.qscale_log2;
+        ry[e] = (x * sn + y * cs) * c.qscale_log2;
+      }
+      split_pair(rx[0], rx[1], hi[half][w], lo[half][w]);
+      split_pair(ry[0], ry[1], hi[half + 2][w], lo[half + 2][w]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    qop_hi[k] = __builtin_bit_cast(bf16x8, make_uint4(hi[k][0], hi[k][1], hi[k][2], hi[k][3]));
+    qop_lo[k] = __builtin_bit_cast(bf16x8, make_uint4(lo[k][0], lo[k][1], lo[k][2], lo[k][3]));
+  }
+}
+
+// Global loads of a tile (all 8 groups issued together; a missing group's
+// base is any in-range row, masked later):
+//   K: group it, thread = (row tid/16, 16-byte chunk tid%16)
+//   V: group it's V^T block ([D][16], as the pool stores it), thread = (dim
+//      tid/2, tokens 8*(tid%2) .. +7)
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t* k, const uint16_t* v,
+                                          const size_t (&gbase)[kTileGroups], int tid,
+                                          uint4 (&kraw)[kTileGroups], uint4 (&vraw)[kTileGroups]) {
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int it = 0; it < kTileGroups; ++it)
+    kraw[it] = *reinterpret_cast<const uint4*>(k + gbase[it] + (size_t)(tid / CH) * D + (tid % CH) * 8);
+#pragma unroll
+  for (int it = 0; it < kTileGroups; ++it)
+    vraw[it] = *reinterpret_cast<const uint4*>(v + gbase[it] + (size_t)(tid >> 1) * kGroupTokens + 8 * (tid & 1));
+}
+
+// The loaded tile into LDS.  V of a key that is missing (gpos < 0) or lies
+// after pos_last is stored as zero: an unwritten pool row may hold NaN, and
+// 0 x NaN would poison the product.
+template <int D>
+__device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt, const uint4 (&kraw)[kTileGroups],
+                                           const uint4 (&vraw)[kTileGroups],
+                                           const int (&gpos)[kTileGroups], int pos_last, int tid) {
+  constexpr int CH = D / 8;
+#pragma unroll
+  for (int it = 0; it < kTileGroups; ++it) {
+    const int key = it * kGroupTokens + tid / CH, ch = tid % CH;
+    *reinterpret_cast<uint4*>(ks + key * D + (ch ^ (key % CH)) * 8) = kraw[it];
+  }
+  const int dim = tid >> 1, hf = tid & 1;
+#pragma unroll
+  for (int it = 0; it < kTileGroups; ++it) {
+    const int gp = gpos[it];
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) keep |= (gp >= 0 && gp + 8 * hf + i <= pos_last) ? (1u << i) : 0u;
+    const uint4 x = keep_bf16(vraw[it], keep);
+    // keys 16*(it%2) + 8hf + 0..7 of quarter it/2: column groups 2hf and
+    // 2hf + 1, half it%2 of their chunks
+    const int c0 = 4 * (it >> 1) + 2 * hf, h = 4 * (it & 1);
+    *reinterpret_cast<uint2*>(vt + dim * kTileKeys + ((c0 ^ (dim & 15)) * 8) + h) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2*>(vt + dim * kTileKeys + (((c0 + 1) ^ (dim & 15)) * 8) + h) = make_uint2(x.z, x.w);
+  }
+}
+
+// S^T of the staged tile for the wave's rows: s[t][n][i] = score (log2
+// units) of key 32t + 16n + 4qg + i for the lane's query row at position
+// tau, -inf where the key is not visible (missing group, or after tau).
+// Returns the lane's maximum; the row maximum needs rows_max.  The operand
+// reads of quarter t + 1 are issued before the products of quarter t
+// (scheduling barriers keep that order), so LDS latency hides under the
+// matrix-core work.
+template <int D>
+__device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&qop_hi)[D / 32],
+                                             const bf16x8 (&qop_lo)[D / 32],
+                                             const int (&gpos)[kTileGroups], int tau, int rl, int qg,
+                                             f32x4 (&s)[4][2]) {
+  constexpr int KS = D / 32;
+  constexpr int NT = kTileGroups / 2;
+  auto load_k = [&](int t, bf16x8 (&kop)[2][KS]) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        kop[n][k] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(ks + (32 * t + 16 * n + rl) * D + (((4 * k + qg) ^ rl) * 8)));
+  };
+  bf16x8 kop[2][2][KS];
+  load_k(0, kop[0]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + 1 < NT) load_k(t + 1, kop[(t + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    s[t][0] = s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        s[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t & 1][n][k], qop_hi[k], s[t][n], 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        s[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t & 1][n][k], qop_lo[k], s[t][n], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int gp = gpos[2 * t + n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = gp >= 0 && gp + 4 * qg + i <= tau;
+        s[t][n][i] = vis ? s[t][n][i] : -INFINITY;
+        tmax = fmaxf(tmax, s[t][n][i]);
+      }
+    }
+  return tmax;
+}
+
+// Probabilities p = 2^(s - mref) of the tile (added to the lane's l) and
+// O^T += V^T P^T.  The V^T operand reads of quarter t + 1 are issued before
+// the products of quarter t.
+template <int D>
+__device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][2], float mref, int rl,
+                                        int qg, float& l, f32x4 (&o)[D / 16]) {
+  constexpr int NB = D / 16;
+  constexpr int NT = kTileGroups / 2;
+  auto load_v = [&](int t, bf16x8 (&vop)[NB]) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      vop[n] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(vt + (16 * n + rl) * kTileKeys + (((4 * t + qg) ^ rl) * 8)));
+  };
+  bf16x8 vop[2][NB];
+  load_v(0, vop[0]);  // in flight during the probabilities
+  __builtin_amdgcn_sched_barrier(0);
+  // k-slot 4n + i of quarter t is key 32t + 16n + 4qg + i
+  bf16x8 pop_hi[NT], pop_lo[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p0 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1)] - mref);
+      const float p1 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1) + 1] - mref);
+      l += p0 + p1;
+      split_pair(p0, p1, ph[k], pl[k]);
+    }
+    pop_hi[t] = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    pop_lo[t] = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t + 1 < NT) load_v(t + 1, vop[(t + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_hi[t], o[n], 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_lo[t], o[n], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+}  // namespace hga

@@ -336,7 +336,10 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int unit = b * c.hkv + h;
+  const int unit = b * c.hkv + h;                 // workspace rows: virtual sequence
+  const int unit_p = (b / r.nq) * c.hkv + h;      // summaries: pool sequence
+  const size_t qhead0 = (size_t)(b / r.nq) * c.hq + (size_t)h * c.hg;
+  const int qt0 = (b % r.nq) * r.lq;              // first query row of this chunk
   const int lq = r.lq;
   int pos0;
   Windows w;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh) {
         const int hc = hh < c.hg ? hh : c.hg - 1;
-        const size_t row = ((size_t)(b * c.hq + h * c.hg + hc) * lq + t) * D;
+        const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t) * D;
         ya[u][hh] = *reinterpret_cast<const QT*>(q + row + 2 * jp);
         yb[u][hh] = *reinterpret_cast<const QT*>(q + row + P + 2 * jp);
       }
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
       const int hc = hh < c.hg ? hh : c.hg - 1;
-      const size_t row = ((size_t)(b * c.hq + h * c.hg + hc) * lq + t0) * D;
+      const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t0) * D;
       xa[hh] = q[row + j];
       xb[hh] = q[row + j + P];
     }
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     int idx = tile0 + wave * (kTile / 4) + it * RPI + rin;
     idx = idx < n_cand ? w.cand_lo + idx : (n_cand > 0 ? w.cand_hi - 1 : 0);
     const float4* rowp =
-        reinterpret_cast<const float4*>(r.chunk_sum + ((size_t)unit * r.max_chunks + idx) * D);
+        reinterpret_cast<const float4*>(r.chunk_sum + ((size_t)unit_p * r.max_chunks + idx) * D);
 #pragma unroll
     for (int v = 0; v < NV; ++v) buf[it][v] = rowp[v * kLanesPerRow + sub];
   }
@@ -588,7 +591,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     step_front<D, BF16>(a, h, b, dyn);
     return;
   }
-  const int unit = b * c.hkv + h;
+  const int unit = b * c.hkv + h;             // lists and workspace: virtual sequence
+  const int unit_p = (b / r.nq) * c.hkv + h;  // summaries: pool sequence
 
   // every load that does not depend on the position goes out first: this
   // lane's qbar slice (for level 2) and the level-1 scores (clamped to the
@@ -667,7 +671,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
       i = i < n2 ? i : n2 - 1;  // clamped: every load issues, extras ignored
       const int gid = (w.cand_lo + sel[i / kGroups]) * kGroups + i % kGroups;
       const float4* rowp = reinterpret_cast<const float4*>(
-          r.group_sum + ((size_t)unit * r.max_chunks * kGroups + gid) * D);
+          r.group_sum + ((size_t)unit_p * r.max_chunks * kGroups + gid) * D);
 #pragma unroll
       for (int v = 0; v < NV; ++v) gb[u][v] = rowp[v * kLanesPerRow + sub];
     }

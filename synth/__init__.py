@@ -25,6 +25,11 @@ of one layer, with K/V/Q ~ N(0, 1) before RoPE:
                  (2048 visible keys = 3.125 %).
 * ``host64k``    as ``decode64k`` with batch 4; the caller keeps the full
                  pool in pinned host memory.
+* ``prompt32k``  whole-prompt prefill of the ``prefill32k`` layer: queries for
+                 all 32768 tokens (every 64-token chunk is a query chunk),
+                 top-20 chunks, top-40 groups (1024 keys per query chunk once
+                 20 chunks are candidates); no planted needles (one planted
+                 direction cannot match the pooled queries of every chunk).
 
 Seeds: sequence b of workload i (1-based, in the order above) draws from
 ``numpy.random.Generator(PCG64(1000*i + b))`` in the order K [Hkv][T][d],
@@ -65,6 +70,9 @@ CONFIGS: Dict[str, dict] = {
                       topk_chunks=52, topk_groups=104, batch=8, lq=1, query_pos0=65535),
     "host64k": dict(index=5, **_LAYER, context=65536, n_sink_chunks=1, n_local_chunks=4,
                     topk_chunks=52, topk_groups=104, batch=4, lq=1, query_pos0=65535),
+    "prompt32k": dict(index=6, **_LAYER, context=32768, n_sink_chunks=1, n_local_chunks=4,
+                      topk_chunks=20, topk_groups=40, batch=1, lq=32768, query_pos0=0,
+                      whole_prompt=True),
 }
 
 
@@ -124,7 +132,9 @@ def generate(name: str, batch: Optional[int] = None, context: Optional[int] = No
         p.update(overrides)
     B = p["batch"] if batch is None else int(batch)
     T = p["context"] if context is None else int(context)
-    if context is not None:
+    if p.get("whole_prompt"):  # every token is a query token
+        p["context"], p["lq"], p["query_pos0"] = T, T, 0
+    elif context is not None:
         p["query_pos0"] = p["query_pos0"] - p["context"] + T
         p["context"] = T
     p["batch"] = B

@@ -166,6 +166,39 @@ def test_fused_steps_reject():
     assert d(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_prefill_prompt_rejects():
+    c = ctypes.byref(cfg())
+    n = hga.hga_prompt_workspace_bytes(cfg(), 1, 32768, 512)
+    assert n >= 4 * 512 * (511 + 128) * 8
+    ws_size = ctypes.c_size_t()
+    w = hga.lib().hga_prompt_workspace_bytes
+    assert w(c, 1, 1000, 512, ctypes.byref(ws_size)) == hga.HGA_ERR_INVALID_ARGUMENT  # T % C
+    assert w(c, 1, 32768, 100, ctypes.byref(ws_size)) == hga.HGA_ERR_INVALID_ARGUMENT
+    f = hga.lib().hga_prefill_prompt
+    # cfg, B, T, q, k_raw, v_raw, k_pool, v_pool, cap, cs, gs, max_chunks, sel, n_sel, max_sel,
+    # out, lse, phases, ws, ws_bytes, stream
+    args = [c, 1, 32768, FAKE, FAKE, FAKE, FAKE, FAKE, 32768, FAKE, FAKE, 512, FAKE, FAKE, 128,
+            FAKE, None, hga.HGA_PROMPT_ALL, FAKE, 1 << 30, None]
+    a = list(args); a[2] = 1000  # not a multiple of the chunk size
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    for ph in (0, 8, -1):
+        a = list(args); a[17] = ph
+        assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT, ph
+    a = list(args); a[4] = None  # append phase without raw keys
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[15] = None  # attend phase without an output
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[8] = 16384  # prompt longer than the pool
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    a = list(args); a[14] = 10
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    a = list(args); a[19] = 4096
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    for over in (dict(qkv_dtype=hga.HGA_F32), dict(head_dim=64)):
+        a = list(args); a[0] = ctypes.byref(cfg(**over))
+        assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
+
+
 def test_gather_and_merge_reject():
     c = ctypes.byref(cfg())
     g = hga.lib().hga_gather
