@@ -188,6 +188,7 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
   r.lq = lq;
   r.nq = 1;
   r.q_tokens = lq;
+  r.pool_once = 0;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
   return hip_status(launch_route(k, r, (hipStream_t)stream));
@@ -300,6 +301,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   r.lq = lq;
   r.nq = 1;
   r.q_tokens = lq;
+  r.pool_once = 0;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
   StepFront f;
@@ -426,6 +428,7 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
     r.lq = kChunk;
     r.nq = nq;
     r.q_tokens = T;
+    r.pool_once = 1;
     r.max_chunks = max_chunks;
     r.max_sel = max_sel;
     hipError_t e = launch_prompt_positions(pos, (int)n_virtual, nq, st);

@@ -30,6 +30,9 @@ struct RouteLaunch {
   // positions, lists and workspace rows are per virtual sequence, summaries
   // per pool sequence.
   int nq, q_tokens;
+  // 1: the multi-token pooled query of each unit is formed by a launch of
+  // its own and read by the tile workgroups (many units, many tiles each)
+  int pool_once;
 };
 // The token work of a fused decode step, run by extra workgroups of the
 // selection launch: the new token's pool append, its raw key into the chunk

@@ -22,6 +22,19 @@ namespace hga {
 constexpr int kTileGroups = kSplitGroups;                 // groups per tile
 constexpr int kTileKeys = kTileGroups * kGroupTokens;     // 128 keys per tile
 
+// 16 raw bytes of a tile row in flight (a vector type, so that arrays of them
+// stay in registers across the loops that prefetch them)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The bf16 elements of x whose bit in keep (bit i = element i) is clear
+// become +0.
+__device__ __forceinline__ u32x4 keep_bf16x8(u32x4 x, uint32_t keep) {
+  auto m = [&](int i) {
+    return ((keep >> (2 * i)) & 1u ? 0x0000FFFFu : 0u) | ((keep >> (2 * i + 1)) & 1u ? 0xFFFF0000u : 0u);
+  };
+  return u32x4{x.x & m(0), x.y & m(1), x.z & m(2), x.w & m(3)};
+}
+
 // The lane's B operand of S^T = K Q^T is its query row at dims 32k + 8qg +
 // 0..7 (k < 4): both halves of the RoPE pairs j = 8qg + i and 32 + 8qg + i,
 // so the lane rotates its own operand.  qrow: the raw bf16 query row.
@@ -71,45 +84,68 @@ __device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 
   }
 }
 
-// Global loads of a tile (all 8 groups issued together; a missing group's
+// Threads that stage a tile: NTHR = 256 (one workgroup of 4 waves) or 512.
+// Thread tid stages groups it = i * (NTHR / 256) + tid / 256 (i < GPT) with
+// the 256-thread maps below applied to sub = tid % 256.
+template <int NTHR>
+struct TileStaging {
+  static_assert(NTHR == 256 || NTHR == 512, "tile staging threads");
+  static constexpr int R = NTHR / 256;               // threads per 256-thread map slot
+  static constexpr int GPT = kTileGroups / R;        // groups per thread
+  template <class X>
+  __device__ static __forceinline__ X pick(const X (&a)[kTileGroups], int i, int half) {
+    if constexpr (R == 1) return a[i];
+    else return half ? a[R * i + 1] : a[R * i];
+  }
+};
+
+// Global loads of a tile (all groups issued together; a missing group's
 // base is any in-range row, masked later):
-//   K: group it, thread = (row tid/16, 16-byte chunk tid%16)
-//   V: group it's V^T block ([D][16], as the pool stores it), thread = (dim
-//      tid/2, tokens 8*(tid%2) .. +7)
-template <int D>
+//   K: group it, sub = (row sub/16, 16-byte chunk sub%16)
+//   V: group it's V^T block ([D][16], as the pool stores it), sub = (dim
+//      sub/2, tokens 8*(sub%2) .. +7)
+template <int D, int NTHR = 256>
 __device__ __forceinline__ void load_tile(const uint16_t* k, const uint16_t* v,
                                           const size_t (&gbase)[kTileGroups], int tid,
-                                          uint4 (&kraw)[kTileGroups], uint4 (&vraw)[kTileGroups]) {
+                                          u32x4 (&kraw)[TileStaging<NTHR>::GPT],
+                                          u32x4 (&vraw)[TileStaging<NTHR>::GPT]) {
+  using TS = TileStaging<NTHR>;
   constexpr int CH = D / 8;
+  const int sub = tid % 256, half = tid / 256;
 #pragma unroll
-  for (int it = 0; it < kTileGroups; ++it)
-    kraw[it] = *reinterpret_cast<const uint4*>(k + gbase[it] + (size_t)(tid / CH) * D + (tid % CH) * 8);
+  for (int i = 0; i < TS::GPT; ++i)
+    kraw[i] = *reinterpret_cast<const u32x4*>(k + TS::pick(gbase, i, half) + (size_t)(sub / CH) * D + (sub % CH) * 8);
 #pragma unroll
-  for (int it = 0; it < kTileGroups; ++it)
-    vraw[it] = *reinterpret_cast<const uint4*>(v + gbase[it] + (size_t)(tid >> 1) * kGroupTokens + 8 * (tid & 1));
+  for (int i = 0; i < TS::GPT; ++i)
+    vraw[i] = *reinterpret_cast<const u32x4*>(v + TS::pick(gbase, i, half) + (size_t)(sub >> 1) * kGroupTokens + 8 * (sub & 1));
 }
 
 // The loaded tile into LDS.  V of a key that is missing (gpos < 0) or lies
 // after pos_last is stored as zero: an unwritten pool row may hold NaN, and
 // 0 x NaN would poison the product.
-template <int D>
-__device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt, const uint4 (&kraw)[kTileGroups],
-                                           const uint4 (&vraw)[kTileGroups],
+template <int D, int NTHR = 256>
+__device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
+                                           const u32x4 (&kraw)[TileStaging<NTHR>::GPT],
+                                           const u32x4 (&vraw)[TileStaging<NTHR>::GPT],
                                            const int (&gpos)[kTileGroups], int pos_last, int tid) {
+  using TS = TileStaging<NTHR>;
   constexpr int CH = D / 8;
+  const int sub = tid % 256, half = tid / 256;
 #pragma unroll
-  for (int it = 0; it < kTileGroups; ++it) {
-    const int key = it * kGroupTokens + tid / CH, ch = tid % CH;
-    *reinterpret_cast<uint4*>(ks + key * D + (ch ^ (key % CH)) * 8) = kraw[it];
+  for (int i = 0; i < TS::GPT; ++i) {
+    const int it = TS::R * i + half;
+    const int key = it * kGroupTokens + sub / CH, ch = sub % CH;
+    *reinterpret_cast<u32x4*>(ks + key * D + (ch ^ (key % CH)) * 8) = kraw[i];
   }
-  const int dim = tid >> 1, hf = tid & 1;
+  const int dim = sub >> 1, hf = sub & 1;
 #pragma unroll
-  for (int it = 0; it < kTileGroups; ++it) {
-    const int gp = gpos[it];
+  for (int i = 0; i < TS::GPT; ++i) {
+    const int it = TS::R * i + half;
+    const int gp = TS::pick(gpos, i, half);
     uint32_t keep = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) keep |= (gp >= 0 && gp + 8 * hf + i <= pos_last) ? (1u << i) : 0u;
-    const uint4 x = keep_bf16(vraw[it], keep);
+    for (int e = 0; e < 8; ++e) keep |= (gp >= 0 && gp + 8 * hf + e <= pos_last) ? (1u << e) : 0u;
+    const u32x4 x = keep_bf16x8(vraw[i], keep);
     // keys 16*(it%2) + 8hf + 0..7 of quarter it/2: column groups 2hf and
     // 2hf + 1, half it%2 of their chunks
     const int c0 = 4 * (it >> 1) + 2 * hf, h = 4 * (it & 1);

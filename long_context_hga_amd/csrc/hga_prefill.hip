@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   // ---- every K/V load of the split, issued before any is used; the query
   // is rotated while they are in flight
-  uint4 kraw[kSplitGroups], vraw[kSplitGroups];
+  u32x4 kraw[kSplitGroups], vraw[kSplitGroups];
   load_tile<D>(static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), gbase, tid, kraw, vraw);
   bf16x8 qop_hi[KS], qop_lo[KS];
   rotate_q<D>(c, qraw, pos0 + row, qg, qop_hi, qop_lo);

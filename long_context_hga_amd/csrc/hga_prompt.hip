@@ -10,8 +10,9 @@
 // are routed as virtual sequences (sequence b, chunk qc) and attended by one
 // launch.
 //
-// attend_prompt_kernel: one workgroup per (query head, query chunk), 256
-// threads, wave w owning query tokens 16w .. 16w + 15 of the chunk.  It
+// attend_prompt_kernel: one workgroup per (two query heads of a KV head,
+// query chunk), 512 threads, wave w owning query tokens 16(w%4) .. +15 of the
+// chunk for head w/4 of the pair, so each staged tile serves both heads.  It
 // walks the chunk's selected list in tiles of 8 groups (hga_mfma_tile.h):
 // the next tile's K/V loads are in flight while the current tile is
 // computed, and the softmax runs online over the tiles (running maximum and
@@ -20,8 +21,8 @@
 //
 // Workgroups are dispatched to the 8 XCDs of the chip in turn (workgroup i
 // on XCD i % 8).  The launch index is remapped so that consecutive work
-// items - the 8 query heads of one KV head and chunk, which read the same
-// K/V - run on the same XCD and share its L2.  The mapping only orders the
+// items - the head pairs of one KV head and chunk, which read the same K/V -
+// run on the same XCD and share its L2.  The mapping only orders the
 // work; any dispatch policy gives the same results.
 #include "hga_mfma_tile.h"
 
@@ -36,16 +37,20 @@ struct PromptArgs {
   const int* n_sel;    // [Bv][Hkv]
   float* out;          // [Bp][Hq][T][d]
   float* lse;          // [Bp][Hq][T] or null
-  int nq, T, cap, max_sel, n_items;  // n_items = Bv * Hq
+  int nq, T, cap, max_sel, n_items;  // n_items = Bv * Hkv * (Hg / HPW)
 };
 
 constexpr int kXcds = 8;
 
-template <int D, int HG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_prompt_kernel(PromptArgs a) {
+// HPW query heads per workgroup (2, or 1 when a KV head has one query head).
+template <int D, int HG, int HPW>
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) void attend_prompt_kernel(PromptArgs a) {
   static_assert(D == 128, "staging maps assume 16 chunks of 16 bytes per key row");
+  static_assert(HG % HPW == 0, "head pairs");
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
+  constexpr int NTHR = 256 * HPW;
+  constexpr int GPT = TileStaging<NTHR>::GPT;
   __shared__ __align__(16) uint16_t ks[kTileKeys * D];
   __shared__ __align__(16) uint16_t vt[D * kTileKeys];
 
@@ -53,15 +58,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int per_xcd = (a.n_items + kXcds - 1) / kXcds;
   const int item = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
   if (item >= a.n_items) return;  // uniform: the whole workgroup leaves
-  const int hj = item % HG, uv = item / HG;  // uv = virtual unit (bv, kvh)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hp = item % (HG / HPW), uv = item / (HG / HPW);  // uv = virtual unit (bv, kvh)
   const int kvh = uv % c.hkv, bv = uv / c.hkv;
-  const int qh = kvh * HG + hj;
+  const int qh = kvh * HG + hp * HPW + wave / 4;  // this wave's query head
   const int bp = bv / a.nq, qc = bv % a.nq;
   const int unit_p = bp * c.hkv + kvh;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, qg = lane >> 4;
-  const int row = wave * 16 + rl;  // query token of this lane within the chunk
+  const int row = (wave % 4) * 16 + rl;  // query token of this lane within the chunk
   const size_t tok = (size_t)(bp * c.hq + qh) * a.T + (size_t)qc * kChunk + row;
   const int pos0 = qc * kChunk;  // the chunk's first position
   const int n_sel = a.n_sel[uv];
@@ -109,10 +114,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int n_tiles = (n_sel + kTileGroups - 1) / kTileGroups;
   int gpos[kTileGroups];
   size_t gbase[kTileGroups];
-  uint4 kraw[kTileGroups], vraw[kTileGroups];
+  u32x4 kraw[GPT], vraw[GPT];
   if (n_tiles > 0) {
     tile_groups(0, gpos, gbase);
-    load_tile<D>(a.k, a.v, gbase, tid, kraw, vraw);
+    load_tile<D, NTHR>(a.k, a.v, gbase, tid, kraw, vraw);
   }
   bf16x8 qop_hi[KS], qop_lo[KS];
   rotate_q<D>(c, qraw, tau, qg, qop_hi, qop_lo);
@@ -123,14 +128,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float m = -INFINITY, l = 0.f;
   for (int t = 0; t < n_tiles; ++t) {
     if (t > 0) __syncthreads();  // every wave is done with the previous tile
-    stage_tile<D>(ks, vt, kraw, vraw, gpos, pos_last, tid);
+    stage_tile<D, NTHR>(ks, vt, kraw, vraw, gpos, pos_last, tid);
     __syncthreads();
     int gcur[kTileGroups];
 #pragma unroll
     for (int it = 0; it < kTileGroups; ++it) gcur[it] = gpos[it];
     if (t + 1 < n_tiles) {  // the next tile's loads fly during this tile
       tile_groups(t + 1, gpos, gbase);
-      load_tile<D>(a.k, a.v, gbase, tid, kraw, vraw);
+      load_tile<D, NTHR>(a.k, a.v, gbase, tid, kraw, vraw);
     }
     f32x4 s[4][2];
     const float tmax = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gcur, tau, rl, qg, s));
@@ -179,13 +184,14 @@ hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStrea
   a.T = p.T;
   a.cap = p.cap;
   a.max_sel = p.max_sel;
-  a.n_items = p.B * p.nq * cfg.hq;
+  const int hpw = cfg.hg >= 2 ? 2 : 1;
+  a.n_items = p.B * p.nq * cfg.hkv * (cfg.hg / hpw);
   const dim3 grid((unsigned)((a.n_items + kXcds - 1) / kXcds * kXcds));
   switch (cfg.hg) {
-    case 1: hipLaunchKernelGGL((attend_prompt_kernel<128, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attend_prompt_kernel<128, 2>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attend_prompt_kernel<128, 4>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((attend_prompt_kernel<128, 8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((attend_prompt_kernel<128, 1, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attend_prompt_kernel<128, 2, 2>), grid, dim3(512), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attend_prompt_kernel<128, 4, 2>), grid, dim3(512), 0, st, a); break;
+    default: hipLaunchKernelGGL((attend_prompt_kernel<128, 8, 2>), grid, dim3(512), 0, st, a); break;
   }
   return hipGetLastError();
 }

@@ -312,9 +312,15 @@ __device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch&
          w->cand_hi - w->cand_lo <= max_cand;
 }
 
-// MULTI: more query tokens than token slices S (chunked prefill); a separate
-// instantiation so that the decode form keeps its small register footprint.
-template <int D, bool BF16, bool MULTI>
+// MODE 0: pooled query of up to S tokens + scores (decode);
+// MODE 1: pooled query of more tokens (chunked prefill) + scores, a separate
+//         instantiation so that the decode form keeps its small register
+//         footprint;
+// MODE 2: the multi-token pooled query only (grid x = 1), stored for MODE 3;
+// MODE 3: scores only, with the stored pooled query.  The whole-prompt
+//         prefill runs 2 then 3, so the query of a chunk is pooled once
+//         instead of once per tile.
+template <int D, bool BF16, int MODE>
 __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   constexpr int P = D / 2;
   constexpr int S = 256 / P;                 // query-token slices
@@ -346,7 +352,10 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) return;  // route_select reports it
   const int n_cand = w.cand_hi - w.cand_lo;
   const int tile0 = blockIdx.x * kTile;
-  if (tile0 >= n_cand && blockIdx.x != 0) return;  // tile 0 always stores qbar
+  constexpr bool multi = MODE == 1 || MODE == 2;
+  constexpr bool pool_q = MODE != 3;    // this launch forms the pooled query
+  constexpr bool score = MODE != 2;     // this launch scores its tile
+  if (tile0 >= n_cand && (blockIdx.x != 0 || !pool_q)) return;  // tile 0 stores qbar
 
   // ---- loads: the query first, then the tile's summary rows.  Rows past
   // the candidates are read from a clamped in-range row (so every load
@@ -357,7 +366,6 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   //   adjacent dims of each half) for tokens sl2, sl2 + S2, ..., in batches
   //   of TB tokens with all their loads in flight (clamped to the last
   //   token; extras ignored).
-  constexpr bool multi = MULTI;
   const int j = tid % P, sl = tid / P;
   const int jp = tid % JP, sl2 = tid / JP;
   const T* q = static_cast<const T*>(r.q);
@@ -377,7 +385,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       }
     }
   };
-  if constexpr (!multi) {
+  if constexpr (!pool_q) {
+  } else if constexpr (!multi) {
     const int t0 = sl < lq ? sl : lq - 1;
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
@@ -393,6 +402,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   float4 buf[ITER][NV];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
+    if constexpr (!score) break;
     int idx = tile0 + wave * (kTile / 4) + it * RPI + rin;
     idx = idx < n_cand ? w.cand_lo + idx : (n_cand > 0 ? w.cand_hi - 1 : 0);
     const float4* rowp =
@@ -406,7 +416,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   // token's position once, and the rotated sums are added over tokens.  The
   // angle of a thread's next token follows by one fp64 rotation by the
   // token stride times omega_j (error ~1e-16 per step).
-  {
+  if constexpr (pool_q) {
     auto to_d = [](T x) -> double {
       if constexpr (BF16) return bf16_to_f(x);
       else return x;
@@ -496,6 +506,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     }
     __syncthreads();
   }
+  if constexpr (!score) return;
 
   // ---- level-1 scores of this tile
 #pragma unroll
@@ -506,7 +517,10 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qv[v][e] = qbar[4 * (v * kLanesPerRow + sub) + e];
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (v * kLanesPerRow + sub) + e;
+      qv[v][e] = pool_q ? qbar[i] : r.qbar[(size_t)unit * D + i];
+    }
   double* scores = r.scores + (size_t)unit * a.max_cand;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -747,9 +761,16 @@ size_t route_select_lds(const KCfg& cfg, int max_chunks) {
 }
 
 template <int D, bool BF16>
-static void launch_tiles(bool multi, dim3 grid, hipStream_t st, const RouteArgs& a) {
-  if (multi) hipLaunchKernelGGL((route_tiles_kernel<D, BF16, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((route_tiles_kernel<D, BF16, false>), grid, dim3(256), 0, st, a);
+static void launch_tiles(bool multi, bool pooled_once, dim3 grid, hipStream_t st,
+                         const RouteArgs& a) {
+  if (pooled_once) {  // pooled query once per unit, then the tiles
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 2>), dim3(1, grid.y, grid.z), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 3>), grid, dim3(256), 0, st, a);
+  } else if (multi) {
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 1>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 0>), grid, dim3(256), 0, st, a);
+  }
 }
 
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
@@ -769,18 +790,18 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   if (cfg.d == 128) {
     if (bf) {
-      launch_tiles<128, true>(multi, grid, st, a);
+      launch_tiles<128, true>(multi, r.pool_once, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
     } else {
-      launch_tiles<128, false>(multi, grid, st, a);
+      launch_tiles<128, false>(multi, r.pool_once, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
     }
   } else {
     if (bf) {
-      launch_tiles<64, true>(multi, grid, st, a);
+      launch_tiles<64, true>(multi, r.pool_once, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
     } else {
-      launch_tiles<64, false>(multi, grid, st, a);
+      launch_tiles<64, false>(multi, r.pool_once, grid, st, a);
       hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
     }
   }
