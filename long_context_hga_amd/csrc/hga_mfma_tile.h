@@ -122,12 +122,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* k, const uint16_t* v,
 
 // The loaded tile into LDS.  V of a key that is missing (gpos < 0) or lies
 // after pos_last is stored as zero: an unwritten pool row may hold NaN, and
-// 0 x NaN would poison the product.
+// 0 x NaN would poison the product.  all_before (uniform): every group is
+// present and ends before the first query position, so nothing is masked.
 template <int D, int NTHR = 256>
 __device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
                                            const u32x4 (&kraw)[TileStaging<NTHR>::GPT],
                                            const u32x4 (&vraw)[TileStaging<NTHR>::GPT],
-                                           const int (&gpos)[kTileGroups], int pos_last, int tid) {
+                                           const int (&gpos)[kTileGroups], int pos_last, int tid,
+                                           bool all_before) {
   using TS = TileStaging<NTHR>;
   constexpr int CH = D / 8;
   const int sub = tid % 256, half = tid / 256;
@@ -141,11 +143,14 @@ __device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
 #pragma unroll
   for (int i = 0; i < TS::GPT; ++i) {
     const int it = TS::R * i + half;
-    const int gp = TS::pick(gpos, i, half);
-    uint32_t keep = 0u;
+    u32x4 x = vraw[i];
+    if (!all_before) {  // uniform
+      const int gp = TS::pick(gpos, i, half);
+      uint32_t keep = 0u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) keep |= (gp >= 0 && gp + 8 * hf + e <= pos_last) ? (1u << e) : 0u;
-    const u32x4 x = keep_bf16x8(vraw[i], keep);
+      for (int e = 0; e < 8; ++e) keep |= (gp >= 0 && gp + 8 * hf + e <= pos_last) ? (1u << e) : 0u;
+      x = keep_bf16x8(x, keep);
+    }
     // keys 16*(it%2) + 8hf + 0..7 of quarter it/2: column groups 2hf and
     // 2hf + 1, half it%2 of their chunks
     const int c0 = 4 * (it >> 1) + 2 * hf, h = 4 * (it & 1);
@@ -156,7 +161,8 @@ __device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
 
 // S^T of the staged tile for the wave's rows: s[t][n][i] = score (log2
 // units) of key 32t + 16n + 4qg + i for the lane's query row at position
-// tau, -inf where the key is not visible (missing group, or after tau).
+// tau, -inf where the key is not visible (missing group, or after tau; with
+// all_before every key is visible).
 // Returns the lane's maximum; the row maximum needs rows_max.  The operand
 // reads of quarter t + 1 are issued before the products of quarter t
 // (scheduling barriers keep that order), so LDS latency hides under the
@@ -165,7 +171,7 @@ template <int D>
 __device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&qop_hi)[D / 32],
                                              const bf16x8 (&qop_lo)[D / 32],
                                              const int (&gpos)[kTileGroups], int tau, int rl, int qg,
-                                             f32x4 (&s)[4][2]) {
+                                             f32x4 (&s)[4][2], bool all_before) {
   constexpr int KS = D / 32;
   constexpr int NT = kTileGroups / 2;
   auto load_k = [&](int t, bf16x8 (&kop)[2][KS]) {
@@ -195,23 +201,30 @@ __device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&
     __builtin_amdgcn_sched_barrier(0);
   }
   float tmax = -INFINITY;
+  if (!all_before) {  // uniform
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int gp = gpos[2 * t + n];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = gp >= 0 && gp + 4 * qg + i <= tau;
+          s[t][n][i] = vis ? s[t][n][i] : -INFINITY;
+        }
+      }
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int gp = gpos[2 * t + n];
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool vis = gp >= 0 && gp + 4 * qg + i <= tau;
-        s[t][n][i] = vis ? s[t][n][i] : -INFINITY;
-        tmax = fmaxf(tmax, s[t][n][i]);
-      }
-    }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[t][n][i]);
   return tmax;
 }
 
 // Probabilities p = 2^(s - mref) of the tile (added to the lane's l) and
-// O^T += V^T P^T.  The V^T operand reads of quarter t + 1 are issued before
+// O^T += V^T P^T.  The V^T operand reads of quarter t + 1 are issued with
 // the products of quarter t.
 template <int D>
 __device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][2], float mref, int rl,
@@ -224,13 +237,8 @@ __device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][
       vop[n] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const uint4*>(vt + (16 * n + rl) * kTileKeys + (((4 * t + qg) ^ rl) * 8)));
   };
-  bf16x8 vop[2][NB];
-  load_v(0, vop[0]);  // in flight during the probabilities
-  __builtin_amdgcn_sched_barrier(0);
   // k-slot 4n + i of quarter t is key 32t + 16n + 4qg + i
-  bf16x8 pop_hi[NT], pop_lo[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  auto probs = [&](int t, bf16x8& hi, bf16x8& lo) {
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -239,19 +247,37 @@ __device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][
       l += p0 + p1;
       split_pair(p0, p1, ph[k], pl[k]);
     }
-    pop_hi[t] = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    pop_lo[t] = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-  }
+    hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+  };
+  // The probabilities of quarter t + 1 are computed while the products of
+  // quarter t run on the matrix core (one product, then a few vector
+  // instructions, in turn).
+  bf16x8 vop[2][NB];
+  bf16x8 pop_hi[2], pop_lo[2];
+  load_v(0, vop[0]);
+  probs(0, pop_hi[0], pop_lo[0]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (t + 1 < NT) load_v(t + 1, vop[(t + 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);
+    const int cur = t & 1, nxt = cur ^ 1;
+    if (t + 1 < NT) {
+      load_v(t + 1, vop[nxt]);
+      probs(t + 1, pop_hi[nxt], pop_lo[nxt]);
+    }
 #pragma unroll
     for (int n = 0; n < NB; ++n)
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_hi[t], o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[cur][n], pop_hi[cur], o[n], 0, 0, 0);
 #pragma unroll
     for (int n = 0; n < NB; ++n)
-      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[t & 1][n], pop_lo[t], o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[cur][n], pop_lo[cur], o[n], 0, 0, 0);
+    if (t + 1 < NT) {
+#pragma unroll
+      for (int i = 0; i < 2 * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector ALU instructions
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }

@@ -98,7 +98,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   load_tile<D>(static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), gbase, tid, kraw, vraw);
   bf16x8 qop_hi[KS], qop_lo[KS];
   rotate_q<D>(c, qraw, pos0 + row, qg, qop_hi, qop_lo);
-  stage_tile<D>(ks, vt, kraw, vraw, gpos, pos_last, tid);
+  bool all_before = true;  // every group present and before the query chunk (uniform)
+#pragma unroll
+  for (int g = 0; g < kSplitGroups; ++g) all_before = all_before && gpos[g] >= 0 && gpos[g] + kGroupTokens <= pos0;
+  stage_tile<D>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before);
   __syncthreads();
   if (wave * 16 >= a.lq) return;  // no query rows in this wave
 
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // split's 128 scores first, then the probabilities and O^T (no running
   // rescale inside a split)
   f32x4 s[4][2];
-  const float m = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gpos, pos0 + row, rl, qg, s));
+  const float m = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gpos, pos0 + row, rl, qg, s, all_before));
   const float mref = m == -INFINITY ? 0.f : m;  // a row with no visible key: p = 0
   float l = 0.f;
   f32x4 o[NB];

@@ -128,7 +128,11 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
   float m = -INFINITY, l = 0.f;
   for (int t = 0; t < n_tiles; ++t) {
     if (t > 0) __syncthreads();  // every wave is done with the previous tile
-    stage_tile<D, NTHR>(ks, vt, kraw, vraw, gpos, pos_last, tid);
+    bool all_before = true;  // every group present and before the chunk (uniform)
+#pragma unroll
+    for (int it = 0; it < kTileGroups; ++it)
+      all_before = all_before && gpos[it] >= 0 && gpos[it] + kGroupTokens <= pos0;
+    stage_tile<D, NTHR>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before);
     __syncthreads();
     int gcur[kTileGroups];
 #pragma unroll
@@ -138,13 +142,15 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
       load_tile<D, NTHR>(a.k, a.v, gbase, tid, kraw, vraw);
     }
     f32x4 s[4][2];
-    const float tmax = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gcur, tau, rl, qg, s));
+    const float tmax = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gcur, tau, rl, qg, s, all_before));
     const float mn = fmaxf(m, tmax);
     const float mref = mn == -INFINITY ? 0.f : mn;
-    const float al = __builtin_amdgcn_exp2f(m - mref);  // 0 while the row had no visible key
-    l *= al;
+    if (__ballot(mn != m)) {  // some row's maximum grew: rescale (by 1 where it did not)
+      const float al = __builtin_amdgcn_exp2f(m - mref);  // 0 while the row had no visible key
+      l *= al;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) o[n] *= al;
+      for (int n = 0; n < NB; ++n) o[n] *= al;
+    }
     m = mn;
     tile_pv<D>(vt, s, mref, rl, qg, l, o);
   }
