@@ -60,8 +60,8 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="eab72420f4d5ec6c70da3f96824a9dcae3f705c7eef8638255bc273854022456",
-    fetch_kib=16748.46 + 1467.05, write_kib=2080.01 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="4882787ea5d0c5406b1f928754cf805b21433c57a31d3db0b6ececee7bca0ef3",
+    fetch_kib=16747.13 + 1468.94, write_kib=2080.01 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):
@@ -111,6 +111,26 @@ def calibrate_copy(n_bytes=512 << 20, reps=4):
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": n_bytes,
                       "bytes_written_per_dispatch": n_bytes, "dispatches": reps}), flush=True)
+
+
+def calibrate_mfma(rounds=2500):
+    """Dense bf16 rate that v_mfma_f32_16x16x32_bf16 reaches on this device
+    (all CUs, 1, 2 and 4 waves per SIMD), from the calibration library."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_hga_amd", "libhga_calib.so"))
+    f = lib.hga_calib_mfma_rate
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                  ctypes.POINTER(ctypes.c_double)]
+    for w in (1, 2, 4):
+        tf, ms = ctypes.c_double(), ctypes.c_double()
+        rc = f(n_cus, w, rounds, ctypes.byref(tf), ctypes.byref(ms))
+        assert rc == 0, rc
+        print(json.dumps({"calibration": "v_mfma_f32_16x16x32_bf16 issue rate", "cus": n_cus,
+                          "waves_per_simd": w, "tflops": tf.value, "ms": ms.value,
+                          "published_peak_tflops": 2500.0}), flush=True)
 
 
 def cpu_baseline(inp, cfg_params, min_seconds=10.0):
@@ -178,6 +198,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="decode sweep over context 4K..64K and batch 8..32 (one JSON line "
                          "per point) instead of the benchmark line")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="only measure the dense bf16 rate of v_mfma_f32_16x16x32_bf16 at 1, 2 and 4 "
+                         "waves per SIMD")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -187,6 +210,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_mfma:
+        calibrate_mfma()
         return
     if args.sweep:
         run_sweep(args)

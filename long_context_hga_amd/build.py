@@ -11,6 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libhga.so")
+CALIB = os.path.join(PKG, "calib")
+CALIB_OUT = os.path.join(PKG, "libhga_calib.so")
 BUILD = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,6 +42,13 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, OUT)
+    # the benchmark's calibration kernels (not part of the HGA path)
+    tmp = CALIB_OUT + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, *sorted(glob.glob(os.path.join(CALIB, "*.hip")))],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the calibration kernels:\n{r.stderr}")
+    os.replace(tmp, CALIB_OUT)
     return OUT
 
 
