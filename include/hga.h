@@ -329,7 +329,14 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
  *   out, lse_opt   as hga_attend
  *   ws             hga_workspace_bytes() of workspace (this call needs room
  *                  for two attention partial sets and two part results)
- * The call creates and releases two HIP events (no memory).
+ * The two-stream form creates and releases two HIP events (no memory).
+ * stream_b = NULL selects the one-stream form: for 1..15 query tokens the
+ * window part's attention and the PCIe copy of the routed groups run as
+ * workgroups of one launch on stream_a (the copy workgroups mostly wait on
+ * PCIe, the attention workgroups use the CUs meanwhile), then the routed
+ * part and the merge follow on stream_a; no events.  (For 16..64 query
+ * tokens the one-stream form runs the parts one after another.)  Both forms
+ * give the same bits.
  * Errors: as hga_attend; HGA_ERR_INVALID_ARGUMENT if the cold pool is not
  * pinned host memory. */
 hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,

@@ -260,14 +260,13 @@ def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, 
                       stream_b=None):
     """Windows from the device pool on stream_a, routed groups copied from the
     pinned host pool and attended on stream_b, merged on stream_a.  stream_a
-    defaults to the current stream; stream_b must be another stream."""
-    if stream_b is None:
-        raise ValueError("hga_attend_tiered needs a second stream (stream_b)")
+    defaults to the current stream; stream_b=None selects the one-stream form
+    (the window attention and the copy share one launch on stream_a)."""
     _check(lib().hga_attend_tiered(_cfg(cfg), B, _ptr(q_raw), lq, _ptr(q_pos0), _ptr(k_hot),
                                    _ptr(v_hot), hot_cap, _ptr(k_cold), _ptr(v_cold), cold_cap,
                                    _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(k_ws), _ptr(v_ws),
                                    _ptr(out), _ptr(lse_opt), _ptr(ws), ws.numel() * ws.element_size(),
-                                   _stream(stream_a), _stream(stream_b)),
+                                   _stream(stream_a), None if stream_b is None else _stream(stream_b)),
            "hga_attend_tiered")
 
 

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include "hga_internal.h"
+#include "hga_gather_dev.h"
 
 using namespace hga;
 
@@ -482,6 +483,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_INVALID_ARGUMENT;
   hipStream_t sa = static_cast<hipStream_t>(stream_a);
   hipStream_t sb = static_cast<hipStream_t>(stream_b);
+  const bool one_stream = stream_b == nullptr;
 
   // one partial buffer: the window part's splits, then the routed part's;
   // one merge over both
@@ -509,6 +511,25 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   ac.src_layout = HGA_SRC_WORKING_SET;
   ac.src_cap = max_sel * kGroupTokens;
   ac.part_sel = HGA_PART_ROUTED;
+
+  if (one_stream) {
+    // one stream: the window part and the transfer share one launch (decode
+    // shapes), then the routed part and the merge follow in order
+    hipError_t e;
+    if (lq <= kMaxLqDecode) {
+      const GatherArgs g = make_gather_args(k, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0,
+                                            HGA_PART_ROUTED, k_ws, v_ws);
+      e = launch_tiered_front(k, ah, g, max_sel * k.hkv * B, sa);
+    } else {
+      e = launch_attend_split(k, ah, sa);
+      if (e == hipSuccess)
+        e = launch_gather(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0,
+                          HGA_PART_ROUTED, k_ws, v_ws, sa);
+    }
+    if (e == hipSuccess) e = launch_attend_split(k, ac, sa);
+    if (e == hipSuccess) e = launch_attend_merge(k, a, sa);
+    return hip_status(e);
+  }
 
   // fork: stream b starts after everything already queued on stream a (the
   // list written by hga_route); join: the merge on stream a waits for b.  The

@@ -129,6 +129,16 @@ hipError_t launch_attend_split(const KCfg& cfg, const AttendLaunch& a, hipStream
   return hipGetLastError();
 }
 
+hipError_t launch_tiered_front(const KCfg& cfg, const AttendLaunch& win, const GatherArgs& g,
+                               int n_items, hipStream_t st) {
+  const AttendArgs x = attend_args(cfg, win);
+  // the window part holds at most the sink, local and current chunks' groups
+  const int max_win = (cfg.n_sink + cfg.n_local + 1) * kGroups;
+  const int ws = (max_win + kSplitGroups - 1) / kSplitGroups;
+  launch_tier_front(x, ws < x.grid_splits ? ws : x.grid_splits, g, n_items, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend_merge(const KCfg& cfg, const AttendLaunch& a, hipStream_t st) {
   launch_combine(attend_args(cfg, a), st);
   return hipGetLastError();

@@ -96,5 +96,10 @@ __device__ __forceinline__ uint4 keep_bf16(uint4 x, uint32_t keep) {
 // Split kernels; the merge kernel of hga_attend.hip combines their partials.
 void launch_decode(const AttendArgs& x, hipStream_t st);   // 1..15 query tokens
 void launch_prefill(const AttendArgs& x, hipStream_t st);  // 16..64 query tokens
+// The host tier's one-launch front: the first win_splits splits of the decode
+// split grid x beside a persistent gather (hga_decode.hip).
+struct GatherArgs;
+void launch_tier_front(const AttendArgs& x, int win_splits, const GatherArgs& g, int n_items,
+                       hipStream_t st);
 
 }  // namespace hga

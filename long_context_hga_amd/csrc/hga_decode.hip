@@ -33,6 +33,7 @@
 // token are masked, and V of a key that is missing or not yet written is
 // zeroed before it meets a zero probability.
 #include "hga_attend_common.h"
+#include "hga_gather_dev.h"
 
 namespace hga {
 
@@ -62,8 +63,10 @@ struct DecodeShared {
   float ob[4][kColRows][D + 4];   // per-wave output rows (rescaled)
 };
 
+// One split workgroup (256 threads): split `split` of KV head h, grid row bz
+// = sequence * column blocks + column block.
 template <int D, int HG, bool BF16>
-__global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
+__device__ __forceinline__ void decode_split(const AttendArgs& args, int split, int h, int bz) {
   constexpr int P = D / 2;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int NB = D / 16;          // 16-dim blocks of the output
@@ -76,10 +79,9 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
   const AttendLaunch& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, qg = lane >> 4;
-  const int split = blockIdx.x, h = blockIdx.y;
   const int n_rows = HG * a.lq;
   const int ncb = (n_rows + kColRows - 1) / kColRows;
-  const int b = blockIdx.z / ncb, cb = blockIdx.z % ncb;
+  const int b = bz / ncb, cb = bz % ncb;
   const int unit = b * c.hkv + h;
   const int pos0 = a.q_pos0[b];
   const int n_sel = a.n_sel[unit];
@@ -329,6 +331,28 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
   }
 }
 
+template <int D, int HG, bool BF16>
+__global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
+  decode_split<D, HG, BF16>(args, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The host tier's one-launch front: workgroups [0, n_win) are the window
+// part's attention splits (linearised split-fastest over the window grid),
+// the rest a persistent gather of the routed groups from the pinned host
+// pool into the working set.  The copy workgroups wait on PCIe most of the
+// time, so the window attention runs beside the transfer instead of before
+// or after it.
+template <int D, int HG, bool BF16>
+__global__ __launch_bounds__(256) void tier_front_kernel(AttendArgs win, int win_x, int win_y, int n_win,
+                                                         GatherArgs g, int n_items) {
+  const int wg = blockIdx.x;
+  if (wg >= n_win) {
+    gather_items(g, n_items, wg - n_win, gridDim.x - n_win);
+    return;
+  }
+  decode_split<D, HG, BF16>(win, wg % win_x, (wg / win_x) % win_y, wg / (win_x * win_y));
+}
+
 template <int D, int HG>
 static void launch_decode_dh(const AttendArgs& x, dim3 grid, hipStream_t st) {
   if (x.cfg.dtype == HGA_BF16)
@@ -345,6 +369,37 @@ static void launch_decode_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
     case 4: launch_decode_dh<D, 4>(x, grid, st); break;
     default: launch_decode_dh<D, 8>(x, grid, st); break;
   }
+}
+
+template <int D, int HG>
+static void launch_front_dh(const AttendArgs& x, int gx, int gy, int n_win, const GatherArgs& g,
+                            int n_items, int n_gwg, hipStream_t st) {
+  const dim3 grid(n_win + n_gwg);
+  if (x.cfg.dtype == HGA_BF16)
+    hipLaunchKernelGGL((tier_front_kernel<D, HG, true>), grid, dim3(256), 0, st, x, gx, gy, n_win, g, n_items);
+  else
+    hipLaunchKernelGGL((tier_front_kernel<D, HG, false>), grid, dim3(256), 0, st, x, gx, gy, n_win, g, n_items);
+}
+
+template <int D>
+static void launch_front_d(const AttendArgs& x, int gx, int gy, int n_win, const GatherArgs& g,
+                           int n_items, int n_gwg, hipStream_t st) {
+  switch (x.cfg.hg) {
+    case 1: launch_front_dh<D, 1>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
+    case 2: launch_front_dh<D, 2>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
+    case 4: launch_front_dh<D, 4>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
+    default: launch_front_dh<D, 8>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
+  }
+}
+
+void launch_tier_front(const AttendArgs& x, int win_splits, const GatherArgs& g, int n_items,
+                       hipStream_t st) {
+  const int ncb = (x.cfg.hg * x.a.lq + kColRows - 1) / kColRows;
+  const int gx = win_splits, gy = x.cfg.hkv;
+  const int n_win = gx * gy * x.a.B * ncb;
+  const int n_gwg = n_items < kGatherWgs ? n_items : kGatherWgs;
+  if (x.cfg.d == 128) launch_front_d<128>(x, gx, gy, n_win, g, n_items, n_gwg, st);
+  else launch_front_d<64>(x, gx, gy, n_win, g, n_items, n_gwg, st);
 }
 
 void launch_decode(const AttendArgs& x, hipStream_t st) {

@@ -71,6 +71,11 @@ struct AttendLaunch {
 hipError_t launch_attend(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
 hipError_t launch_attend_split(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
 hipError_t launch_attend_merge(const KCfg& cfg, const AttendLaunch& a, hipStream_t st);
+// Host tier in one stream: the window part's decode splits (win, lq <= 15)
+// and the gather g of n_items (slot, KV head, sequence) items in one launch.
+struct GatherArgs;
+hipError_t launch_tiered_front(const KCfg& cfg, const AttendLaunch& win, const GatherArgs& g,
+                               int n_items, hipStream_t st);
 size_t attend_ws_bytes(const KCfg& cfg, int B, int lq, int max_sel);
 
 // Whole-prompt prefill: attention of every query chunk of the prompt over

@@ -42,12 +42,15 @@ def run_tiered(st, kc, vc, q, lq, pos_t, side):
     return s, out, lse
 
 
-@pytest.mark.parametrize("B,T", [(2, 8192), (1, 4096)])
-def test_tiered_decode_equals_device_path_and_oracle(B, T):
+@pytest.mark.parametrize("B,T,form", [(2, 8192, "two streams"), (1, 4096, "two streams"),
+                                      (2, 8192, "one launch"), (1, 4096, "one launch")])
+def test_tiered_decode_equals_device_path_and_oracle(B, T, form):
+    """Both forms: two streams (copy + routed attention on the second), and
+    one stream with the window attention and the copy in one launch."""
     inp = synth.generate("host64k", batch=B, context=T)
     st = gh.build_state(inp)
     kc, vc = pinned_copy(st.k_pool), pinned_copy(st.v_pool)
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if form == "two streams" else None
     q = gh.query_slice(st, 0)
     s, out, lse = run_tiered(st, kc, vc, q, 1, st.pos0, side)
     assert (out - s.out).abs().max().item() <= 1e-5
@@ -88,18 +91,36 @@ def test_tiered_reads_only_window_rows_of_the_device_pool():
     assert torch.equal(out, out0)
 
 
-def test_tiered_prefill_chunk():
-    """A 64-token query chunk through the host tier (MFMA attention on both
-    streams) equals the device path."""
+@pytest.mark.parametrize("form", ["two streams", "one stream"])
+def test_tiered_prefill_chunk(form):
+    """A 64-token query chunk through the host tier (MFMA attention for both
+    parts) equals the device path."""
     inp = synth.generate("prefill32k", context=4096)
     st = gh.build_state(inp)
     kc, vc = pinned_copy(st.k_pool), pinned_copy(st.v_pool)
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if form == "two streams" else None
     q = st.q.contiguous()
     s, out, lse = run_tiered(st, kc, vc, q, 64, st.pos0, side)
     assert torch.isfinite(out).all()
     assert (out - s.out).abs().max().item() <= 1e-5
     assert (lse - s.lse).abs().max().item() <= 1e-5
+
+
+def test_tiered_forms_give_the_same_bits():
+    """The one-launch front (window attention beside the copy) and the
+    two-stream form write identical outputs; several decode tokens in a row
+    through the same buffers."""
+    inp = synth.generate("host64k", batch=2, context=8192)
+    st = gh.build_state(inp)
+    kc, vc = pinned_copy(st.k_pool), pinned_copy(st.v_pool)
+    side = torch.cuda.Stream()
+    q = gh.query_slice(st, 0)
+    for p in (8191, 8190, 8128):
+        pos_t = torch.full((st.B,), p, dtype=torch.int32, device="cuda")
+        _, out2, lse2 = run_tiered(st, kc, vc, q, 1, pos_t, side)
+        _, out1, lse1 = run_tiered(st, kc, vc, q, 1, pos_t, None)
+        assert torch.isfinite(out1).all(), p
+        assert torch.equal(out1, out2) and torch.equal(lse1, lse2), p
 
 
 def test_append_into_pinned_host_pool_equals_device_append():
