@@ -351,6 +351,25 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     s0 = reps[0]["s"]
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 
+    # hga_gather from the HBM pool into a working set (the same lists): its
+    # own copy rate, read + write
+    kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]), dtype=reps[0]["k_pool"].dtype,
+                     device="cuda")
+    vw = torch.empty_like(kw)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(20)]
+    torch.cuda._sleep(int(1e8))
+    for i, (e0, e1) in enumerate(gev):
+        x = reps[i % R]
+        e0.record()
+        hga.hga_gather(cfg, B, x["k_pool"], x["v_pool"], T, 0, x["s"].sel, x["s"].n_sel,
+                       st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
+        e1.record()
+    torch.cuda.synchronize()
+    gather_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
+    gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
+    del kw, vw
+
     ab = algorithmic_bytes(p, B)
     achieved = ab["attend"] / (attend_ms * 1e-3) / 1e9
     out = {
@@ -382,6 +401,10 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
                      "frac": achieved / HBM_PEAK_GBS, "traffic": attend_traffic(),
                      "bytes_per_launch": ab["attend"], "launch_ms": attend_ms,
                      "route_launch_ms": route_ms, "route_bytes_per_launch": ab["route"]},
+        "gather_hbm": {"kernel": "hga_gather, HBM pool -> HBM working set (same lists)",
+                       "launch_ms": gather_ms, "bytes_read_and_written": gather_bytes,
+                       "achieved_GBps": gather_bytes / (gather_ms * 1e-3) / 1e9,
+                       "frac_of_8TBps": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
     del reps, st
     torch.cuda.synchronize()

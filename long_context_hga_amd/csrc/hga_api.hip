@@ -213,7 +213,7 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
     return HGA_ERR_INVALID_ARGUMENT;
   const KCfg k = make_kcfg(cfg);
   return hip_status(launch_gather(k, B, kp, vp, pool_cap, sel_groups, n_sel, max_sel, q_pos0, part,
-                                  k_ws, v_ws, (hipStream_t)stream));
+                                  k_ws, v_ws, pool_is_host != 0, (hipStream_t)stream));
 }
 
 hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
@@ -524,7 +524,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
       e = launch_attend_split(k, ah, sa);
       if (e == hipSuccess)
         e = launch_gather(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0,
-                          HGA_PART_ROUTED, k_ws, v_ws, sa);
+                          HGA_PART_ROUTED, k_ws, v_ws, true, sa);
     }
     if (e == hipSuccess) e = launch_attend_split(k, ac, sa);
     if (e == hipSuccess) e = launch_attend_merge(k, a, sa);
@@ -547,7 +547,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   if (e == hipSuccess) e = hipStreamWaitEvent(sb, fork, 0);
   if (e == hipSuccess)
     e = launch_gather(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0, HGA_PART_ROUTED,
-                      k_ws, v_ws, sb);
+                      k_ws, v_ws, true, sb);
   if (e == hipSuccess) e = launch_attend_split(k, ac, sb);
   if (e == hipSuccess) e = hipEventRecord(join, sb);
   if (e == hipSuccess) e = hipStreamWaitEvent(sa, join, 0);

@@ -11,11 +11,15 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a, int n_items) 
 
 hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
                          int pool_cap, const int* sel, const int* n_sel, int max_sel,
-                         const int* q_pos0, int part, void* k_ws, void* v_ws, hipStream_t st) {
+                         const int* q_pos0, int part, void* k_ws, void* v_ws, bool from_host,
+                         hipStream_t st) {
   const GatherArgs a = make_gather_args(cfg, k_pool, v_pool, pool_cap, sel, n_sel, max_sel, q_pos0,
                                         part, k_ws, v_ws);
   const int n_items = max_sel * cfg.hkv * B;
-  const int n_wg = n_items < kGatherWgs ? n_items : kGatherWgs;
+  // over PCIe a few hundred workgroups keep the link busy and leave CUs to
+  // other work; from HBM every group gets its own workgroup so that all its
+  // loads are in flight at once
+  const int n_wg = from_host ? (n_items < kGatherWgs ? n_items : kGatherWgs) : n_items;
   hipLaunchKernelGGL(gather_kernel, dim3(n_wg), dim3(256), 0, st, a, n_items);
   return hipGetLastError();
 }

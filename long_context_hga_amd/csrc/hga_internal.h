@@ -93,9 +93,12 @@ struct PromptLaunch {
 hipError_t launch_prompt_positions(int* pos, int n_virtual, int nq, hipStream_t st);
 hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStream_t st);
 
+// from_host: the pool is pinned host memory read over PCIe (a small
+// persistent grid); otherwise one workgroup per copied group.
 hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
                          int pool_cap, const int* sel, const int* n_sel, int max_sel,
-                         const int* q_pos0, int part, void* k_ws, void* v_ws, hipStream_t st);
+                         const int* q_pos0, int part, void* k_ws, void* v_ws, bool from_host,
+                         hipStream_t st);
 
 hipError_t launch_merge(int B, int hq, int lq, int d, const float* oa, const float* la,
                         const float* ob, const float* lb, float* out, float* lse, hipStream_t st);
