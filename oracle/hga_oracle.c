@@ -62,6 +62,7 @@ typedef struct {
   double theta;       /* RoPE base */
   double hf_wavelength; /* pair j is high-frequency iff 2*pi/omega_j < this */
   int pool_bf16;      /* 1: pool keys stored as bf16 (RNE); 0: as fp32 (RNE) */
+  int rep_integer;    /* representative position of a span: 0: a + (n-1)/2; 1: a + n/2 */
 } ora_cfg;
 
 /* ---------------------------------------------------------------- RoPE
@@ -92,13 +93,14 @@ void ora_rope(const ora_cfg* c, const double* x, double pos, double* out) {
 
 /* --------------------------------------------------------- summaries
  * Summary of the span of n tokens starting at position a (raw, pre-RoPE keys
- * kraw[n][d]).  Representative position r = a + (n-1)/2 (the span midpoint).
+ * kraw[n][d]).  Representative position r = a + (n-1)/2 (the span midpoint;
+ * the page does not fix it), or a + n/2 with rep_integer (the variant).
  *   HF pair j: mean over the span of the per-token rotated pair.
  *   LF pair j: the mean raw pair, rotated to r.
  */
 void ora_span_summary(const ora_cfg* c, const double* kraw, long a, int n, double* out) {
   int d = c->d, h = d / 2;
-  double r = (double)a + 0.5 * (double)(n - 1);
+  double r = (double)a + (c->rep_integer ? 0.5 * (double)n : 0.5 * (double)(n - 1));
   for (int j = 0; j < h; ++j) {
     double w = ora_omega(c, j);
     double sa = 0.0, sb = 0.0;

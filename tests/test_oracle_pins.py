@@ -21,8 +21,9 @@ from synth import bf16_bits, bf16_to_f32
 RNG = np.random.default_rng(12345)
 
 
-def cfg(d=64, hq=1, hkv=1, C=64, G=4, ns=1, nl=2, kc=2, kg=4, theta=1e4, hf=64.0, bf16=False):
-    return oracle.make_cfg(d, hq, hkv, C, G, ns, nl, kc, kg, theta, hf, bf16)
+def cfg(d=64, hq=1, hkv=1, C=64, G=4, ns=1, nl=2, kc=2, kg=4, theta=1e4, hf=64.0, bf16=False,
+        rep_integer=False):
+    return oracle.make_cfg(d, hq, hkv, C, G, ns, nl, kc, kg, theta, hf, bf16, rep_integer)
 
 
 def omegas(c):
@@ -97,12 +98,26 @@ def test_hf_classification_closed_form():
     assert all(oracle.is_hf(cfg(hf=math.inf), j) for j in range(32))
 
 
+def test_hf_classification_at_group_wavelength():
+    """The variant lambda_hf = g = 16: 4 HF pairs at d = 64, theta = 1e4 and 5
+    at d = 128, theta = 1e6 (the closed form of the bound)."""
+    for d, theta, n_hf in [(64, 1e4, 4), (128, 1e6, 5)]:
+        c = cfg(d=d, theta=theta, hf=16.0)
+        flags = [oracle.is_hf(c, j) for j in range(d // 2)]
+        assert flags == [j < n_hf for j in range(d // 2)]
+        bound = (d / 2) * math.log(16 / (2 * math.pi)) / math.log(theta)
+        assert n_hf == math.floor(bound) + 1
+
+
 # ------------------------------------------------------------- summaries
+@pytest.mark.parametrize("rep_integer", [False, True])
 @pytest.mark.parametrize("n,a", [(64, 0), (16, 48), (64, 65472), (16, 1000)])
-def test_summary_all_lowfreq_is_rotated_mean(n, a):
-    c = cfg(d=128, theta=1e6, hf=0.0)
+def test_summary_all_lowfreq_is_rotated_mean(n, a, rep_integer):
+    """All pairs low-frequency: the raw mean rotated to the representative
+    position, the midpoint a + (n-1)/2 or, in the variant, a + n/2."""
+    c = cfg(d=128, theta=1e6, hf=0.0, rep_integer=rep_integer)
     k = RNG.standard_normal((n, 128))
-    r = a + (n - 1) / 2
+    r = a + (n / 2 if rep_integer else (n - 1) / 2)
     want = from_complex(as_complex(k.mean(axis=0)) * np.exp(1j * r * omegas(c)))
     np.testing.assert_allclose(oracle.span_summary(c, k, a), want, rtol=0, atol=1e-12)
 
@@ -132,6 +147,20 @@ def test_summary_constant_key_dirichlet_closed_form(d, theta, n, a):
     want = from_complex(as_complex(k0) * factor * np.exp(1j * r * w))
     # fp64 angles near 65535 rad carry ~1e-11 rad of rounding
     np.testing.assert_allclose(oracle.span_summary(c, k, a), want, rtol=0, atol=1e-10)
+
+
+def test_representative_position_moves_only_lowfreq_pairs():
+    """The variant changes LF pairs by a half-step rotation (omega_j / 2) and
+    leaves HF pairs exactly as they were."""
+    d, a, n = 128, 64 * 77, 64
+    k = RNG.standard_normal((n, d))
+    mid = oracle.span_summary(cfg(d=d, theta=1e6, hf=64.0), k, a)
+    intg = oracle.span_summary(cfg(d=d, theta=1e6, hf=64.0, rep_integer=True), k, a)
+    w = omegas(cfg(d=d, theta=1e6))
+    hf = 2 * np.pi / w < 64.0
+    zm, zi = as_complex(mid), as_complex(intg)
+    np.testing.assert_array_equal(zi[hf], zm[hf])
+    np.testing.assert_allclose(zi[~hf], zm[~hf] * np.exp(0.5j * w[~hf]), rtol=0, atol=1e-12)
 
 
 def test_summary_mixed_is_per_pair_choice():
