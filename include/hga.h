@@ -88,12 +88,14 @@ typedef struct {
   double rope_theta;       /* RoPE base: omega_j = theta^(-2j/d), pairs (j, j+d/2) */
   double hf_wavelength;    /* pair j is high-frequency iff 2*pi/omega_j < this */
   int32_t qkv_dtype;       /* hga_dtype of q, k, v and of the K/V pool */
+  int32_t rep_position;    /* position the low-frequency pairs of a span's summary are
+                              rotated to: 0 = the midpoint a + (n-1)/2, 1 = a + n/2 */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
  * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
- * theta <= 1), HGA_ERR_UNSUPPORTED for valid shapes this build does not
- * implement. */
+ * theta <= 1, rep_position outside {0, 1}), HGA_ERR_UNSUPPORTED for valid
+ * shapes this build does not implement. */
 hga_status hga_validate(const hga_config* cfg);
 
 /* Worst-case length of a selected-group list for queries of up to max_lq
@@ -131,7 +133,8 @@ hga_status hga_workspace_reset(void* ws, size_t ws_bytes, void* stream);
  *          chunk summary and its G group summaries are written: for pair j,
  *          high-frequency pairs take the mean of the per-token rotated pair,
  *          low-frequency pairs take the mean raw pair rotated to the span's
- *          midpoint a + (n-1)/2.  NULL (both) skips the summaries.
+ *          representative position (cfg->rep_position: the midpoint
+ *          a + (n-1)/2, or a + n/2).  NULL (both) skips the summaries.
  * A decode step that completes a chunk passes that chunk's 64 raw keys (the
  * rows already in the pool are rewritten with identical values).
  * Errors: HGA_ERR_OUT_OF_RANGE if pos0 + n_tok > pool_cap or a completed

@@ -60,19 +60,22 @@ class hga_config(ctypes.Structure):
         ("rope_theta", ctypes.c_double),
         ("hf_wavelength", ctypes.c_double),
         ("qkv_dtype", ctypes.c_int32),
+        ("rep_position", ctypes.c_int32),
     ]
 
 
 def config_from(p: dict, **over) -> hga_config:
     """hga_config from a plain dict with the field names above (``dtype`` may
-    be given as "bf16"/"f32" instead of ``qkv_dtype``)."""
+    be given as "bf16"/"f32" instead of ``qkv_dtype``; ``rep_position``
+    defaults to 0, the span midpoint)."""
     q = dict(p)
     q.update(over)
     dt = q.get("qkv_dtype", HGA_BF16 if q.get("dtype") == "bf16" else HGA_F32)
     return hga_config(int(q["head_dim"]), int(q["n_q_heads"]), int(q["n_kv_heads"]),
                       int(q["chunk_size"]), int(q["groups_per_chunk"]), int(q["n_sink_chunks"]),
                       int(q["n_local_chunks"]), int(q["topk_chunks"]), int(q["topk_groups"]),
-                      float(q["rope_theta"]), float(q["hf_wavelength"]), int(dt))
+                      float(q["rope_theta"]), float(q["hf_wavelength"]), int(dt),
+                      int(q.get("rep_position", 0)))
 
 
 _lib = None

@@ -4,8 +4,8 @@
 // HGA technical summary (gist.science), "Kernmechanisme" item 3: summaries
 // come from the projected keys with no new layers; high-frequency RoPE pairs
 // are rotated per token and then averaged, low-frequency pairs are averaged
-// raw and then rotated to the span's representative position (taken as the
-// midpoint a + (n-1)/2).
+// raw and then rotated to the span's representative position (the midpoint
+// a + (n-1)/2 by default; a + n/2 as a configured variant).
 //
 // 256 threads = P pairs x S token slices (P = d/2).  Each thread loads its
 // pair for all tokens of its slice at once, rotates them in fp64, stepping the
@@ -129,7 +129,7 @@ __device__ __forceinline__ void build_span(
     gb /= kGroupTokens;
     if (!hf) {
       double cs, sn;
-      rope_cs((double)(c0 + s * kGroupTokens) + 0.5 * (kGroupTokens - 1), w, &cs, &sn);
+      rope_cs((double)(c0 + s * kGroupTokens) + 0.5 * (kGroupTokens - 1) + cfg.rep_shift, w, &cs, &sn);
       const double ra = ga * cs - gb * sn, rb = ga * sn + gb * cs;
       ga = ra;
       gb = rb;
@@ -148,7 +148,7 @@ __device__ __forceinline__ void build_span(
     cb /= kChunk;
     if (!hf) {
       double cs, sn;
-      rope_cs((double)c0 + 0.5 * (kChunk - 1), w, &cs, &sn);
+      rope_cs((double)c0 + 0.5 * (kChunk - 1) + cfg.rep_shift, w, &cs, &sn);
       const double ra = ca * cs - cb * sn, rb = ca * sn + cb * cs;
       ca = ra;
       cb = rb;

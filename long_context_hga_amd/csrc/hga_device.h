@@ -21,6 +21,7 @@ struct KCfg {
   float qscale_log2;               // log2(e) / sqrt(d)
   double inv_sqrt_d;
   unsigned long long hf_mask;      // bit j: pair j is high-frequency
+  double rep_shift;                // representative position a + (n-1)/2 + rep_shift
   double omega[kMaxPairs];         // theta^(-2j/d), computed on the host in fp64
 };
 

@@ -60,7 +60,11 @@ __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, i
     const int slot = item % a.max_sel;
     const int unit = item / a.max_sel;  // b * Hkv + h
     const int b = unit / a.hkv;
+    // the list length and the slot's group id are read together (the slot
+    // index is always inside the list buffer); the id is used only if the
+    // slot is listed
     const int n_sel = a.n_sel[unit];
+    const int gid = a.sel[(size_t)unit * a.max_sel + slot];
     if (n_sel < 0 || slot >= n_sel) continue;  // uniform over the workgroup
     if (a.part != HGA_PART_ALL) {
       const int pos0 = a.q_pos0[b];
@@ -71,7 +75,6 @@ __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, i
       const bool routed = slot >= lp.n_head && slot < lp.n_head + lp.n_routed;
       if ((a.part == HGA_PART_ROUTED) != routed) continue;
     }
-    const int gid = a.sel[(size_t)unit * a.max_sel + slot];
     if (gid < 0 || (size_t)(gid + 1) * kGroupTokens > (size_t)a.pool_cap) continue;
     const int n = kGroupTokens * a.row_vecs;  // uint4 per group
     const size_t src = ((size_t)unit * a.pool_cap + (size_t)gid * kGroupTokens) * a.row_vecs;
