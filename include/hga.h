@@ -90,12 +90,18 @@ typedef struct {
   int32_t qkv_dtype;       /* hga_dtype of q, k, v and of the K/V pool */
   int32_t rep_position;    /* position the low-frequency pairs of a span's summary are
                               rotated to: 0 = the midpoint a + (n-1)/2, 1 = a + n/2 */
+  int32_t route_per_head;  /* 0: one selected list per (sequence, KV head), routed with
+                              the mean of its query heads; 1: one list per (sequence,
+                              query head), routed with that head's query alone.  With 1
+                              the list arrays are [B][Hq][...] instead of [B][Hkv][...],
+                              a working set [B][Hq][max_sel*16][d]; hga_prefill_prompt
+                              and hga_attend_tiered return HGA_ERR_UNSUPPORTED */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
  * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
- * theta <= 1, rep_position outside {0, 1}), HGA_ERR_UNSUPPORTED for valid
- * shapes this build does not implement. */
+ * theta <= 1, rep_position or route_per_head outside {0, 1}),
+ * HGA_ERR_UNSUPPORTED for valid shapes this build does not implement. */
 hga_status hga_validate(const hga_config* cfg);
 
 /* Worst-case length of a selected-group list for queries of up to max_lq

@@ -18,9 +18,12 @@ constexpr int64_t kMaxGridZ = 65535;
 
 // Third grid dimension of the attention split kernels: B * (16-row column
 // blocks of Hg*lq query rows) for decode, B for prefill.
+// Selected lists per sequence: one per KV head, or one per query head.
+int64_t lists_of(const hga_config* c) { return c->route_per_head ? c->n_q_heads : c->n_kv_heads; }
+
 int64_t grid_z_of(const hga_config* c, int B, int lq) {
   if (lq >= 16) return B;
-  const int rows = c->n_q_heads / c->n_kv_heads * lq;
+  const int rows = (c->route_per_head ? 1 : c->n_q_heads / c->n_kv_heads) * lq;
   return (int64_t)B * ((rows + 15) / 16);
 }
 
@@ -31,7 +34,8 @@ hga_status check_cfg(const hga_config* c) {
       c->chunk_size % c->groups_per_chunk != 0 || c->n_sink_chunks < 0 || c->n_local_chunks < 0 ||
       c->topk_chunks < 0 || c->topk_groups < 0 || !(c->rope_theta > 1.0) ||
       !(c->hf_wavelength >= 0.0) || (c->qkv_dtype != HGA_F32 && c->qkv_dtype != HGA_BF16) ||
-      (c->rep_position != 0 && c->rep_position != 1))
+      (c->rep_position != 0 && c->rep_position != 1) ||
+      (c->route_per_head != 0 && c->route_per_head != 1))
     return HGA_ERR_INVALID_ARGUMENT;
   const int hg = c->n_q_heads / c->n_kv_heads;
   if ((c->head_dim != 64 && c->head_dim != 128) || c->chunk_size != kChunk ||
@@ -46,6 +50,9 @@ KCfg make_kcfg(const hga_config* c) {
   k.hq = c->n_q_heads;
   k.hkv = c->n_kv_heads;
   k.hg = c->n_q_heads / c->n_kv_heads;
+  k.lists = c->route_per_head ? c->n_q_heads : c->n_kv_heads;
+  k.lhg = c->route_per_head ? 1 : k.hg;
+  k.kvdiv = c->route_per_head ? k.hg : 1;
   k.n_sink = c->n_sink_chunks;
   k.n_local = c->n_local_chunks;
   k.topk_c = c->topk_chunks;
@@ -90,8 +97,8 @@ int tiered_rec_splits(const hga_config* c) {
   return (w + 7) / 8 + (c->topk_groups + 7) / 8;
 }
 size_t tiered_ws_bytes(const hga_config* c, const KCfg& k, int B, int lq) {
-  const int pf = ((2 * k.hg + 3) / 4 * 4) + k.hg * k.d;
-  return (size_t)B * k.hkv * lq * tiered_rec_splits(c) * pf * sizeof(float);
+  const int pf = ((2 * k.lhg + 3) / 4 * 4) + k.lhg * k.d;
+  return (size_t)B * k.lists * lq * tiered_rec_splits(c) * pf * sizeof(float);
 }
 
 }  // namespace
@@ -171,7 +178,7 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
       max_chunks <= 0 || !sel_groups || !n_sel || !ws)
     return HGA_ERR_INVALID_ARGUMENT;
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
-  if ((int64_t)B * cfg->n_kv_heads > kMaxUnits) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)B * lists_of(cfg) > kMaxUnits) return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
   const size_t need = route_ws_bytes(k, B, max_chunks);
@@ -186,7 +193,7 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
   r.chunk_scores = chunk_scores_opt;
   const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
   r.scores = static_cast<double*>(ws);
-  r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
+  r.qbar = r.scores + (size_t)B * k.lists * max_cand;
   r.B = B;
   r.lq = lq;
   r.nq = 1;
@@ -208,7 +215,7 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
       !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
       (part != HGA_PART_ALL && !q_pos0))
     return HGA_ERR_INVALID_ARGUMENT;
-  if ((int64_t)max_sel * cfg->n_kv_heads * B > INT32_MAX) return HGA_ERR_UNSUPPORTED;
+  if ((int64_t)max_sel * lists_of(cfg) * B > INT32_MAX) return HGA_ERR_UNSUPPORTED;
   const void* kp = k_pool;
   const void* vp = v_pool;
   if (pool_is_host && (!pinned_device_ptr(k_pool, &kp) || !pinned_device_ptr(v_pool, &vp)))
@@ -237,7 +244,7 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
+  if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (ws_bytes < attend_ws_bytes(k, B, lq, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
@@ -280,7 +287,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_UNSUPPORTED;
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
+  if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (route_select_lds(k, max_chunks) > kMaxRouteLds) return HGA_ERR_UNSUPPORTED;
@@ -299,7 +306,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   r.chunk_scores = nullptr;
   const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
   r.scores = static_cast<double*>(ws);
-  r.qbar = r.scores + (size_t)B * k.hkv * max_cand;
+  r.qbar = r.scores + (size_t)B * k.lists * max_cand;
   r.B = B;
   r.lq = lq;
   r.nq = 1;
@@ -395,7 +402,8 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
   if ((phases & (HGA_PROMPT_ROUTE | HGA_PROMPT_ATTEND)) && !q_raw) return HGA_ERR_INVALID_ARGUMENT;
   if ((phases & HGA_PROMPT_ATTEND) && !out) return HGA_ERR_INVALID_ARGUMENT;
   if (T > pool_cap || T / kChunk > max_chunks) return HGA_ERR_OUT_OF_RANGE;
-  if (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128) return HGA_ERR_UNSUPPORTED;
+  if (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128 || cfg->route_per_head)
+    return HGA_ERR_UNSUPPORTED;
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   const int nq = T / kChunk;
@@ -423,7 +431,7 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
     r.chunk_scores = nullptr;
     const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
     r.scores = static_cast<double*>(ws);
-    r.qbar = r.scores + (size_t)n_virtual * k.hkv * max_cand;
+    r.qbar = r.scores + (size_t)n_virtual * k.lists * max_cand;
     int* pos = reinterpret_cast<int*>(static_cast<char*>(ws) +
                                       round_up(route_ws_bytes(k, (int)n_virtual, max_chunks), 256));
     r.q_pos0 = pos;
@@ -466,6 +474,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              void* ws, size_t ws_bytes, void* stream_a, void* stream_b) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
+  if (cfg->route_per_head) return HGA_ERR_UNSUPPORTED;
   if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
       hot_cap <= 0 || hot_cap % kGroupTokens != 0 || !k_cold || !v_cold || cold_cap <= 0 ||
       cold_cap % kGroupTokens != 0 || !sel_groups || !n_sel ||
@@ -475,7 +484,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode || tiered_rec_splits(cfg) > kMaxListDecode / 8)
     return HGA_ERR_UNSUPPORTED;
-  if ((int64_t)B * cfg->n_kv_heads * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
+  if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (ws_bytes < tiered_ws_bytes(cfg, k, B, lq)) return HGA_ERR_WORKSPACE_TOO_SMALL;
@@ -521,7 +530,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     if (lq <= kMaxLqDecode) {
       const GatherArgs g = make_gather_args(k, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0,
                                             HGA_PART_ROUTED, k_ws, v_ws);
-      e = launch_tiered_front(k, ah, g, max_sel * k.hkv * B, sa);
+      e = launch_tiered_front(k, ah, g, max_sel * k.lists * B, sa);
     } else {
       e = launch_attend_split(k, ah, sa);
       if (e == hipSuccess)

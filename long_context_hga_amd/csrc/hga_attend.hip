@@ -28,7 +28,7 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
   const int lane = threadIdx.x;
   const int hh = blockIdx.x % HG, ut = blockIdx.x / HG;  // ut = unit * lq + tq
   const int unit = ut / a.lq, tq = ut % a.lq;
-  const int b = unit / c.hkv, h = unit % c.hkv;
+  const int b = unit / c.lists, h = unit % c.lists;
   const size_t orow = ((size_t)(b * c.hq + h * HG + hh) * a.lq + tq) * D + lane * EPL;
   // every split's (m, l, o) is read before the list length is known
   // (splits that did not run are read but not used)
@@ -93,13 +93,13 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
 
 size_t attend_ws_bytes(const KCfg& cfg, int B, int lq, int max_sel) {
   const int n_splits = (max_sel + kSplitGroups - 1) / kSplitGroups;
-  const int pf = ((2 * cfg.hg + 3) / 4 * 4) + cfg.hg * cfg.d;
-  return (size_t)B * cfg.hkv * lq * n_splits * pf * sizeof(float);
+  const int pf = ((2 * cfg.lhg + 3) / 4 * 4) + cfg.lhg * cfg.d;
+  return (size_t)B * cfg.lists * lq * n_splits * pf * sizeof(float);
 }
 
 template <int D>
 static void launch_combine_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
-  switch (x.cfg.hg) {
+  switch (x.cfg.lhg) {
     case 1: hipLaunchKernelGGL((attend_combine_kernel<D, 1>), grid, dim3(64), 0, st, x); break;
     case 2: hipLaunchKernelGGL((attend_combine_kernel<D, 2>), grid, dim3(64), 0, st, x); break;
     case 4: hipLaunchKernelGGL((attend_combine_kernel<D, 4>), grid, dim3(64), 0, st, x); break;
@@ -108,7 +108,7 @@ static void launch_combine_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
 }
 
 static void launch_combine(const AttendArgs& x, hipStream_t st) {
-  const dim3 grid(x.a.B * x.cfg.hkv * x.a.lq * x.cfg.hg);
+  const dim3 grid(x.a.B * x.cfg.lists * x.a.lq * x.cfg.lhg);
   if (x.cfg.d == 128) launch_combine_d<128>(x, grid, st);
   else launch_combine_d<64>(x, grid, st);
 }

@@ -82,7 +82,8 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
   const int n_rows = HG * a.lq;
   const int ncb = (n_rows + kColRows - 1) / kColRows;
   const int b = bz / ncb, cb = bz % ncb;
-  const int unit = b * c.hkv + h;
+  const int unit = b * c.lists + h;               // the list (and its partial records)
+  const int unit_p = b * c.hkv + h / c.kvdiv;       // the pool rows of its KV head
   const int pos0 = a.q_pos0[b];
   const int n_sel = a.n_sel[unit];
   const int* sel = a.sel + (size_t)unit * a.max_sel;
@@ -134,7 +135,7 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
       gid = gid < 0 ? 0 : (gid > max_gid ? max_gid : gid);
       const size_t blk = a.src_layout == HGA_SRC_WORKING_SET
                              ? ((size_t)unit * a.max_sel + slot)
-                             : ((size_t)unit * (a.src_cap / kGroupTokens) + gid);
+                             : ((size_t)unit_p * (a.src_cap / kGroupTokens) + gid);
       kb[g] = blk * kGroupTokens * D;  // K rows of the group, row-major
       vb[g] = blk * kGroupTokens * D;  // V^T block of the group, [D][16]
     }
@@ -363,7 +364,7 @@ static void launch_decode_dh(const AttendArgs& x, dim3 grid, hipStream_t st) {
 
 template <int D>
 static void launch_decode_d(const AttendArgs& x, dim3 grid, hipStream_t st) {
-  switch (x.cfg.hg) {
+  switch (x.cfg.lhg) {
     case 1: launch_decode_dh<D, 1>(x, grid, st); break;
     case 2: launch_decode_dh<D, 2>(x, grid, st); break;
     case 4: launch_decode_dh<D, 4>(x, grid, st); break;
@@ -384,7 +385,7 @@ static void launch_front_dh(const AttendArgs& x, int gx, int gy, int n_win, cons
 template <int D>
 static void launch_front_d(const AttendArgs& x, int gx, int gy, int n_win, const GatherArgs& g,
                            int n_items, int n_gwg, hipStream_t st) {
-  switch (x.cfg.hg) {
+  switch (x.cfg.lhg) {
     case 1: launch_front_dh<D, 1>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
     case 2: launch_front_dh<D, 2>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
     case 4: launch_front_dh<D, 4>(x, gx, gy, n_win, g, n_items, n_gwg, st); break;
@@ -394,8 +395,8 @@ static void launch_front_d(const AttendArgs& x, int gx, int gy, int n_win, const
 
 void launch_tier_front(const AttendArgs& x, int win_splits, const GatherArgs& g, int n_items,
                        hipStream_t st) {
-  const int ncb = (x.cfg.hg * x.a.lq + kColRows - 1) / kColRows;
-  const int gx = win_splits, gy = x.cfg.hkv;
+  const int ncb = (x.cfg.lhg * x.a.lq + kColRows - 1) / kColRows;
+  const int gx = win_splits, gy = x.cfg.lists;
   const int n_win = gx * gy * x.a.B * ncb;
   const int n_gwg = n_items < kGatherWgs ? n_items : kGatherWgs;
   if (x.cfg.d == 128) launch_front_d<128>(x, gx, gy, n_win, g, n_items, n_gwg, st);
@@ -403,8 +404,8 @@ void launch_tier_front(const AttendArgs& x, int win_splits, const GatherArgs& g,
 }
 
 void launch_decode(const AttendArgs& x, hipStream_t st) {
-  const int ncb = (x.cfg.hg * x.a.lq + kColRows - 1) / kColRows;
-  const dim3 grid(x.grid_splits, x.cfg.hkv, x.a.B * ncb);
+  const int ncb = (x.cfg.lhg * x.a.lq + kColRows - 1) / kColRows;
+  const dim3 grid(x.grid_splits, x.cfg.lists, x.a.B * ncb);
   if (x.cfg.d == 128) launch_decode_d<128>(x, grid, st);
   else launch_decode_d<64>(x, grid, st);
 }

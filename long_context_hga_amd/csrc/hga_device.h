@@ -16,6 +16,11 @@ constexpr int kGroups = 4;
 // Everything a kernel needs to know about the configuration, passed by value.
 struct KCfg {
   int d, hq, hkv, hg;
+  // Selected lists: `lists` per sequence, each shared by `lhg` query heads and
+  // reading KV head (list index) / kvdiv.  One list per KV head (lists = hkv,
+  // lhg = hg, kvdiv = 1) or, routing per query head, one per query head
+  // (lists = hq, lhg = 1, kvdiv = hg).
+  int lists, lhg, kvdiv;
   int n_sink, n_local, topk_c, topk_g;
   int dtype;                       // hga_dtype
   float qscale_log2;               // log2(e) / sqrt(d)

@@ -15,7 +15,7 @@ hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void*
                          hipStream_t st) {
   const GatherArgs a = make_gather_args(cfg, k_pool, v_pool, pool_cap, sel, n_sel, max_sel, q_pos0,
                                         part, k_ws, v_ws);
-  const int n_items = max_sel * cfg.hkv * B;
+  const int n_items = max_sel * cfg.lists * B;
   // over PCIe a few hundred workgroups keep the link busy and leave CUs to
   // other work; from HBM every group gets its own workgroup so that all its
   // loads are in flight at once

@@ -23,7 +23,7 @@ struct GatherArgs {
   const int* sel;
   const int* n_sel;
   const int* q_pos0;
-  int hkv, n_sink, n_local, pool_cap, max_sel, part, row_vecs;  // row_vecs: uint4 per token row
+  int lists, kvdiv, hkv, n_sink, n_local, pool_cap, max_sel, part, row_vecs;  // row_vecs: uint4 per token row
 };
 
 // A persistent grid of at most kGatherWgs workgroups walks the (slot, KV
@@ -44,6 +44,8 @@ inline GatherArgs make_gather_args(const KCfg& cfg, const void* k_pool, const vo
   a.sel = sel;
   a.n_sel = n_sel;
   a.q_pos0 = q_pos0;
+  a.lists = cfg.lists;
+  a.kvdiv = cfg.kvdiv;
   a.hkv = cfg.hkv;
   a.n_sink = cfg.n_sink;
   a.n_local = cfg.n_local;
@@ -58,8 +60,9 @@ inline GatherArgs make_gather_args(const KCfg& cfg, const void* k_pool, const vo
 __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, int wg, int n_wg) {
   for (int item = wg; item < n_items; item += n_wg) {
     const int slot = item % a.max_sel;
-    const int unit = item / a.max_sel;  // b * Hkv + h
-    const int b = unit / a.hkv;
+    const int unit = item / a.max_sel;  // b * lists + list
+    const int b = unit / a.lists;
+    const int unit_p = b * a.hkv + (unit % a.lists) / a.kvdiv;  // pool rows of its KV head
     // the list length and the slot's group id are read together (the slot
     // index is always inside the list buffer); the id is used only if the
     // slot is listed
@@ -77,7 +80,7 @@ __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, i
     }
     if (gid < 0 || (size_t)(gid + 1) * kGroupTokens > (size_t)a.pool_cap) continue;
     const int n = kGroupTokens * a.row_vecs;  // uint4 per group
-    const size_t src = ((size_t)unit * a.pool_cap + (size_t)gid * kGroupTokens) * a.row_vecs;
+    const size_t src = ((size_t)unit_p * a.pool_cap + (size_t)gid * kGroupTokens) * a.row_vecs;
     const size_t dst = ((size_t)unit * a.max_sel + slot) * kGroupTokens * a.row_vecs;
     for (int i = threadIdx.x; i < n; i += 256) {
       const uint4 kv = a.k_pool[src + i];

@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const AttendLaunch& a = args.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sp = blockIdx.x, qh = blockIdx.y, b = blockIdx.z;
-  const int kvh = qh / HG, hj = qh % HG;
-  const int unit = b * c.hkv + kvh;
+  const int lst = qh / HG, hj = qh % HG;        // HG = query heads per list
+  const int unit = b * c.lists + lst;           // the list (and its partial records)
+  const int unit_p = b * c.hkv + lst / c.kvdiv;  // the pool rows of its KV head
   const int rl = lane & 15, qg = lane >> 4;  // C-layout column (query row) and row group
   const int row = wave * 16 + rl;            // query token of this lane
   const int pos0 = a.q_pos0[b];
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       gid = gid < 0 ? 0 : (gid > max_gid ? max_gid : gid);
       gbase[g] = a.src_layout == HGA_SRC_WORKING_SET
                      ? ((size_t)unit * a.max_sel + slot) * kGroupTokens * D
-                     : ((size_t)unit * a.src_cap + (size_t)gid * kGroupTokens) * D;
+                     : ((size_t)unit_p * a.src_cap + (size_t)gid * kGroupTokens) * D;
     }
   }
   // ---- every K/V load of the split, issued before any is used; the query
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 void launch_prefill(const AttendArgs& x, hipStream_t st) {
   const dim3 grid(x.grid_splits, x.cfg.hq, x.a.B);
-  switch (x.cfg.hg) {
+  switch (x.cfg.lhg) {
     case 1: hipLaunchKernelGGL((attend_prefill_kernel<128, 1>), grid, dim3(256), 0, st, x); break;
     case 2: hipLaunchKernelGGL((attend_prefill_kernel<128, 2>), grid, dim3(256), 0, st, x); break;
     case 4: hipLaunchKernelGGL((attend_prefill_kernel<128, 4>), grid, dim3(256), 0, st, x); break;

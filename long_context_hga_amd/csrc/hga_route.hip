@@ -342,9 +342,9 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int unit = b * c.hkv + h;                 // workspace rows: virtual sequence
-  const int unit_p = (b / r.nq) * c.hkv + h;      // summaries: pool sequence
-  const size_t qhead0 = (size_t)(b / r.nq) * c.hq + (size_t)h * c.hg;
+  const int unit = b * c.lists + h;                  // workspace rows: virtual sequence, list
+  const int unit_p = (b / r.nq) * c.hkv + h / c.kvdiv;  // summaries: pool sequence, KV head
+  const size_t qhead0 = (size_t)(b / r.nq) * c.hq + (size_t)h * c.lhg;
   const int qt0 = (b % r.nq) * r.lq;              // first query row of this chunk
   const int lq = r.lq;
   int pos0;
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       const int t = tt < lq ? tt : lq - 1;
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh) {
-        const int hc = hh < c.hg ? hh : c.hg - 1;
+        const int hc = hh < c.lhg ? hh : c.lhg - 1;
         const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t) * D;
         ya[u][hh] = *reinterpret_cast<const QT*>(q + row + 2 * jp);
         yb[u][hh] = *reinterpret_cast<const QT*>(q + row + P + 2 * jp);
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     const int t0 = sl < lq ? sl : lq - 1;
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
-      const int hc = hh < c.hg ? hh : c.hg - 1;
+      const int hc = hh < c.lhg ? hh : c.lhg - 1;
       const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t0) * D;
       xa[hh] = q[row + j];
       xb[hh] = q[row + j + P];
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
         double x = 0.0, y = 0.0;
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh)
-          if (hh < c.hg) {
+          if (hh < c.lhg) {
             x += to_d(xa[hh]);
             y += to_d(xb[hh]);
           }
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
             double x[2] = {0.0, 0.0}, y[2] = {0.0, 0.0};
 #pragma unroll
             for (int hh = 0; hh < 8; ++hh)
-              if (hh < c.hg) {
+              if (hh < c.lhg) {
                 if constexpr (BF16) {
                   x[0] += bf16_to_f((uint16_t)(ya[u][hh] & 0xFFFFu));
                   x[1] += bf16_to_f((uint16_t)(ya[u][hh] >> 16));
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
         sa += qpart[u][tid][0];
         sb += qpart[u][tid][1];
       }
-      const double inv = 1.0 / (double)(c.hg * lq);
+      const double inv = 1.0 / (double)(c.lhg * lq);
       qbar[tid] = sa * inv;
       qbar[tid + P] = sb * inv;
       if (blockIdx.x == 0) {
@@ -601,12 +601,12 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  if (blockIdx.z == 1) {  // a fused decode step's token work
-    step_front<D, BF16>(a, h, b, dyn);
+  if (blockIdx.z == 1) {  // a fused step's token work, once per KV head
+    if (h % c.kvdiv == 0) step_front<D, BF16>(a, h / c.kvdiv, b, dyn);
     return;
   }
-  const int unit = b * c.hkv + h;             // lists and workspace: virtual sequence
-  const int unit_p = (b / r.nq) * c.hkv + h;  // summaries: pool sequence
+  const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
+  const int unit_p = (b / r.nq) * c.hkv + h / c.kvdiv;  // summaries: pool sequence, KV head
 
   // every load that does not depend on the position goes out first: this
   // lane's qbar slice (for level 2) and the level-1 scores (clamped to the
@@ -750,7 +750,7 @@ static int max_cand_of(const KCfg& cfg, int max_chunks) {
 }
 
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks) {
-  return (size_t)B * cfg.hkv * (max_cand_of(cfg, max_chunks) + cfg.d) * sizeof(double);
+  return (size_t)B * cfg.lists * (max_cand_of(cfg, max_chunks) + cfg.d) * sizeof(double);
 }
 
 size_t route_select_lds(const KCfg& cfg, int max_chunks) {
@@ -784,8 +784,8 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   size_t lds = route_select_lds(cfg, r.max_chunks);
   const size_t front_lds = (size_t)256 * 2 * sizeof(double);  // build_span scratch: S*P*2 doubles
   if (front && lds < front_lds) lds = front_lds;
-  dim3 grid(n_tiles, cfg.hkv, r.B);
-  dim3 sgrid(cfg.hkv, r.B, front ? 2 : 1);
+  dim3 grid(n_tiles, cfg.lists, r.B);
+  dim3 sgrid(cfg.lists, r.B, front ? 2 : 1);
   const bool bf = cfg.dtype == HGA_BF16;
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   if (cfg.d == 128) {

@@ -72,3 +72,79 @@ def test_variants_change_the_summaries():
         assert not torch.equal(st.chunk_sum, base.chunk_sum), v
         assert not torch.equal(st.group_sum, base.group_sum), v
         assert torch.equal(st.k_pool, base.k_pool)  # the pool does not depend on them
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 4), (8, 4)])
+def test_route_per_query_head(hq, hkv):
+    """One list per query head, routed with that head's own rotated query
+    (the oracle run with a single query head per unit), attended over its KV
+    head: decode (1 and 7 query tokens) and a 64-token prefill chunk; the
+    fused decode step gives the bits of the separate calls; the gather copies
+    each head's list."""
+    import long_context_hga_amd as hga
+    over = dict(n_q_heads=hq, n_kv_heads=hkv, route_per_head=1, needles=0)
+    inp = synth.generate("prefill32k", batch=2, context=4096, overrides=over)
+    st = gh.build_state(inp)
+    p1 = dict(inp.params, n_q_heads=1, n_kv_heads=1)
+    ocfg = oracle.cfg_from(p1)          # one query head per routing unit
+    ucfg = oracle.cfg_from(inp.params)  # summaries / pool (independent of the routing)
+    uc = UnitCache(inp, ucfg)
+    B, hg, max_sel = st.B, hq // hkv, st.max_sel
+    for pos, lq in ((4095, 1), (3000, 7), (4032, 64)):
+        q = st.q[:, :, :lq].contiguous()
+        pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+        sel = torch.full((B, hq, max_sel), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.full((B, hq), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((B, hq, lq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((B, hq, lq), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(hga.hga_workspace_bytes(st.cfg, B, st.T, lq), dtype=torch.uint8,
+                         device="cuda")
+        hga.hga_route(st.cfg, B, q, lq, pos_t, st.chunk_sum, st.group_sum, st.max_chunks, sel,
+                      n_sel, max_sel, None, ws)
+        hga.hga_attend(st.cfg, B, q, lq, pos_t, st.k_pool, st.v_pool, hga.HGA_SRC_POOL, st.T,
+                       sel, n_sel, max_sel, hga.HGA_PART_ALL, out, lse, ws)
+        torch.cuda.synchronize()
+        sel_h, nsel_h, out_h = sel.cpu().numpy(), n_sel.cpu().numpy(), out.cpu().numpy()
+        lists_differ = False
+        for b in range(B):
+            for qh in range(hq):
+                cs, gs, kp, v = uc.get(b, qh // hg)
+                qu = inp.f64(inp.q[b, qh:qh + 1, :lq])
+                g = sel_h[b, qh, :nsel_h[b, qh]]
+                osel, margins, oscores = oracle.select(ocfg, qu, pos, cs, gs)
+                check_selection(ocfg, g, osel, margins, oscores, pos, lq)
+                o_ref, _ = oracle.attend(ocfg, qu, pos, kp, v, g)
+                assert max_abs(out_h[b, qh:qh + 1], o_ref) <= ATOL_OUT, (pos, lq, b, qh)
+                if qh % hg and not (g.size == sel_h[b, qh - 1, :nsel_h[b, qh - 1]].size and
+                                    (g == sel_h[b, qh - 1, :nsel_h[b, qh - 1]]).all()):
+                    lists_differ = True
+        assert lists_differ  # the heads of a KV head do route differently
+        if lq == 1:
+            # gather of every head's list == the pool rows it names
+            kw = torch.zeros((B, hq, max_sel * 16, 128), dtype=st.k_pool.dtype, device="cuda")
+            vw = torch.zeros_like(kw)
+            hga.hga_gather(st.cfg, B, st.k_pool, st.v_pool, st.T, 0, sel, n_sel, max_sel, pos_t,
+                           hga.HGA_PART_ALL, kw, vw)
+            out2 = torch.full_like(out, float("nan"))
+            hga.hga_attend(st.cfg, B, q, lq, pos_t, kw, vw, hga.HGA_SRC_WORKING_SET, st.T, sel,
+                           n_sel, max_sel, hga.HGA_PART_ALL, out2, None, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out2, out)
+            b, qh = 1, hq - 1
+            gid = int(sel[b, qh, 5])
+            assert torch.equal(kw[b, qh, 5 * 16:6 * 16], st.k_pool[b, qh // hg, gid * 16:gid * 16 + 16])
+            # the fused step (append + refresh of the chunk the token ends + route +
+            # attend) gives the same bits
+            stage = st.k_raw[:, :, pos // 64 * 64:pos // 64 * 64 + 64].contiguous()
+            sel3 = torch.full_like(sel, -7)
+            n3 = torch.full_like(n_sel, -7)
+            out3 = torch.full_like(out, float("nan"))
+            kp3, vp3 = st.k_pool.clone(), st.v_pool.clone()
+            cs3, gs3 = st.chunk_sum.clone(), st.group_sum.clone()
+            hga.hga_decode_step(st.cfg, B, q, st.k_raw[:, :, pos].contiguous(),
+                                st.v_raw[:, :, pos].contiguous(), pos_t, kp3, vp3, st.T, stage,
+                                cs3, gs3, st.max_chunks, sel3, n3, max_sel, out3, None,
+                                torch.zeros_like(ws))
+            torch.cuda.synchronize()
+            assert torch.equal(n3, n_sel) and torch.equal(out3, out)
+            assert torch.equal(kp3, st.k_pool) and torch.equal(cs3, st.chunk_sum)
