@@ -71,12 +71,15 @@ def algorithmic_bytes(p, B):
     max_sel = (p["n_sink_chunks"] + p["n_local_chunks"] + 1) * p["groups_per_chunk"] + p["topk_groups"]
     ct = p["query_pos0"] // p["chunk_size"]
     n_cand = ct - p["n_local_chunks"] - p["n_sink_chunks"]
-    kv = max_sel * g * d * 2 * 2 * hkv           # selected K and V rows, bf16
+    lists = hq if p.get("route_per_head") else hkv  # selected lists per sequence
+    kv = max_sel * g * d * 2 * 2 * lists         # selected K and V rows of every list, bf16
     q = hq * d * 2
     o = hq * d * 4
-    idx = hkv * max_sel * 4
+    idx = lists * max_sel * 4
     attend = B * (kv + q + o + idx)
-    route = B * (n_cand * d * 4 * hkv + p["topk_chunks"] * p["groups_per_chunk"] * d * 4 * hkv + q + idx)
+    # level-1 rows of every list, level-2 rows of its kept chunks
+    route = B * (n_cand * d * 4 * lists + p["topk_chunks"] * p["groups_per_chunk"] * d * 4 * lists
+                 + q + idx)
     # new token: raw K, V in, rotated K, V out; refresh: 64 raw keys in, 1 + G rows out
     refresh = B * hkv * (4 * d * 2 + p["chunk_size"] * d * 2 + (1 + p["groups_per_chunk"]) * d * 4)
     return dict(attend=attend, route=route, refresh=refresh, total=attend + route + refresh)
@@ -391,7 +394,8 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
                                f"{p['n_sink_chunks']} sink + {p['n_local_chunks']} local chunks, "
                                f"top-{p['topk_chunks']} chunks, top-{p['topk_groups']} groups "
                                f"({st.max_sel * 16} keys, {100.0 * st.max_sel * 16 / T:.3g}%), "
-                               "pool in HBM",
+                               + ("one list per query head, " if p.get("route_per_head") else "")
+                               + "pool in HBM",
                    "batch": B, "context": T, "replicas": R,
                    "timing": "HIP graph of R steps, replayed",
                    "step_bytes_algorithmic": ab["total"],
@@ -415,7 +419,8 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
 # Decode sweep: context 4K..64K and batch 8..32 at 64K.  4K is the 4K decode
 # workload as defined (batch 1, top-8 chunks, top-16 groups); 8K and 16K keep
 # its budget at batch 8 (the windows alone are 384 tokens, above 3.125 % of
-# 8K); 32K and 64K use the 3.125 % budgets of the 32K and 64K workloads.
+# 8K); 32K and 64K use the 3.125 % budgets of the 32K and 64K workloads.  The
+# last point routes per query head (one list per head instead of per KV head).
 SWEEP = [
     ("decode4k", None, None, None),
     ("decode64k", 8, 8192, dict(topk_chunks=8, topk_groups=16)),
@@ -424,6 +429,7 @@ SWEEP = [
     ("decode64k", 8, 65536, None),
     ("decode64k", 16, 65536, None),
     ("decode64k", 32, 65536, None),
+    ("decode64k", 8, 65536, dict(route_per_head=1)),
 ]
 
 

@@ -150,11 +150,13 @@ hga_status hga_build_summaries(const hga_config* cfg, int32_t B, const void* k_r
                                void* v_pool, int32_t pool_cap, float* chunk_sum,
                                float* group_sum, int32_t max_chunks, void* stream);
 
-/* Two-level routing ("Kernmechanisme" item 2) for each (sequence b, KV head).
+/* Two-level routing ("Kernmechanisme" item 2) for each (sequence b, KV head),
+ * or, with cfg->route_per_head, each (sequence b, query head): the list arrays
+ * below are then [B][Hq][...].
  *   q_raw   [B][Hq][lq][d] raw queries of positions q_pos0[b] .. +lq-1, which
  *           must lie in one chunk c_t (device q_pos0 [B] int32)
- *   The routing query is the mean over the KV head's query heads and query
- *   tokens of RoPE(q, position).  Level 1 scores the candidate chunks
+ *   The routing query is the mean over the KV head's query heads (or the one
+ *   query head) and the query tokens of RoPE(q, position).  Level 1 scores the candidate chunks
  *   n_sink <= c < c_t - n_local as qbar . chunk_sum[c] / sqrt(d) and keeps
  *   the top_k_c by (score desc, id asc); level 2 scores the G groups of each
  *   kept chunk the same way and keeps the global top k_g.  Summaries of all

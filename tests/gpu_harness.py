@@ -101,10 +101,12 @@ class Step:
 def alloc_step(st: State, lq: int) -> Step:
     p = st.inp.params
     B, hkv, hq, d = st.B, p["n_kv_heads"], p["n_q_heads"], p["head_dim"]
+    lists = hq if p.get("route_per_head") else hkv  # one list per query head or per KV head
     return Step(
-        sel=torch.full((B, hkv, st.max_sel), -7, dtype=torch.int32, device="cuda"),
-        n_sel=torch.full((B, hkv), -7, dtype=torch.int32, device="cuda"),
-        scores=torch.full((B, hkv, st.max_chunks), float("nan"), dtype=torch.float64, device="cuda"),
+        sel=torch.full((B, lists, st.max_sel), -7, dtype=torch.int32, device="cuda"),
+        n_sel=torch.full((B, lists), -7, dtype=torch.int32, device="cuda"),
+        scores=torch.full((B, lists, st.max_chunks), float("nan"), dtype=torch.float64,
+                          device="cuda"),
         out=torch.full((B, hq, lq, d), float("nan"), dtype=torch.float32, device="cuda"),
         lse=torch.full((B, hq, lq), float("nan"), dtype=torch.float32, device="cuda"))
 
