@@ -39,6 +39,14 @@ namespace hga {
 
 constexpr int kColRows = 16;  // query rows per column block
 
+// 16 bytes of K or V read once per step: a non-temporal load (the rows are
+// not reused, so they need not displace cached lines)
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 8 fp32 values (two uint4) -> bf16x8 hi and lo operands
 __device__ __forceinline__ void split8(const uint4& x0, const uint4& x1, bf16x8& hi, bf16x8& lo) {
   uint32_t h[4], l[4];
@@ -157,8 +165,8 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 #pragma unroll
         for (int e = 0; e < EV; ++e) {
           const size_t off = kbase + (size_t)t * D + 32 * k + 8 * qg + 4 * e;
-          kraw[n][k][e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + off)
-                               : *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k) + off);
+          kraw[n][k][e] = BF16 ? load_stream(static_cast<const uint16_t*>(a.k) + off)
+                               : load_stream(static_cast<const float*>(a.k) + off);
         }
     }
     const size_t vbase = (qg >> 1) ? vb[1] : vb[0];
@@ -167,8 +175,8 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 #pragma unroll
       for (int e = 0; e < EV; ++e) {
         const size_t off = vbase + (size_t)(16 * nb + rl) * kGroupTokens + 8 * (qg & 1) + 4 * e;
-        vraw[nb][e] = BF16 ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + off)
-                           : *reinterpret_cast<const uint4*>(static_cast<const float*>(a.v) + off);
+        vraw[nb][e] = BF16 ? load_stream(static_cast<const uint16_t*>(a.v) + off)
+                           : load_stream(static_cast<const float*>(a.v) + off);
       }
   }
 
