@@ -43,6 +43,7 @@ class OraCfg(ctypes.Structure):
         ("hf_wavelength", ctypes.c_double),
         ("pool_bf16", ctypes.c_int),
         ("rep_integer", ctypes.c_int),
+        ("rope_interleaved", ctypes.c_int),
     ]
 
 
@@ -107,18 +108,21 @@ def _i(a):
 
 
 def make_cfg(d, hq, hkv, C, G, n_sink, n_local, topk_c, topk_g, theta, hf_wavelength,
-             pool_bf16=True, rep_integer=False) -> OraCfg:
+             pool_bf16=True, rep_integer=False, rope_interleaved=False) -> OraCfg:
     return OraCfg(d, hq, hkv, C, G, n_sink, n_local, topk_c, topk_g, float(theta),
-                  float(hf_wavelength), int(bool(pool_bf16)), int(bool(rep_integer)))
+                  float(hf_wavelength), int(bool(pool_bf16)), int(bool(rep_integer)),
+                  int(bool(rope_interleaved)))
 
 
 def cfg_from(p: dict) -> OraCfg:
     """Build the oracle config from a plain dict (keys as in ``synth.CONFIGS``;
-    ``rep_position`` 1 selects the representative position a + n/2)."""
+    ``rep_position`` 1 selects the representative position a + n/2,
+    ``rope_style`` 1 interleaved RoPE pairs)."""
     return make_cfg(p["head_dim"], p["n_q_heads"], p["n_kv_heads"], p["chunk_size"],
                     p["groups_per_chunk"], p["n_sink_chunks"], p["n_local_chunks"],
                     p["topk_chunks"], p["topk_groups"], p["rope_theta"], p["hf_wavelength"],
-                    p["dtype"] == "bf16", p.get("rep_position", 0) == 1)
+                    p["dtype"] == "bf16", p.get("rep_position", 0) == 1,
+                    p.get("rope_style", 0) == 1)
 
 
 def omega(cfg, j):

@@ -63,13 +63,21 @@ typedef struct {
   double hf_wavelength; /* pair j is high-frequency iff 2*pi/omega_j < this */
   int pool_bf16;      /* 1: pool keys stored as bf16 (RNE); 0: as fp32 (RNE) */
   int rep_integer;    /* representative position of a span: 0: a + (n-1)/2; 1: a + n/2 */
+  int rope_interleaved; /* RoPE pairs: 0: (x_j, x_{j+d/2}); 1: (x_{2j}, x_{2j+1}) */
 } ora_cfg;
 
 /* ---------------------------------------------------------------- RoPE
- * Pairs are (x_j, x_{j+d/2}) for j < d/2 (half-split convention).  Pair j
+ * Pairs are (x_j, x_{j+d/2}) for j < d/2 (half-split convention) or, with
+ * rope_interleaved, (x_{2j}, x_{2j+1}) (the interleaved variant; the page
+ * does not say which).  Pair j
  * turns at angular frequency omega_j = theta^(-2j/d); at position p it is
  * rotated by the angle p*omega_j:  (a, b) -> (a cos - b sin, a sin + b cos).
  */
+/* Dims of the two members of pair j: half-split (j, j + d/2) or, in the
+ * interleaved variant, (2j, 2j + 1). */
+static int pa(const ora_cfg* c, int j) { return c->rope_interleaved ? 2 * j : j; }
+static int pb(const ora_cfg* c, int j) { return c->rope_interleaved ? 2 * j + 1 : j + c->d / 2; }
+
 double ora_omega(const ora_cfg* c, int j) {
   return pow(c->theta, -2.0 * (double)j / (double)c->d);
 }
@@ -85,9 +93,9 @@ void ora_rope(const ora_cfg* c, const double* x, double pos, double* out) {
   for (int j = 0; j < h; ++j) {
     double ang = pos * ora_omega(c, j);
     double cs = cos(ang), sn = sin(ang);
-    double a = x[j], b = x[j + h];
-    out[j] = a * cs - b * sn;
-    out[j + h] = a * sn + b * cs;
+    double a = x[pa(c, j)], b = x[pb(c, j)];
+    out[pa(c, j)] = a * cs - b * sn;
+    out[pb(c, j)] = a * sn + b * cs;
   }
 }
 
@@ -107,21 +115,21 @@ void ora_span_summary(const ora_cfg* c, const double* kraw, long a, int n, doubl
     if (ora_is_hf(c, j)) {
       for (int i = 0; i < n; ++i) {
         double ang = (double)(a + i) * w;
-        double ka = kraw[(long)i * d + j], kb = kraw[(long)i * d + j + h];
+        double ka = kraw[(long)i * d + pa(c, j)], kb = kraw[(long)i * d + pb(c, j)];
         sa += ka * cos(ang) - kb * sin(ang);
         sb += ka * sin(ang) + kb * cos(ang);
       }
-      out[j] = sa / n;
-      out[j + h] = sb / n;
+      out[pa(c, j)] = sa / n;
+      out[pb(c, j)] = sb / n;
     } else {
       for (int i = 0; i < n; ++i) {
-        sa += kraw[(long)i * d + j];
-        sb += kraw[(long)i * d + j + h];
+        sa += kraw[(long)i * d + pa(c, j)];
+        sb += kraw[(long)i * d + pb(c, j)];
       }
       sa /= n;
       sb /= n;
-      out[j] = sa * cos(r * w) - sb * sin(r * w);
-      out[j + h] = sa * sin(r * w) + sb * cos(r * w);
+      out[pa(c, j)] = sa * cos(r * w) - sb * sin(r * w);
+      out[pb(c, j)] = sa * sin(r * w) + sb * cos(r * w);
     }
   }
 }

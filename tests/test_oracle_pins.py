@@ -22,8 +22,9 @@ RNG = np.random.default_rng(12345)
 
 
 def cfg(d=64, hq=1, hkv=1, C=64, G=4, ns=1, nl=2, kc=2, kg=4, theta=1e4, hf=64.0, bf16=False,
-        rep_integer=False):
-    return oracle.make_cfg(d, hq, hkv, C, G, ns, nl, kc, kg, theta, hf, bf16, rep_integer)
+        rep_integer=False, interleaved=False):
+    return oracle.make_cfg(d, hq, hkv, C, G, ns, nl, kc, kg, theta, hf, bf16, rep_integer,
+                           interleaved)
 
 
 def omegas(c):
@@ -71,6 +72,35 @@ def test_rope_matches_library_half_split():
     ref = lib_rope(x, pos, c)
     got = np.stack([oracle.rope(c, x[i], pos[i]) for i in range(7)])
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_rope_interleaved_matches_library():
+    """The interleaved variant against transformers' GPT-J rotary embedding
+    (pairs (x_2j, x_2j+1)), fp64."""
+    mod = pytest.importorskip("transformers.models.gptj.modeling_gptj")
+    c = cfg(d=128, theta=1e6, interleaved=True)
+    x = RNG.standard_normal((7, 128))
+    pos = np.array([0, 1, 5, 63, 1000, 32767, 65535], dtype=np.float64)
+    ang = torch.tensor(pos)[:, None] * torch.tensor(omegas(c))[None, :]  # [n][d/2]
+    xt = torch.tensor(x)[None, :, None, :]                                # [1][n][1][d]
+    ref = mod.apply_rotary_pos_emb(xt, ang.sin()[None], ang.cos()[None])[0, :, 0].numpy()
+    got = np.stack([oracle.rope(c, x[i], pos[i]) for i in range(7)])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_interleaved_is_a_permutation_of_half_split():
+    """Rotating, summarising and routing with interleaved pairs equals the
+    half-split path on inputs whose dims are permuted (2j, 2j+1) -> (j, j+d/2),
+    permuted back."""
+    d = 128
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # interleaved dim of half-split dim
+    ci = cfg(d=d, theta=1e6, interleaved=True)
+    ch = cfg(d=d, theta=1e6)
+    x = RNG.standard_normal(d)
+    np.testing.assert_array_equal(oracle.rope(ci, x, 4321)[perm], oracle.rope(ch, x[perm], 4321))
+    k = RNG.standard_normal((64, d))
+    np.testing.assert_array_equal(oracle.span_summary(ci, k, 640)[perm],
+                                  oracle.span_summary(ch, k[:, perm], 640))
 
 
 def test_rope_invariants():
