@@ -85,7 +85,7 @@ typedef struct {
   int32_t n_local_chunks;  /* chunks just before the current one, always visible */
   int32_t topk_chunks;     /* level-1 budget k_c */
   int32_t topk_groups;     /* level-2 budget k_g (global over the k_c*G groups) */
-  double rope_theta;       /* RoPE base: omega_j = theta^(-2j/d), pairs (j, j+d/2) */
+  double rope_theta;       /* RoPE base: omega_j = theta^(-2j/d) for pair j */
   double hf_wavelength;    /* pair j is high-frequency iff 2*pi/omega_j < this */
   int32_t qkv_dtype;       /* hga_dtype of q, k, v and of the K/V pool */
   int32_t rep_position;    /* position the low-frequency pairs of a span's summary are
@@ -96,11 +96,14 @@ typedef struct {
                               the list arrays are [B][Hq][...] instead of [B][Hkv][...],
                               a working set [B][Hq][max_sel*16][d]; hga_prefill_prompt
                               and hga_attend_tiered return HGA_ERR_UNSUPPORTED */
+  int32_t rope_style;      /* RoPE pairs: 0 = (x_j, x_{j+d/2}) (half-split), 1 =
+                              (x_{2j}, x_{2j+1}) (interleaved); the pool keys, the
+                              summaries and the rotated queries follow it */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
  * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
- * theta <= 1, rep_position or route_per_head outside {0, 1}),
+ * theta <= 1, rep_position, route_per_head or rope_style outside {0, 1}),
  * HGA_ERR_UNSUPPORTED for valid shapes this build does not implement. */
 hga_status hga_validate(const hga_config* cfg);
 

@@ -62,13 +62,14 @@ class hga_config(ctypes.Structure):
         ("qkv_dtype", ctypes.c_int32),
         ("rep_position", ctypes.c_int32),
         ("route_per_head", ctypes.c_int32),
+        ("rope_style", ctypes.c_int32),
     ]
 
 
 def config_from(p: dict, **over) -> hga_config:
     """hga_config from a plain dict with the field names above (``dtype`` may
-    be given as "bf16"/"f32" instead of ``qkv_dtype``; ``rep_position`` and
-    ``route_per_head`` default to 0)."""
+    be given as "bf16"/"f32" instead of ``qkv_dtype``; ``rep_position``,
+    ``route_per_head`` and ``rope_style`` default to 0)."""
     q = dict(p)
     q.update(over)
     dt = q.get("qkv_dtype", HGA_BF16 if q.get("dtype") == "bf16" else HGA_F32)
@@ -76,7 +77,8 @@ def config_from(p: dict, **over) -> hga_config:
                       int(q["chunk_size"]), int(q["groups_per_chunk"]), int(q["n_sink_chunks"]),
                       int(q["n_local_chunks"]), int(q["topk_chunks"]), int(q["topk_groups"]),
                       float(q["rope_theta"]), float(q["hf_wavelength"]), int(dt),
-                      int(q.get("rep_position", 0)), int(q.get("route_per_head", 0)))
+                      int(q.get("rep_position", 0)), int(q.get("route_per_head", 0)),
+                      int(q.get("rope_style", 0)))
 
 
 _lib = None

@@ -35,7 +35,8 @@ hga_status check_cfg(const hga_config* c) {
       c->topk_chunks < 0 || c->topk_groups < 0 || !(c->rope_theta > 1.0) ||
       !(c->hf_wavelength >= 0.0) || (c->qkv_dtype != HGA_F32 && c->qkv_dtype != HGA_BF16) ||
       (c->rep_position != 0 && c->rep_position != 1) ||
-      (c->route_per_head != 0 && c->route_per_head != 1))
+      (c->route_per_head != 0 && c->route_per_head != 1) ||
+      (c->rope_style != 0 && c->rope_style != 1))
     return HGA_ERR_INVALID_ARGUMENT;
   const int hg = c->n_q_heads / c->n_kv_heads;
   if ((c->head_dim != 64 && c->head_dim != 128) || c->chunk_size != kChunk ||
@@ -61,6 +62,7 @@ KCfg make_kcfg(const hga_config* c) {
   k.inv_sqrt_d = 1.0 / sqrt((double)c->head_dim);
   k.qscale_log2 = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
   k.rep_shift = c->rep_position == 1 ? 0.5 : 0.0;
+  k.interleaved = c->rope_style == 1;
   k.hf_mask = 0;
   for (int j = 0; j < c->head_dim / 2; ++j) {
     k.omega[j] = pow(c->rope_theta, -2.0 * (double)j / (double)c->head_dim);

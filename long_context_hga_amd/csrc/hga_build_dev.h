@@ -44,6 +44,7 @@ __device__ __forceinline__ void build_span(
   const int j = tid % P, s = tid / P;
   const bool complete = c0 >= lo && c0 + kChunk <= hi;
   const bool hf = (cfg.hf_mask >> j) & 1ull;
+  const int ja = pair_a(cfg, j), jb = pair_b(cfg, j);  // dims of the pair's members
   const double w = cfg.omega[j];
 
   // every load of this thread first (TS tokens of pair j), unconditionally
@@ -56,10 +57,10 @@ __device__ __forceinline__ void build_span(
     p = p < lo ? lo : (p >= hi ? hi - 1 : p);
     const T* kr = krow(p);
     const T* vr = kp ? vrow(p) : kr;
-    xa[i] = kr[j];
-    xb[i] = kr[j + P];
-    ya[i] = vr[j];
-    yb[i] = vr[j + P];
+    xa[i] = kr[ja];
+    xb[i] = kr[jb];
+    ya[i] = vr[ja];
+    yb[i] = vr[jb];
   }
   // angles of consecutive positions by rotation: (cos, sin)(p w) from
   // (cos, sin)(p0 w) and (cos, sin)(w) in fp64 (error ~1e-16 per step)
@@ -73,8 +74,8 @@ __device__ __forceinline__ void build_span(
     const int p = p_first + i;
     if (p >= lo && p < hi) {
       if (stage) {
-        stage[(size_t)(p - c0) * D + j] = xa[i];
-        stage[(size_t)(p - c0) * D + j + P] = xb[i];
+        stage[(size_t)(p - c0) * D + ja] = xa[i];
+        stage[(size_t)(p - c0) * D + jb] = xb[i];
       }
       double ka, kb;
       if constexpr (BF16) {
@@ -89,16 +90,16 @@ __device__ __forceinline__ void build_span(
       if (kp) {
         const size_t prow = (size_t)p * D;
         if constexpr (BF16) {
-          kp[prow + j] = f64_to_bf16_rne(ra);
-          kp[prow + j + P] = f64_to_bf16_rne(rb);
+          kp[prow + ja] = f64_to_bf16_rne(ra);
+          kp[prow + jb] = f64_to_bf16_rne(rb);
         } else {
-          kp[prow + j] = (float)ra;
-          kp[prow + j + P] = (float)rb;
+          kp[prow + ja] = (float)ra;
+          kp[prow + jb] = (float)rb;
         }
         // V: each 16-token group is stored transposed, a [D][16] block
         const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
-        vp[vcol + (size_t)j * kGroupTokens] = ya[i];
-        vp[vcol + (size_t)(j + P) * kGroupTokens] = yb[i];
+        vp[vcol + (size_t)ja * kGroupTokens] = ya[i];
+        vp[vcol + (size_t)jb * kGroupTokens] = yb[i];
       }
       if (hf) {
         sa += ra;
@@ -135,8 +136,8 @@ __device__ __forceinline__ void build_span(
       gb = rb;
     }
     float* gs = gs_rows + (size_t)s * D;
-    gs[j] = (float)ga;
-    gs[j + P] = (float)gb;
+    gs[ja] = (float)ga;
+    gs[jb] = (float)gb;
   }
   if (s == 0) {
     double ca = 0.0, cb = 0.0;
@@ -153,8 +154,8 @@ __device__ __forceinline__ void build_span(
       ca = ra;
       cb = rb;
     }
-    cs_row[j] = (float)ca;
-    cs_row[j + P] = (float)cb;
+    cs_row[ja] = (float)ca;
+    cs_row[jb] = (float)cb;
   }
 }
 

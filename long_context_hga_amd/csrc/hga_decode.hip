@@ -109,11 +109,11 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
     const int tq = gr / HG, hh = gr % HG;
     const size_t row = ((size_t)(b * c.hq + h * HG + hh) * a.lq + tq) * D;
     if constexpr (BF16) {
-      qx[i] = static_cast<const uint16_t*>(a.q)[row + jr];
-      qy[i] = static_cast<const uint16_t*>(a.q)[row + jr + P];
+      qx[i] = static_cast<const uint16_t*>(a.q)[row + pair_a(c, jr)];
+      qy[i] = static_cast<const uint16_t*>(a.q)[row + pair_b(c, jr)];
     } else {
-      qx[i] = __float_as_uint(static_cast<const float*>(a.q)[row + jr]);
-      qy[i] = __float_as_uint(static_cast<const float*>(a.q)[row + jr + P]);
+      qx[i] = __float_as_uint(static_cast<const float*>(a.q)[row + pair_a(c, jr)]);
+      qy[i] = __float_as_uint(static_cast<const float*>(a.q)[row + pair_b(c, jr)]);
     }
   }
 
@@ -200,10 +200,10 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
       }
       uint32_t hi, lo;
       split_pair(rx, ry, hi, lo);
-      sh.qhi[r][jr] = (uint16_t)(hi & 0xFFFFu);
-      sh.qhi[r][jr + P] = (uint16_t)(hi >> 16);
-      sh.qlo[r][jr] = (uint16_t)(lo & 0xFFFFu);
-      sh.qlo[r][jr + P] = (uint16_t)(lo >> 16);
+      sh.qhi[r][pair_a(c, jr)] = (uint16_t)(hi & 0xFFFFu);
+      sh.qhi[r][pair_b(c, jr)] = (uint16_t)(hi >> 16);
+      sh.qlo[r][pair_a(c, jr)] = (uint16_t)(lo & 0xFFFFu);
+      sh.qlo[r][pair_b(c, jr)] = (uint16_t)(lo >> 16);
     }
   }
   __syncthreads();

@@ -21,6 +21,7 @@ struct KCfg {
   // lhg = hg, kvdiv = 1) or, routing per query head, one per query head
   // (lists = hq, lhg = 1, kvdiv = hg).
   int lists, lhg, kvdiv;
+  int interleaved;                 // RoPE pairs (2j, 2j+1) instead of (j, j + d/2)
   int n_sink, n_local, topk_c, topk_g;
   int dtype;                       // hga_dtype
   float qscale_log2;               // log2(e) / sqrt(d)
@@ -29,6 +30,12 @@ struct KCfg {
   double rep_shift;                // representative position a + (n-1)/2 + rep_shift
   double omega[kMaxPairs];         // theta^(-2j/d), computed on the host in fp64
 };
+
+// Dims of the two members of RoPE pair j.
+__host__ __device__ __forceinline__ int pair_a(const KCfg& c, int j) { return c.interleaved ? 2 * j : j; }
+__host__ __device__ __forceinline__ int pair_b(const KCfg& c, int j) {
+  return c.interleaved ? 2 * j + 1 : j + c.d / 2;
+}
 
 // ------------------------------------------------------------ numerics
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }

@@ -36,7 +36,8 @@ __device__ __forceinline__ u32x4 keep_bf16x8(u32x4 x, uint32_t keep) {
 }
 
 // The lane's B operand of S^T = K Q^T is its query row at dims 32k + 8qg +
-// 0..7 (k < 4): both halves of the RoPE pairs j = 8qg + i and 32 + 8qg + i,
+// 0..7 (k < 4): both halves of the RoPE pairs j = 8qg + i and 32 + 8qg + i
+// (half-split pairs), or pairs 16k + 4qg + 0..3 whole (interleaved pairs),
 // so the lane rotates its own operand.  qrow: the raw bf16 query row.
 template <int D>
 __device__ __forceinline__ void load_q_raw(const uint16_t* qrow, int qg, uint4 (&qraw)[D / 32]) {
@@ -55,6 +56,30 @@ __device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 
   constexpr int KS = D / 32;
   const double tau_d = (double)tau;
   uint32_t hi[KS][4], lo[KS][4];
+  if (c.interleaved) {
+    // pairs (2j, 2j + 1): each 32-bit word of the operand holds one pair,
+    // j = 16k + 4qg + w
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const uint32_t wv[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int j = 16 * k + 4 * qg + w;
+        const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
+        const float fr = (float)(turns - rint(turns));
+        const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+        const float x = __uint_as_float(wv[w] << 16);
+        const float y = __uint_as_float(wv[w] & 0xFFFF0000u);
+        split_pair((x * cs - y * sn) * c.qscale_log2, (x * sn + y * cs) * c.qscale_log2, hi[k][w], lo[k][w]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      qop_hi[k] = __builtin_bit_cast(bf16x8, make_uint4(hi[k][0], hi[k][1], hi[k][2], hi[k][3]));
+      qop_lo[k] = __builtin_bit_cast(bf16x8, make_uint4(lo[k][0], lo[k][1], lo[k][2], lo[k][3]));
+    }
+    return;
+  }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {  // pairs j = 32*half + 8qg + i
     const uint32_t wx[4] = {qraw[half].x, qraw[half].y, qraw[half].z, qraw[half].w};

@@ -371,6 +371,10 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const T* q = static_cast<const T*>(r.q);
   T xa[8], xb[8];
   QT ya[TB][8], yb[TB][8];
+  // dims of the two 2-element loads of pairs 2jp, 2jp + 1: half-split (a of
+  // both, b of both) or interleaved (a, b of pair 2jp; a, b of pair 2jp + 1)
+  const int qoa = c.interleaved ? 4 * jp : 2 * jp;
+  const int qob = c.interleaved ? 4 * jp + 2 : P + 2 * jp;
   auto load_batch = [&](int u0) {  // tokens sl2 + (u0 + u) * S2, u < TB
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
@@ -380,8 +384,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       for (int hh = 0; hh < 8; ++hh) {
         const int hc = hh < c.lhg ? hh : c.lhg - 1;
         const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t) * D;
-        ya[u][hh] = *reinterpret_cast<const QT*>(q + row + 2 * jp);
-        yb[u][hh] = *reinterpret_cast<const QT*>(q + row + P + 2 * jp);
+        ya[u][hh] = *reinterpret_cast<const QT*>(q + row + qoa);
+        yb[u][hh] = *reinterpret_cast<const QT*>(q + row + qob);
       }
     }
   };
@@ -392,8 +396,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     for (int hh = 0; hh < 8; ++hh) {
       const int hc = hh < c.lhg ? hh : c.lhg - 1;
       const size_t row = ((qhead0 + hc) * r.q_tokens + qt0 + t0) * D;
-      xa[hh] = q[row + j];
-      xb[hh] = q[row + j + P];
+      xa[hh] = q[row + pair_a(c, j)];
+      xb[hh] = q[row + pair_b(c, j)];
     }
   } else {
     load_batch(0);
@@ -456,17 +460,22 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 #pragma unroll
             for (int hh = 0; hh < 8; ++hh)
               if (hh < c.lhg) {
+                double e0, e1, e2, e3;  // the four loaded elements in load order
                 if constexpr (BF16) {
-                  x[0] += bf16_to_f((uint16_t)(ya[u][hh] & 0xFFFFu));
-                  x[1] += bf16_to_f((uint16_t)(ya[u][hh] >> 16));
-                  y[0] += bf16_to_f((uint16_t)(yb[u][hh] & 0xFFFFu));
-                  y[1] += bf16_to_f((uint16_t)(yb[u][hh] >> 16));
+                  e0 = bf16_to_f((uint16_t)(ya[u][hh] & 0xFFFFu));
+                  e1 = bf16_to_f((uint16_t)(ya[u][hh] >> 16));
+                  e2 = bf16_to_f((uint16_t)(yb[u][hh] & 0xFFFFu));
+                  e3 = bf16_to_f((uint16_t)(yb[u][hh] >> 16));
                 } else {
-                  x[0] += ya[u][hh].x;
-                  x[1] += ya[u][hh].y;
-                  y[0] += yb[u][hh].x;
-                  y[1] += yb[u][hh].y;
+                  e0 = ya[u][hh].x;
+                  e1 = ya[u][hh].y;
+                  e2 = yb[u][hh].x;
+                  e3 = yb[u][hh].y;
                 }
+                x[0] += e0;
+                x[1] += c.interleaved ? e2 : e1;
+                y[0] += c.interleaved ? e1 : e2;
+                y[1] += e3;
               }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -497,11 +506,11 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
         sb += qpart[u][tid][1];
       }
       const double inv = 1.0 / (double)(c.lhg * lq);
-      qbar[tid] = sa * inv;
-      qbar[tid + P] = sb * inv;
+      qbar[pair_a(c, tid)] = sa * inv;
+      qbar[pair_b(c, tid)] = sb * inv;
       if (blockIdx.x == 0) {
-        r.qbar[(size_t)unit * D + tid] = sa * inv;
-        r.qbar[(size_t)unit * D + tid + P] = sb * inv;
+        r.qbar[(size_t)unit * D + pair_a(c, tid)] = sa * inv;
+        r.qbar[(size_t)unit * D + pair_b(c, tid)] = sb * inv;
       }
     }
     __syncthreads();

@@ -43,7 +43,7 @@ def test_validate():
     assert hga.hga_validate(hga.config_from(synth.CONFIGS["tiny"])) == hga.HGA_OK
     bad = [dict(head_dim=127), dict(n_q_heads=30), dict(groups_per_chunk=3), dict(rope_theta=1.0),
            dict(topk_chunks=-1), dict(hf_wavelength=float("nan")), dict(qkv_dtype=7),
-           dict(rep_position=2), dict(route_per_head=-1)]
+           dict(rep_position=2), dict(route_per_head=-1), dict(rope_style=3)]
     for b in bad:
         assert hga.hga_validate(cfg(**b)) == hga.HGA_ERR_INVALID_ARGUMENT, b
     unsup = [dict(head_dim=96), dict(chunk_size=128), dict(groups_per_chunk=8),

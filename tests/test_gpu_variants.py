@@ -1,7 +1,8 @@
 """GPU parity of the routing / summary variants against the fp64 oracle with
 the same switches: the high-frequency threshold at the group length
-(lambda_hf = g = 16 instead of C = 64) and the representative position
-a + n/2 instead of the midpoint a + (n-1)/2 (tests/oracle_ref.py rules:
+(lambda_hf = g = 16 instead of C = 64), the representative position a + n/2
+instead of the midpoint a + (n-1)/2, interleaved RoPE pairs, and routing per
+query head (tests/oracle_ref.py rules:
 summaries within 1 fp32 ulp, selections exact where the margins allow,
 outputs within the attention tolerance)."""
 import pytest
@@ -20,7 +21,8 @@ if not torch.cuda.is_available():
 import gpu_harness as gh  # noqa: E402
 
 VARIANTS = [dict(hf_wavelength=16.0), dict(rep_position=1),
-            dict(hf_wavelength=16.0, rep_position=1)]
+            dict(hf_wavelength=16.0, rep_position=1), dict(rope_style=1),
+            dict(rope_style=1, rep_position=1)]
 
 
 def vid(v):
@@ -71,7 +73,10 @@ def test_variants_change_the_summaries():
         st = gh.build_state(synth.generate("prefill32k", context=1024, overrides=dict(v, needles=0)))
         assert not torch.equal(st.chunk_sum, base.chunk_sum), v
         assert not torch.equal(st.group_sum, base.group_sum), v
-        assert torch.equal(st.k_pool, base.k_pool)  # the pool does not depend on them
+        if "rope_style" not in v:  # the pool depends only on the pairing
+            assert torch.equal(st.k_pool, base.k_pool)
+        else:
+            assert not torch.equal(st.k_pool, base.k_pool)
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 4), (8, 4)])
@@ -148,3 +153,51 @@ def test_route_per_query_head(hq, hkv):
             torch.cuda.synchronize()
             assert torch.equal(n3, n_sel) and torch.equal(out3, out)
             assert torch.equal(kp3, st.k_pool) and torch.equal(cs3, st.chunk_sum)
+
+
+def test_interleaved_whole_prompt_and_fused_step():
+    """Interleaved RoPE pairs through the whole-prompt prefill (every chunk of
+    a 512-token prompt against the oracle) and the fused decode step (the
+    bits of the separate calls)."""
+    import long_context_hga_amd as hga
+    inp = synth.generate("prompt32k", context=512, overrides=dict(rope_style=1))
+    st = gh.build_state(inp, max_lq=64)
+    cfg = oracle.cfg_from(inp.params)
+    uc = UnitCache(inp, cfg)
+    T, nq, hg = st.T, st.T // 64, 8
+    sel = torch.full((1, nq, 4, st.max_sel), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((1, nq, 4), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((1, 32, T, 128), float("nan"), dtype=torch.float32, device="cuda")
+    kp, vp = torch.zeros_like(st.k_pool), torch.zeros_like(st.v_pool)
+    cs, gs = torch.zeros_like(st.chunk_sum), torch.zeros_like(st.group_sum)
+    ws = torch.zeros(hga.hga_prompt_workspace_bytes(st.cfg, 1, T, st.max_chunks),
+                     dtype=torch.uint8, device="cuda")
+    hga.hga_prefill_prompt(st.cfg, 1, T, st.q, st.k_raw, st.v_raw, kp, vp, T, cs, gs,
+                           st.max_chunks, sel, n_sel, st.max_sel, out, None, ws)
+    torch.cuda.synchronize()
+    sel_h, nsel_h, out_h = sel.cpu().numpy(), n_sel.cpu().numpy(), out.cpu().numpy()
+    for qc in range(nq):
+        for h in range(4):
+            cs_, gs_, kpo, vpo = uc.get(0, h)
+            qu = q_unit(inp, cfg, 0, h, qc * 64, 64)
+            g = sel_h[0, qc, h, :nsel_h[0, qc, h]]
+            osel, margins, oscores = oracle.select(cfg, qu, qc * 64, cs_, gs_)
+            check_selection(cfg, g, osel, margins, oscores, qc * 64, 64)
+            o_ref, _ = oracle.attend(cfg, qu, qc * 64, kpo, vpo, g)
+            assert max_abs(out_h[0, h * hg:(h + 1) * hg, qc * 64:(qc + 1) * 64], o_ref) <= ATOL_OUT
+    # fused decode step at the last position == route + attend
+    dinp = synth.generate("decode64k", batch=2, context=2048, overrides=dict(rope_style=1))
+    dst = gh.build_state(dinp)
+    q = gh.query_slice(dst, 0)
+    s1 = gh.alloc_step(dst, 1)
+    gh.route(dst, q, 1, dst.pos0, s1)
+    gh.attend(dst, q, 1, dst.pos0, s1)
+    pos = int(dinp.pos0[0])
+    stage = dst.k_raw[:, :, pos // 64 * 64:pos // 64 * 64 + 64].contiguous()
+    s2 = gh.alloc_step(dst, 1)
+    hga.hga_decode_step(dst.cfg, 2, q, dst.k_raw[:, :, pos].contiguous(),
+                        dst.v_raw[:, :, pos].contiguous(), dst.pos0, dst.k_pool, dst.v_pool, dst.T,
+                        stage, dst.chunk_sum, dst.group_sum, dst.max_chunks, s2.sel, s2.n_sel,
+                        dst.max_sel, s2.out, s2.lse, torch.zeros_like(dst.ws))
+    torch.cuda.synchronize()
+    assert torch.equal(s1.n_sel, s2.n_sel) and torch.equal(s1.out, s2.out)
