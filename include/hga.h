@@ -360,6 +360,47 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              int32_t max_sel, void* k_ws, void* v_ws, float* out, float* lse_opt,
                              void* ws, size_t ws_bytes, void* stream_a, void* stream_b);
 
+/* Workspace of hga_warm_gather (host only). */
+hga_status hga_warm_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_sel,
+                                    size_t* bytes);
+
+/* Warm tier of a pinned host pool (page section "Geheugenarchitectuur": a
+ * bounded LRU cache in device memory holds recently routed data between the
+ * hot windows and summaries and the cold host pool).  The cache holds 16-token
+ * groups, the unit that routing selects and attention reads: n_warm slots per
+ * (sequence, list).  For the routed part of each list written by hga_route
+ * (as hga_gather with HGA_PART_ROUTED selects it):
+ *   - a group found in the unit's cache is a hit: its stamp becomes `step`;
+ *   - each miss, in list order, takes the least recently used slot that is
+ *     not a hit this step (stamp order, ties by slot index, empty slots
+ *     first), is copied from the pinned host pool over PCIe into that slot,
+ *     and the slot's tag and stamp are rewritten;
+ *   - every routed list slot s of the working set receives its group (from
+ *     PCIe for a miss, from the cache for a hit), rows 16*s .. of
+ *     k_ws / v_ws [B][lists][max_sel*16][d] -- what hga_gather with
+ *     HGA_PART_ROUTED would write; window slots are not touched.
+ *   k_cold, v_cold  the pool in pinned host memory, as hga_gather
+ *   k_warm, v_warm  [B][lists][n_warm][16][d] qkv_dtype device memory: slot w
+ *                   holds a group's K rows and its V^T block (the pool's
+ *                   group layout)
+ *   warm_tags [B][lists][n_warm] int32, warm_used [B][lists][n_warm] int32:
+ *                   caller-owned state kept across calls; before the first
+ *                   call fill warm_tags with -1 and warm_used with 0
+ *   n_warm          topk_groups <= n_warm <= 1024 (else HGA_ERR_OUT_OF_RANGE)
+ *   step            > 0, larger on every call (the LRU stamp)
+ *   hits_opt [B][lists] int32 (nullable): routed groups found in the cache
+ *   ws              hga_warm_workspace_bytes() of workspace (the fill plan)
+ * Two launches on `stream`; the working set is then ready for hga_attend with
+ * HGA_PART_ROUTED and HGA_SRC_WORKING_SET.
+ * Errors: HGA_ERR_INVALID_ARGUMENT if the host pool is not pinned or step <= 0;
+ * HGA_ERR_UNSUPPORTED for max_sel > 256. */
+hga_status hga_warm_gather(const hga_config* cfg, int32_t B, const void* k_cold, const void* v_cold,
+                           int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
+                           int32_t max_sel, const int32_t* q_pos0, void* k_warm, void* v_warm,
+                           int32_t* warm_tags, int32_t* warm_used, int32_t n_warm, int32_t step,
+                           void* k_ws, void* v_ws, int32_t* hits_opt, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Exact merge of two attention results over disjoint token sets:
  * out = (e^{lse_a} out_a + e^{lse_b} out_b) / (e^{lse_a} + e^{lse_b}),
  * lse_out = log(e^{lse_a} + e^{lse_b}) (lse_out nullable).  Rows are

@@ -37,7 +37,8 @@ HGA_PROMPT_ALL = 7
 EXPORTED = ("hga_validate", "hga_max_selected", "hga_workspace_bytes", "hga_workspace_reset",
             "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_decode_step",
             "hga_prefill_step", "hga_prompt_workspace_bytes", "hga_prefill_prompt",
-            "hga_attend_tiered", "hga_merge_partials", "hga_status_string", "hga_version")
+            "hga_attend_tiered", "hga_warm_workspace_bytes", "hga_warm_gather",
+            "hga_merge_partials", "hga_status_string", "hga_version")
 
 
 class HgaError(RuntimeError):
@@ -113,6 +114,9 @@ def lib() -> ctypes.CDLL:
                                    _P, _I, _P, ctypes.c_size_t, _P],
             "hga_attend_tiered": [_C, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P,
                                   _P, _P, _P, ctypes.c_size_t, _P, _P],
+            "hga_warm_workspace_bytes": [_C, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
+            "hga_warm_gather": [_C, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
+                                _P, _P, _P, ctypes.c_size_t, _P],
             "hga_merge_partials": [_C, _I, _I, _P, _P, _P, _P, _P, _P, _P],
         }
         for name, args in sig.items():
@@ -274,6 +278,24 @@ def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, 
                                    _ptr(out), _ptr(lse_opt), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream_a), None if stream_b is None else _stream(stream_b)),
            "hga_attend_tiered")
+
+
+def hga_warm_workspace_bytes(cfg, B: int, max_sel: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().hga_warm_workspace_bytes(_cfg(cfg), B, max_sel, ctypes.byref(out)),
+           "hga_warm_workspace_bytes")
+    return out.value
+
+
+def hga_warm_gather(cfg, B, k_cold, v_cold, cold_cap, sel_groups, n_sel, max_sel, q_pos0, k_warm,
+                    v_warm, warm_tags, warm_used, n_warm, step, k_ws, v_ws, hits_opt, ws,
+                    stream=None):
+    _check(lib().hga_warm_gather(_cfg(cfg), B, _ptr(k_cold), _ptr(v_cold), cold_cap,
+                                 _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(q_pos0),
+                                 _ptr(k_warm), _ptr(v_warm), _ptr(warm_tags), _ptr(warm_used),
+                                 n_warm, step, _ptr(k_ws), _ptr(v_ws), _ptr(hits_opt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)),
+           "hga_warm_gather")
 
 
 def hga_merge_partials(cfg, B, lq, out_a, lse_a, out_b, lse_b, out, lse_out=None, stream=None):

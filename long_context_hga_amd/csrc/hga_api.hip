@@ -571,6 +571,41 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   return hip_status(e);
 }
 
+hga_status hga_warm_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_sel,
+                                    size_t* bytes) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (!bytes || B <= 0 || max_sel <= 0) return HGA_ERR_INVALID_ARGUMENT;
+  *bytes = round_up(warm_ws_bytes(make_kcfg(cfg), B, max_sel), 256);
+  return HGA_OK;
+}
+
+hga_status hga_warm_gather(const hga_config* cfg, int32_t B, const void* k_cold, const void* v_cold,
+                           int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
+                           int32_t max_sel, const int32_t* q_pos0, void* k_warm, void* v_warm,
+                           int32_t* warm_tags, int32_t* warm_used, int32_t n_warm, int32_t step,
+                           void* k_ws, void* v_ws, int32_t* hits_opt, void* ws, size_t ws_bytes,
+                           void* stream) {
+  hga_status s = check_cfg(cfg);
+  if (s != HGA_OK) return s;
+  if (B <= 0 || !k_cold || !v_cold || cold_cap <= 0 || cold_cap % kGroupTokens != 0 ||
+      !sel_groups || !n_sel || max_sel <= 0 || !q_pos0 || !k_warm || !v_warm || !warm_tags ||
+      !warm_used || !k_ws || !v_ws || !ws || step <= 0)
+    return HGA_ERR_INVALID_ARGUMENT;
+  if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
+  if (n_warm < cfg->topk_groups || n_warm < 1 || n_warm > 1024) return HGA_ERR_OUT_OF_RANGE;
+  if ((int64_t)B * lists_of(cfg) * max_sel > INT32_MAX) return HGA_ERR_UNSUPPORTED;
+  const KCfg k = make_kcfg(cfg);
+  if (ws_bytes < warm_ws_bytes(k, B, max_sel)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  const void* kc = nullptr;
+  const void* vc = nullptr;
+  if (!pinned_device_ptr(k_cold, &kc) || !pinned_device_ptr(v_cold, &vc))
+    return HGA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_warm(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0, k_warm,
+                                v_warm, warm_tags, warm_used, n_warm, step, k_ws, v_ws, hits_opt,
+                                static_cast<int*>(ws), static_cast<hipStream_t>(stream)));
+}
+
 hga_status hga_merge_partials(const hga_config* cfg, int32_t B, int32_t lq, const float* out_a,
                               const float* lse_a, const float* out_b, const float* lse_b,
                               float* out, float* lse_out, void* stream) {

@@ -95,6 +95,16 @@ hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStrea
 
 // from_host: the pool is pinned host memory read over PCIe (a small
 // persistent grid); otherwise one workgroup per copied group.
+// Warm tier: LRU update of the routed groups of every list over n_warm
+// cache slots per unit, then the fill of the working set (misses over PCIe
+// from the pinned pool, hits from the cache).  plan: workspace of
+// warm_ws_bytes.
+hipError_t launch_warm(const KCfg& cfg, int B, const void* k_cold, const void* v_cold, int cap,
+                       const int* sel, const int* n_sel, int max_sel, const int* q_pos0,
+                       void* k_warm, void* v_warm, int* tags, int* used, int n_warm, int step,
+                       void* k_ws, void* v_ws, int* hits, int* plan, hipStream_t st);
+size_t warm_ws_bytes(const KCfg& cfg, int B, int max_sel);
+
 hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
                          int pool_cap, const int* sel, const int* n_sel, int max_sel,
                          const int* q_pos0, int part, void* k_ws, void* v_ws, bool from_host,

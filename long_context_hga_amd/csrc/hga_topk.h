@@ -1,0 +1,273 @@
+// Exact top-k of fp64 scores on one wave or one 256-thread workgroup, in the
+// order (score descending, index ascending); shared by the routing (level-1
+// and level-2 selection) and the warm tier (least recently used slots).
+#pragma once
+
+#include "hga_internal.h"
+
+namespace hga {
+
+// Top-k by one wave, no barriers: the k best of s[0..n) (LDS, fp64; order
+// score descending, index ascending) are written ascending by index to out
+// (LDS); returns min(k, n).  hist (256 ints), bl and win (n ints each) are
+// LDS scratch.  A 256-bin histogram between the min and max score finds the
+// bin holding the k-th largest score; every score in a higher bin is kept,
+// and the boundary bin is resolved exactly by rank counting.  Counts use a
+// DPP scan and ballot / mbcnt.
+//   n <= 1024: scores stay in registers (element i in slot i / 64 of lane
+//   i % 64); longer lists stream from LDS in the same passes.
+struct TopkScratch {
+  int* hist;  // 256
+  int* bl;    // boundary members, by index
+  int* win;   // 1 if the boundary member at that list position is kept
+};
+
+__device__ __forceinline__ int topk_bin(double x, double mn, double scale) {
+  const double f = (x - mn) * scale;
+  const int b = f >= 0.0 ? (int)f : 0;  // monotone in x; NaN -> 0
+  return b > 255 ? 255 : b;
+}
+
+// Boundary bin and how many of its members are kept, from the histogram.
+__device__ __forceinline__ void topk_cut(const int* hist, int k, int* bs, int* need) {
+  const int lane = threadIdx.x & 63;
+  const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+            h3 = hist[4 * lane + 3];
+  const int local = h0 + h1 + h2 + h3;
+  const int pre = wave_incl_scan(local);
+  const int total = __builtin_amdgcn_readlane(pre, 63);
+  const int suf = total - pre + local;  // scores in bins >= 4*lane
+  const int above = suf - local;
+  int bs_l, ab_l;
+  const int c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1;
+  if (c3 >= k) { bs_l = 4 * lane + 3; ab_l = above; }
+  else if (c2 >= k) { bs_l = 4 * lane + 2; ab_l = c3; }
+  else if (c1 >= k) { bs_l = 4 * lane + 1; ab_l = c2; }
+  else { bs_l = 4 * lane; ab_l = c1; }
+  const int src = __ffsll((long long)__ballot(above < k && k <= suf)) - 1;
+  *bs = __builtin_amdgcn_readlane(bs_l, src);
+  *need = k - __builtin_amdgcn_readlane(ab_l, src);
+}
+
+// Ranks the nb boundary members; win[t] = 1 for the `need` best.
+__device__ __forceinline__ void topk_rank(const double* s, int nb, int need, const int* bl, int* win) {
+  const int lane = threadIdx.x & 63;
+  for (int t = lane; t < nb; t += 64) {
+    const int i = bl[t];
+    const double si = s[i];
+    int r = 0;
+    for (int u = 0; u < nb; ++u) {
+      const int jx = bl[u];
+      const double sj = s[jx];
+      r += (sj > si) || (sj == si && jx < i);
+    }
+    win[t] = r < need;
+  }
+}
+
+__device__ int wave_topk(const double* s, int n, int k, int* out, const TopkScratch& sc) {
+  constexpr int SL = 16;
+  const int lane = threadIdx.x & 63;
+  if (k <= 0) return 0;
+  if (k >= n) {
+    for (int i = lane; i < n; i += 64) out[i] = i;
+    return n;
+  }
+  for (int j = 0; j < 4; ++j) sc.hist[4 * lane + j] = 0;
+  int cnt = 0;
+  if (n <= 64 * SL) {
+    double x[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const int i = 64 * j + lane;
+      x[j] = s[i < n ? i : n - 1];
+    }
+    double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const bool v = 64 * j + lane < n;
+      mn = fmin(mn, v ? x[j] : INFINITY);
+      mx = fmax(mx, v ? x[j] : -INFINITY);
+    }
+    mn = wave_ext_d<false>(mn);
+    mx = wave_ext_d<true>(mx);
+    const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+    int bins[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) bins[j] = 64 * j + lane < n ? topk_bin(x[j], mn, scale) : -1;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < SL; ++j)
+      if (bins[j] >= 0) atomicAdd(&sc.hist[bins[j]], 1);
+    __builtin_amdgcn_wave_barrier();
+    int bs, need;
+    topk_cut(sc.hist, k, &bs, &need);
+    int nb = 0, bpos[SL];
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const unsigned long long m = __ballot(bins[j] == bs);
+      bpos[j] = nb + lanes_below(m);
+      if (bins[j] == bs) sc.bl[bpos[j]] = 64 * j + lane;
+      nb += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    topk_rank(s, nb, need, sc.bl, sc.win);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < SL; ++j) {
+      const bool keep = bins[j] > bs || (bins[j] == bs && sc.win[bpos[j]]);
+      const unsigned long long m = __ballot(keep);
+      if (keep) out[cnt + lanes_below(m)] = 64 * j + lane;
+      cnt += __popcll(m);
+    }
+  } else {
+    double mn = INFINITY, mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) {
+      mn = fmin(mn, s[i]);
+      mx = fmax(mx, s[i]);
+    }
+    mn = wave_ext_d<false>(mn);
+    mx = wave_ext_d<true>(mx);
+    const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < n; i += 64) atomicAdd(&sc.hist[topk_bin(s[i], mn, scale)], 1);
+    __builtin_amdgcn_wave_barrier();
+    int bs, need;
+    topk_cut(sc.hist, k, &bs, &need);
+    int nb = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const bool e = i < n && topk_bin(s[i], mn, scale) == bs;
+      const unsigned long long m = __ballot(e);
+      if (e) sc.bl[nb + lanes_below(m)] = i;
+      nb += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    topk_rank(s, nb, need, sc.bl, sc.win);
+    __builtin_amdgcn_wave_barrier();
+    int seen = 0;  // boundary members met so far, in index order
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int bi = i < n ? topk_bin(s[i], mn, scale) : -1;
+      const unsigned long long mb = __ballot(bi == bs);
+      const bool keep = bi > bs || (bi == bs && sc.win[seen + lanes_below(mb)]);
+      seen += __popcll(mb);
+      const unsigned long long m = __ballot(keep);
+      if (keep) out[cnt + lanes_below(m)] = i;
+      cnt += __popcll(m);
+    }
+  }
+  return cnt;
+}
+
+// Top-k by a whole 256-thread workgroup (n <= 1024, all threads call it with
+// the same arguments): the k best of s[0..n) (LDS, fp64; order score
+// descending, index ascending) are written ascending by index to out (LDS);
+// returns min(k, n) in every thread.  Thread t owns elements 4t..4t+3, so
+// the kept indices come out in order from one exclusive scan of per-thread
+// counts.  Same histogram / cut / boundary-rank steps as wave_topk, with a
+// quarter of the elements per lane.  Scratch: hist (256 ints), bl (n ints),
+// red (8 doubles), ints (8 ints).
+//
+// Every barrier is a round of LDS latency for the whole workgroup, so the
+// range of the scores is not reduced here: the threads that write s call
+// topk_publish before the barrier that publishes s, which also clears the
+// histogram.  The boundary bin is then found by every wave from the same
+// histogram, with no barrier between the count and the cut.
+struct BlockTopkScratch {
+  int* hist;
+  int* bl;
+  double* red;
+  int* ints;
+};
+
+// Called by all 256 threads before the barrier that publishes the scores:
+// mn / mx are the min and max of the scores this thread wrote (+inf / -inf if
+// none).
+__device__ __forceinline__ void topk_publish(double mn, double mx, const BlockTopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  mn = wave_ext_d<false>(mn);
+  mx = wave_ext_d<true>(mx);
+  if (lane == 0) {
+    sc.red[wave] = mn;
+    sc.red[4 + wave] = mx;
+  }
+  sc.hist[tid] = 0;
+  if (tid == 0) sc.ints[2] = 0;  // boundary members collected
+}
+
+__device__ int block_topk(const double* s, int n, int k, int* out, const BlockTopkScratch& sc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (k <= 0) return 0;
+  if (k >= n) {
+    for (int i = tid; i < n; i += 256) out[i] = i;
+    __syncthreads();
+    return n;
+  }
+  double x[4];
+  bool v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * tid + e;
+    v[e] = i < n;
+    x[e] = s[v[e] ? i : n - 1];
+  }
+  const double mn = fmin(fmin(sc.red[0], sc.red[1]), fmin(sc.red[2], sc.red[3]));
+  const double mx = fmax(fmax(sc.red[4], sc.red[5]), fmax(sc.red[6], sc.red[7]));
+  const double scale = mx > mn ? 256.0 / (mx - mn) : 0.0;
+  int bin[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bin[e] = v[e] ? topk_bin(x[e], mn, scale) : -1;
+    if (bin[e] >= 0) atomicAdd(&sc.hist[bin[e]], 1);
+  }
+  __syncthreads();
+  int bs, need;
+  topk_cut(sc.hist, k, &bs, &need);  // the same result in every wave
+  const int nb = sc.hist[bs];
+  int keep = 0;  // bit e: element 4t+e kept
+#pragma unroll
+  for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs ? 1 : 0) << e;
+  if (nb == need) {  // the whole boundary bin is kept
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (bin[e] == bs ? 1 : 0) << e;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (bin[e] == bs) sc.bl[atomicAdd(&sc.ints[2], 1)] = 4 * tid + e;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (bin[e] == bs) {
+        const int i = 4 * tid + e;
+        int r = 0;
+        for (int u = 0; u < nb; u += 4) {  // 4 members per round of LDS reads
+          int j[4];
+          double sj[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) j[q] = sc.bl[u + q < nb ? u + q : nb - 1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sj[q] = s[j[q]];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            r += (u + q < nb) && ((sj[q] > x[e]) || (sj[q] == x[e] && j[q] < i));
+        }
+        keep |= (r < need ? 1 : 0) << e;
+      }
+    }
+  }
+  // kept indices in ascending order: exclusive scan of per-thread counts
+  const int cnt = __popc(keep);
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) sc.ints[4 + wave] = incl;
+  __syncthreads();
+  int off = incl - cnt;
+  for (int w = 0; w < wave; ++w) off += sc.ints[4 + w];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (keep & (1 << e)) out[off++] = 4 * tid + e;
+  __syncthreads();
+  return k;
+}
+
+}  // namespace hga

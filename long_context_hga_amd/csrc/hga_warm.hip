@@ -1,0 +1,220 @@
+// Warm tier of a host-memory pool: a bounded LRU cache in device memory of
+// recently routed groups.
+//
+// HGA technical summary (gist.science), "Geheugenarchitectuur": summaries and
+// the always-visible windows are hot in accelerator memory, a bounded LRU
+// cache in accelerator memory holds recently routed chunks (warm), and the
+// full token K/V history stays in host RAM (cold).  The cache holds the unit
+// the routing delivers and the attention reads, the 16-token group, so a miss
+// moves only the selected group across PCIe.
+//
+// Per (sequence, list) unit the cache has n_warm slots, each one group of K
+// (4 KiB at d = 128, bf16) and its V^T block, with a tag (group id, -1 =
+// empty) and the step that last used it.  One call:
+//   warm_update_kernel (one workgroup per unit): the routed groups of the
+//     unit's list that are cached are hits (their stamps renewed); each miss
+//     takes the least recently used slot that is not a hit this step (ties
+//     by slot index, empty slots first), in list order; tags and stamps are
+//     rewritten and the fill plan (slot and source of every routed list
+//     position) goes to the workspace;
+//   warm_fill_kernel (persistent grid): a miss copies its group from the
+//     pinned host pool over PCIe into its cache slot and into the working
+//     set, a hit copies its cache slot into the working set.
+// The working set then holds the routed part of every list, as hga_gather
+// with HGA_PART_ROUTED would leave it.
+#include "hga_topk.h"
+
+namespace hga {
+
+struct WarmArgs {
+  const int* sel;      // [units][max_sel]
+  const int* n_sel;    // [units]
+  const int* q_pos0;   // [B]
+  const uint4* k_cold;  // pinned host pool (device mapping), [units_kv][cap][row]
+  const uint4* v_cold;
+  uint4* k_warm;        // [units][W][16 rows]
+  uint4* v_warm;
+  uint4* k_ws;          // [units][max_sel * 16 rows]
+  uint4* v_ws;
+  int* tags;           // [units][W]
+  int* used;           // [units][W]
+  int* hits;           // [units] or null
+  int* slot_of;        // workspace [units][max_sel]: cache slot of a routed list position, else -1
+  int* src_of;         // workspace [units][max_sel]: group to fetch (miss), -1 for a hit
+  int lists, hkv, kvdiv, n_sink, n_local, cap, max_sel, W, step, row_vecs;
+};
+
+constexpr int kMaxWarm = 1024;  // slots per unit (the workgroup top-k bound)
+
+__global__ __launch_bounds__(256) void warm_update_kernel(WarmArgs a) {
+  __shared__ int s_tag[kMaxWarm];
+  __shared__ int s_used[kMaxWarm];
+  __shared__ int s_hit[kMaxWarm];      // 1 if the slot is a hit this step
+  __shared__ double s_score[kMaxWarm];  // victim preference
+  __shared__ int s_bl[kMaxWarm];        // top-k scratch: boundary members
+  __shared__ int s_victim[kMaxWarm];    // chosen slots, ascending
+  __shared__ int hist[256];
+  __shared__ double red[8];
+  __shared__ int ints[8];
+  __shared__ int wave_miss[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int unit = blockIdx.x;
+  const int b = unit / a.lists;
+  const int W = a.W;
+  int* slot_of = a.slot_of + (size_t)unit * a.max_sel;
+  int* src_of = a.src_of + (size_t)unit * a.max_sel;
+  for (int i = tid; i < a.max_sel; i += 256) {
+    slot_of[i] = -1;
+    src_of[i] = -1;
+  }
+  const int n_sel = a.n_sel[unit];
+  const int* sel = a.sel + (size_t)unit * a.max_sel;
+  if (n_sel <= 0 || n_sel > a.max_sel) {  // no usable list: nothing routed
+    if (a.hits && tid == 0) a.hits[unit] = 0;
+    return;
+  }
+  const int pos0 = a.q_pos0[b];
+  const ListParts lp = list_parts(n_sel, sel[n_sel - 1] * kGroupTokens, pos0, a.n_sink, a.n_local);
+  const int n_routed = lp.n_routed < 0 ? 0 : lp.n_routed;
+  for (int s = tid; s < W; s += 256) {
+    s_tag[s] = a.tags[(size_t)unit * W + s];
+    s_used[s] = a.used[(size_t)unit * W + s];
+    s_hit[s] = 0;
+  }
+  __syncthreads();
+  // hits: routed list position n_head + i (thread i) scans the tags
+  int my_gid = -1, my_slot = -1;
+  // (a group id outside the pool is not routed data: it is neither cached nor
+  // fetched, and its working-set slot is left as it was)
+  bool routed = false;
+  if (tid < n_routed) {
+    my_gid = sel[lp.n_head + tid];
+    routed = my_gid >= 0 && (size_t)(my_gid + 1) * kGroupTokens <= (size_t)a.cap;
+    if (routed) {
+      for (int s = 0; s < W; ++s)
+        if (s_tag[s] == my_gid) my_slot = s;
+      if (my_slot >= 0) s_hit[my_slot] = 1;
+    }
+  }
+  const bool miss = routed && my_slot < 0;
+  // misses in list order: exclusive scan of the miss flags
+  const int incl = wave_incl_scan(miss ? 1 : 0);
+  if (lane == 63) wave_miss[wave] = incl;
+  __syncthreads();
+  int m = 0, before = 0;
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wave_miss[w] : 0;
+    m += wave_miss[w];
+  }
+  const int my_rank = before + incl - (miss ? 1 : 0);
+  // victim preference: least recently used first (empty slots carry stamp
+  // 0; every stamp is below this call's step), hits last (never needed: the
+  // misses fit in the other slots); thread t writes slots t, t + 256, ...
+  const BlockTopkScratch sc{hist, s_bl, red, ints};
+  double mn = INFINITY, mx = -INFINITY;
+  for (int s = tid; s < W; s += 256) {
+    const double v = s_hit[s] ? -(double)a.step - 1.0 : -(double)s_used[s];
+    s_score[s] = v;
+    mn = fmin(mn, v);
+    mx = fmax(mx, v);
+  }
+  topk_publish(mn, mx, sc);
+  __syncthreads();
+  block_topk(s_score, W, m, s_victim, sc);  // ends with a barrier
+  if (miss) {
+    const int slot = s_victim[my_rank];
+    s_tag[slot] = my_gid;
+    s_used[slot] = a.step;
+    slot_of[lp.n_head + tid] = slot;
+    src_of[lp.n_head + tid] = my_gid;
+  } else if (routed) {
+    s_used[my_slot] = a.step;
+    slot_of[lp.n_head + tid] = my_slot;
+  }
+  __syncthreads();
+  for (int s = tid; s < W; s += 256) {
+    a.tags[(size_t)unit * W + s] = s_tag[s];
+    a.used[(size_t)unit * W + s] = s_used[s];
+  }
+  if (a.hits) {  // routed groups found in the cache
+    const int h = wave_incl_scan(routed && !miss ? 1 : 0);
+    if (lane == 63) wave_miss[wave] = h;  // every wave read wave_miss before the top-k barriers
+    __syncthreads();
+    if (tid == 0) a.hits[unit] = wave_miss[0] + wave_miss[1] + wave_miss[2] + wave_miss[3];
+  }
+}
+
+// Persistent grid: item = (list position, unit).
+__global__ __launch_bounds__(256) void warm_fill_kernel(WarmArgs a, int n_items) {
+  const int n = kGroupTokens * a.row_vecs;  // uint4 per group and tensor
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int p = item % a.max_sel, unit = item / a.max_sel;
+    const int slot = a.slot_of[(size_t)unit * a.max_sel + p];
+    if (slot < 0) continue;  // uniform over the workgroup
+    const int src = a.src_of[(size_t)unit * a.max_sel + p];
+    const size_t wdst = ((size_t)unit * a.W + slot) * n;
+    const size_t dst = ((size_t)unit * a.max_sel + p) * n;
+    if (src >= 0) {  // miss: host pool -> cache slot and working set
+      const int unit_p = (unit / a.lists) * a.hkv + (unit % a.lists) / a.kvdiv;
+      const size_t from = ((size_t)unit_p * a.cap + (size_t)src * kGroupTokens) * a.row_vecs;
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 kv = a.k_cold[from + i];
+        const uint4 vv = a.v_cold[from + i];
+        a.k_warm[wdst + i] = kv;
+        a.v_warm[wdst + i] = vv;
+        a.k_ws[dst + i] = kv;
+        a.v_ws[dst + i] = vv;
+      }
+    } else {  // hit: cache slot -> working set
+      for (int i = threadIdx.x; i < n; i += 256) {
+        const uint4 kv = a.k_warm[wdst + i];
+        const uint4 vv = a.v_warm[wdst + i];
+        a.k_ws[dst + i] = kv;
+        a.v_ws[dst + i] = vv;
+      }
+    }
+  }
+}
+
+hipError_t launch_warm(const KCfg& cfg, int B, const void* k_cold, const void* v_cold, int cap,
+                       const int* sel, const int* n_sel, int max_sel, const int* q_pos0,
+                       void* k_warm, void* v_warm, int* tags, int* used, int n_warm, int step,
+                       void* k_ws, void* v_ws, int* hits, int* plan, hipStream_t st) {
+  WarmArgs a;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.q_pos0 = q_pos0;
+  a.k_cold = static_cast<const uint4*>(k_cold);
+  a.v_cold = static_cast<const uint4*>(v_cold);
+  a.k_warm = static_cast<uint4*>(k_warm);
+  a.v_warm = static_cast<uint4*>(v_warm);
+  a.k_ws = static_cast<uint4*>(k_ws);
+  a.v_ws = static_cast<uint4*>(v_ws);
+  a.tags = tags;
+  a.used = used;
+  a.hits = hits;
+  const int units = B * cfg.lists;
+  a.slot_of = plan;
+  a.src_of = plan + (size_t)units * max_sel;
+  a.lists = cfg.lists;
+  a.hkv = cfg.hkv;
+  a.kvdiv = cfg.kvdiv;
+  a.n_sink = cfg.n_sink;
+  a.n_local = cfg.n_local;
+  a.cap = cap;
+  a.max_sel = max_sel;
+  a.W = n_warm;
+  a.step = step;
+  a.row_vecs = cfg.d * (cfg.dtype == HGA_BF16 ? 2 : 4) / 16;
+  hipLaunchKernelGGL(warm_update_kernel, dim3(units), dim3(256), 0, st, a);
+  const int n_items = units * max_sel;
+  const int n_wg = n_items < 256 ? n_items : 256;
+  hipLaunchKernelGGL(warm_fill_kernel, dim3(n_wg), dim3(256), 0, st, a, n_items);
+  return hipGetLastError();
+}
+
+size_t warm_ws_bytes(const KCfg& cfg, int B, int max_sel) {
+  return (size_t)2 * B * cfg.lists * max_sel * sizeof(int);
+}
+
+}  // namespace hga

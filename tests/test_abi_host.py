@@ -200,6 +200,28 @@ def test_prefill_prompt_rejects():
         assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
 
 
+def test_warm_gather_rejects():
+    c = ctypes.byref(cfg())
+    f = hga.lib().hga_warm_gather
+    # cfg, B, k_cold, v_cold, cap, sel, n_sel, max_sel, pos, k_warm, v_warm, tags, used, n_warm,
+    # step, k_ws, v_ws, hits, ws, ws_bytes, stream
+    args = [c, 4, FAKE, FAKE, 65536, FAKE, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 256, 1, FAKE,
+            FAKE, None, FAKE, 1 << 30, None]
+    a = list(args); a[13] = 50  # fewer slots than topk_groups
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    a = list(args); a[13] = 2048
+    assert f(*a) == hga.HGA_ERR_OUT_OF_RANGE
+    a = list(args); a[14] = 0  # the step stamp must be positive
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[11] = None
+    assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
+    a = list(args); a[19] = 16
+    assert f(*a) == hga.HGA_ERR_WORKSPACE_TOO_SMALL
+    # valid sizes reach the pinned-pool check: FAKE is not pinned host memory
+    assert f(*args) == hga.HGA_ERR_INVALID_ARGUMENT
+    assert hga.hga_warm_workspace_bytes(cfg(), 4, 128) >= 2 * 4 * 4 * 128 * 4
+
+
 def test_gather_and_merge_reject():
     c = ctypes.byref(cfg())
     g = hga.lib().hga_gather
