@@ -371,10 +371,10 @@ hga_status hga_warm_workspace_bytes(const hga_config* cfg, int32_t B, int32_t ma
  * (sequence, list).  For the routed part of each list written by hga_route
  * (as hga_gather with HGA_PART_ROUTED selects it):
  *   - a group found in the unit's cache is a hit: its stamp becomes `step`;
- *   - each miss, in list order, takes the least recently used slot that is
- *     not a hit this step (stamp order, ties by slot index, empty slots
- *     first), is copied from the pinned host pool over PCIe into that slot,
- *     and the slot's tag and stamp are rewritten;
+ *   - the i-th miss in list order takes the i-th least recently used slot
+ *     that is not a hit this step (stamp order, ties by slot index, empty
+ *     slots first), is copied from the pinned host pool over PCIe into that
+ *     slot, and the slot's tag and stamp are rewritten;
  *   - every routed list slot s of the working set receives its group (from
  *     PCIe for a miss, from the cache for a hit), rows 16*s .. of
  *     k_ws / v_ws [B][lists][max_sel*16][d] -- what hga_gather with

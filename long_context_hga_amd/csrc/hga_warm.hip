@@ -11,18 +11,19 @@
 // Per (sequence, list) unit the cache has n_warm slots, each one group of K
 // (4 KiB at d = 128, bf16) and its V^T block, with a tag (group id, -1 =
 // empty) and the step that last used it.  One call:
-//   warm_update_kernel (one workgroup per unit): the routed groups of the
-//     unit's list that are cached are hits (their stamps renewed); each miss
-//     takes the least recently used slot that is not a hit this step (ties
-//     by slot index, empty slots first), in list order; tags and stamps are
-//     rewritten and the fill plan (slot and source of every routed list
-//     position) goes to the workspace;
+//   warm_update_kernel (one workgroup per unit): the tags go into an LDS
+//     hash table; the routed groups of the unit's list found there are hits
+//     (their stamps renewed); the i-th miss in list order takes the i-th
+//     least recently used slot that is not a hit this step (stamp order,
+//     ties by slot index, empty slots first); tags and stamps are rewritten
+//     and the fill plan (slot and source of every routed list position) goes
+//     to the workspace;
 //   warm_fill_kernel (persistent grid): a miss copies its group from the
 //     pinned host pool over PCIe into its cache slot and into the working
 //     set, a hit copies its cache slot into the working set.
 // The working set then holds the routed part of every list, as hga_gather
 // with HGA_PART_ROUTED would leave it.
-#include "hga_topk.h"
+#include "hga_internal.h"
 
 namespace hga {
 
@@ -44,42 +45,59 @@ struct WarmArgs {
   int lists, hkv, kvdiv, n_sink, n_local, cap, max_sel, W, step, row_vecs;
 };
 
-constexpr int kMaxWarm = 1024;  // slots per unit (the workgroup top-k bound)
+constexpr int kMaxWarm = 1024;  // slots per unit
+constexpr int kWarmHash = 2048; // open-addressing table of the tags (>= 2 * kMaxWarm)
+
+__device__ __forceinline__ int warm_hash(int gid) {
+  return (int)(((uint32_t)gid * 2654435761u) >> 21);  // 11 bits
+}
 
 __global__ __launch_bounds__(256) void warm_update_kernel(WarmArgs a) {
   __shared__ int s_tag[kMaxWarm];
   __shared__ int s_used[kMaxWarm];
   __shared__ int s_hit[kMaxWarm];      // 1 if the slot is a hit this step
-  __shared__ double s_score[kMaxWarm];  // victim preference
-  __shared__ int s_bl[kMaxWarm];        // top-k scratch: boundary members
-  __shared__ int s_victim[kMaxWarm];    // chosen slots, ascending
-  __shared__ int hist[256];
-  __shared__ double red[8];
-  __shared__ int ints[8];
+  __shared__ int s_victim[kMaxWarm];    // s_victim[r]: the r-th least recently used free slot
+  __shared__ __align__(16) int s_key[kMaxWarm];  // victim order key of a slot
   __shared__ int wave_miss[4];
+  __shared__ int s_hkey[kWarmHash];    // tag hash: group id (-1 = empty)
+  __shared__ int s_hval[kWarmHash];    // its slot
+  __shared__ int s_sel[256];            // the unit's list (max_sel <= 256)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = blockIdx.x;
   const int b = unit / a.lists;
   const int W = a.W;
   int* slot_of = a.slot_of + (size_t)unit * a.max_sel;
   int* src_of = a.src_of + (size_t)unit * a.max_sel;
-  for (int i = tid; i < a.max_sel; i += 256) {
-    slot_of[i] = -1;
-    src_of[i] = -1;
-  }
-  const int n_sel = a.n_sel[unit];
+  // every load the unit needs goes out at once: its list, count and position,
+  // the tags and the stamps
   const int* sel = a.sel + (size_t)unit * a.max_sel;
-  if (n_sel <= 0 || n_sel > a.max_sel) {  // no usable list: nothing routed
-    if (a.hits && tid == 0) a.hits[unit] = 0;
-    return;
-  }
+  const int n_sel = a.n_sel[unit];
   const int pos0 = a.q_pos0[b];
-  const ListParts lp = list_parts(n_sel, sel[n_sel - 1] * kGroupTokens, pos0, a.n_sink, a.n_local);
-  const int n_routed = lp.n_routed < 0 ? 0 : lp.n_routed;
+  if (tid < a.max_sel) s_sel[tid] = sel[tid];
   for (int s = tid; s < W; s += 256) {
     s_tag[s] = a.tags[(size_t)unit * W + s];
     s_used[s] = a.used[(size_t)unit * W + s];
     s_hit[s] = 0;
+  }
+  for (int h = tid; h < kWarmHash; h += 256) s_hkey[h] = -1;
+  for (int i = tid; i < a.max_sel; i += 256) {
+    slot_of[i] = -1;
+    src_of[i] = -1;
+  }
+  if (n_sel <= 0 || n_sel > a.max_sel) {  // no usable list: nothing routed (uniform)
+    if (a.hits && tid == 0) a.hits[unit] = 0;
+    return;
+  }
+  __syncthreads();
+  const ListParts lp = list_parts(n_sel, s_sel[n_sel - 1] * kGroupTokens, pos0, a.n_sink, a.n_local);
+  const int n_routed = lp.n_routed < 0 ? 0 : lp.n_routed;
+  // the cached tags into the hash table (tags are distinct; linear probing)
+  for (int s = tid; s < W; s += 256) {
+    const int t = s_tag[s];
+    if (t < 0) continue;
+    int h = warm_hash(t);
+    while (atomicCAS(&s_hkey[h], -1, t) != -1) h = (h + 1) & (kWarmHash - 1);
+    s_hval[h] = s;
   }
   __syncthreads();
   // hits: routed list position n_head + i (thread i) scans the tags
@@ -88,11 +106,14 @@ __global__ __launch_bounds__(256) void warm_update_kernel(WarmArgs a) {
   // fetched, and its working-set slot is left as it was)
   bool routed = false;
   if (tid < n_routed) {
-    my_gid = sel[lp.n_head + tid];
+    my_gid = s_sel[lp.n_head + tid];
     routed = my_gid >= 0 && (size_t)(my_gid + 1) * kGroupTokens <= (size_t)a.cap;
     if (routed) {
-      for (int s = 0; s < W; ++s)
-        if (s_tag[s] == my_gid) my_slot = s;
+      for (int h = warm_hash(my_gid); s_hkey[h] != -1; h = (h + 1) & (kWarmHash - 1))
+        if (s_hkey[h] == my_gid) {
+          my_slot = s_hval[h];
+          break;
+        }
       if (my_slot >= 0) s_hit[my_slot] = 1;
     }
   }
@@ -107,20 +128,31 @@ __global__ __launch_bounds__(256) void warm_update_kernel(WarmArgs a) {
     m += wave_miss[w];
   }
   const int my_rank = before + incl - (miss ? 1 : 0);
-  // victim preference: least recently used first (empty slots carry stamp
-  // 0; every stamp is below this call's step), hits last (never needed: the
-  // misses fit in the other slots); thread t writes slots t, t + 256, ...
-  const BlockTopkScratch sc{hist, s_bl, red, ints};
-  double mn = INFINITY, mx = -INFINITY;
-  for (int s = tid; s < W; s += 256) {
-    const double v = s_hit[s] ? -(double)a.step - 1.0 : -(double)s_used[s];
-    s_score[s] = v;
-    mn = fmin(mn, v);
-    mx = fmax(mx, v);
-  }
-  topk_publish(mn, mx, sc);
+  // victims: the non-hit slots ranked by (stamp, slot index) -- empty slots
+  // carry stamp 0 and every stamp is below this call's step -- and the m
+  // first taken.  A slot's rank is the count of slots before it in that
+  // order; hits carry the key INT_MAX and are never counted.  The keys are
+  // read 16 bytes at a time by every thread at once (LDS broadcasts).
+  const int W4 = (W + 3) / 4;
+  for (int s = tid; s < 4 * W4; s += 256) s_key[s] = (s >= W || s_hit[s]) ? 0x7FFFFFFF : s_used[s];
   __syncthreads();
-  block_topk(s_score, W, m, s_victim, sc);  // ends with a barrier
+  const int4* key4 = reinterpret_cast<const int4*>(s_key);
+  for (int s = tid; s < W; s += 256) {
+    const int key = s_key[s];
+    if (key == 0x7FFFFFFF) continue;
+    int r = 0;
+#pragma unroll 8
+    for (int t4 = 0; t4 < W4; ++t4) {
+      const int4 v = key4[t4];
+      const int t = 4 * t4;
+      r += (v.x < key || (v.x == key && t < s)) ? 1 : 0;
+      r += (v.y < key || (v.y == key && t + 1 < s)) ? 1 : 0;
+      r += (v.z < key || (v.z == key && t + 2 < s)) ? 1 : 0;
+      r += (v.w < key || (v.w == key && t + 3 < s)) ? 1 : 0;
+    }
+    if (r < m) s_victim[r] = s;
+  }
+  __syncthreads();
   if (miss) {
     const int slot = s_victim[my_rank];
     s_tag[slot] = my_gid;

@@ -4,9 +4,9 @@ device memory of recently routed groups in front of the pinned host pool.
 Over a sequence of decode steps whose queries drift, every step's working set
 must hold exactly the groups hga_gather (HGA_PART_ROUTED) copies from the host
 pool, and the cache state (tags, stamps) and hit counts must equal a host
-simulation of the LRU policy: hits renew their stamp; misses, in list order,
-take the least recently used non-hit slots (stamp order, ties by slot index,
-empty slots first), assigned in ascending slot order."""
+simulation of the LRU policy: hits renew their stamp; the i-th miss in list
+order takes the i-th least recently used non-hit slot (stamp order, ties by
+slot index, empty slots first)."""
 import numpy as np
 import pytest
 
@@ -40,7 +40,7 @@ def lru_step(tags, used, routed, step):
         used[s] = step
     order = sorted((s for s in range(len(tags)) if s not in hit_slots),
                    key=lambda s: (used[s], s))
-    victims = sorted(order[:len(misses)])
+    victims = order[:len(misses)]
     for g, s in zip(misses, victims):
         tags[s] = g
         used[s] = step
