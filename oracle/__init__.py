@@ -79,6 +79,14 @@ def lib():
         L.ora_round_bf16.restype = ctypes.c_double
         L.ora_round_bf16_vec.argtypes = [_dp, ctypes.c_long, _dp]
         L.ora_pool.argtypes = [c, _dp, ctypes.c_long, ctypes.c_long, _dp]
+        L.ora_fp8_scale.argtypes = [ctypes.c_double]
+        L.ora_fp8_scale.restype = ctypes.c_double
+        L.ora_fp8_encode.argtypes = [ctypes.c_double]
+        L.ora_fp8_encode.restype = ctypes.c_int
+        L.ora_fp8_decode.argtypes = [ctypes.c_int]
+        L.ora_fp8_decode.restype = ctypes.c_double
+        L.ora_fp8_rows.argtypes = [_dp, ctypes.c_long, ctypes.c_int, _ip, _dp, _dp]
+        L.ora_pool_fp8.argtypes = [c, _dp, ctypes.c_long, ctypes.c_long, _ip, _dp, _dp]
         L.ora_windows.argtypes = [c, ctypes.c_long, _lp, _lp, _lp]
         L.ora_windows.restype = ctypes.c_int
         L.ora_pooled_query.argtypes = [c, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_long, _dp]
@@ -172,6 +180,43 @@ def pool(cfg, kraw, pos0=0):
     out = np.empty_like(kraw)
     lib().ora_pool(ctypes.byref(cfg), kp, int(pos0), kraw.shape[0], out.ctypes.data_as(_dp))
     return out
+
+
+def fp8_scale(amax):
+    return lib().ora_fp8_scale(float(amax))
+
+
+def fp8_encode(y):
+    return lib().ora_fp8_encode(float(y))
+
+
+def fp8_decode(code):
+    return lib().ora_fp8_decode(int(code))
+
+
+def fp8_rows(x):
+    """Rows x [n][d] -> (codes int32 [n][d], scales [n], dequantised [n][d])."""
+    x, xp = _d(x)
+    n, d = x.shape
+    codes = np.zeros((n, d), dtype=np.int32)
+    scales = np.zeros(n)
+    deq = np.zeros((n, d))
+    lib().ora_fp8_rows(xp, n, d, codes.ctypes.data_as(_ip), scales.ctypes.data_as(_dp),
+                       deq.ctypes.data_as(_dp))
+    return codes, scales, deq
+
+
+def pool_fp8(cfg, kraw, pos0=0):
+    """FP8 pool keys for raw keys kraw [n][d] at positions pos0..: (codes,
+    scales, dequantised rows)."""
+    kraw, kp = _d(kraw)
+    n, d = kraw.shape
+    codes = np.zeros((n, d), dtype=np.int32)
+    scales = np.zeros(n)
+    deq = np.zeros((n, d))
+    lib().ora_pool_fp8(ctypes.byref(cfg), kp, int(pos0), n, codes.ctypes.data_as(_ip),
+                       scales.ctypes.data_as(_dp), deq.ctypes.data_as(_dp))
+    return codes, scales, deq
 
 
 def windows(cfg, ct):

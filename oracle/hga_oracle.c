@@ -226,6 +226,78 @@ static double dot(const double* x, const double* y, int d) {
 /* Pooled routing query of one KV head: mean over its hg query heads and lq
  * query tokens (positions pos0..pos0+lq-1) of RoPE(q, position).
  * q is [hg][lq][d], raw (pre-RoPE). */
+/* ------------------------------------------------------ fp8 pool
+ * The FP8 pool variant stores each (token, KV head) row of the rotated keys,
+ * and of the values, as OCP E4M3FN codes times one power-of-two scale.
+ * E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; normal values
+ * (1 + m/8) 2^(e-7) for e = 1..15 (except e = 15, m = 7: NaN), subnormal
+ * values m 2^-9; the largest finite value is 448.
+ * Scale of a row: the smallest power of two s with max|x| <= 448 s (1 for a
+ * zero row); codes: x / s (exact) rounded to nearest even E4M3FN. */
+double ora_fp8_scale(double amax) {
+  if (!(amax > 0.0)) return 1.0;
+  int E;
+  double f = 2.0 * frexp(amax, &E);  /* amax = f 2^(E-1), f in [1, 2) */
+  E -= 1;
+  /* amax <= 1.75 2^(8+k) <=> f 2^(E-8-k) <= 1.75 */
+  int k = f <= 1.75 ? E - 8 : E - 7;
+  return ldexp(1.0, k);
+}
+
+/* |y| <= 448 -> E4M3FN code, rounding to nearest even. */
+int ora_fp8_encode(double y) {
+  int sign = y < 0.0 ? 0x80 : 0;
+  double a = fabs(y);
+  if (a == 0.0) return sign;
+  int E;
+  frexp(a, &E);
+  E -= 1;                       /* a in [2^E, 2^(E+1)) */
+  if (E < -6) {                 /* subnormal range: quantum 2^-9 */
+    double m = rint(a * 512.0);
+    if (m >= 8.0) return sign | (1 << 3);  /* rounds up to 2^-6 */
+    return sign | (int)m;
+  }
+  double q = rint(ldexp(a, 3 - E));  /* 8..16 */
+  if (q >= 16.0) {
+    q = 8.0;
+    E += 1;
+  }
+  return sign | ((E + 7) << 3) | ((int)q - 8);
+}
+
+double ora_fp8_decode(int code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  if (e == 15 && m == 7) v = NAN;
+  return (code & 0x80) ? -v : v;
+}
+
+/* Quantise rows x[n][d] (fp64): codes[n][d] and scales[n]; deq[n][d] (nullable)
+ * receives code values times scale. */
+void ora_fp8_rows(const double* x, long n, int d, int* codes, double* scales, double* deq) {
+  for (long i = 0; i < n; ++i) {
+    double amax = 0.0;
+    for (int e = 0; e < d; ++e) amax = fmax(amax, fabs(x[i * d + e]));
+    double sc = ora_fp8_scale(amax);
+    scales[i] = sc;
+    for (int e = 0; e < d; ++e) {
+      int cd = ora_fp8_encode(x[i * d + e] / sc);
+      codes[i * d + e] = cd;
+      if (deq) deq[i * d + e] = ora_fp8_decode(cd) * sc;
+    }
+  }
+}
+
+/* FP8 pool keys: the rotated keys (fp64, unrounded) quantised per row. */
+void ora_pool_fp8(const ora_cfg* c, const double* kraw, long pos0, long n, int* codes,
+                  double* scales, double* deq) {
+  int d = c->d;
+  double* rot = (double*)malloc(sizeof(double) * d * n);
+  for (long i = 0; i < n; ++i) ora_rope(c, kraw + i * d, (double)(pos0 + i), rot + i * d);
+  ora_fp8_rows(rot, n, d, codes, scales, deq);
+  free(rot);
+}
+
 void ora_pooled_query(const ora_cfg* c, const double* q, int hg, int lq, long pos0, double* qbar) {
   int d = c->d;
   double* tmp = (double*)malloc(sizeof(double) * d);

@@ -460,3 +460,51 @@ def test_exact_ties_break_by_ascending_id():
     assert margins[0] == 0.0 and margins[1] == 0.0
     routed = [g for g in sel if 1 <= g // 4 < 13]
     assert routed == [13, 14, 15]
+
+
+# ------------------------------------------------------------- fp8 pool
+def test_fp8_decode_matches_torch_e4m3fn():
+    """Every E4M3FN code decodes as torch's float8_e4m3fn does."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_decode(c) for c in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_fp8_encode_matches_torch_rounding():
+    """Round to nearest even into E4M3FN, against torch's float32 ->
+    float8_e4m3fn conversion, on random values across the normal and
+    subnormal ranges and on exact halfway points."""
+    rng = np.random.default_rng(8)
+    y = np.concatenate([rng.uniform(-448, 448, 4000),
+                        rng.uniform(-2.0 ** -5, 2.0 ** -5, 2000),
+                        rng.standard_normal(2000) * 3.0]).astype(np.float32)
+    vals = np.array([oracle.fp8_decode(c) for c in range(256)])
+    fin = np.sort(np.unique(vals[np.isfinite(vals)]))
+    halfway = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)  # exact in fp32
+    y = np.concatenate([y, halfway, -halfway, np.float32([0.0, 448.0, -448.0, 2.0 ** -9])])
+    ref = torch.tensor(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(int)
+    got = np.array([oracle.fp8_encode(float(v)) for v in y])
+    neg_zero = (y == 0) & np.signbit(y)
+    np.testing.assert_array_equal(got[~neg_zero], ref[~neg_zero])
+
+
+def test_fp8_row_scale_is_the_smallest_fitting_power_of_two():
+    rng = np.random.default_rng(9)
+    for amax in np.concatenate([rng.uniform(1e-6, 1e6, 500), [448.0, 448.0 * 2 ** -20, 1.0, 0.0]]):
+        s = oracle.fp8_scale(amax)
+        assert s > 0 and math.frexp(s)[0] == 0.5  # a power of two
+        if amax == 0:
+            assert s == 1.0
+            continue
+        assert amax / s <= 448.0 and amax / (s / 2) > 448.0
+    x = rng.standard_normal((5, 128)) * np.array([1e-3, 1.0, 30.0, 500.0, 1e4])[:, None]
+    codes, scales, deq = oracle.fp8_rows(x)
+    for i in range(5):
+        assert scales[i] == oracle.fp8_scale(np.abs(x[i]).max())
+        want = np.array([oracle.fp8_decode(oracle.fp8_encode(v / scales[i])) for v in x[i]]) * scales[i]
+        np.testing.assert_array_equal(deq[i], want)
+        # within half a quantum of the rounded binade (3 mantissa bits)
+        assert np.all(np.abs(deq[i] - x[i]) <= np.maximum(np.abs(x[i]) * 2.0 ** -4, 2.0 ** -10 * scales[i]))
