@@ -99,11 +99,22 @@ typedef struct {
   int32_t rope_style;      /* RoPE pairs: 0 = (x_j, x_{j+d/2}) (half-split), 1 =
                               (x_{2j}, x_{2j+1}) (interleaved); the pool keys, the
                               summaries and the rotated queries follow it */
+  int32_t pool_dtype;      /* 0: the K/V pool holds qkv_dtype; 1: the FP8 pool (bf16
+                              inputs, head_dim 128): each (token, KV head) row of the
+                              rotated keys and of the values as OCP E4M3FN codes times
+                              the smallest power of two s with max|x| <= 448 s.  A pool
+                              buffer then holds the codes, [B][Hkv][cap][d] bytes (V in
+                              transposed group blocks), followed by the row scales,
+                              [B][Hkv][cap] fp32.  Supported by hga_build_summaries,
+                              hga_route, hga_attend (1..15 query tokens, HGA_SRC_POOL)
+                              and hga_decode_step; other entry points return
+                              HGA_ERR_UNSUPPORTED */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
  * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
- * theta <= 1, rep_position, route_per_head or rope_style outside {0, 1}),
+ * theta <= 1, rep_position, route_per_head, rope_style or pool_dtype outside
+ * {0, 1}),
  * HGA_ERR_UNSUPPORTED for valid shapes this build does not implement. */
 hga_status hga_validate(const hga_config* cfg);
 

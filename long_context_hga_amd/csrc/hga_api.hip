@@ -36,12 +36,14 @@ hga_status check_cfg(const hga_config* c) {
       !(c->hf_wavelength >= 0.0) || (c->qkv_dtype != HGA_F32 && c->qkv_dtype != HGA_BF16) ||
       (c->rep_position != 0 && c->rep_position != 1) ||
       (c->route_per_head != 0 && c->route_per_head != 1) ||
-      (c->rope_style != 0 && c->rope_style != 1))
+      (c->rope_style != 0 && c->rope_style != 1) || (c->pool_dtype != 0 && c->pool_dtype != 1))
     return HGA_ERR_INVALID_ARGUMENT;
   const int hg = c->n_q_heads / c->n_kv_heads;
   if ((c->head_dim != 64 && c->head_dim != 128) || c->chunk_size != kChunk ||
       c->groups_per_chunk != kGroups || (hg != 1 && hg != 2 && hg != 4 && hg != 8))
     return HGA_ERR_UNSUPPORTED;
+  if (c->pool_dtype == 1 && (c->qkv_dtype != HGA_BF16 || c->head_dim != 128))
+    return HGA_ERR_UNSUPPORTED;  // the FP8 pool: bf16 inputs, head_dim 128
   return HGA_OK;
 }
 
@@ -63,6 +65,7 @@ KCfg make_kcfg(const hga_config* c) {
   k.qscale_log2 = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
   k.rep_shift = c->rep_position == 1 ? 0.5 : 0.0;
   k.interleaved = c->rope_style == 1;
+  k.pool8 = c->pool_dtype == 1;
   k.hf_mask = 0;
   for (int j = 0; j < c->head_dim / 2; ++j) {
     k.omega[j] = pow(c->rope_theta, -2.0 * (double)j / (double)c->head_dim);
@@ -212,6 +215,7 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
                       void* k_ws, void* v_ws, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
+  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 ||
       !sel_groups || !n_sel || max_sel <= 0 ||
       !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
@@ -244,6 +248,9 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   // takes K/V as bf16 operands unrounded; an fp32 pool would need a
   // three-product split)
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
+    return HGA_ERR_UNSUPPORTED;
+  // the FP8 pool: decode shapes reading the pool itself
+  if (cfg->pool_dtype == 1 && (lq > kMaxLqDecode || src_layout != HGA_SRC_POOL))
     return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
@@ -287,6 +294,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_INVALID_ARGUMENT;
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
+  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
@@ -396,6 +404,7 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
                               void* ws, size_t ws_bytes, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
+  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || T <= 0 || T % kChunk != 0 || phases <= 0 || (phases & ~HGA_PROMPT_ALL) ||
       !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 || !chunk_sum ||
       !group_sum || max_chunks <= 0 || !sel_groups || !n_sel || !ws)
@@ -476,6 +485,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              void* ws, size_t ws_bytes, void* stream_a, void* stream_b) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
+  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (cfg->route_per_head) return HGA_ERR_UNSUPPORTED;
   if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
       hot_cap <= 0 || hot_cap % kGroupTokens != 0 || !k_cold || !v_cold || cold_cap <= 0 ||
@@ -588,6 +598,7 @@ hga_status hga_warm_gather(const hga_config* cfg, int32_t B, const void* k_cold,
                            void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
+  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || !k_cold || !v_cold || cold_cap <= 0 || cold_cap % kGroupTokens != 0 ||
       !sel_groups || !n_sel || max_sel <= 0 || !q_pos0 || !k_warm || !v_warm || !warm_tags ||
       !warm_used || !k_ws || !v_ws || !ws || step <= 0)

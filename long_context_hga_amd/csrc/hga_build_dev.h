@@ -25,14 +25,37 @@ namespace hga {
 // consecutive rows); NULL = no summaries.  krow(p) / vrow(p) return the raw
 // key / value row of position p in [lo, hi).  stage (nullable): the chunk's
 // staging rows, [C][D]; the raw key of each position in [lo, hi) is copied
-// to row p - c0.  part: LDS scratch of S*P*2 doubles.  Called by all 256
-// threads of a workgroup with uniform arguments.
+// to row p - c0.  part: LDS scratch of S*P*2 doubles.  f8 (with f8.k set,
+// in place of kp / vp; head_dim 128): the append writes the FP8 pool instead,
+// E4M3FN codes of each rotated key row and value row with their row scales.
+// Called by all 256 threads of a workgroup with uniform arguments.
+struct Fp8Rows {
+  uint8_t* k = nullptr;  // the unit's K codes [cap][D]
+  uint8_t* v = nullptr;  // the unit's V^T codes [cap/16][D][16]
+  float* ks = nullptr;   // the unit's K row scales [cap]
+  float* vs = nullptr;   // the unit's V row scales [cap]
+};
+
+// The FP8 pool buffers: codes of every unit ([units][cap][D] bytes, V in
+// transposed group blocks), then the row scales ([units][cap] fp32).
+__device__ __forceinline__ Fp8Rows fp8_rows_of(void* k_pool, void* v_pool, int units, int cap, int d,
+                                               int unit) {
+  Fp8Rows r;
+  const size_t codes = (size_t)units * cap * d;
+  r.k = static_cast<uint8_t*>(k_pool) + (size_t)unit * cap * d;
+  r.v = static_cast<uint8_t*>(v_pool) + (size_t)unit * cap * d;
+  r.ks = reinterpret_cast<float*>(static_cast<uint8_t*>(k_pool) + codes) + (size_t)unit * cap;
+  r.vs = reinterpret_cast<float*>(static_cast<uint8_t*>(v_pool) + codes) + (size_t)unit * cap;
+  return r;
+}
+
 template <int D, bool BF16, class KRow, class VRow>
 __device__ __forceinline__ void build_span(
     const KCfg& cfg, int c0, int lo, int hi, KRow krow, VRow vrow,
     typename std::conditional<BF16, uint16_t, float>::type* kp,
     typename std::conditional<BF16, uint16_t, float>::type* vp, float* cs_row, float* gs_rows,
-    double* part_lds, typename std::conditional<BF16, uint16_t, float>::type* stage = nullptr) {
+    double* part_lds, typename std::conditional<BF16, uint16_t, float>::type* stage = nullptr,
+    Fp8Rows f8 = {}) {
   constexpr int P = D / 2;               // pairs
   constexpr int S = 256 / P;             // token slices
   constexpr int TS = kChunk / S;         // tokens per slice
@@ -56,7 +79,7 @@ __device__ __forceinline__ void build_span(
     int p = c0 + s * TS + i;
     p = p < lo ? lo : (p >= hi ? hi - 1 : p);
     const T* kr = krow(p);
-    const T* vr = kp ? vrow(p) : kr;
+    const T* vr = (kp || f8.k) ? vrow(p) : kr;
     xa[i] = kr[ja];
     xb[i] = kr[jb];
     ya[i] = vr[ja];
@@ -100,6 +123,23 @@ __device__ __forceinline__ void build_span(
         const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
         vp[vcol + (size_t)ja * kGroupTokens] = ya[i];
         vp[vcol + (size_t)jb * kGroupTokens] = yb[i];
+      }
+      if constexpr (D == 128 && BF16) {
+        if (f8.k) {  // uniform; the wave holds the 64 pairs of this token
+          const double va = bf16_to_f(ya[i]), vb = bf16_to_f(yb[i]);
+          const double sk = fp8_row_scale(wave_ext_d<true>(fmax(fabs(ra), fabs(rb))));
+          const double sv = fp8_row_scale(wave_ext_d<true>(fmax(fabs(va), fabs(vb))));
+          const size_t prow = (size_t)p * D;
+          f8.k[prow + ja] = (uint8_t)fp8_code(ra / sk);
+          f8.k[prow + jb] = (uint8_t)fp8_code(rb / sk);
+          const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
+          f8.v[vcol + (size_t)ja * kGroupTokens] = (uint8_t)fp8_code(va / sv);
+          f8.v[vcol + (size_t)jb * kGroupTokens] = (uint8_t)fp8_code(vb / sv);
+          if (j == 0) {
+            f8.ks[p] = (float)sk;
+            f8.vs[p] = (float)sv;
+          }
+        }
       }
       if (hf) {
         sa += ra;

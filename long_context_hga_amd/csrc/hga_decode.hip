@@ -71,9 +71,23 @@ struct DecodeShared {
   float ob[4][kColRows][D + 4];   // per-wave output rows (rescaled)
 };
 
+// 8 E4M3FN codes -> the same 8 values as bf16 (exact: every E4M3FN value is a
+// bf16 value), via v_cvt_pk_f32_fp8.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]),
+                                               pack_bf16x2(f2[0], f2[1]), pack_bf16x2(f3[0], f3[1])));
+}
+
 // One split workgroup (256 threads): split `split` of KV head h, grid row bz
-// = sequence * column blocks + column block.
-template <int D, int HG, bool BF16>
+// = sequence * column blocks + column block.  FP8: the pool holds E4M3FN
+// codes with power-of-two row scales (bf16 inputs): the codes enter the
+// matrix cores as bf16, the K row scale multiplies the scores and the V row
+// scale the probabilities (both exact).
+template <int D, int HG, bool BF16, bool FP8 = false>
 __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, int h, int bz) {
   constexpr int P = D / 2;
   constexpr int KS = D / 32;          // k-steps of QK^T
@@ -154,7 +168,34 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
   //   V^T (A of O^T): dim 16*blk + rl, keys 8qg..8qg+7 = group qg/2,
   //   tokens 8*(qg%2)..+7
   uint4 kraw[2][KS][EV], vraw[NB][EV];
-  {
+  uint2 k8[2][KS], v8[NB];  // FP8: 8 codes per operand
+  float ksc[8], vsc[8];     // FP8: row scales of the lane's keys 8qg .. 8qg + 7
+  if constexpr (FP8) {
+    const uint8_t* kc = static_cast<const uint8_t*>(a.k);
+    const uint8_t* vc = static_cast<const uint8_t*>(a.v);
+    const size_t kbase = (rl >> 3) ? kb[1] : kb[0];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int t = 8 * ((rl >> 2) & 1) + 4 * n + (rl & 3);
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        k8[n][k] = *reinterpret_cast<const uint2*>(kc + kbase + (size_t)t * D + 32 * k + 8 * qg);
+    }
+    const size_t vbase = (qg >> 1) ? vb[1] : vb[0];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      v8[nb] = *reinterpret_cast<const uint2*>(vc + vbase + (size_t)(16 * nb + rl) * kGroupTokens + 8 * (qg & 1));
+    // the scales follow the codes of every pool unit; row = group row * 16 + token
+    const size_t codes = (size_t)a.B * c.hkv * a.src_cap * D;
+    const size_t srow = ((qg >> 1) ? kb[1] : kb[0]) / D + 8 * (qg & 1);
+    const float4* kq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kc + codes) + srow);
+    const float4* vq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(vc + codes) + srow);
+    const float4 k0 = kq[0], k1 = kq[1], w0 = vq[0], w1 = vq[1];
+    ksc[0] = k0.x; ksc[1] = k0.y; ksc[2] = k0.z; ksc[3] = k0.w;
+    ksc[4] = k1.x; ksc[5] = k1.y; ksc[6] = k1.z; ksc[7] = k1.w;
+    vsc[0] = w0.x; vsc[1] = w0.y; vsc[2] = w0.z; vsc[3] = w0.w;
+    vsc[4] = w1.x; vsc[5] = w1.y; vsc[6] = w1.z; vsc[7] = w1.w;
+  } else {
     const int gk = rl >> 3;
     const size_t kbase = gk ? kb[1] : kb[0];
 #pragma unroll
@@ -228,7 +269,11 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
       s[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        if constexpr (BF16) {
+        if constexpr (FP8) {
+          const bf16x8 kop = fp8x8_to_bf16(k8[n][k]);
+          s[n] = mfma(kop, qop_hi[k], s[n]);
+          s[n] = mfma(kop, qop_lo[k], s[n]);
+        } else if constexpr (BF16) {
           const bf16x8 kop = __builtin_bit_cast(bf16x8, kraw[n][k][0]);
           s[n] = mfma(kop, qop_hi[k], s[n]);
           s[n] = mfma(kop, qop_lo[k], s[n]);
@@ -250,20 +295,12 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool vis = gp >= 0 && t0 + 4 * n + i <= tau;
-        sv[4 * n + i] = vis ? s[n][i] : -INFINITY;
+        const float sc = FP8 ? s[n][i] * ksc[4 * n + i] : s[n][i];
+        sv[4 * n + i] = vis ? sc : -INFINITY;
         mx = fmaxf(mx, sv[4 * n + i]);
       }
     m = rows_max(mx);
     const float mref = m == -INFINITY ? 0.f : m;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float p0 = exp2f(sv[2 * k] - mref), p1 = exp2f(sv[2 * k + 1] - mref);
-      l += p0 + p1;
-      split_pair(p0, p1, ph[k], pl[k]);
-    }
-    const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
     // V of keys that are missing or after the last query token -> 0 (such
     // rows may never have been written)
     const bool partial = gpos[0] < 0 || gpos[1] < 0 || gpos[0] + kGroupTokens - 1 > pos_last ||
@@ -274,9 +311,36 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) keep |= (gp >= 0 && t0 + i <= pos_last) ? (1u << i) : 0u;
     }
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float p0 = exp2f(sv[2 * k] - mref), p1 = exp2f(sv[2 * k + 1] - mref);
+      l += p0 + p1;
+      if constexpr (FP8) {  // the V row scale joins the probability (a kept key only)
+        p0 = (keep >> (2 * k)) & 1u ? p0 * vsc[2 * k] : 0.f;
+        p1 = (keep >> (2 * k + 1)) & 1u ? p1 * vsc[2 * k + 1] : 0.f;
+      }
+      split_pair(p0, p1, ph[k], pl[k]);
+    }
+    const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (BF16) {
+      if constexpr (FP8) {
+        uint2 vv = v8[nb];
+        if (partial) {  // masked bytes -> +0
+          uint32_t mlo = 0u, mhi = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mlo |= (keep >> i) & 1u ? 0xFFu << (8 * i) : 0u;
+            mhi |= (keep >> (4 + i)) & 1u ? 0xFFu << (8 * i) : 0u;
+          }
+          vv = make_uint2(vv.x & mlo, vv.y & mhi);
+        }
+        const bf16x8 vop = fp8x8_to_bf16(vv);
+        o[nb] = mfma(vop, pop_hi, o[nb]);
+        o[nb] = mfma(vop, pop_lo, o[nb]);
+      } else if constexpr (BF16) {
         const uint4 vv = partial ? keep_bf16(vraw[nb][0], keep) : vraw[nb][0];
         const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
         o[nb] = mfma(vop, pop_hi, o[nb]);
@@ -340,9 +404,9 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
   }
 }
 
-template <int D, int HG, bool BF16>
+template <int D, int HG, bool BF16, bool FP8 = false>
 __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
-  decode_split<D, HG, BF16>(args, blockIdx.x, blockIdx.y, blockIdx.z);
+  decode_split<D, HG, BF16, FP8>(args, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // The host tier's one-launch front: workgroups [0, n_win) are the window
@@ -364,6 +428,12 @@ __global__ __launch_bounds__(256) void tier_front_kernel(AttendArgs win, int win
 
 template <int D, int HG>
 static void launch_decode_dh(const AttendArgs& x, dim3 grid, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (x.cfg.pool8) {
+      hipLaunchKernelGGL((attend_decode_kernel<D, HG, true, true>), grid, dim3(256), 0, st, x);
+      return;
+    }
+  }
   if (x.cfg.dtype == HGA_BF16)
     hipLaunchKernelGGL((attend_decode_kernel<D, HG, true>), grid, dim3(256), 0, st, x);
   else

@@ -22,6 +22,7 @@ struct KCfg {
   // (lists = hq, lhg = 1, kvdiv = hg).
   int lists, lhg, kvdiv;
   int interleaved;                 // RoPE pairs (2j, 2j+1) instead of (j, j + d/2)
+  int pool8;                       // K/V pool of E4M3FN codes with per-row scales
   int n_sink, n_local, topk_c, topk_g;
   int dtype;                       // hga_dtype
   float qscale_log2;               // log2(e) / sqrt(d)
@@ -30,6 +31,36 @@ struct KCfg {
   double rep_shift;                // representative position a + (n-1)/2 + rep_shift
   double omega[kMaxPairs];         // theta^(-2j/d), computed on the host in fp64
 };
+
+// FP8 pool rows (OCP E4M3FN: sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; largest finite value 448): a row's scale is the smallest power of two
+// s with max|x| <= 448 s (1 for a zero row), its codes x / s (exact) rounded
+// to nearest even.
+__device__ __forceinline__ double fp8_row_scale(double amax) {
+  if (!(amax > 0.0)) return 1.0;
+  int e;
+  const double f = 2.0 * frexp(amax, &e);  // amax = f 2^(e-1), f in [1, 2)
+  e -= 1;
+  return ldexp(1.0, f <= 1.75 ? e - 8 : e - 7);
+}
+__device__ __forceinline__ uint32_t fp8_code(double y) {  // |y| <= 448
+  const uint32_t sign = y < 0.0 ? 0x80u : 0u;
+  const double a = fabs(y);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  e -= 1;                                  // a in [2^e, 2^(e+1))
+  if (e < -6) {                            // subnormal codes: steps of 2^-9
+    const double m = rint(a * 512.0);
+    return sign | (m >= 8.0 ? 8u : (uint32_t)m);  // 8 = the smallest normal code
+  }
+  double q = rint(ldexp(a, 3 - e));        // 8 .. 16
+  if (q >= 16.0) {
+    q = 8.0;
+    e += 1;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | ((uint32_t)q - 8u);
+}
 
 // Dims of the two members of RoPE pair j.
 __host__ __device__ __forceinline__ int pair_a(const KCfg& c, int j) { return c.interleaved ? 2 * j : j; }

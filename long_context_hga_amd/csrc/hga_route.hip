@@ -312,8 +312,11 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * lq * D;
   const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * lq * D;
   T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
-  T* kp = static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
-  T* vp = static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
+  // a plain pool, or the FP8 pool (codes and row scales)
+  T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
+  T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
+  const Fp8Rows f8 = c.pool8 ? fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit)
+                             : Fp8Rows{};
   auto knew = [&](int p) { return kn + (size_t)(p - pos) * D; };
   auto vnew = [&](int p) { return vn + (size_t)(p - pos) * D; };
   const int chunk = pos / kChunk;
@@ -321,10 +324,10 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
   const bool ends = pos + lq - c0 == kChunk;  // uniform
   if (ends && pos == c0) {  // the whole chunk in this step: one pass
-    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
+    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage, f8);
     return;
   }
-  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
+  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage, f8);
   if (ends) {
     build_span<D, BF16>(
         c, c0, c0, c0 + kChunk,

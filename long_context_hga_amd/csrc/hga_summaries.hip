@@ -43,13 +43,17 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   const T* kr = static_cast<const T*>(a.k_raw) + (size_t)unit * a.n_tok * D;
   const T* vr = static_cast<const T*>(a.v_new) + (size_t)unit * a.n_tok * D;
   const int lo = a.pos0;
-  T* kp = a.k_pool ? static_cast<T*>(a.k_pool) + (size_t)unit * a.pool_cap * D : nullptr;
-  T* vp = a.k_pool ? static_cast<T*>(a.v_pool) + (size_t)unit * a.pool_cap * D : nullptr;
+  // a plain pool, or the FP8 pool (codes and row scales)
+  const bool pool = a.k_pool != nullptr, f8 = pool && a.cfg.pool8;
+  T* kp = pool && !f8 ? static_cast<T*>(a.k_pool) + (size_t)unit * a.pool_cap * D : nullptr;
+  T* vp = pool && !f8 ? static_cast<T*>(a.v_pool) + (size_t)unit * a.pool_cap * D : nullptr;
+  const Fp8Rows rows8 = f8 ? fp8_rows_of(a.k_pool, a.v_pool, a.B * a.cfg.hkv, a.pool_cap, D, unit)
+                           : Fp8Rows{};
   float* cs = a.chunk_sum ? a.chunk_sum + ((size_t)unit * a.max_chunks + chunk) * D : nullptr;
   float* gs = a.chunk_sum ? a.group_sum + ((size_t)unit * a.max_chunks + chunk) * kGroups * D : nullptr;
   build_span<D, BF16>(
       a.cfg, chunk * kChunk, lo, lo + a.n_tok, [&](int p) { return kr + (size_t)(p - lo) * D; },
-      [&](int p) { return vr + (size_t)(p - lo) * D; }, kp, vp, cs, gs, part);
+      [&](int p) { return vr + (size_t)(p - lo) * D; }, kp, vp, cs, gs, part, nullptr, rows8);
 }
 
 hipError_t launch_build(const KCfg& cfg, int B, const void* k_raw, const void* v_new, int pos0,

@@ -43,7 +43,8 @@ def test_validate():
     assert hga.hga_validate(hga.config_from(synth.CONFIGS["tiny"])) == hga.HGA_OK
     bad = [dict(head_dim=127), dict(n_q_heads=30), dict(groups_per_chunk=3), dict(rope_theta=1.0),
            dict(topk_chunks=-1), dict(hf_wavelength=float("nan")), dict(qkv_dtype=7),
-           dict(rep_position=2), dict(route_per_head=-1), dict(rope_style=3)]
+           dict(rep_position=2), dict(route_per_head=-1), dict(rope_style=3),
+           dict(pool_dtype=2)]
     for b in bad:
         assert hga.hga_validate(cfg(**b)) == hga.HGA_ERR_INVALID_ARGUMENT, b
     unsup = [dict(head_dim=96), dict(chunk_size=128), dict(groups_per_chunk=8),
@@ -198,6 +199,25 @@ def test_prefill_prompt_rejects():
     for over in (dict(qkv_dtype=hga.HGA_F32), dict(head_dim=64)):
         a = list(args); a[0] = ctypes.byref(cfg(**over))
         assert f(*a) == hga.HGA_ERR_UNSUPPORTED, over
+
+
+def test_fp8_pool_limits():
+    """The FP8 pool needs bf16 inputs and head_dim 128, and runs the decode
+    paths only."""
+    assert hga.hga_validate(cfg(pool_dtype=1)) == hga.HGA_OK
+    assert hga.hga_validate(cfg(pool_dtype=1, qkv_dtype=hga.HGA_F32)) == hga.HGA_ERR_UNSUPPORTED
+    assert hga.hga_validate(cfg(pool_dtype=1, head_dim=64)) == hga.HGA_ERR_UNSUPPORTED
+    c = ctypes.byref(cfg(pool_dtype=1))
+    f = hga.lib().hga_attend
+    args = [c, 8, FAKE, 1, FAKE, FAKE, FAKE, 0, 65536, FAKE, FAKE, 128, 0, FAKE, None, FAKE,
+            1 << 30, None]
+    a = list(args); a[3] = 32  # prefill shape
+    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
+    a = list(args); a[7] = hga.HGA_SRC_WORKING_SET
+    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
+    g = hga.lib().hga_gather
+    assert g(c, 8, FAKE, FAKE, 65536, 0, FAKE, FAKE, 128, None, 0, FAKE, FAKE, None) == \
+        hga.HGA_ERR_UNSUPPORTED
 
 
 def test_warm_gather_rejects():
