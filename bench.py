@@ -72,7 +72,8 @@ def algorithmic_bytes(p, B):
     ct = p["query_pos0"] // p["chunk_size"]
     n_cand = ct - p["n_local_chunks"] - p["n_sink_chunks"]
     lists = hq if p.get("route_per_head") else hkv  # selected lists per sequence
-    kv = max_sel * g * d * 2 * 2 * lists         # selected K and V rows of every list, bf16
+    row = d + 4 if p.get("pool_dtype") == 1 else d * 2  # bytes per K (or V) row: FP8 + scale, or bf16
+    kv = max_sel * g * row * 2 * lists           # selected K and V rows of every list
     q = hq * d * 2
     o = hq * d * 4
     idx = lists * max_sel * 4
@@ -268,6 +269,13 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     kt = st.k_raw[:, :, pos:pos + 1].contiguous()
     vt = st.v_raw[:, :, pos:pos + 1].contiguous()
     kc = st.k_raw[:, :, c0:c0 + 64].contiguous()
+    if p.get("pool_dtype") == 1:  # the FP8 pool: codes then row scales, built from the raw K/V
+        nbytes = B * p["n_kv_heads"] * T * (p["head_dim"] + 4)
+        st.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        st.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        hga.hga_build_summaries(st.cfg, B, st.k_raw, st.v_raw, 0, T, st.k_pool, st.v_pool, T, None,
+                                None, st.max_chunks)
+        torch.cuda.synchronize()
     R = max(1, args.replicas if replicas is None else replicas)
     reps = []
     for r in range(R):
@@ -355,23 +363,25 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 
     # hga_gather from the HBM pool into a working set (the same lists): its
-    # own copy rate, read + write
-    kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]), dtype=reps[0]["k_pool"].dtype,
-                     device="cuda")
-    vw = torch.empty_like(kw)
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(20)]
-    torch.cuda._sleep(int(1e8))
-    for i, (e0, e1) in enumerate(gev):
-        x = reps[i % R]
-        e0.record()
-        hga.hga_gather(cfg, B, x["k_pool"], x["v_pool"], T, 0, x["s"].sel, x["s"].n_sel,
-                       st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
-        e1.record()
-    torch.cuda.synchronize()
-    gather_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
-    gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
-    del kw, vw
+    # own copy rate, read + write (the FP8 pool has no gather)
+    gather_ms, gather_bytes = float("nan"), 0
+    if p.get("pool_dtype", 0) == 0:
+        kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
+                         dtype=reps[0]["k_pool"].dtype, device="cuda")
+        vw = torch.empty_like(kw)
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        torch.cuda._sleep(int(1e8))
+        for i, (e0, e1) in enumerate(gev):
+            x = reps[i % R]
+            e0.record()
+            hga.hga_gather(cfg, B, x["k_pool"], x["v_pool"], T, 0, x["s"].sel, x["s"].n_sel,
+                           st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
+            e1.record()
+        torch.cuda.synchronize()
+        gather_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
+        gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
+        del kw, vw
 
     ab = algorithmic_bytes(p, B)
     achieved = ab["attend"] / (attend_ms * 1e-3) / 1e9
@@ -395,6 +405,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
                                f"top-{p['topk_chunks']} chunks, top-{p['topk_groups']} groups "
                                f"({st.max_sel * 16} keys, {100.0 * st.max_sel * 16 / T:.3g}%), "
                                + ("one list per query head, " if p.get("route_per_head") else "")
+                               + ("FP8 pool (E4M3FN + row scales) " if p.get("pool_dtype") == 1 else "")
                                + "pool in HBM",
                    "batch": B, "context": T, "replicas": R,
                    "timing": "HIP graph of R steps, replayed",
@@ -419,8 +430,9 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
 # Decode sweep: context 4K..64K and batch 8..32 at 64K.  4K is the 4K decode
 # workload as defined (batch 1, top-8 chunks, top-16 groups); 8K and 16K keep
 # its budget at batch 8 (the windows alone are 384 tokens, above 3.125 % of
-# 8K); 32K and 64K use the 3.125 % budgets of the 32K and 64K workloads.  The
-# last point routes per query head (one list per head instead of per KV head).
+# 8K); 32K and 64K use the 3.125 % budgets of the 32K and 64K workloads.  Then
+# one point routes per query head (one list per head instead of per KV head)
+# and two read the FP8 pool (E4M3FN codes with row scales).
 SWEEP = [
     ("decode4k", None, None, None),
     ("decode64k", 8, 8192, dict(topk_chunks=8, topk_groups=16)),
@@ -430,6 +442,8 @@ SWEEP = [
     ("decode64k", 16, 65536, None),
     ("decode64k", 32, 65536, None),
     ("decode64k", 8, 65536, dict(route_per_head=1)),
+    ("decode64k", 8, 65536, dict(pool_dtype=1)),
+    ("decode64k", 32, 65536, dict(pool_dtype=1)),
 ]
 
 

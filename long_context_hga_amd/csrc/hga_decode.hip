@@ -46,6 +46,11 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream8(const void* p) {  // 8 bytes read once
+  const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // 8 fp32 values (two uint4) -> bf16x8 hi and lo operands
 __device__ __forceinline__ void split8(const uint4& x0, const uint4& x1, bf16x8& hi, bf16x8& lo) {
@@ -179,12 +184,12 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
       const int t = 8 * ((rl >> 2) & 1) + 4 * n + (rl & 3);
 #pragma unroll
       for (int k = 0; k < KS; ++k)
-        k8[n][k] = *reinterpret_cast<const uint2*>(kc + kbase + (size_t)t * D + 32 * k + 8 * qg);
+        k8[n][k] = load_stream8(kc + kbase + (size_t)t * D + 32 * k + 8 * qg);
     }
     const size_t vbase = (qg >> 1) ? vb[1] : vb[0];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      v8[nb] = *reinterpret_cast<const uint2*>(vc + vbase + (size_t)(16 * nb + rl) * kGroupTokens + 8 * (qg & 1));
+      v8[nb] = load_stream8(vc + vbase + (size_t)(16 * nb + rl) * kGroupTokens + 8 * (qg & 1));
     // the scales follow the codes of every pool unit; row = group row * 16 + token
     const size_t codes = (size_t)a.B * c.hkv * a.src_cap * D;
     const size_t srow = ((qg >> 1) ? kb[1] : kb[0]) / D + 8 * (qg & 1);
