@@ -60,8 +60,8 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="e3ea2204702050d7a9333b4f3efd77cba0c2e2ce9cb78d39af4504a3e397c224",
-    fetch_kib=16751.07 + 1469.49, write_kib=2080.01 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="aa6b2e1bf9bbb64260006c959078abb4a19bde55e1c7282259fffb75e0835519",
+    fetch_kib=16745.93 + 1469.92, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):

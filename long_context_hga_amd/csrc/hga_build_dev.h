@@ -49,6 +49,49 @@ __device__ __forceinline__ Fp8Rows fp8_rows_of(void* k_pool, void* v_pool, int u
   return r;
 }
 
+// One token's rows into the FP8 pool (bf16 inputs, head_dim 128), as
+// build_span writes them: wave 0 rotates and quantises the key row (lane j:
+// pair j, the angle stepped from the first position of the token's slice
+// exactly as build_span steps it), wave 1 quantises the value row.
+__device__ __forceinline__ void fp8_append_row(const KCfg& cfg, const uint16_t* kn, const uint16_t* vn,
+                                            int c0, int p, Fp8Rows f8) {
+  constexpr int D = 128, P = D / 2, TS = kChunk / (256 / P);
+  const int wave = threadIdx.x >> 6, j = threadIdx.x & 63;
+  if (wave > 1) return;
+  const int ja = pair_a(cfg, j), jb = pair_b(cfg, j);
+  double xa, xb;
+  if (wave == 0) {
+    const double w = cfg.omega[j];
+    const int p_first = c0 + (p - c0) / TS * TS;
+    double cs, sn, cd, sd;
+    rope_cs((double)p_first, w, &cs, &sn);
+    sincos(w, &sd, &cd);
+    for (int i = p_first; i < p; ++i) {
+      const double c2 = cs * cd - sn * sd;
+      sn = sn * cd + cs * sd;
+      cs = c2;
+    }
+    const double ka = bf16_to_f(kn[ja]), kb = bf16_to_f(kn[jb]);
+    xa = ka * cs - kb * sn;
+    xb = ka * sn + kb * cs;
+  } else {
+    xa = bf16_to_f(vn[ja]);
+    xb = bf16_to_f(vn[jb]);
+  }
+  const double sc = fp8_row_scale(wave_ext_d<true>(fmax(fabs(xa), fabs(xb))));
+  const uint8_t ca = (uint8_t)fp8_code(xa / sc), cb = (uint8_t)fp8_code(xb / sc);
+  if (wave == 0) {
+    f8.k[(size_t)p * D + ja] = ca;
+    f8.k[(size_t)p * D + jb] = cb;
+    if (j == 0) f8.ks[p] = (float)sc;
+  } else {
+    const size_t vcol = (size_t)(p / kGroupTokens) * D * kGroupTokens + p % kGroupTokens;
+    f8.v[vcol + (size_t)ja * kGroupTokens] = ca;
+    f8.v[vcol + (size_t)jb * kGroupTokens] = cb;
+    if (j == 0) f8.vs[p] = (float)sc;
+  }
+}
+
 template <int D, bool BF16, class KRow, class VRow>
 __device__ __forceinline__ void build_span(
     const KCfg& cfg, int c0, int lo, int hi, KRow krow, VRow vrow,

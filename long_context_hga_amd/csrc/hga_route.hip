@@ -312,11 +312,17 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * lq * D;
   const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * lq * D;
   T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
-  // a plain pool, or the FP8 pool (codes and row scales)
+  // a plain pool, or the FP8 pool (codes and row scales; one decode token per
+  // step, appended by a small routine of its own)
   T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
   T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
-  const Fp8Rows f8 = c.pool8 ? fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit)
-                             : Fp8Rows{};
+  if constexpr (D == 128 && BF16) {
+    if (c.pool8) {  // lq = 1 (checked on the host)
+      const Fp8Rows f8 = fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit);
+      fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + (size_t)unit * D,
+                     static_cast<const uint16_t*>(f.v_new) + (size_t)unit * D, c0, pos, f8);
+    }
+  }
   auto knew = [&](int p) { return kn + (size_t)(p - pos) * D; };
   auto vnew = [&](int p) { return vn + (size_t)(p - pos) * D; };
   const int chunk = pos / kChunk;
@@ -324,10 +330,10 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
   const bool ends = pos + lq - c0 == kChunk;  // uniform
   if (ends && pos == c0) {  // the whole chunk in this step: one pass
-    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage, f8);
+    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
     return;
   }
-  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage, f8);
+  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
   if (ends) {
     build_span<D, BF16>(
         c, c0, c0, c0 + kChunk,
