@@ -822,6 +822,7 @@ def run_host64k(args):
     s = gh.alloc_step(st, 1)
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
+    tier_events = (torch.cuda.Event(), torch.cuda.Event())  # fork / join of the two-stream form
 
     def step(second):
         # the new token goes to the device window pool and, over PCIe, to the host pool
@@ -833,7 +834,8 @@ def run_host64k(args):
                       s.n_sel, st.max_sel, None, st.ws)
         hga.hga_attend_tiered(cfg, B, q, 1, st.pos0, st.k_pool, st.v_pool, T, k_cold, v_cold, T,
                               s.sel, s.n_sel, st.max_sel, kw, vw, s.out, s.lse, st.ws,
-                              stream_a=main, stream_b=second)
+                              stream_a=main, stream_b=second,
+                              events=tier_events if second is not None else None)
         hga.hga_build_summaries(cfg, B, kc, None, c0, 64, None, None, T, st.chunk_sum,
                                 st.group_sum, st.max_chunks)
 
@@ -979,7 +981,7 @@ def run_host64k(args):
     t_tiered = timed(lambda: hga.hga_attend_tiered(cfg, B, q, 1, st.pos0, st.k_pool, st.v_pool, T,
                                                    k_cold, v_cold, T, s.sel, s.n_sel, st.max_sel,
                                                    kw, vw, s.out, s.lse, st.ws, stream_a=main,
-                                                   stream_b=side), reps)
+                                                   stream_b=side, events=tier_events), reps)
     t_tiered_one = timed(lambda: hga.hga_attend_tiered(cfg, B, q, 1, st.pos0, st.k_pool, st.v_pool,
                                                        T, k_cold, v_cold, T, s.sel, s.n_sel,
                                                        st.max_sel, kw, vw, s.out, s.lse, st.ws,

@@ -188,7 +188,12 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
                      int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel, int32_t max_sel,
                      double* chunk_scores_opt, void* ws, size_t ws_bytes, void* stream);
 
-/* Gather of the selected token K/V into a compact working set.
+/* Gather of the selected token K/V into a compact working set: after routing,
+ * the original token-level keys and values of the selected groups are fetched
+ * into accelerator memory for the exact attention (HGA technical summary,
+ * gist.science, "Kernmechanisme" item 4), from the device pool or, for the
+ * cold tier of "Geheugenarchitectuur" (full K/V history in host RAM), from a
+ * pinned host pool over PCIe.
  *   k_pool, v_pool as written by hga_build_summaries (pool_cap a multiple of
  *           16): device memory, or pinned host memory (pool_is_host = 1, read
  *           directly over PCIe).
@@ -354,7 +359,11 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
  *   out, lse_opt   as hga_attend
  *   ws             hga_workspace_bytes() of workspace (this call needs room
  *                  for two attention partial sets and two part results)
- * The two-stream form creates and releases two HIP events (no memory).
+ * The two-stream form records the caller's two HIP events: ev_fork on
+ * stream_a (stream_b waits for it) and ev_join on stream_b (stream_a waits for
+ * it before the merge); both are hipEvent_t created by the caller (timing may
+ * be disabled), distinct, and not recorded elsewhere while the call's work is
+ * queued.  The call creates and destroys nothing.
  * stream_b = NULL selects the one-stream form: for 1..15 query tokens the
  * window part's attention and the PCIe copy of the routed groups run as
  * workgroups of one launch on stream_a (the copy workgroups mostly wait on
@@ -363,13 +372,15 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
  * tokens the one-stream form runs the parts one after another.)  Both forms
  * give the same bits.
  * Errors: as hga_attend; HGA_ERR_INVALID_ARGUMENT if the cold pool is not
- * pinned host memory. */
+ * pinned host memory, or if stream_b is set and the two events are missing or
+ * the same. */
 hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
                              const int32_t* q_pos0, const void* k_hot, const void* v_hot,
                              int32_t hot_cap, const void* k_cold, const void* v_cold,
                              int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
                              int32_t max_sel, void* k_ws, void* v_ws, float* out, float* lse_opt,
-                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b);
+                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b,
+                             void* ev_fork, void* ev_join);
 
 /* Workspace of hga_warm_gather (host only). */
 hga_status hga_warm_workspace_bytes(const hga_config* cfg, int32_t B, int32_t max_sel,
@@ -412,7 +423,11 @@ hga_status hga_warm_gather(const hga_config* cfg, int32_t B, const void* k_cold,
                            void* k_ws, void* v_ws, int32_t* hits_opt, void* ws, size_t ws_bytes,
                            void* stream);
 
-/* Exact merge of two attention results over disjoint token sets:
+/* Exact merge of two attention results over disjoint token sets, so that
+ * attention computed in parts equals softmax attention over their union (the
+ * exactness of "Kernmechanisme" item 4 when the hot windows and the cold
+ * routed groups of "Geheugenarchitectuur" are attended separately; HGA
+ * technical summary, gist.science):
  * out = (e^{lse_a} out_a + e^{lse_b} out_b) / (e^{lse_a} + e^{lse_b}),
  * lse_out = log(e^{lse_a} + e^{lse_b}) (lse_out nullable).  Rows are
  * [B][Hq][lq], each of d fp32 values.  out may alias out_a or out_b. */

@@ -114,7 +114,7 @@ def lib() -> ctypes.CDLL:
             "hga_prefill_prompt": [_C, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P,
                                    _P, _I, _P, ctypes.c_size_t, _P],
             "hga_attend_tiered": [_C, _I, _P, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P,
-                                  _P, _P, _P, ctypes.c_size_t, _P, _P],
+                                  _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P],
             "hga_warm_workspace_bytes": [_C, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
             "hga_warm_gather": [_C, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _P,
                                 _P, _P, _P, ctypes.c_size_t, _P],
@@ -151,6 +151,17 @@ def _stream(s):
     if isinstance(s, int):
         return s
     return s.cuda_stream
+
+
+def _event(e):
+    """hipEvent_t of a torch.cuda.Event (torch creates its event on the first
+    record, so an unused one is recorded once on the current stream) or a raw
+    handle."""
+    if isinstance(e, int):
+        return e
+    if not e.cuda_event:
+        e.record()
+    return e.cuda_event
 
 
 def _check(st: int, where: str):
@@ -268,16 +279,24 @@ def hga_prefill_prompt(cfg, B, T, q_raw, k_raw, v_raw, k_pool, v_pool, pool_cap,
 
 def hga_attend_tiered(cfg, B, q_raw, lq, q_pos0, k_hot, v_hot, hot_cap, k_cold, v_cold, cold_cap,
                       sel_groups, n_sel, max_sel, k_ws, v_ws, out, lse_opt, ws, stream_a=None,
-                      stream_b=None):
+                      stream_b=None, events=None):
     """Windows from the device pool on stream_a, routed groups copied from the
     pinned host pool and attended on stream_b, merged on stream_a.  stream_a
     defaults to the current stream; stream_b=None selects the one-stream form
-    (the window attention and the copy share one launch on stream_a)."""
+    (the window attention and the copy share one launch on stream_a).  With
+    stream_b, ``events`` is a pair of torch.cuda.Event (fork, join) that the
+    call records; they are created once by the caller and reused."""
+    ev = (None, None)
+    if stream_b is not None:
+        if events is None or len(events) != 2:
+            raise ValueError("hga_attend_tiered with stream_b needs events=(fork, join)")
+        ev = tuple(_event(e) for e in events)
     _check(lib().hga_attend_tiered(_cfg(cfg), B, _ptr(q_raw), lq, _ptr(q_pos0), _ptr(k_hot),
                                    _ptr(v_hot), hot_cap, _ptr(k_cold), _ptr(v_cold), cold_cap,
                                    _ptr(sel_groups), _ptr(n_sel), max_sel, _ptr(k_ws), _ptr(v_ws),
                                    _ptr(out), _ptr(lse_opt), _ptr(ws), ws.numel() * ws.element_size(),
-                                   _stream(stream_a), None if stream_b is None else _stream(stream_b)),
+                                   _stream(stream_a), None if stream_b is None else _stream(stream_b),
+                                   ev[0], ev[1]),
            "hga_attend_tiered")
 
 

@@ -324,6 +324,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   r.pool_once = 0;
   r.max_chunks = max_chunks;
   r.max_sel = max_sel;
+  r.pool_cap = pool_cap;
   StepFront f;
   f.k_new = k_new;
   f.v_new = v_new;
@@ -482,7 +483,8 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              int32_t hot_cap, const void* k_cold, const void* v_cold,
                              int32_t cold_cap, const int32_t* sel_groups, const int32_t* n_sel,
                              int32_t max_sel, void* k_ws, void* v_ws, float* out, float* lse_opt,
-                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b) {
+                             void* ws, size_t ws_bytes, void* stream_a, void* stream_b,
+                             void* ev_fork, void* ev_join) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
   if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
@@ -500,6 +502,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_UNSUPPORTED;
   const KCfg k = make_kcfg(cfg);
   if (ws_bytes < tiered_ws_bytes(cfg, k, B, lq)) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (stream_b && (!ev_fork || !ev_join || ev_fork == ev_join)) return HGA_ERR_INVALID_ARGUMENT;
   const void* kc = nullptr;
   const void* vc = nullptr;
   if (!pinned_device_ptr(k_cold, &kc) || !pinned_device_ptr(v_cold, &vc))
@@ -558,13 +561,9 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   // list written by hga_route); join: the merge on stream a waits for b.  The
   // window part is queued right behind the fork, ahead of the transfer, so
   // its workgroups take their CUs before the copy kernel's waves (which
-  // mostly wait on PCIe) fill the rest.
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return HGA_ERR_HIP;
-  if (hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) {
-    (void)hipEventDestroy(fork);
-    return HGA_ERR_HIP;
-  }
+  // mostly wait on PCIe) fill the rest.  The two events are the caller's.
+  hipEvent_t fork = static_cast<hipEvent_t>(ev_fork);
+  hipEvent_t join = static_cast<hipEvent_t>(ev_join);
   hipError_t e = hipEventRecord(fork, sa);
   if (e == hipSuccess) e = launch_attend_split(k, ah, sa);
   if (e == hipSuccess) e = hipStreamWaitEvent(sb, fork, 0);
@@ -575,9 +574,6 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
   if (e == hipSuccess) e = hipEventRecord(join, sb);
   if (e == hipSuccess) e = hipStreamWaitEvent(sa, join, 0);
   if (e == hipSuccess) e = launch_attend_merge(k, a, sa);
-  // the events are released once the work that references them completes
-  (void)hipEventDestroy(fork);
-  (void)hipEventDestroy(join);
   return hip_status(e);
 }
 

@@ -33,6 +33,9 @@ struct RouteLaunch {
   // 1: the multi-token pooled query of each unit is formed by a launch of
   // its own and read by the tile workgroups (many units, many tiles each)
   int pool_once;
+  // > 0 (a fused step): tokens per unit of the pool the step appends to; a
+  // position whose tokens do not fit is unusable (n_sel = -1)
+  int pool_cap = 0;
 };
 // The token work of a fused decode step, run by extra workgroups of the
 // selection launch: the new token's pool append, its raw key into the chunk

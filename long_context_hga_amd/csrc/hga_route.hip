@@ -40,14 +40,14 @@ struct RouteArgs {
 };
 
 // Position and candidate range of a unit; false if the query position is
-// unusable (negative, query tokens spanning two chunks, or a query chunk
-// beyond the summary table).
+// unusable (negative, query tokens spanning two chunks, a query chunk beyond
+// the summary table, or, in a fused step, tokens beyond the pool).
 __device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch& r, int max_cand,
                                                int b, int* pos0, Windows* w) {
   *pos0 = r.q_pos0[b];
   *w = windows_of(*pos0 / kChunk, c.n_sink, c.n_local);
   return *pos0 >= 0 && (*pos0 % kChunk) + r.lq <= kChunk && *pos0 / kChunk < r.max_chunks &&
-         w->cand_hi - w->cand_lo <= max_cand;
+         w->cand_hi - w->cand_lo <= max_cand && (r.pool_cap <= 0 || *pos0 + r.lq <= r.pool_cap);
 }
 
 // MODE 0: pooled query of up to S tokens + scores (decode);
@@ -312,15 +312,17 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * lq * D;
   const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * lq * D;
   T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
-  // a plain pool, or the FP8 pool (codes and row scales; one decode token per
-  // step, appended by a small routine of its own)
+  // a plain pool, or the FP8 pool (codes and row scales of each of the step's
+  // tokens, appended one row at a time by a small routine of its own)
   T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
   T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
   if constexpr (D == 128 && BF16) {
-    if (c.pool8) {  // lq = 1 (checked on the host)
+    if (c.pool8) {  // lq <= 15 (checked on the host)
       const Fp8Rows f8 = fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit);
-      fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + (size_t)unit * D,
-                     static_cast<const uint16_t*>(f.v_new) + (size_t)unit * D, c0, pos, f8);
+      for (int p = pos; p < pos + lq; ++p)
+        fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + ((size_t)unit * lq + (p - pos)) * D,
+                       static_cast<const uint16_t*>(f.v_new) + ((size_t)unit * lq + (p - pos)) * D,
+                       c0, p, f8);
     }
   }
   auto knew = [&](int p) { return kn + (size_t)(p - pos) * D; };

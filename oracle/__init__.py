@@ -90,6 +90,8 @@ def lib():
         L.ora_windows.argtypes = [c, ctypes.c_long, _lp, _lp, _lp]
         L.ora_windows.restype = ctypes.c_int
         L.ora_pooled_query.argtypes = [c, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_long, _dp]
+        L.ora_group_scores.argtypes = [c, _dp, ctypes.c_int, ctypes.c_long, _dp, ctypes.c_long,
+                                       _dp]
         L.ora_select.argtypes = [c, _dp, ctypes.c_int, ctypes.c_long, _dp, _dp, _ip, ctypes.c_int,
                                  _dp, _dp]
         L.ora_select.restype = ctypes.c_int
@@ -97,6 +99,9 @@ def lib():
                                  _dp, _dp]
         L.ora_merge.argtypes = [ctypes.c_int, ctypes.c_long, _dp, _dp, _dp, _dp, _dp, _dp]
         L.ora_gather.argtypes = [c, _dp, _ip, ctypes.c_int, _dp]
+        L.ora_warm_step.argtypes = [ctypes.c_int, _ip, _ip, _ip, ctypes.c_int, ctypes.c_int, _ip,
+                                    _ip]
+        L.ora_warm_step.restype = ctypes.c_int
         L.ora_step.argtypes = [c, ctypes.c_int, _dp, ctypes.c_int, _lp, _dp, _dp, ctypes.c_long,
                                _dp, _dp, ctypes.c_long, _ip, _ip, ctypes.c_int, _dp]
         L.ora_step.restype = ctypes.c_int
@@ -258,6 +263,19 @@ def select(cfg, q, pos0, chunk_sum, group_sum, max_sel=1 << 16):
     return sel[:n].copy(), margins, scores[:ncand].copy()
 
 
+def group_scores(cfg, q, pos0, group_sum):
+    """Level-2 score of every group id before the query chunk: the pooled
+    routing query of q [hg][lq][d] (raw, at positions pos0..) dotted with
+    group_sum [n][d], over sqrt(d)."""
+    q, qp = _d(q)
+    gs, gsp = _d(group_sum)
+    n = min(gs.shape[0], (int(pos0) // cfg.C) * cfg.G)
+    out = np.zeros(max(n, 1))
+    lib().ora_group_scores(ctypes.byref(cfg), qp, q.shape[1], int(pos0), gsp, n,
+                           out.ctypes.data_as(_dp))
+    return out[:n].copy()
+
+
 def attend(cfg, q, pos0, kpool, vpool, sel_groups):
     """q [hg][lq][d] raw; kpool/vpool [T][d].  Returns (out [hg][lq][d], lse [hg][lq])."""
     q, qp = _d(q)
@@ -292,6 +310,24 @@ def gather(cfg, pool_, sel_groups):
     out = np.empty((sel.size * g, cfg.d))
     lib().ora_gather(ctypes.byref(cfg), pp, selp, sel.size, out.ctypes.data_as(_dp))
     return out
+
+
+def warm_step(tags, used, routed, step_no):
+    """One call of the warm-tier LRU policy for one unit.  tags, used: int
+    arrays [n_warm] (copies are updated and returned); routed: the distinct
+    routed group ids in list order.  Returns (tags, used, slot [n], hit [n],
+    n_hits)."""
+    tags, tp = _i(np.array(tags, dtype=np.int32, copy=True))
+    used, up = _i(np.array(used, dtype=np.int32, copy=True))
+    routed, rp = _i(np.asarray(routed, dtype=np.int32))
+    n = routed.size
+    slot = np.zeros(max(n, 1), dtype=np.int32)
+    hit = np.zeros(max(n, 1), dtype=np.int32)
+    nh = lib().ora_warm_step(tags.size, tp, up, rp, n, int(step_no), slot.ctypes.data_as(_ip),
+                             hit.ctypes.data_as(_ip))
+    if nh < 0:
+        raise ValueError("more misses than free slots")
+    return tags, used, slot[:n].copy(), hit[:n].copy(), nh
 
 
 def step(cfg, q, pos0, chunk_sum, group_sum, kpool, vpool, max_sel):

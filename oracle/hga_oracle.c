@@ -311,6 +311,19 @@ void ora_pooled_query(const ora_cfg* c, const double* q, int hg, int lq, long po
   free(tmp);
 }
 
+/* Level-2 routing score of every group id g < n_groups:
+ * qbar . group_sum[g] / sqrt(d), with qbar the pooled routing query that
+ * ora_select forms from q [hg][lq][d] at positions pos0.. (the scores of the
+ * groups of the chosen chunks are the ones level 2 ranks). */
+void ora_group_scores(const ora_cfg* c, const double* q, int lq, long pos0,
+                      const double* group_sum, long n_groups, double* out) {
+  int d = c->d, hg = c->hq / c->hkv;
+  double* qbar = (double*)malloc(sizeof(double) * d);
+  ora_pooled_query(c, q, hg, lq, pos0, qbar);
+  for (long g = 0; g < n_groups; ++g) out[g] = dot(qbar, group_sum + g * d, d) / sqrt((double)d);
+  free(qbar);
+}
+
 /* Two-level selection for one (sequence, KV head).
  *   q           [hg][lq][d] raw query of the KV head's query heads
  *   pos0, lq    query tokens pos0..pos0+lq-1, all inside chunk ct
@@ -445,6 +458,66 @@ void ora_gather(const ora_cfg* c, const double* pool, const int* sel_groups, int
   int d = c->d, g = c->C / c->G;
   for (int s = 0; s < n_sel; ++s)
     memcpy(ws + (long)s * g * d, pool + (long)sel_groups[s] * g * d, sizeof(double) * g * d);
+}
+
+/* ----------------------------------------------------------- warm tier
+ * "Geheugenarchitectuur": between the hot tier (summaries and the always
+ * visible windows in accelerator memory) and the cold tier (the full token
+ * K/V history in host memory) sits a bounded least-recently-used cache in
+ * accelerator memory of recently routed data.  One call for one unit:
+ *   n_warm slots, tags[s] = the cached group id (-1: empty), used[s] = the
+ *   step that last used the slot (0: never); routed[0..n) the distinct group
+ *   ids the routing chose this step, in list order.
+ *   A routed group found among the tags is a hit: its slot's stamp becomes
+ *   `step`.  The misses, in list order, take the slots that are not hits in
+ *   increasing order of (stamp, slot index) -- the least recently used first,
+ *   empty slots (stamp 0) before any used one -- one slot each; a taken
+ *   slot's tag becomes the group and its stamp `step`.
+ * slot[i] receives the slot holding routed[i] after the call, hit[i] 1 for a
+ * hit.  Returns the number of hits, or -1 if the misses outnumber the slots
+ * that are not hits (nothing is changed then). */
+int ora_warm_step(int n_warm, int* tags, int* used, const int* routed, int n, int step, int* slot,
+                  int* hit) {
+  int* is_hit = (int*)calloc(n_warm > 0 ? n_warm : 1, sizeof(int));
+  int n_hit = 0, n_miss = 0;
+  for (int i = 0; i < n; ++i) {
+    slot[i] = -1;
+    hit[i] = 0;
+    for (int s = 0; s < n_warm; ++s)
+      if (tags[s] == routed[i]) {
+        slot[i] = s;
+        hit[i] = 1;
+        is_hit[s] = 1;
+      }
+    if (hit[i]) n_hit += 1;
+    else n_miss += 1;
+  }
+  if (n_miss > n_warm - n_hit) {
+    free(is_hit);
+    return -1;
+  }
+  for (int i = 0; i < n; ++i)
+    if (hit[i]) used[slot[i]] = step;
+  /* each miss in turn takes the least recently used slot still free */
+  int* taken = (int*)calloc(n_warm > 0 ? n_warm : 1, sizeof(int));
+  for (int i = 0; i < n; ++i) {
+    if (hit[i]) continue;
+    int best = -1;
+    for (int s = 0; s < n_warm; ++s) {
+      if (is_hit[s] || taken[s]) continue;
+      if (best < 0 || used[s] < used[best]) best = s; /* ties keep the lower slot index */
+    }
+    taken[best] = 1;
+    slot[i] = best;
+  }
+  for (int i = 0; i < n; ++i)
+    if (!hit[i]) {
+      tags[slot[i]] = routed[i];
+      used[slot[i]] = step;
+    }
+  free(taken);
+  free(is_hit);
+  return n_hit;
 }
 
 /* ------------------------------------------------ batched driver (timing)

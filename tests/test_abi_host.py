@@ -122,7 +122,7 @@ def test_attend_tiered_rejects():
     c = ctypes.byref(cfg())
     f = hga.lib().hga_attend_tiered
     args = [c, 4, FAKE, 1, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, 65536, FAKE, FAKE, 128, FAKE, FAKE,
-            FAKE, None, FAKE, 1 << 30, None, None]
+            FAKE, None, FAKE, 1 << 30, None, None, None, None]
     a = list(args); a[8] = None  # no cold pool
     assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT
     a = list(args); a[14] = None  # no working set
@@ -133,6 +133,11 @@ def test_attend_tiered_rejects():
     assert f(*a) == hga.HGA_ERR_UNSUPPORTED
     a = list(args); a[0] = ctypes.byref(cfg(qkv_dtype=hga.HGA_F32)); a[3] = 32
     assert f(*a) == hga.HGA_ERR_UNSUPPORTED
+    # the two-stream form needs the caller's two distinct events
+    n = hga.hga_workspace_bytes(cfg(), 4, 65536, 1)
+    for ev in ((None, None), (FAKE, None), (None, FAKE), (FAKE, FAKE)):
+        a = list(args); a[19] = n; a[21] = FAKE; a[22], a[23] = ev
+        assert f(*a) == hga.HGA_ERR_INVALID_ARGUMENT, ev
     # hga_workspace_bytes covers the tiered call: with that size the call gets
     # past the workspace check and rejects the cold pool, which is not pinned
     n = hga.hga_workspace_bytes(cfg(), 4, 65536, 1)

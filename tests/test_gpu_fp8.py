@@ -95,6 +95,7 @@ def test_fp8_decode_attention_against_oracle(lq):
     cfg = oracle.cfg_from(inp.params)
     uc = UnitCache(inp, cfg)
     q = gh.query_slice(st, 0) if lq == 1 else st.q[:, :, :1].repeat(1, 1, lq, 1).contiguous()
+    deq = {}
     for pos in (4095 - lq + 1, 3000, 1280):
         pos_t = torch.full((st.B,), pos, dtype=torch.int32, device="cuda")
         s = gh.alloc_step(st, lq)
@@ -110,8 +111,12 @@ def test_fp8_decode_attention_against_oracle(lq):
                 qu = inp.f64(qh[b, h * 8:(h + 1) * 8])
                 g = sel[b, h, :nsel[b, h]]
                 osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
-                check_selection(cfg, g, osel, margins, oscores, pos, lq)
-                kd, vd = pool.deq(b, h)
+                check_selection(cfg, g, osel, margins, oscores, pos, lq,
+                                oracle.group_scores(cfg, qu, pos, gs))
+                if (b, h) not in deq:  # the oracle's own FP8 pool
+                    deq[b, h] = (oracle.pool_fp8(cfg, inp.f64(inp.k[b, h]), 0)[2],
+                                 oracle.fp8_rows(inp.f64(inp.v[b, h]))[2])
+                kd, vd = deq[b, h]
                 o_ref, _ = oracle.attend(cfg, qu, pos, kd, vd, g)
                 assert max_abs(out[b, h * 8:(h + 1) * 8], o_ref) <= ATOL_OUT, (pos, b, h)
 
@@ -156,3 +161,61 @@ def test_fp8_decode_step_equals_separate_calls():
         assert torch.equal(sa.n_sel, sb.n_sel) and torch.equal(sa.out, sb.out), p
     assert torch.equal(pa.k, pb.k) and torch.equal(pa.v, pb.v)
     assert torch.equal(csa, csb) and torch.equal(gsa, gsb)
+
+
+@pytest.mark.parametrize("pos,lq", [(20 * 64 + 59, 5), (30 * 64 + 3, 15), (2047, 1)])
+def test_fp8_prefill_step_equals_separate_calls(pos, lq):
+    """hga_prefill_step with 1..15 query tokens on the FP8 pool appends every
+    one of its tokens (the same codes and scales as hga_build_summaries over
+    those tokens) and gives the bits of the separate calls."""
+    inp, st, _ = fp8_state(batch=2, context=4096, max_lq=lq)
+    B, T = st.B, st.T
+    q = st.q[:, :, :lq].contiguous()
+    pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+    kn = st.k_raw[:, :, pos:pos + lq].contiguous()
+    vn = st.v_raw[:, :, pos:pos + lq].contiguous()
+    c0 = pos // 64 * 64
+    ends = pos + lq == c0 + 64
+    print(f"[fp8 prefill step] pos {pos} lq {lq}", flush=True)
+
+    def fresh():
+        pool = Fp8Pool(B, 4, T, 128)
+        cs, gs = torch.zeros_like(st.chunk_sum), torch.zeros_like(st.group_sum)
+        hga.hga_build_summaries(st.cfg, B, st.k_raw[:, :, :pos].contiguous(),
+                                st.v_raw[:, :, :pos].contiguous(), 0, pos, pool.k, pool.v, T, cs,
+                                gs, st.max_chunks)
+        return pool, cs, gs
+
+    pa, csa, gsa = fresh()
+    sa = gh.alloc_step(st, lq)
+    hga.hga_build_summaries(st.cfg, B, kn, vn, pos, lq, pa.k, pa.v, T, None, None, st.max_chunks)
+    if ends:
+        hga.hga_build_summaries(st.cfg, B, st.k_raw[:, :, c0:c0 + 64].contiguous(), None, c0, 64,
+                                None, None, T, csa, gsa, st.max_chunks)
+    hga.hga_route(st.cfg, B, q, lq, pos_t, csa, gsa, st.max_chunks, sa.sel, sa.n_sel, st.max_sel,
+                  None, st.ws)
+    hga.hga_attend(st.cfg, B, q, lq, pos_t, pa.k, pa.v, hga.HGA_SRC_POOL, T, sa.sel, sa.n_sel,
+                   st.max_sel, hga.HGA_PART_ALL, sa.out, sa.lse, st.ws)
+    pb, csb, gsb = fresh()
+    stage = torch.zeros_like(st.k_raw[:, :, :64])
+    stage[:, :, :pos - c0] = st.k_raw[:, :, c0:pos]
+    sb = gh.alloc_step(st, lq)
+    hga.hga_prefill_step(st.cfg, B, q, lq, kn, vn, pos_t, pb.k, pb.v, T, stage, csb, gsb,
+                         st.max_chunks, sb.sel, sb.n_sel, st.max_sel, sb.out, sb.lse,
+                         torch.zeros_like(st.ws))
+    torch.cuda.synchronize()
+    assert (sb.n_sel > 0).all()
+    assert torch.equal(sa.n_sel, sb.n_sel) and torch.equal(sa.sel, sb.sel)
+    assert torch.equal(sa.out, sb.out) and torch.equal(sa.lse, sb.lse)
+    assert torch.equal(pa.k, pb.k) and torch.equal(pa.v, pb.v)
+    assert torch.equal(csa, csb) and torch.equal(gsa, gsb)
+    # every appended row holds the oracle quantiser's scale
+    cfg = oracle.cfg_from(inp.params)
+    for b in range(B):
+        for h in range(4):
+            _, oscales, _ = oracle.pool_fp8(cfg, inp.f64(inp.k[b, h, pos:pos + lq]), pos)
+            _, ks = pb.k_rows(b, h)
+            np.testing.assert_array_equal(ks[pos:pos + lq], oscales)
+            _, vscales, _ = oracle.fp8_rows(inp.f64(inp.v[b, h, pos:pos + lq]))
+            _, vs = pb.v_rows(b, h)
+            np.testing.assert_array_equal(vs[pos:pos + lq], vscales)

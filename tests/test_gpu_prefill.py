@@ -57,7 +57,8 @@ def run_prefill(inp, st, pos, lq, tok0=0, cfg_over=None, check_sel=True, uc=None
             g = sel[b, h, :nsel[b, h]]
             if check_sel:
                 osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
-                check_selection(cfg, g, osel, margins, oscores, pos, lq)
+                check_selection(cfg, g, osel, margins, oscores, pos, lq,
+                                oracle.group_scores(cfg, qu, pos, gs))
             o_ref, l_ref = oracle.attend(cfg, qu, pos, kp, v, g)
             err = max_abs(out[b, h * hg:(h + 1) * hg], o_ref)
             worst = max(worst, err)

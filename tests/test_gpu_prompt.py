@@ -73,7 +73,8 @@ def check_chunks(inp, pr, chunks):
                 qu = q_unit(inp, cfg, b, h, pos, 64)
                 g = sel[b, qc, h, :nsel[b, qc, h]]
                 osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
-                check_selection(cfg, g, osel, margins, oscores, pos, 64)
+                check_selection(cfg, g, osel, margins, oscores, pos, 64,
+                                oracle.group_scores(cfg, qu, pos, gs))
                 o_ref, l_ref = oracle.attend(cfg, qu, pos, kp, v, g)
                 got = out[b, h * hg:(h + 1) * hg, pos:pos + 64]
                 err = max_abs(got, o_ref)

@@ -47,7 +47,8 @@ def run(inp, st, pos, lq):
             qu = q_unit(inp, cfg, b, h, 0, lq)
             g = sel[b, h, :nsel[b, h]]
             osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
-            check_selection(cfg, g, osel, margins, oscores, pos, lq)
+            check_selection(cfg, g, osel, margins, oscores, pos, lq,
+                            oracle.group_scores(cfg, qu, pos, gs))
             o_ref, _ = oracle.attend(cfg, qu, pos, kp, v, g)
             assert max_abs(out[b, h * hg:(h + 1) * hg], o_ref) <= ATOL_OUT, (pos, lq, b, h)
 
@@ -102,7 +103,8 @@ def test_prompt_shapes(shape):
                 qu = q_unit(inp, cfg, b, h, pos, 64)
                 g = sel_h[b, qc, h, :nsel_h[b, qc, h]]
                 osel, margins, oscores = oracle.select(cfg, qu, pos, cs_, gs_)
-                check_selection(cfg, g, osel, margins, oscores, pos, 64)
+                check_selection(cfg, g, osel, margins, oscores, pos, 64,
+                                oracle.group_scores(cfg, qu, pos, gs_))
                 o_ref, _ = oracle.attend(cfg, qu, pos, kpo, vpo, g)
                 err = max_abs(out_h[b, h * hg:(h + 1) * hg, pos:pos + 64], o_ref)
                 assert err <= ATOL_OUT, (b, qc, h, err)

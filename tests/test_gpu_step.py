@@ -110,6 +110,41 @@ def test_decode_step_invalid_position_writes_nothing():
     assert not stage.any()
 
 
+def test_step_position_beyond_pool_writes_nothing():
+    """Summary tables longer than the pool: a step whose tokens do not fit the
+    pool is unusable (n_sel = -1, NaN outputs) and writes nothing, while the
+    last position that fits works."""
+    inp = synth.generate("decode64k", batch=1, context=2048)
+    st = gh.build_state(inp, max_lq=10)
+    cap = 1008  # 63 groups; the summary tables hold 32 chunks (2048 tokens)
+    kp = st.k_pool[:, :, :cap].contiguous()
+    vp = st.v_pool[:, :, :cap].contiguous()
+    kp0, vp0 = kp.clone(), vp.clone()
+    cs0, gs0 = st.chunk_sum.clone(), st.group_sum.clone()
+    stage = torch.zeros_like(st.k_raw[:, :, :64])
+    for bad, lq in ((1008, 1), (1500, 1), (2047, 1), (1000, 10)):
+        print(f"[beyond pool] pos {bad} lq {lq}", flush=True)
+        s = gh.alloc_step(st, lq)
+        pos_t = torch.full((1,), bad, dtype=torch.int32, device="cuda")
+        hga.hga_prefill_step(st.cfg, 1, st.q[:, :, :lq].contiguous(), lq,
+                             st.k_raw[:, :, :lq].contiguous(), st.v_raw[:, :, :lq].contiguous(),
+                             pos_t, kp, vp, cap, stage, st.chunk_sum, st.group_sum, st.max_chunks,
+                             s.sel, s.n_sel, st.max_sel, s.out, s.lse, st.ws)
+        torch.cuda.synchronize()
+        assert (s.n_sel == -1).all() and torch.isnan(s.out).all(), bad
+    assert torch.equal(kp, kp0) and torch.equal(vp, vp0)
+    assert torch.equal(st.chunk_sum, cs0) and torch.equal(st.group_sum, gs0)
+    assert not stage.any()
+    s = gh.alloc_step(st, 1)
+    pos_t = torch.full((1,), cap - 1, dtype=torch.int32, device="cuda")
+    hga.hga_decode_step(st.cfg, 1, gh.query_slice(st, 0), st.k_raw[:, :, cap - 1].contiguous(),
+                        st.v_raw[:, :, cap - 1].contiguous(), pos_t, kp, vp, cap, stage,
+                        st.chunk_sum, st.group_sum, st.max_chunks, s.sel, s.n_sel, st.max_sel,
+                        s.out, s.lse, st.ws)
+    torch.cuda.synchronize()
+    assert (s.n_sel > 0).all() and torch.isfinite(s.out).all()
+
+
 @pytest.mark.parametrize("B,T,pos,lq", [(1, 4096, 4032, 64),       # the whole last chunk
                                         (2, 4096, 40 * 64, 64),    # a whole chunk mid-context
                                         (2, 4096, 30 * 64 + 47, 17),  # ends its chunk

@@ -37,7 +37,8 @@ def run_tiered(st, kc, vc, q, lq, pos_t, side):
     lse = torch.full_like(s.lse, float("nan"))
     ws2 = torch.zeros_like(st.ws)
     hga.hga_attend_tiered(st.cfg, st.B, q, lq, pos_t, st.k_pool, st.v_pool, st.T, kc, vc, st.T,
-                          s.sel, s.n_sel, st.max_sel, kw, vw, out, lse, ws2, stream_b=side)
+                          s.sel, s.n_sel, st.max_sel, kw, vw, out, lse, ws2, stream_b=side,
+                          events=(torch.cuda.Event(), torch.cuda.Event()))
     torch.cuda.synchronize()
     return s, out, lse
 
@@ -86,7 +87,8 @@ def test_tiered_reads_only_window_rows_of_the_device_pool():
     vw = torch.zeros_like(kw)
     out = torch.full_like(out0, float("nan"))
     hga.hga_attend_tiered(st.cfg, 1, q, 1, st.pos0, st.k_pool, st.v_pool, st.T, kc, vc, st.T,
-                          s0.sel, s0.n_sel, st.max_sel, kw, vw, out, None, st.ws, stream_b=side)
+                          s0.sel, s0.n_sel, st.max_sel, kw, vw, out, None, st.ws, stream_b=side,
+                          events=(torch.cuda.Event(), torch.cuda.Event()))
     torch.cuda.synchronize()
     assert torch.equal(out, out0)
 

@@ -60,7 +60,8 @@ def test_variant_summaries_route_attend(variant):
                 qu = q_unit(inp, cfg, b, h, 0, lq)
                 g = sel[b, h, :nsel[b, h]]
                 osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
-                check_selection(cfg, g, osel, margins, oscores, pos, lq)
+                check_selection(cfg, g, osel, margins, oscores, pos, lq,
+                                oracle.group_scores(cfg, qu, pos, gs))
                 o_ref, _ = oracle.attend(cfg, qu, pos, kp, v, g)
                 assert max_abs(out[b, h * hg:(h + 1) * hg], o_ref) <= ATOL_OUT, (pos, lq, b, h)
 
@@ -117,7 +118,8 @@ def test_route_per_query_head(hq, hkv):
                 qu = inp.f64(inp.q[b, qh:qh + 1, :lq])
                 g = sel_h[b, qh, :nsel_h[b, qh]]
                 osel, margins, oscores = oracle.select(ocfg, qu, pos, cs, gs)
-                check_selection(ocfg, g, osel, margins, oscores, pos, lq)
+                check_selection(ocfg, g, osel, margins, oscores, pos, lq,
+                                oracle.group_scores(ocfg, qu, pos, gs))
                 o_ref, _ = oracle.attend(ocfg, qu, pos, kp, v, g)
                 assert max_abs(out_h[b, qh:qh + 1], o_ref) <= ATOL_OUT, (pos, lq, b, qh)
                 if qh % hg and not (g.size == sel_h[b, qh - 1, :nsel_h[b, qh - 1]].size and
@@ -182,7 +184,8 @@ def test_interleaved_whole_prompt_and_fused_step():
             qu = q_unit(inp, cfg, 0, h, qc * 64, 64)
             g = sel_h[0, qc, h, :nsel_h[0, qc, h]]
             osel, margins, oscores = oracle.select(cfg, qu, qc * 64, cs_, gs_)
-            check_selection(cfg, g, osel, margins, oscores, qc * 64, 64)
+            check_selection(cfg, g, osel, margins, oscores, qc * 64, 64,
+                            oracle.group_scores(cfg, qu, qc * 64, gs_))
             o_ref, _ = oracle.attend(cfg, qu, qc * 64, kpo, vpo, g)
             assert max_abs(out_h[0, h * hg:(h + 1) * hg, qc * 64:(qc + 1) * 64], o_ref) <= ATOL_OUT
     # fused decode step at the last position == route + attend

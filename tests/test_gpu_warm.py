@@ -1,12 +1,15 @@
 """GPU checks of the warm tier (hga_warm_gather): a bounded LRU cache in
 device memory of recently routed groups in front of the pinned host pool.
 
-Over a sequence of decode steps whose queries drift, every step's working set
-must hold exactly the groups hga_gather (HGA_PART_ROUTED) copies from the host
-pool, and the cache state (tags, stamps) and hit counts must equal a host
-simulation of the LRU policy: hits renew their stamp; the i-th miss in list
-order takes the i-th least recently used non-hit slot (stamp order, ties by
-slot index, empty slots first)."""
+Over a sequence of decode steps whose queries drift, every step's cache state
+(tags, stamps) and hit counts must equal the oracle's warm-tier policy
+(oracle.warm_step: hits renew their stamp; the i-th miss in list order takes
+the i-th least recently used non-hit slot, stamp order, ties by slot index,
+empty slots first), and the working set must hold the oracle's gather of its
+own pool for the routed groups (values bit-exact, keys within the pool-key
+rule) as well as exactly what hga_gather (HGA_PART_ROUTED) copies.  The
+attention through the cache is compared with the oracle's attention over the
+list and with the device path."""
 import numpy as np
 import pytest
 
@@ -14,7 +17,7 @@ torch = pytest.importorskip("torch")
 
 import oracle
 import synth
-from oracle_ref import window_groups
+from oracle_ref import ATOL_OUT, UnitCache, check_pool_keys, max_abs, q_unit, window_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -29,22 +32,6 @@ def pinned_copy(t):
     h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
     h.copy_(t)
     return h
-
-
-def lru_step(tags, used, routed, step):
-    """Host model of one call for one unit; returns the hit count."""
-    slot_of = {int(t): s for s, t in enumerate(tags) if t >= 0}
-    hit_slots = {slot_of[g] for g in routed if g in slot_of}
-    misses = [g for g in routed if g not in slot_of]
-    for s in hit_slots:
-        used[s] = step
-    order = sorted((s for s in range(len(tags)) if s not in hit_slots),
-                   key=lambda s: (used[s], s))
-    victims = order[:len(misses)]
-    for g, s in zip(misses, victims):
-        tags[s] = g
-        used[s] = step
-    return len(hit_slots)
 
 
 @pytest.mark.parametrize("n_warm,drift", [(208, 0.25), (104, 0.5)])
@@ -64,8 +51,9 @@ def test_warm_cache_matches_gather_and_lru_model(n_warm, drift):
     kw = torch.zeros((B, hkv, max_sel * 16, 128), dtype=st.k_pool.dtype, device="cuda")
     vw = torch.zeros_like(kw)
     kref, vref = torch.zeros_like(kw), torch.zeros_like(vw)
-    m_tags = np.full((B, hkv, n_warm), -1, dtype=np.int64)
-    m_used = np.zeros((B, hkv, n_warm), dtype=np.int64)
+    m_tags = np.full((B, hkv, n_warm), -1, dtype=np.int32)
+    m_used = np.zeros((B, hkv, n_warm), dtype=np.int32)
+    uc = UnitCache(inp, cfg)
     pos = int(inp.pos0[0])
     wins, _, _ = window_groups(cfg, pos, 1)
     rng = np.random.default_rng(77)
@@ -90,9 +78,16 @@ def test_warm_cache_matches_gather_and_lru_model(n_warm, drift):
                 rows_t = torch.tensor(rows, device="cuda")
                 assert torch.equal(kw[b, h, rows_t], kref[b, h, rows_t]), (step, b, h)
                 assert torch.equal(vw[b, h, rows_t], vref[b, h, rows_t]), (step, b, h)
-                n_hit = lru_step(m_tags[b, h], m_used[b, h], routed, step)
+                m_tags[b, h], m_used[b, h], _, _, n_hit = oracle.warm_step(
+                    m_tags[b, h], m_used[b, h], routed, step)
                 assert int(hits[b, h]) == n_hit, (step, b, h, int(hits[b, h]), n_hit)
                 total_hits += n_hit
+                if step in (1, 8):  # the working set against the oracle's gather of its pool
+                    _, _, kpo, vpo = uc.get(b, h)
+                    kr = inp.f64(gh.dev_to_np_bf16(kw[b, h, rows_t]))
+                    check_pool_keys(kr, oracle.gather(cfg, kpo, routed), True)
+                    vr = inp.f64(gh.v_rows(vw[b:b + 1, h:h + 1])[0, 0][rows].view(np.uint16))
+                    np.testing.assert_array_equal(vr, oracle.gather(cfg, vpo, routed))
         np.testing.assert_array_equal(tags.cpu().numpy(), m_tags)
         np.testing.assert_array_equal(used.cpu().numpy(), m_used)
         # the next query drifts from this one
@@ -107,6 +102,8 @@ def test_warm_then_attend_equals_device_path():
     inp = synth.generate("host64k", batch=2, context=8192)
     st = gh.build_state(inp)
     B, max_sel = st.B, st.max_sel
+    cfg = oracle.cfg_from(inp.params)
+    uc = UnitCache(inp, cfg)
     kc, vc = pinned_copy(st.k_pool), pinned_copy(st.v_pool)
     k_warm = torch.zeros((B, 4, 128, 16, 128), dtype=st.k_pool.dtype, device="cuda")
     v_warm = torch.zeros_like(k_warm)
@@ -133,3 +130,12 @@ def test_warm_then_attend_equals_device_path():
         torch.cuda.synchronize()
         assert (om - s.out).abs().max().item() <= 1e-5, step
         assert (lm - s.lse).abs().max().item() <= 1e-5, step
+        out = om.cpu().numpy()
+        sel, nsel = s.sel.cpu().numpy(), s.n_sel.cpu().numpy()
+        pos = int(inp.pos0[0])
+        for b in range(B):
+            for h in range(4):
+                _, _, kpo, vpo = uc.get(b, h)
+                o_ref, _ = oracle.attend(cfg, q_unit(inp, cfg, b, h, 0, 1), pos, kpo, vpo,
+                                         sel[b, h, :nsel[b, h]])
+                assert max_abs(out[b, h * 8:(h + 1) * 8], o_ref) <= ATOL_OUT, (step, b, h)

@@ -508,3 +508,180 @@ def test_fp8_row_scale_is_the_smallest_fitting_power_of_two():
         np.testing.assert_array_equal(deq[i], want)
         # within half a quantum of the rounded binade (3 mantissa bits)
         assert np.all(np.abs(deq[i] - x[i]) <= np.maximum(np.abs(x[i]) * 2.0 ** -4, 2.0 ** -10 * scales[i]))
+
+
+def test_pool_fp8_quantises_the_library_rotation():
+    """FP8 pool keys: each row of transformers' half-split RoPE at its own
+    position, divided by the smallest power of two that brings its largest
+    magnitude within 448, converted by torch to float8_e4m3fn.  Quantising
+    before the rotation, or rotating to the wrong first position, fails."""
+    c = cfg(d=128, theta=1e6, bf16=True)
+    rng = np.random.default_rng(21)
+    kraw = rng.standard_normal((48, 128)) * np.geomspace(1e-3, 3e3, 48)[:, None]
+    pos0 = 40000
+    codes, scales, deq = oracle.pool_fp8(c, kraw, pos0)
+    rot = lib_rope(kraw, np.arange(pos0, pos0 + 48), c)
+    amax = np.abs(rot).max(axis=1)
+    want_scale = 2.0 ** np.ceil(np.log2(amax / 448.0))
+    np.testing.assert_array_equal(scales, want_scale)
+    y = torch.tensor(rot / want_scale[:, None])
+    want = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    np.testing.assert_array_equal(codes, want)
+    np.testing.assert_array_equal(
+        deq, y.to(torch.float8_e4m3fn).to(torch.float64).numpy() * want_scale[:, None])
+    # the same rows quantised at another first position differ
+    other, _, _ = oracle.pool_fp8(c, kraw, pos0 + 1)
+    assert (other != codes).mean() > 0.3
+
+
+def test_group_scores_rank_level2_and_equal_mean_token_logits():
+    """Level-2 scores: the groups ora_select routes are the top-k_g of
+    ora_group_scores over the groups of its level-1 chunks (numpy lexsort);
+    with all-HF summaries a group's score is the mean over the query heads,
+    query tokens and the group's tokens of the exact rotated logits."""
+    d, hg, lq = 64, 4, 3
+    c = oracle.make_cfg(d, hg, 1, 64, 4, 1, 1, 3, 6, 1e4, 64.0, False)
+    k = RNG.standard_normal((64 * 20, d))
+    cs, gs = oracle.summaries(c, k)
+    q = RNG.standard_normal((hg, lq, d))
+    pos0 = 64 * 19 + 10
+    sel, _, s1 = oracle.select(c, q, pos0, cs, gs)
+    g_sc = oracle.group_scores(c, q, pos0, gs)
+    assert g_sc.shape == (19 * 4,)
+    cand = np.arange(1, 18)
+    l1 = cand[np.lexsort((cand, -s1))[:3]]
+    groups = np.array([ch * 4 + j for ch in l1 for j in range(4)])
+    top = set(groups[np.lexsort((groups, -g_sc[groups]))[:6]])
+    assert top == {g for g in sel if 1 <= g // 4 < 18}
+    ch = oracle.make_cfg(d, hg, 1, 64, 4, 1, 1, 3, 6, 1e4, math.inf, False)
+    cs, gs = oracle.summaries(ch, k)
+    g_sc = oracle.group_scores(ch, q, pos0, gs)
+    qrot = np.stack([lib_rope(q[h], np.arange(pos0, pos0 + lq), ch) for h in range(hg)])
+    krot = lib_rope(k, np.arange(k.shape[0]), ch)
+    for gid in (0, 5, 33, 75):
+        logits = qrot.reshape(-1, d) @ krot[gid * 16:(gid + 1) * 16].T / math.sqrt(d)
+        assert g_sc[gid] == pytest.approx(logits.mean(), rel=1e-11, abs=1e-13)
+
+
+@pytest.mark.parametrize("lq", [1, 3])
+def test_step_equals_per_unit_select_and_attend(lq):
+    """The batched driver gives, unit by unit, the bits of ora_select then
+    ora_attend on that unit's own slices (distinct content and positions per
+    unit, so a wrong per-unit stride shows)."""
+    d, hq, hkv, T = 64, 4, 2, 1024
+    hg = hq // hkv
+    c = oracle.make_cfg(d, hq, hkv, 64, 4, 1, 2, 2, 4, 1e4, 64.0, True)
+    rng = np.random.default_rng(31)
+    U = 5
+    kraw = rng.standard_normal((U, T, d))
+    v = rng.standard_normal((U, T, d))
+    q = rng.standard_normal((U, hg, lq, d))
+    pos = np.array([1021, 700, 64 * 9 + 3, 960, 129])
+    cs = np.stack([oracle.summaries(c, kraw[u])[0] for u in range(U)])
+    gs = np.stack([oracle.summaries(c, kraw[u])[1] for u in range(U)])
+    kp = np.stack([oracle.pool(c, kraw[u], 0) for u in range(U)])
+    max_sel = 40
+    sel, nsel, out = oracle.step(c, q, pos, cs, gs, kp, v, max_sel)
+    for u in range(U):
+        s_u, _, _ = oracle.select(c, q[u], pos[u], cs[u], gs[u])
+        assert nsel[u] == s_u.size
+        np.testing.assert_array_equal(sel[u, :nsel[u]], s_u)
+        o_u, _ = oracle.attend(c, q[u], pos[u], kp[u], v[u], s_u)
+        np.testing.assert_array_equal(out[u], o_u)
+
+
+# ------------------------------------------------------------- warm tier
+def _warm_brute(tags, used, routed):
+    """Every assignment of the misses to slots that are not hits, kept when
+    the taken slots are the least recently used ones by (stamp, slot index)
+    and the misses take them in list order."""
+    W = len(tags)
+    where = {int(t): s for s, t in enumerate(tags) if t >= 0}
+    hits = {where[g] for g in routed if g in where}
+    misses = [g for g in routed if g not in where]
+    free = [s for s in range(W) if s not in hits]
+    key = lambda s: (used[s], s)
+    found = []
+    for perm in itertools.permutations(free, len(misses)):
+        taken = set(perm)
+        least = all(key(a) < key(b) for a in taken for b in free if b not in taken)
+        ordered = all(key(perm[i]) < key(perm[i + 1]) for i in range(len(perm) - 1))
+        if least and ordered:
+            found.append(perm)
+    return found, hits
+
+
+def test_warm_policy_brute_force():
+    rng = np.random.default_rng(41)
+    for trial in range(300):
+        W = int(rng.integers(1, 7))
+        universe = rng.permutation(20)[:W + 4]
+        n_cached = int(rng.integers(0, W + 1))
+        tags = np.full(W, -1)
+        tags[rng.permutation(W)[:n_cached]] = universe[:n_cached]
+        used = np.where(tags >= 0, rng.integers(1, 4, W), 0)
+        n = int(rng.integers(0, W + 1))
+        routed = [int(x) for x in rng.permutation(universe)[:n]]
+        found, hits = _warm_brute(tags, used, routed)
+        misses = [g for g in routed if g not in set(tags.tolist())]
+        if len(misses) > W - len(hits):
+            with pytest.raises(ValueError):
+                oracle.warm_step(tags, used, routed, 5)
+            continue
+        assert len(found) == 1, (tags, used, routed, found)
+        t2, u2, slot, hit, nh = oracle.warm_step(tags, used, routed, 5)
+        assert nh == len(hits) == int(hit.sum())
+        assert tuple(int(slot[i]) for i, g in enumerate(routed) if g in misses) == found[0]
+        for i, g in enumerate(routed):
+            assert t2[slot[i]] == g and u2[slot[i]] == 5
+        kept = [s for s in range(W) if s not in set(slot.tolist())]
+        np.testing.assert_array_equal(t2[kept], tags[kept])
+        np.testing.assert_array_equal(u2[kept], used[kept])
+
+
+def test_warm_policy_is_textbook_lru_for_one_access_per_step():
+    """With one routed group per step the policy is the textbook LRU cache
+    (move to the most recent end on a hit; on a miss with the cache full,
+    evict the least recent): the same set of cached groups after every step."""
+    from collections import OrderedDict
+    rng = np.random.default_rng(43)
+    W = 6
+    tags, used = np.full(W, -1), np.zeros(W, dtype=int)
+    ref = OrderedDict()
+    for step in range(1, 400):
+        g = int(rng.zipf(1.5)) % 25
+        tags, used, _, hit, _ = oracle.warm_step(tags, used, [g], step)
+        if g in ref:
+            ref.move_to_end(g)
+            assert hit[0] == 1
+        else:
+            if len(ref) == W:
+                ref.popitem(last=False)
+            ref[g] = True
+            assert hit[0] == 0
+        assert set(int(t) for t in tags if t >= 0) == set(ref)
+
+
+def test_warm_policy_invariants_over_many_steps():
+    rng = np.random.default_rng(47)
+    W = 16
+    tags, used = np.full(W, -1), np.zeros(W, dtype=int)
+    seen = set()
+    for step in range(1, 80):
+        routed = [int(x) for x in rng.permutation(40)[:int(rng.integers(1, 9))]]
+        before = set(int(t) for t in tags if t >= 0)
+        tags, used, slot, hit, nh = oracle.warm_step(tags, used, routed, step)
+        assert nh == len(before & set(routed))
+        assert len(set(int(t) for t in tags if t >= 0)) == int((tags >= 0).sum())  # distinct tags
+        for i, g in enumerate(routed):
+            assert tags[slot[i]] == g and used[slot[i]] == step
+        seen |= set(routed)
+    # a cache at least as large as the universe never evicts
+    tags, used = np.full(64, -1), np.zeros(64, dtype=int)
+    seen = set()
+    for step in range(1, 60):
+        routed = [int(x) for x in rng.permutation(40)[:int(rng.integers(1, 9))]]
+        tags, used, _, _, nh = oracle.warm_step(tags, used, routed, step)
+        assert nh == len(seen & set(routed))
+        seen |= set(routed)
+        assert set(int(t) for t in tags if t >= 0) == seen
