@@ -170,7 +170,7 @@ def test_fp8_prefill_step_equals_separate_calls(pos, lq):
     those tokens) and gives the bits of the separate calls."""
     inp, st, _ = fp8_state(batch=2, context=4096, max_lq=lq)
     B, T = st.B, st.T
-    q = st.q[:, :, :lq].contiguous()
+    q = st.q[:, :, :1].repeat(1, 1, lq, 1).contiguous()  # the workload holds one query token
     pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
     kn = st.k_raw[:, :, pos:pos + lq].contiguous()
     vn = st.v_raw[:, :, pos:pos + lq].contiguous()

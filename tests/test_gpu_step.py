@@ -126,7 +126,8 @@ def test_step_position_beyond_pool_writes_nothing():
         print(f"[beyond pool] pos {bad} lq {lq}", flush=True)
         s = gh.alloc_step(st, lq)
         pos_t = torch.full((1,), bad, dtype=torch.int32, device="cuda")
-        hga.hga_prefill_step(st.cfg, 1, st.q[:, :, :lq].contiguous(), lq,
+        q = st.q[:, :, :1].repeat(1, 1, lq, 1).contiguous()  # the workload holds one token
+        hga.hga_prefill_step(st.cfg, 1, q, lq,
                              st.k_raw[:, :, :lq].contiguous(), st.v_raw[:, :, :lq].contiguous(),
                              pos_t, kp, vp, cap, stage, st.chunk_sum, st.group_sum, st.max_chunks,
                              s.sel, s.n_sel, st.max_sel, s.out, s.lse, st.ws)
