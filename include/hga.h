@@ -28,8 +28,9 @@
  *     return HGA_ERR_UNSUPPORTED (there is no slow fallback path).
  *   - A workspace serves one stream at a time.  Two calls that may run
  *     concurrently need two workspaces.
- *   - No global mutable state; the library is safe to call from several host
- *     threads on different streams.
+ *   - No global mutable state (save the per-device address of the static
+ *     scratch of hga_decode_step_noalloc, set once under a lock); the library
+ *     is safe to call from several host threads on different streams.
  */
 #ifndef HGA_H_
 #define HGA_H_
@@ -265,6 +266,32 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
                            int32_t max_chunks, int32_t* sel_groups, int32_t* n_sel,
                            int32_t max_sel, float* out, float* lse_opt, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Bytes of the static device scratch array behind hga_decode_step_noalloc. */
+#define HGA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* hga_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, results and errors, except that there is no workspace
+ * argument.  Its scratch (the routing scores and the attention partials)
+ * lives in a static device array of HGA_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on every GPU it runs on until the process ends; the array of
+ * the current device (hipGetDevice) is used, so `stream` must belong to that
+ * device.  The call allocates and frees nothing.  Every call on one GPU shares
+ * that GPU's array and nothing in it carries from one call to the next, so
+ * calls that may overlap on one GPU (concurrent streams, several host
+ * threads) race: serialise them.
+ * Errors: as hga_decode_step; HGA_ERR_WORKSPACE_TOO_SMALL when the scratch
+ * the call needs (what hga_workspace_bytes(cfg, B, max_chunks * C, 1) gives)
+ * exceeds HGA_NOALLOC_SCRATCH_BYTES (for the 32/4-head, head_dim 128 layer at
+ * 64K context that is batch 64 and beyond); HGA_ERR_HIP if the scratch address
+ * cannot be obtained. */
+hga_status hga_decode_step_noalloc(const hga_config* cfg, int32_t B, const void* q_raw,
+                                   const void* k_new, const void* v_new, const int32_t* q_pos0,
+                                   void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
+                                   float* chunk_sum, float* group_sum, int32_t max_chunks,
+                                   int32_t* sel_groups, int32_t* n_sel, int32_t max_sel,
+                                   float* out, float* lse_opt, void* stream);
 
 /* One fused chunked-prefill step: for each sequence b, the lq query tokens at
  * positions q_pos0[b] .. q_pos0[b] + lq - 1, all inside one chunk, are

@@ -38,7 +38,7 @@ EXPORTED = ("hga_validate", "hga_max_selected", "hga_workspace_bytes", "hga_work
             "hga_build_summaries", "hga_route", "hga_gather", "hga_attend", "hga_decode_step",
             "hga_prefill_step", "hga_prompt_workspace_bytes", "hga_prefill_prompt",
             "hga_attend_tiered", "hga_warm_workspace_bytes", "hga_warm_gather",
-            "hga_merge_partials", "hga_status_string", "hga_version")
+            "hga_merge_partials", "hga_status_string", "hga_version", "hga_decode_step_noalloc")
 
 
 class HgaError(RuntimeError):
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
                            ctypes.c_size_t, _P],
             "hga_decode_step": [_C, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P, _I,
                                 _P, _P, _P, ctypes.c_size_t, _P],
+            "hga_decode_step_noalloc": [_C, _I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P,
+                                        _P, _I, _P, _P, _P],
             "hga_prefill_step": [_C, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _P,
                                  _I, _P, _P, _P, ctypes.c_size_t, _P],
             "hga_prompt_workspace_bytes": [_C, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)],
@@ -246,6 +248,23 @@ def hga_decode_step(cfg, B, q_raw, k_new, v_new, q_pos0, k_pool, v_pool, pool_ca
                                  _ptr(n_sel), max_sel, _ptr(out), _ptr(lse_opt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)),
            "hga_decode_step")
+
+
+HGA_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def hga_decode_step_noalloc(cfg, B, q_raw, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap,
+                            k_stage, chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel,
+                            out, lse_opt, stream=None):
+    """hga_decode_step with the library's static per-GPU scratch instead of a
+    workspace (for callers that cannot allocate); calls on one GPU must not
+    overlap."""
+    _check(lib().hga_decode_step_noalloc(_cfg(cfg), B, _ptr(q_raw), _ptr(k_new), _ptr(v_new),
+                                         _ptr(q_pos0), _ptr(k_pool), _ptr(v_pool), pool_cap,
+                                         _ptr(k_stage), _ptr(chunk_sum), _ptr(group_sum),
+                                         max_chunks, _ptr(sel_groups), _ptr(n_sel), max_sel,
+                                         _ptr(out), _ptr(lse_opt), _stream(stream)),
+           "hga_decode_step_noalloc")
 
 
 def hga_prefill_step(cfg, B, q_raw, lq, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,

@@ -1,7 +1,10 @@
 // C ABI of the HGA hot path: host-side validation, workspace layout and
 // launches.  Every check runs before anything is enqueued; no entry point
-// allocates, frees or synchronises.
+// allocates, frees or synchronises.  The one piece of library state is the
+// per-device address of the static scratch array of hga_decode_step_noalloc.
 #include <math.h>
+
+#include <mutex>
 
 #include "hga_internal.h"
 #include "hga_gather_dev.h"
@@ -285,7 +288,8 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
                              void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
                              float* chunk_sum, float* group_sum, int32_t max_chunks,
                              int32_t* sel_groups, int32_t* n_sel, int32_t max_sel, float* out,
-                             float* lse_opt, void* ws, size_t ws_bytes, void* stream) {
+                             float* lse_opt, void* ws, size_t ws_bytes, void* stream,
+                             bool launch = true) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
   if (B <= 0 || lq <= 0 || lq > kChunk || !q_raw || !k_new || !v_new || !q_pos0 || !k_pool ||
@@ -304,6 +308,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   const size_t need_r = route_ws_bytes(k, B, max_chunks);
   const size_t need_a = attend_ws_bytes(k, B, lq, max_sel);
   if (ws_bytes < need_r || ws_bytes < need_a) return HGA_ERR_WORKSPACE_TOO_SMALL;
+  if (!launch) return HGA_OK;  // the checks only
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   RouteLaunch r;
@@ -367,6 +372,60 @@ hga_status hga_decode_step(const hga_config* cfg, int32_t B, const void* q_raw, 
   return fused_step(cfg, B, q_raw, 1, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
                     chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
                     ws_bytes, stream);
+}
+
+// Scratch of hga_decode_step_noalloc: one array per GPU (each device holds
+// its own copy from the library's load until the process ends).  Host code
+// never uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, below.
+static __device__ __align__(256) unsigned char scratch[HGA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// Device address of the scratch array on the current device.
+hga_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return HGA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return HGA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return HGA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HGA_OK;
+}
+}  // namespace
+
+hga_status hga_decode_step_noalloc(const hga_config* cfg, int32_t B, const void* q_raw,
+                                   const void* k_new, const void* v_new, const int32_t* q_pos0,
+                                   void* k_pool, void* v_pool, int32_t pool_cap, void* k_stage,
+                                   float* chunk_sum, float* group_sum, int32_t max_chunks,
+                                   int32_t* sel_groups, int32_t* n_sel, int32_t max_sel,
+                                   float* out, float* lse_opt, void* stream) {
+  // every check first, against the scratch size (a stand-in pointer: nothing
+  // is launched)
+  hga_status s = fused_step(cfg, B, q_raw, 1, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap,
+                            k_stage, chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel,
+                            out, lse_opt, reinterpret_cast<void*>(uintptr_t(256)),
+                            HGA_NOALLOC_SCRATCH_BYTES, stream, false);
+  if (s != HGA_OK) return s;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != HGA_OK) return s;
+  return fused_step(cfg, B, q_raw, 1, k_new, v_new, q_pos0, k_pool, v_pool, pool_cap, k_stage,
+                    chunk_sum, group_sum, max_chunks, sel_groups, n_sel, max_sel, out, lse_opt, ws,
+                    HGA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hga_status hga_prefill_step(const hga_config* cfg, int32_t B, const void* q_raw, int32_t lq,
