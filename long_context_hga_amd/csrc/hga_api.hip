@@ -199,7 +199,7 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
   r.sel = sel_groups;
   r.n_sel = n_sel;
   r.chunk_scores = chunk_scores_opt;
-  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+  const int max_cand = route_score_ld(k, max_chunks);  // padded score rows
   r.scores = static_cast<double*>(ws);
   r.qbar = r.scores + (size_t)B * k.lists * max_cand;
   r.B = B;
@@ -319,7 +319,7 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
   r.sel = sel_groups;
   r.n_sel = n_sel;
   r.chunk_scores = nullptr;
-  const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+  const int max_cand = route_score_ld(k, max_chunks);  // padded score rows
   r.scores = static_cast<double*>(ws);
   r.qbar = r.scores + (size_t)B * k.lists * max_cand;
   r.B = B;
@@ -500,7 +500,7 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
     r.sel = sel_groups;
     r.n_sel = n_sel;
     r.chunk_scores = nullptr;
-    const int max_cand = max_chunks > k.n_sink ? max_chunks - k.n_sink : 1;
+    const int max_cand = route_score_ld(k, max_chunks);  // padded score rows
     r.scores = static_cast<double*>(ws);
     r.qbar = r.scores + (size_t)n_virtual * k.lists * max_cand;
     int* pos = reinterpret_cast<int*>(static_cast<char*>(ws) +

@@ -65,7 +65,7 @@ __device__ __forceinline__ void fp8_append_row(const KCfg& cfg, const uint16_t* 
     const int p_first = c0 + (p - c0) / TS * TS;
     double cs, sn, cd, sd;
     rope_cs((double)p_first, w, &cs, &sn);
-    sincos(w, &sd, &cd);
+    sincos_rad(w, &sd, &cd);
     for (int i = p_first; i < p; ++i) {
       const double c2 = cs * cd - sn * sd;
       sn = sn * cd + cs * sd;
@@ -133,7 +133,7 @@ __device__ __forceinline__ void build_span(
   const int p_first = c0 + s * TS;
   double cs, sn, cd, sd;
   rope_cs((double)p_first, w, &cs, &sn);
-  sincos(w, &sd, &cd);
+  sincos_rad(w, &sd, &cd);
   double sa = 0.0, sb = 0.0;
 #pragma unroll
   for (int i = 0; i < TS; ++i) {

@@ -84,9 +84,45 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return uint16_t((u + bias) >> 16);
 }
 
+// sin and cos of x radians in fp64, |x| < 2^31, with short straight-line code
+// (it runs cold, once per workgroup, on the routing and summary paths).
+// x = k pi/2 + r with k = rint(2x / pi); r = x - k pi/2 from a two-part pi/2
+// (fused multiply-adds keep each product k p exact; the dropped third part
+// is below 1.5e-33 k), so |r| <= pi/4 to ~2e-16.  Then Taylor series in r^2:
+// sin to r^17 / 17!, cos to r^16 / 16! (truncation below 5e-17 at pi/4), and
+// the quadrant k mod 4 picks the signs and the swap.
+__device__ __forceinline__ void sincos_rad(double x, double* s, double* c) {
+  const double k = rint(x * 0.63661977236758134308);       // 2 / pi
+  double r = fma(-k, 1.5707963267948966192, x);             // pi/2 rounded to double
+  r = fma(-k, 6.123233995736766036e-17, r);                 // pi/2 minus that
+  const double r2 = r * r;
+  double ps = 1.0 / 355687428096000.0;                      // 1 / 17!
+  ps = fma(ps, r2, -1.0 / 1307674368000.0);                 // 1 / 15!
+  ps = fma(ps, r2, 1.0 / 6227020800.0);
+  ps = fma(ps, r2, -1.0 / 39916800.0);
+  ps = fma(ps, r2, 1.0 / 362880.0);
+  ps = fma(ps, r2, -1.0 / 5040.0);
+  ps = fma(ps, r2, 1.0 / 120.0);
+  ps = fma(ps, r2, -1.0 / 6.0);
+  const double sr = fma(ps * r2, r, r);
+  double pc = 1.0 / 20922789888000.0;                       // 1 / 16!
+  pc = fma(pc, r2, -1.0 / 87178291200.0);                   // 1 / 14!
+  pc = fma(pc, r2, 1.0 / 479001600.0);
+  pc = fma(pc, r2, -1.0 / 3628800.0);
+  pc = fma(pc, r2, 1.0 / 40320.0);
+  pc = fma(pc, r2, -1.0 / 720.0);
+  pc = fma(pc, r2, 1.0 / 24.0);
+  pc = fma(pc, r2, -0.5);
+  const double cr = fma(pc, r2, 1.0);
+  const int q = (int)((long long)k & 3);
+  const double ss = (q & 1) ? cr : sr, cc = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -ss : ss;
+  *c = ((q + 1) & 2) ? -cc : cc;
+}
+
 // Angle p*omega (fp64) -> (cos, sin) in fp64.
 __device__ __forceinline__ void rope_cs(double pos, double omega, double* c, double* s) {
-  sincos(pos * omega, s, c);
+  sincos_rad(pos * omega, s, c);
 }
 
 // ------------------------------------------------ cross-lane reductions

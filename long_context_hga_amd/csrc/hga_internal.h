@@ -53,6 +53,9 @@ struct StepFront {
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
                         const StepFront* front = nullptr);
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks);
+// Row stride of the level-1 scores in the route workspace; the pooled query
+// rows follow B * lists * route_score_ld doubles from the start.
+int route_score_ld(const KCfg& cfg, int max_chunks);
 size_t route_select_lds(const KCfg& cfg, int max_chunks);
 
 struct AttendLaunch {

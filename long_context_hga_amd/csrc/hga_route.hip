@@ -13,17 +13,22 @@
 //    each, one wave instruction covering 8 rows), fp64 dot, fp64 DPP sum over
 //    the 8 lanes, fp64 score to the workspace.  Tile 0 also stores qbar.
 //  route_select: one workgroup per (sequence, KV head).  Level-1 top-k over
-//    the scores, level-2 scores of the G groups of every kept chunk (all row
-//    loads in flight at once), level-2 top-k, and the ascending group list.
-//    The kernel boundary makes the first launch's scores visible to the
-//    second with plain loads.
-// Top-k (the whole workgroup for up to 1024 scores, one wave streaming from
-// LDS beyond): a 256-bin histogram between the min and max score finds the
-// bin holding the k-th largest score; every score in a higher bin is kept,
-// and the boundary bin is resolved exactly by rank counting with the order
-// (score descending, id ascending).  Scores stay
-// fp64 throughout, so the kept set equals the fp64 reference wherever its
-// score gap exceeds the error of the fp32-stored summaries.
+//    the scores, level-2 scores of the G groups of every kept chunk, level-2
+//    top-k, and the ascending group list.  The kernel boundary makes the
+//    first launch's scores visible to the second with plain loads.
+// The tile workgroups issue their query and summary-row loads before the
+// position arrives, and also store the score range of every 16 rows, so the
+// selection can bin its scores without a reduction of its own.
+// Selection (route_select_fast_kernel, up to 1024 candidates and 64 kept
+// chunks): histogram selection with member slots (hga_topk.h), two workgroup
+// barriers, each wave loading the group rows of its own kept chunks as soon as
+// its cut is known, and the level-2 choice on one wave.  Longer candidate
+// lists run route_select_kernel: a 256-bin histogram between the min and max
+// score finds the bin holding the k-th largest score, every score in a
+// higher bin is kept, and the boundary bin is resolved exactly by rank
+// counting with the order (score descending, id ascending).  Scores stay fp64
+// throughout, so the kept set equals the fp64 reference wherever its score
+// gap exceeds the error of the fp32-stored summaries.
 #include "hga_build_dev.h"
 #include "hga_topk.h"
 
@@ -36,7 +41,11 @@ struct RouteArgs {
   KCfg cfg;
   RouteLaunch r;
   int max_cand;
-  StepFront f;  // used by the workgroups with blockIdx.z == 1 of route_select
+  int score_ld;     // workspace row stride of the level-1 scores (max_cand rounded up to 4)
+  int n_tiles;      // tile workgroups per unit
+  double* ranges;   // workspace [units][n_tiles * 4] of (min, max): the level-1 scores of
+                    // rows 16 l .. 16 l + 15 of the candidates (wave l % 4 of tile l / 4)
+  StepFront f;      // used by the workgroups with blockIdx.z == 1 of route_select
 };
 
 // Position and candidate range of a unit; false if the query position is
@@ -85,19 +94,15 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const size_t qhead0 = (size_t)(b / r.nq) * c.hq + (size_t)h * c.lhg;
   const int qt0 = (b % r.nq) * r.lq;              // first query row of this chunk
   const int lq = r.lq;
-  int pos0;
-  Windows w;
-  if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) return;  // route_select reports it
-  const int n_cand = w.cand_hi - w.cand_lo;
   const int tile0 = blockIdx.x * kTile;
   constexpr bool multi = MODE == 1 || MODE == 2;
   constexpr bool pool_q = MODE != 3;    // this launch forms the pooled query
   constexpr bool score = MODE != 2;     // this launch scores its tile
-  if (tile0 >= n_cand && (blockIdx.x != 0 || !pool_q)) return;  // tile 0 stores qbar
 
-  // ---- loads: the query first, then the tile's summary rows.  Rows past
-  // the candidates are read from a clamped in-range row (so every load
-  // issues together) and ignored.
+  // ---- loads, issued before the position arrives: the query first, then
+  // the tile's summary rows (candidates start at chunk n_sink whatever the
+  // position).  Rows past the table are read from a clamped in-range row
+  // (so every load issues together) and ignored.
   //   up to S query tokens: thread (j, sl) loads pair j of every query head
   //   of this KV head for token sl;
   //   more tokens (prefill): thread (jp, sl2) loads pairs 2jp, 2jp + 1 (two
@@ -145,13 +150,19 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     if constexpr (!score) break;
-    int idx = tile0 + wave * (kTile / 4) + it * RPI + rin;
-    idx = idx < n_cand ? w.cand_lo + idx : (n_cand > 0 ? w.cand_hi - 1 : 0);
+    int row = c.n_sink + tile0 + wave * (kTile / 4) + it * RPI + rin;
+    row = row < r.max_chunks ? row : r.max_chunks - 1;
     const float4* rowp =
-        reinterpret_cast<const float4*>(r.chunk_sum + ((size_t)unit_p * r.max_chunks + idx) * D);
+        reinterpret_cast<const float4*>(r.chunk_sum + ((size_t)unit_p * r.max_chunks + row) * D);
 #pragma unroll
     for (int v = 0; v < NV; ++v) buf[it][v] = rowp[v * kLanesPerRow + sub];
   }
+
+  int pos0;
+  Windows w;
+  if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) return;  // route_select reports it
+  const int n_cand = w.cand_hi - w.cand_lo;
+  if (tile0 >= n_cand && (blockIdx.x != 0 || !pool_q)) return;  // tile 0 stores qbar
 
   // ---- pooled routing query (fp64): the query heads of this KV head are
   // summed per token and dim, the head sum of each token is rotated to the
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       for (int e = 0; e < 2; ++e) {
         const double wj = c.omega[2 * jp + e];
         rope_cs((double)(pos0 + sl2), wj, &cs[e], &sn[e]);
-        sincos((double)S2 * wj, &sd[e], &cd[e]);
+        sincos_rad((double)S2 * wj, &sd[e], &cd[e]);
       }
       for (int u0 = 0; u0 < TPT && sl2 + u0 * S2 < lq; u0 += TB) {
         if (u0 > 0) load_batch(u0);
@@ -268,7 +279,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       const int i = 4 * (v * kLanesPerRow + sub) + e;
       qv[v][e] = pool_q ? qbar[i] : r.qbar[(size_t)unit * D + i];
     }
-  double* scores = r.scores + (size_t)unit * a.max_cand;
+  double* scores = r.scores + (size_t)unit * a.score_ld;
+  double rmn = INFINITY, rmx = -INFINITY;  // this wave's score range (its 16 rows)
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int idx = tile0 + wave * (kTile / 4) + it * RPI + rin;
@@ -284,9 +296,16 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     if (sub == 0 && idx < n_cand) {
       const double sc = d * c.inv_sqrt_d;
       scores[idx] = sc;
+      rmn = fmin(rmn, sc);
+      rmx = fmax(rmx, sc);
       if (r.chunk_scores) r.chunk_scores[(size_t)unit * r.max_chunks + w.cand_lo + idx] = sc;
     }
   }
+  rmn = wave_ext_d<false>(rmn);
+  rmx = wave_ext_d<true>(rmx);
+  if (lane == 0)
+    reinterpret_cast<double2*>(a.ranges)[(size_t)unit * a.n_tiles * 4 + blockIdx.x * 4 + wave] =
+        make_double2(rmn, rmx);
 }
 
 // Token work of a fused step for unit (h, b), on one workgroup: the raw
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
-  const double* scores = r.scores + (size_t)unit * a.max_cand;
+  const double* scores = r.scores + (size_t)unit * a.score_ld;
   constexpr int SPT = 4;  // scores per thread in flight
   double v4[SPT];
 #pragma unroll
@@ -503,16 +522,325 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   if (tid == 0) r.n_sel[unit] = n_sel;
 }
 
+// Selection for up to kFastMaxCand candidates and kFastMaxKept level-1
+// chunks, with two workgroup barriers.  Thread t owns candidates 4t..4t+3 (so
+// wave w owns a contiguous quarter of them).
+//  1. Every load goes out first (scores, the per-wave score ranges that
+//     route_tiles wrote, qbar, position); the level-1 counts are cleared and
+//     a barrier passes while the loads are in flight.
+//  2. Bins between the global min and max (from the ranges), counts and
+//     member slots (sel_add), scores to LDS; barrier.
+//  3. Every wave finds the cut (sel_cut), keeps its candidates above it and
+//     the boundary members ranked within the need, lists its kept chunks in
+//     order (ballot), and at once loads and scores the G group rows of its
+//     own kept chunks into its own region (no wait for the other waves).
+//     Waves 1..3 have already written the sink, local and current groups.
+//  4. After a barrier, wave 0 selects the routed groups over the regions
+//     (concatenated, they run in ascending group order), with the same
+//     histogram on a wave of its own, and writes them to the list.
+// A boundary bin with more members than slots (rare) is ranked among all of
+// its members: level 1 collects them with one more barrier (taken by the
+// whole workgroup, as the counts are shared), level 2 within wave 0.
+constexpr int kFastMaxCand = 1024;
+constexpr int kFastMaxKept = 64;  // level-1 chunks kept: level 2 ranks <= 256 groups
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
+  constexpr int NV = D / 32;
+  constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
+  constexpr int U = 8;                     // level-2 row passes in flight per wave
+  __shared__ int s_fine[kSelBins];
+  __shared__ int s_coarse[kSelCoarse];
+  __shared__ int s_slot[kSelBins * kSelSlots];
+  __shared__ __align__(16) double s_vals[kFastMaxCand];  // level-1 scores; token-plane scratch
+  __shared__ int s_kl[4][KPW];             // kept candidate indices of each wave, ascending
+  __shared__ double s_l2[4][kGroups * KPW];  // level-2 scores of each wave's rows
+  __shared__ int s_n2[4];
+  __shared__ int s_nbl;                    // overflowed boundary members collected
+  __shared__ int s_bl[kFastMaxCand];
+
+  const KCfg& c = a.cfg;
+  const RouteLaunch& r = a.r;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  if (blockIdx.z == 1) {  // a fused step's token work, once per KV head
+    if (h % c.kvdiv == 0) step_front<D, BF16>(a, h / c.kvdiv, b, s_vals);
+    return;
+  }
+  const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
+  const int unit_p = (b / r.nq) * c.hkv + h / c.kvdiv;  // summaries: pool sequence, KV head
+
+  // ---- 1. loads (clamped into the workspace rows; unused entries ignored)
+  const int sub = lane % kLanesPerRow, g8 = lane / kLanesPerRow;
+  double qv[NV][4];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+  const double* scores = r.scores + (size_t)unit * a.score_ld;
+  double x[4];
+  {
+    const int i0 = 4 * tid < a.score_ld - 3 ? 4 * tid : a.score_ld - 4;  // score_ld: 4 k >= 4
+    const double2 p0 = *reinterpret_cast<const double2*>(scores + i0);
+    const double2 p1 = *reinterpret_cast<const double2*>(scores + i0 + 2);
+    x[0] = p0.x; x[1] = p0.y; x[2] = p1.x; x[3] = p1.y;
+  }
+  const int n_rng = a.n_tiles * 4;
+  const double2 rng = reinterpret_cast<const double2*>(a.ranges)[(size_t)unit * n_rng +
+                                                                 (lane < n_rng ? lane : n_rng - 1)];
+  const SelHist hh{s_fine, s_coarse, s_slot};
+  sel_clear(hh, tid, 256);
+  if (tid == 0) s_nbl = 0;
+  __syncthreads();
+
+  int pos0;
+  Windows w;
+  if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) {
+    if (tid == 0) r.n_sel[unit] = -1;
+    return;
+  }
+  const int n_cand = w.cand_hi - w.cand_lo;
+  const int ct = pos0 / kChunk;
+  const int k1 = c.topk_c < n_cand ? c.topk_c : n_cand;
+  const int k2 = c.topk_g < k1 * kGroups ? c.topk_g : k1 * kGroups;
+  const int last = pos0 + r.lq - 1;
+  const int n_head = w.sink_end * kGroups;
+  const int n_tail = (ct - w.local_begin) * kGroups + (last / kGroupTokens - ct * kGroups + 1);
+  int* out = r.sel + (size_t)unit * r.max_sel;
+  if (wave != 0) {  // the window groups: sink | (routed) | local | current
+    for (int i = tid - 64; i < n_head + n_tail; i += 192) {
+      const bool head = i < n_head;
+      out[head ? i : i + k2] = head ? i : w.local_begin * kGroups + (i - n_head);
+    }
+  }
+
+  // ---- 2. level-1 bins and counts
+  const bool all1 = k1 >= n_cand;  // every candidate kept (uniform)
+  int bin[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bin[e] = -1;
+  if (!all1) {
+    // range of the scores: entry l covers rows 16 l .. 16 l + 15 of the tiles
+    const bool rv = lane < n_rng && 16 * lane < n_cand;
+    const double mn = wave_ext_d<false>(rv ? rng.x : INFINITY);
+    const double mx = wave_ext_d<true>(rv ? rng.y : -INFINITY);
+    const double scale = mx > mn ? (double)kSelBins / (mx - mn) : 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * tid + e;
+      if (i < n_cand) {
+        bin[e] = topk_bin_n<kSelBins>(x[e], mn, scale);
+        sel_add(hh, bin[e], i);
+      }
+    }
+    if (4 * tid < kFastMaxCand) {
+      *reinterpret_cast<double2*>(&s_vals[4 * tid]) = make_double2(x[0], x[1]);
+      *reinterpret_cast<double2*>(&s_vals[4 * tid + 2]) = make_double2(x[2], x[3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. the cut, this wave's kept chunks, their group rows
+  uint32_t keep = 0;
+  if (all1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (4 * tid + e < n_cand ? 1u : 0u) << e;
+  } else if (k1 > 0) {
+    int bs, need, nb;
+    sel_cut(hh, k1, &bs, &need, &nb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs || (bin[e] == bs && nb == need) ? 1u : 0u) << e;
+    if (nb != need) {  // uniform: the boundary bin is split
+      if (nb <= kSelSlots) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (bin[e] == bs && sel_rank_slots(hh, bs, nb, 4 * tid + e, x[e], s_vals) < need)
+            keep |= 1u << e;
+      } else {  // more members than slots: collect them all (the whole workgroup)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (bin[e] == bs) s_bl[atomicAdd(&s_nbl, 1)] = 4 * tid + e;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (bin[e] != bs) continue;
+          int rk = 0;
+          for (int u = 0; u < nb; ++u) {
+            const int m = s_bl[u];
+            const double v = s_vals[m];
+            rk += (v > x[e]) || (v == x[e] && m < 4 * tid + e);
+          }
+          if (rk < need) keep |= 1u << e;
+        }
+      }
+    }
+  }
+  // this wave's kept chunks in candidate order
+  const int kc = __popc(keep);
+  const int kincl = wave_incl_scan(kc);
+  const int kw = __builtin_amdgcn_readlane(kincl, 63);  // kept by this wave (<= k1 <= KPW)
+  {
+    int o = kincl - kc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((keep >> e) & 1u) s_kl[wave][o++] = 4 * tid + e;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // group rows: 8 lanes per 512-byte row, 8 rows per pass, U passes in flight
+  const int n2w = kw * kGroups;
+  double mn2 = INFINITY, mx2 = -INFINITY;
+  for (int base = 0; base < n2w; base += 8 * U) {
+    float4 gb[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int i = base + 8 * u + g8;
+      i = i < n2w ? i : n2w - 1;  // clamped: every load issues, extras ignored
+      const int gid = (w.cand_lo + s_kl[wave][i / kGroups]) * kGroups + i % kGroups;
+      const float4* rowp = reinterpret_cast<const float4*>(
+          r.group_sum + ((size_t)unit_p * r.max_chunks * kGroups + gid) * D);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) gb[u][v] = rowp[v * kLanesPerRow + sub];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + 8 * u + g8;
+      double d = 0.0;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        d = fma((double)gb[u][v].x, qv[v][0], d);
+        d = fma((double)gb[u][v].y, qv[v][1], d);
+        d = fma((double)gb[u][v].z, qv[v][2], d);
+        d = fma((double)gb[u][v].w, qv[v][3], d);
+      }
+      d = group8_sum_d(d) * c.inv_sqrt_d;
+      if (sub == 0 && i < n2w) s_l2[wave][i] = d;
+    }
+  }
+  if (lane == 0) s_n2[wave] = n2w;
+  __syncthreads();
+
+  // ---- 4. level 2 on wave 0: element e of the concatenated regions (e =
+  // 64 j + lane); its region, and with it its group id, from the counts
+  if (wave != 0) return;
+  const int c0n = s_n2[0], c1n = s_n2[1], c2n = s_n2[2], c3n = s_n2[3];
+  const int n2 = c0n + c1n + c2n + c3n;  // = k1 * G
+  double y[4];
+  int gid[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = 64 * j + lane;
+    int rg = 0;
+    if (e >= c0n) { e -= c0n; rg = 1;
+      if (e >= c1n) { e -= c1n; rg = 2;
+        if (e >= c2n) { e -= c2n; rg = 3; } } }
+    const bool ok = 64 * j + lane < n2;
+    const int ee = ok ? e : 0;
+    y[j] = ok ? s_l2[rg][ee] : 0.0;
+    gid[j] = ok ? (w.cand_lo + s_kl[rg][ee / kGroups]) * kGroups + ee % kGroups : 0;
+  }
+  uint32_t keep2 = 0;
+  if (k2 >= n2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) keep2 |= (64 * j + lane < n2 ? 1u : 0u) << j;
+  } else if (k2 > 0) {
+    // the level-1 counts are free now (every wave is past its cut)
+    double mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (64 * j + lane < n2) {
+        mn = fmin(mn, y[j]);
+        mx = fmax(mx, y[j]);
+      }
+    mn = wave_ext_d<false>(mn);
+    mx = wave_ext_d<true>(mx);
+    const double scale = mx > mn ? (double)kSelBins / (mx - mn) : 0.0;
+    sel_clear(hh, lane, 64);
+    __builtin_amdgcn_wave_barrier();
+    int bin2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bin2[j] = -1;
+      if (64 * j + lane < n2) {
+        bin2[j] = topk_bin_n<kSelBins>(y[j], mn, scale);
+        sel_add(hh, bin2[j], 64 * j + lane);
+        s_vals[64 * j + lane] = y[j];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    int bs, need, nb;
+    sel_cut(hh, k2, &bs, &need, &nb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      keep2 |= (bin2[j] > bs || (bin2[j] == bs && nb == need) ? 1u : 0u) << j;
+    if (nb != need) {
+      if (nb <= kSelSlots) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (bin2[j] == bs && sel_rank_slots(hh, bs, nb, 64 * j + lane, y[j], s_vals) < need)
+            keep2 |= 1u << j;
+      } else {  // all members, in element order, within the wave
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned long long m = __ballot(bin2[j] == bs);
+          if (bin2[j] == bs) s_bl[cnt + lanes_below(m)] = 64 * j + lane;
+          cnt += __popcll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (bin2[j] != bs) continue;
+          int rk = 0;
+          for (int u = 0; u < nb; ++u) {
+            const int m = s_bl[u];
+            const double v = s_vals[m];
+            rk += (v > y[j]) || (v == y[j] && m < 64 * j + lane);
+          }
+          if (rk < need) keep2 |= 1u << j;
+        }
+      }
+    }
+  }
+  // routed groups in element order = ascending group id
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool kp = (keep2 >> j) & 1u;
+    const unsigned long long m = __ballot(kp);
+    if (kp) out[n_head + cnt + lanes_below(m)] = gid[j];
+    cnt += __popcll(m);
+  }
+  if (lane == 0) r.n_sel[unit] = n_head + k2 + n_tail;
+}
+
+// The fast selection applies when every unit has at most kFastMaxCand
+// candidates and level 1 keeps at most kFastMaxKept chunks.
+static bool fast_select(const KCfg& cfg, int max_cand) {
+  return max_cand <= kFastMaxCand && cfg.topk_c <= kFastMaxKept;
+}
+
 static int max_cand_of(const KCfg& cfg, int max_chunks) {
   return max_chunks > cfg.n_sink ? max_chunks - cfg.n_sink : 1;
 }
 
+// Workspace per unit: level-1 scores (row stride rounded up to 4), the pooled
+// query, and the score range of every 16 rows (wave) of every tile.
+static int score_ld_of(int max_cand) { return (max_cand + 3) / 4 * 4; }
+static int n_tiles_of(int max_cand) { return (max_cand + kTile - 1) / kTile; }
+
+int route_score_ld(const KCfg& cfg, int max_chunks) {
+  return score_ld_of(max_cand_of(cfg, max_chunks));
+}
+
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks) {
-  return (size_t)B * cfg.lists * (max_cand_of(cfg, max_chunks) + cfg.d) * sizeof(double);
+  const int mc = max_cand_of(cfg, max_chunks);
+  return (size_t)B * cfg.lists * (score_ld_of(mc) + cfg.d + 8 * n_tiles_of(mc)) * sizeof(double);
 }
 
 size_t route_select_lds(const KCfg& cfg, int max_chunks) {
   const int max_cand = max_cand_of(cfg, max_chunks);
+  if (fast_select(cfg, max_cand)) return 0;  // static LDS only
   const int n2 = cfg.topk_c * kGroups;
   const size_t nmax = (size_t)(max_cand > n2 ? max_cand : n2);
   return nmax * (sizeof(double) + 3 * sizeof(int)) + (size_t)n2 * sizeof(int);
@@ -537,8 +865,13 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   a.cfg = cfg;
   a.r = r;
   a.max_cand = max_cand_of(cfg, r.max_chunks);
+  a.score_ld = score_ld_of(a.max_cand);
+  a.n_tiles = n_tiles_of(a.max_cand);
+  // the workspace holds the scores with stride score_ld, then qbar, then the
+  // ranges (the callers place qbar at B * lists * score_ld)
+  a.ranges = r.qbar + (size_t)r.B * cfg.lists * cfg.d;
   if (front) a.f = *front;
-  const int n_tiles = (a.max_cand + kTile - 1) / kTile;
+  const int n_tiles = a.n_tiles;
   size_t lds = route_select_lds(cfg, r.max_chunks);
   const size_t front_lds = (size_t)256 * 2 * sizeof(double);  // build_span scratch: S*P*2 doubles
   if (front && lds < front_lds) lds = front_lds;
@@ -546,21 +879,26 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   dim3 sgrid(cfg.lists, r.B, front ? 2 : 1);
   const bool bf = cfg.dtype == HGA_BF16;
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
+  const bool fast = fast_select(cfg, a.max_cand);
   if (cfg.d == 128) {
     if (bf) {
       launch_tiles<128, true>(multi, r.pool_once, grid, st, a);
-      hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
+      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<128, true>), sgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
     } else {
       launch_tiles<128, false>(multi, r.pool_once, grid, st, a);
-      hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
+      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<128, false>), sgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
     }
   } else {
     if (bf) {
       launch_tiles<64, true>(multi, r.pool_once, grid, st, a);
-      hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
+      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<64, true>), sgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
     } else {
       launch_tiles<64, false>(multi, r.pool_once, grid, st, a);
-      hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
+      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<64, false>), sgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
     }
   }
   return hipGetLastError();

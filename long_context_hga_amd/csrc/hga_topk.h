@@ -270,4 +270,92 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
   return k;
 }
 
+// ---------------------------------------------------------------------------
+// Histogram selection with member slots (the routing's fast selection).
+// Scores are binned into kSelBins fine bins between their min and max (a
+// monotone map), counted in LDS together with kSelBins / 16 coarse bins, and
+// each fine bin records the indices of its first kSelSlots members.  The bin
+// bs of the k-th best is found by one wave in two short scans (the coarse bin
+// holding it, then its 16 fine bins); every element in a higher bin is kept,
+// and when bs holds more members than the `need` it contributes, they are
+// ranked exactly (score descending, index ascending) among the members its
+// slots list (or, when the bin overflowed its slots, among all members).
+constexpr int kSelBins = 1024;
+constexpr int kSelCoarse = kSelBins / 16;
+constexpr int kSelSlots = 4;
+
+struct SelHist {
+  int* fine;    // kSelBins counts
+  int* coarse;  // kSelCoarse counts
+  int* slot;    // kSelBins * kSelSlots member indices
+};
+
+template <int NB>
+__device__ __forceinline__ int topk_bin_n(double x, double mn, double scale) {
+  const double f = (x - mn) * scale;
+  const int b = f >= 0.0 ? (int)f : 0;  // monotone in x; NaN -> 0
+  return b > NB - 1 ? NB - 1 : b;
+}
+
+// Zeroes the counts; threads t = 0, step, 2 step, ... of the caller share it.
+__device__ __forceinline__ void sel_clear(const SelHist& h, int t, int step) {
+  for (int i = t; i < kSelBins; i += step) h.fine[i] = 0;
+  for (int i = t; i < kSelCoarse; i += step) h.coarse[i] = 0;
+}
+
+// Counts element idx in bin b and records it while the bin has free slots.
+__device__ __forceinline__ void sel_add(const SelHist& h, int b, int idx) {
+  const int at = atomicAdd(&h.fine[b], 1);
+  atomicAdd(&h.coarse[b >> 4], 1);
+  if (at < kSelSlots) h.slot[b * kSelSlots + at] = idx;
+}
+
+// The bin bs of the k-th best (count(bins > bs) < k <= count(bins >= bs)),
+// need = k - count(bins > bs) and nb = count(bs), from complete counts; run
+// by a whole wave (every lane gets the result).  1 <= k <= total.
+__device__ __forceinline__ void sel_cut(const SelHist& h, int k, int* bs, int* need, int* nb) {
+  static_assert(kSelCoarse == 64, "one coarse bin per lane");
+  const int lane = threadIdx.x & 63;
+  const int cc = h.coarse[lane];
+  const int pre = wave_incl_scan(cc);
+  const int total = __builtin_amdgcn_readlane(pre, 63);
+  const int suf = total - pre + cc;  // count in coarse bins >= lane
+  const int above = suf - cc;        // count in coarse bins > lane
+  const int C = __ffsll((long long)__ballot(above < k && k <= suf)) - 1;
+  const int above_c = __builtin_amdgcn_readlane(above, C);
+  // the 16 fine bins of C, highest first: lane l of each 16-lane row holds
+  // bin 16 C + 15 - l; a row-local inclusive scan counts bins >= it in C
+  const int fl = lane & 15;
+  const int fc = h.fine[16 * C + 15 - fl];
+  int f = fc;
+  f += __builtin_amdgcn_update_dpp(0, f, 0x111, 0xF, 0xF, true);
+  f += __builtin_amdgcn_update_dpp(0, f, 0x112, 0xF, 0xF, true);
+  f += __builtin_amdgcn_update_dpp(0, f, 0x114, 0xF, 0xF, true);
+  f += __builtin_amdgcn_update_dpp(0, f, 0x118, 0xF, 0xF, true);
+  const int L = __ffsll((long long)(__ballot(above_c + f >= k) & 0xFFFFull)) - 1;
+  const int fL = __builtin_amdgcn_readlane(f, L), cL = __builtin_amdgcn_readlane(fc, L);
+  *bs = 16 * C + 15 - L;
+  *need = k - (above_c + fL - cL);
+  *nb = cL;
+}
+
+// Rank of element (i, x) of the boundary bin bs among its slot-listed
+// members (valid when nb <= kSelSlots): the members scoring higher, or equal
+// with a lower index.  vals: the scores by element index (LDS).
+__device__ __forceinline__ int sel_rank_slots(const SelHist& h, int bs, int nb, int i, double x,
+                                              const double* vals) {
+  int m[kSelSlots];
+#pragma unroll
+  for (int u = 0; u < kSelSlots; ++u) m[u] = h.slot[bs * kSelSlots + u];
+  int r = 0;
+#pragma unroll
+  for (int u = 0; u < kSelSlots; ++u) {
+    if (u < nb) {
+      const double v = vals[m[u]];
+      r += (v > x) || (v == x && m[u] < i);
+    }
+  }
+  return r;
+}
+
 }  // namespace hga
