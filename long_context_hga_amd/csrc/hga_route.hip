@@ -523,24 +523,22 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 }
 
 // Selection for up to kFastMaxCand candidates and kFastMaxKept level-1
-// chunks, with two workgroup barriers.  Thread t owns candidates 4t..4t+3 (so
-// wave w owns a contiguous quarter of them).
+// chunks.  Thread t owns candidates 4t..4t+3 (so wave w owns a contiguous
+// quarter of them).
 //  1. Every load goes out first (scores, the per-wave score ranges that
-//     route_tiles wrote, qbar, position); the level-1 counts are cleared and
-//     a barrier passes while the loads are in flight.
-//  2. Bins between the global min and max (from the ranges), counts and
-//     member slots (sel_add), scores to LDS; barrier.
-//  3. Every wave finds the cut (sel_cut), keeps its candidates above it and
-//     the boundary members ranked within the need, lists its kept chunks in
-//     order (ballot), and at once loads and scores the G group rows of its
-//     own kept chunks into its own region (no wait for the other waves).
-//     Waves 1..3 have already written the sink, local and current groups.
-//  4. After a barrier, wave 0 selects the routed groups over the regions
-//     (concatenated, they run in ascending group order), with the same
-//     histogram on a wave of its own, and writes them to the list.
-// A boundary bin with more members than slots (rare) is ranked among all of
-// its members: level 1 collects them with one more barrier (taken by the
-// whole workgroup, as the counts are shared), level 2 within wave 0.
+//     route_tiles wrote, qbar, position); both levels' counts are cleared and
+//     a barrier passes while the loads are in flight.  Waves 1..3 write the
+//     sink, local and current groups of the list (their slots follow from the
+//     position and the budgets alone).
+//  2. Level 1 (sel_level, all threads): bins between the min and max of the
+//     ranges, counts and member slots, a barrier, then in every wave the cut
+//     and the boundary ranking.
+//  3. Each wave lists its kept chunks in order (ballot) and at once loads and
+//     scores the G group rows of its own kept chunks into its own region, with
+//     the range of those scores; barrier.
+//  4. Level 2 (sel_level again): thread t takes element t of the regions
+//     concatenated (ascending group order); the kept groups are written in
+//     that order after one more barrier for the per-wave counts.
 constexpr int kFastMaxCand = 1024;
 constexpr int kFastMaxKept = 64;  // level-1 chunks kept: level 2 ranks <= 256 groups
 
@@ -549,14 +547,16 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
   constexpr int U = 8;                     // level-2 row passes in flight per wave
-  __shared__ int s_fine[kSelBins];
-  __shared__ int s_coarse[kSelCoarse];
-  __shared__ int s_slot[kSelBins * kSelSlots];
-  __shared__ __align__(16) double s_vals[kFastMaxCand];  // level-1 scores; token-plane scratch
+  __shared__ int s_fine[kSelBins], s_fine2[kSelBins];
+  __shared__ int s_coarse[kSelCoarse], s_coarse2[kSelCoarse];
+  __shared__ int s_slot[kSelBins * kSelSlots];  // both levels (level 2 starts after a barrier)
+  __shared__ __align__(16) double s_vals[kFastMaxCand];  // scores by element; token-plane scratch
   __shared__ int s_kl[4][KPW];             // kept candidate indices of each wave, ascending
   __shared__ double s_l2[4][kGroups * KPW];  // level-2 scores of each wave's rows
   __shared__ int s_n2[4];
-  __shared__ int s_nbl;                    // overflowed boundary members collected
+  __shared__ double s_r2[8];               // level-2 score range of each wave (min, max)
+  __shared__ int s_k2[4];                  // level-2 groups kept by each wave
+  __shared__ int s_nbl[2];                 // overflowed boundary members collected
   __shared__ int s_bl[kFastMaxCand];
 
   const KCfg& c = a.cfg;
@@ -589,9 +589,10 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   const int n_rng = a.n_tiles * 4;
   const double2 rng = reinterpret_cast<const double2*>(a.ranges)[(size_t)unit * n_rng +
                                                                  (lane < n_rng ? lane : n_rng - 1)];
-  const SelHist hh{s_fine, s_coarse, s_slot};
-  sel_clear(hh, tid, 256);
-  if (tid == 0) s_nbl = 0;
+  const SelHist h1{s_fine, s_coarse, s_slot}, h2{s_fine2, s_coarse2, s_slot};
+  sel_clear(h1, tid, 256);
+  sel_clear(h2, tid, 256);
+  if (tid < 2) s_nbl[tid] = 0;
   __syncthreads();
 
   int pos0;
@@ -615,68 +616,22 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
     }
   }
 
-  // ---- 2. level-1 bins and counts
-  const bool all1 = k1 >= n_cand;  // every candidate kept (uniform)
-  int bin[4];
+  // ---- 2. level 1
+  uint32_t keep = 0;
+  if (k1 >= n_cand) {  // every candidate kept (uniform)
 #pragma unroll
-  for (int e = 0; e < 4; ++e) bin[e] = -1;
-  if (!all1) {
+    for (int e = 0; e < 4; ++e) keep |= (4 * tid + e < n_cand ? 1u : 0u) << e;
+  } else if (k1 > 0) {
     // range of the scores: entry l covers rows 16 l .. 16 l + 15 of the tiles
     const bool rv = lane < n_rng && 16 * lane < n_cand;
     const double mn = wave_ext_d<false>(rv ? rng.x : INFINITY);
     const double mx = wave_ext_d<true>(rv ? rng.y : -INFINITY);
-    const double scale = mx > mn ? (double)kSelBins / (mx - mn) : 0.0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * tid + e;
-      if (i < n_cand) {
-        bin[e] = topk_bin_n<kSelBins>(x[e], mn, scale);
-        sel_add(hh, bin[e], i);
-      }
-    }
-    if (4 * tid < kFastMaxCand) {
-      *reinterpret_cast<double2*>(&s_vals[4 * tid]) = make_double2(x[0], x[1]);
-      *reinterpret_cast<double2*>(&s_vals[4 * tid + 2]) = make_double2(x[2], x[3]);
-    }
+    auto idx = [&](int e) { return 4 * tid + e < n_cand ? 4 * tid + e : -1; };
+    keep = sel_level(x[0], x[1], x[2], x[3], idx(0), idx(1), idx(2), idx(3), k1, mn, mx, s_fine,
+                     s_coarse, s_slot, s_vals, s_bl, &s_nbl[0]);
   }
-  __syncthreads();
 
-  // ---- 3. the cut, this wave's kept chunks, their group rows
-  uint32_t keep = 0;
-  if (all1) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keep |= (4 * tid + e < n_cand ? 1u : 0u) << e;
-  } else if (k1 > 0) {
-    int bs, need, nb;
-    sel_cut(hh, k1, &bs, &need, &nb);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs || (bin[e] == bs && nb == need) ? 1u : 0u) << e;
-    if (nb != need) {  // uniform: the boundary bin is split
-      if (nb <= kSelSlots) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (bin[e] == bs && sel_rank_slots(hh, bs, nb, 4 * tid + e, x[e], s_vals) < need)
-            keep |= 1u << e;
-      } else {  // more members than slots: collect them all (the whole workgroup)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (bin[e] == bs) s_bl[atomicAdd(&s_nbl, 1)] = 4 * tid + e;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (bin[e] != bs) continue;
-          int rk = 0;
-          for (int u = 0; u < nb; ++u) {
-            const int m = s_bl[u];
-            const double v = s_vals[m];
-            rk += (v > x[e]) || (v == x[e] && m < 4 * tid + e);
-          }
-          if (rk < need) keep |= 1u << e;
-        }
-      }
-    }
-  }
-  // this wave's kept chunks in candidate order
+  // ---- 3. this wave's kept chunks in candidate order, their group rows
   const int kc = __popc(keep);
   const int kincl = wave_incl_scan(kc);
   const int kw = __builtin_amdgcn_readlane(kincl, 63);  // kept by this wave (<= k1 <= KPW)
@@ -714,104 +669,54 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
         d = fma((double)gb[u][v].w, qv[v][3], d);
       }
       d = group8_sum_d(d) * c.inv_sqrt_d;
-      if (sub == 0 && i < n2w) s_l2[wave][i] = d;
+      if (sub == 0 && i < n2w) {
+        s_l2[wave][i] = d;
+        mn2 = fmin(mn2, d);
+        mx2 = fmax(mx2, d);
+      }
     }
   }
-  if (lane == 0) s_n2[wave] = n2w;
+  mn2 = wave_ext_d<false>(mn2);
+  mx2 = wave_ext_d<true>(mx2);
+  if (lane == 0) {
+    s_n2[wave] = n2w;
+    s_r2[wave] = mn2;
+    s_r2[4 + wave] = mx2;
+  }
   __syncthreads();
 
-  // ---- 4. level 2 on wave 0: element e of the concatenated regions (e =
-  // 64 j + lane); its region, and with it its group id, from the counts
-  if (wave != 0) return;
-  const int c0n = s_n2[0], c1n = s_n2[1], c2n = s_n2[2], c3n = s_n2[3];
-  const int n2 = c0n + c1n + c2n + c3n;  // = k1 * G
-  double y[4];
-  int gid[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int e = 64 * j + lane;
-    int rg = 0;
+  // ---- 4. level 2: thread t takes element t of the concatenated regions
+  const int c0n = s_n2[0], c1n = s_n2[1], c2n = s_n2[2];
+  const int n2 = c0n + c1n + c2n + s_n2[3];  // = k1 * G <= 256
+  double y = 0.0;
+  int gid = 0;
+  if (tid < n2) {
+    int e = tid, rg = 0;
     if (e >= c0n) { e -= c0n; rg = 1;
       if (e >= c1n) { e -= c1n; rg = 2;
         if (e >= c2n) { e -= c2n; rg = 3; } } }
-    const bool ok = 64 * j + lane < n2;
-    const int ee = ok ? e : 0;
-    y[j] = ok ? s_l2[rg][ee] : 0.0;
-    gid[j] = ok ? (w.cand_lo + s_kl[rg][ee / kGroups]) * kGroups + ee % kGroups : 0;
+    y = s_l2[rg][e];
+    gid = (w.cand_lo + s_kl[rg][e / kGroups]) * kGroups + e % kGroups;
   }
-  uint32_t keep2 = 0;
-  if (k2 >= n2) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) keep2 |= (64 * j + lane < n2 ? 1u : 0u) << j;
-  } else if (k2 > 0) {
-    // the level-1 counts are free now (every wave is past its cut)
-    double mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (64 * j + lane < n2) {
-        mn = fmin(mn, y[j]);
-        mx = fmax(mx, y[j]);
-      }
-    mn = wave_ext_d<false>(mn);
-    mx = wave_ext_d<true>(mx);
-    const double scale = mx > mn ? (double)kSelBins / (mx - mn) : 0.0;
-    sel_clear(hh, lane, 64);
-    __builtin_amdgcn_wave_barrier();
-    int bin2[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bin2[j] = -1;
-      if (64 * j + lane < n2) {
-        bin2[j] = topk_bin_n<kSelBins>(y[j], mn, scale);
-        sel_add(hh, bin2[j], 64 * j + lane);
-        s_vals[64 * j + lane] = y[j];
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    int bs, need, nb;
-    sel_cut(hh, k2, &bs, &need, &nb);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      keep2 |= (bin2[j] > bs || (bin2[j] == bs && nb == need) ? 1u : 0u) << j;
-    if (nb != need) {
-      if (nb <= kSelSlots) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (bin2[j] == bs && sel_rank_slots(hh, bs, nb, 64 * j + lane, y[j], s_vals) < need)
-            keep2 |= 1u << j;
-      } else {  // all members, in element order, within the wave
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned long long m = __ballot(bin2[j] == bs);
-          if (bin2[j] == bs) s_bl[cnt + lanes_below(m)] = 64 * j + lane;
-          cnt += __popcll(m);
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (bin2[j] != bs) continue;
-          int rk = 0;
-          for (int u = 0; u < nb; ++u) {
-            const int m = s_bl[u];
-            const double v = s_vals[m];
-            rk += (v > y[j]) || (v == y[j] && m < 64 * j + lane);
-          }
-          if (rk < need) keep2 |= 1u << j;
-        }
-      }
-    }
+  bool kept2 = tid < n2;
+  if (k2 < n2 && k2 > 0) {  // uniform
+    const double mn = fmin(fmin(s_r2[0], s_r2[1]), fmin(s_r2[2], s_r2[3]));
+    const double mx = fmax(fmax(s_r2[4], s_r2[5]), fmax(s_r2[6], s_r2[7]));
+    kept2 = sel_level(y, 0.0, 0.0, 0.0, tid < n2 ? tid : -1, -1, -1, -1, k2, mn, mx, s_fine2,
+                      s_coarse2, s_slot, s_vals, s_bl, &s_nbl[1]) & 1u;
+  } else if (k2 <= 0) {
+    kept2 = false;
   }
-  // routed groups in element order = ascending group id
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool kp = (keep2 >> j) & 1u;
-    const unsigned long long m = __ballot(kp);
-    if (kp) out[n_head + cnt + lanes_below(m)] = gid[j];
-    cnt += __popcll(m);
+  // the kept groups in element order = ascending group id
+  const unsigned long long m = __ballot(kept2);
+  if (lane == 0) s_k2[wave] = __popcll(m);
+  __syncthreads();
+  if (kept2) {
+    int off = lanes_below(m);
+    for (int v = 0; v < wave; ++v) off += s_k2[v];
+    out[n_head + off] = gid;
   }
-  if (lane == 0) r.n_sel[unit] = n_head + k2 + n_tail;
+  if (tid == 0) r.n_sel[unit] = n_head + k2 + n_tail;
 }
 
 // The fast selection applies when every unit has at most kFastMaxCand

@@ -358,4 +358,64 @@ __device__ __forceinline__ int sel_rank_slots(const SelHist& h, int bs, int nb, 
   return r;
 }
 
+// One level of the selection, run by all 256 threads of the workgroup (the
+// routing calls it for both levels, so the second call runs from a warm
+// instruction cache).  Thread t holds up to 4 elements: x[e] with element
+// index id[e] (< 0: no element).  Of the n elements the k best are kept
+// (1 <= k < n); mn / mx bound the scores.  The counts (fine, coarse) are zero
+// on entry (the caller clears them a barrier earlier); slot receives the
+// member slots, vals (indexed by element) the scores for the boundary
+// ranking; bl / nbl (nbl zero on entry) collect the members of a boundary
+// bin that overflowed its slots.  Returns bit e set iff element e is kept.
+__device__ __noinline__ uint32_t sel_level(double x0, double x1, double x2, double x3, int i0,
+                                           int i1, int i2, int i3, int k, double mn, double mx,
+                                           int* fine, int* coarse, int* slot, double* vals,
+                                           int* bl, int* nbl) {
+  const SelHist h{fine, coarse, slot};  // by pointer: a struct argument would go through scratch
+  const double x[4] = {x0, x1, x2, x3};
+  const int id[4] = {i0, i1, i2, i3};
+  // a monotone map to bins (the scale needs no more than fp32)
+  const double scale = mx > mn ? (double)((float)kSelBins / (float)(mx - mn)) : 0.0;
+  int bin[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bin[e] = -1;
+    if (id[e] >= 0) {
+      bin[e] = topk_bin_n<kSelBins>(x[e], mn, scale);
+      sel_add(h, bin[e], id[e]);
+      vals[id[e]] = x[e];
+    }
+  }
+  __syncthreads();
+  int bs, need, nb;
+  sel_cut(h, k, &bs, &need, &nb);
+  uint32_t keep = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs || (bin[e] == bs && nb == need) ? 1u : 0u) << e;
+  if (nb == need) return keep;  // uniform
+  if (nb <= kSelSlots) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (bin[e] == bs && sel_rank_slots(h, bs, nb, id[e], x[e], vals) < need) keep |= 1u << e;
+    return keep;
+  }
+  // more members than slots (uniform): collect them all, then rank
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (bin[e] == bs) bl[atomicAdd(nbl, 1)] = id[e];
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (bin[e] != bs) continue;
+    int r = 0;
+    for (int u = 0; u < nb; ++u) {
+      const int m = bl[u];
+      const double v = vals[m];
+      r += (v > x[e]) || (v == x[e] && m < id[e]);
+    }
+    if (r < need) keep |= 1u << e;
+  }
+  return keep;
+}
+
 }  // namespace hga
