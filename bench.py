@@ -22,14 +22,20 @@ through the replicas, so the timed traffic comes from HBM and not from the
 consecutive steps.
 
 Prints one JSON line.  ``value`` = decoded query tokens per second per layer
-(B tokens per step).  ``roofline`` covers the dominant kernel (hga_attend's
-split kernel plus its merge, the same kernels as the step's attention):
-algorithmic bytes per launch / its mean launch duration, measured with HIP
-events around hga_attend calls on the launch stream (the step run through the
-separate entry points) while a spin kernel keeps the queue filled ahead (so
-host launch latency does not enter).
+(B tokens per step), over exactly --steps graph-replayed steps;
+``timing_distribution`` gives the per-step median, p10 and p90 over at least
+1000 further replays (each between two events).  ``roofline`` covers the
+dominant call, the longer of the routing call (tile + selection kernels) and
+the attention call (split + merge kernels): algorithmic bytes per launch / its
+mean launch duration, measured with HIP events around the calls on the launch
+stream (the step run through the separate entry points) while a spin kernel
+keeps the queue filled ahead (so host launch latency does not enter);
+``roofline_other_call`` the other one; ``roofline_step`` the whole step's
+algorithmic bytes over its graph-timed duration.  ``summary_build`` times the
+bulk build of the whole context and the refresh of one completed chunk.
 ``cpu_baseline`` times the fp64 CPU oracle doing the same step, repeated for
-about 10 s, on this host's cores.
+about 10 s, on this host's cores, and on one thread (``single_thread``), with
+the host CPU model.
 
 ``--workload prefill32k`` runs the chunked-prefill leg instead: one 64-token
 query chunk at 32K context (append + summaries of the chunk, routing with the
@@ -62,6 +68,11 @@ HBM_PEAK_GBS = 8000.0
 ATTEND_TRAFFIC = dict(
     source_sha256="aa6b2e1bf9bbb64260006c959078abb4a19bde55e1c7282259fffb75e0835519",
     fetch_kib=16745.93 + 1469.92, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
+
+
+# The same for the routing entry point (its tile kernel plus its selection
+# kernel), or None when not taken on the current routing sources.
+ROUTE_TRAFFIC = None
 
 
 def algorithmic_bytes(p, B):
@@ -100,6 +111,24 @@ def attend_traffic():
     """HBM bytes per hga_attend call from the stored counter figures, or None."""
     t = ATTEND_TRAFFIC
     if t is None or t["source_sha256"] != attend_source_sha():
+        return None
+    return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
+
+
+def route_source_sha():
+    """sha256 of the routing sources (tile and selection kernels)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("hga_route.hip", "hga_topk.h"):
+        with open(os.path.join(ROOT, "long_context_hga_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def route_traffic():
+    """HBM bytes per hga_route call from the stored counter figures, or None."""
+    t = ROUTE_TRAFFIC
+    if t is None or t["source_sha256"] != route_source_sha():
         return None
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
 
@@ -180,11 +209,40 @@ def cpu_baseline(inp, cfg_params, min_seconds=10.0):
         oracle.step(cfg, q, np.full(U, pos), cs, gs, kp, vp, max_sel)
         times.append(time.perf_counter() - t0)
     med = float(np.median(times))
-    return {"value": B / med, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+    total = time.perf_counter() - t_start
+    # the same step on one thread (route + attend of every unit; fewer runs)
+    threads = oracle.max_threads()
+    oracle.set_threads(1)
+    t1s = []
+    t_one = time.perf_counter()
+    try:
+        while len(t1s) < 2 or time.perf_counter() - t_one < min_seconds / 2:
+            t0 = time.perf_counter()
+            oracle.step(cfg, q, np.full(U, pos), cs, gs, kp, vp, max_sel)
+            t1s.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(threads)
+    med1 = float(np.median(t1s))
+    return {"value": B / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpu": host_cpu_model(),
             "sample": f"the full step: all {B} sequences x {hkv} KV heads, append + chunk refresh + "
                       f"route + attend of one decode token at position {pos} (context {T}); fp64 C "
                       f"oracle, OpenMP over the {U} units; median of {len(times)} runs "
-                      f"({med * 1e3:.1f} ms each, {time.perf_counter() - t_start:.1f} s total)"}
+                      f"({med * 1e3:.1f} ms each, {total:.1f} s total)",
+            "single_thread": {"value": B / med1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"route + attend of the same {U} units on one thread "
+                                        f"(no append or refresh); median of {len(t1s)} runs "
+                                        f"({med1 * 1e3:.1f} ms each)"}}
+
+
+def host_cpu_model():
+    """The host CPU's model name and logical CPU count, from /proc/cpuinfo."""
+    try:
+        names = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                 if l.startswith("model name")]
+        return f"{names[0]} ({len(names)} logical CPUs visible)" if names else None
+    except OSError:
+        return None
 
 
 def main():
@@ -325,25 +383,10 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     torch.cuda.synchronize()
     eager_out = [x["s"].out.clone() for x in reps]
 
-    # whole-step throughput: one HIP graph holds R consecutive steps (one per
-    # replica); the timed region replays it
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for r in range(R):
-            step(r)
-    for _ in range(max(1, args.warmup // R)):
-        g.replay()
-    torch.cuda.synchronize()
-    n_rep = max(1, args.steps // R)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(n_rep):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    steps_timed = n_rep * R
-    ms_step = t0.elapsed_time(t1) / steps_timed
+    # whole-step throughput: HIP graphs of consecutive steps (one per
+    # replica); the timed region replays them for exactly --steps steps, then
+    # the per-step distribution over many more replays
+    ms_step, steps_timed, dist = time_graph_exact(step, R, args)
     for r, x in enumerate(reps):  # graph replays reproduce the eager results
         assert torch.equal(x["s"].out, eager_out[r]), "graph replay differs from eager run"
 
@@ -383,8 +426,49 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
         gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
         del kw, vw
 
+    # summary build: the bulk build of the whole context (every unit's pool
+    # and summaries) and the refresh of one completed chunk, event-timed
+    build_ms, chunk_ms = float("nan"), float("nan")
+    if p.get("pool_dtype", 0) == 0:
+        x = reps[0]
+        shape = (B, p["n_kv_heads"], T, p["head_dim"])
+        kraw = torch.randn(shape, device="cuda").to(torch.bfloat16).view(x["kc"].dtype)
+        vraw = torch.randn(shape, device="cuda").to(torch.bfloat16).view(x["kc"].dtype)
+        be = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+        def bulk():
+            hga.hga_build_summaries(cfg, B, kraw, vraw, 0, T, x["k_pool"], x["v_pool"], T,
+                                    x["chunk_sum"], x["group_sum"], st.max_chunks)
+        bulk()  # warm
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(1e8))
+        be[0].record()
+        bulk()
+        be[1].record()
+        for _ in range(20):
+            hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
+                                    x["group_sum"], st.max_chunks)
+        be[2].record()
+        torch.cuda.synchronize()
+        build_ms = be[0].elapsed_time(be[1])
+        chunk_ms = be[1].elapsed_time(be[2]) / 20
+        del kraw
+
     ab = algorithmic_bytes(p, B)
-    achieved = ab["attend"] / (attend_ms * 1e-3) / 1e9
+    calls = {
+        "hga_route call (tile + selection kernels)": (route_ms, ab["route"]),
+        "hga_attend call (split + merge kernels)": (attend_ms, ab["attend"]),
+    }
+    dom = max(calls, key=lambda k: calls[k][0])  # the call that takes longest
+    def roof(name, traffic):
+        ms, nb = calls[name]
+        ach = nb / (ms * 1e-3) / 1e9
+        return {"kernel": name, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                "bytes_per_launch": nb, "launch_ms": ms}
+    traffic = {"hga_attend call (split + merge kernels)": attend_traffic(),
+               "hga_route call (tile + selection kernels)": route_traffic()}
+    step_gbs = ab["total"] / (ms_step * 1e-3) / 1e9
     out = {
         "metric": "routed-attention query tokens/s per layer at 64K ctx; achieved HBM GB/s vs peak",
         "value": B / (ms_step * 1e-3),
@@ -411,11 +495,21 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
                    "timing": "HIP graph of R steps, replayed",
                    "step_bytes_algorithmic": ab["total"],
                    "step_GBps_algorithmic": ab["total"] / (ms_step * 1e-3) / 1e9},
-        "roofline": {"kernel": "hga_attend (split + merge kernels)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": attend_traffic(),
-                     "bytes_per_launch": ab["attend"], "launch_ms": attend_ms,
-                     "route_launch_ms": route_ms, "route_bytes_per_launch": ab["route"]},
+        "timing_distribution": dist,
+        "roofline": roof(dom, traffic[dom]),
+        "roofline_other_call": [roof(k, traffic[k]) for k in calls if k != dom][0],
+        "roofline_step": {"scope": "whole fused step (graph-timed), algorithmic bytes of the "
+                                   "append, chunk refresh, routing and attention",
+                          "bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                          "bytes_per_step": ab["total"], "ms_per_step": ms_step},
+        "summary_build": {"bulk_ms": build_ms, "bulk_tokens": B * p["n_kv_heads"] * T,
+                          "bulk_Mtokens_per_s": B * p["n_kv_heads"] * T / (build_ms * 1e-3) / 1e6,
+                          "chunk_refresh_ms": chunk_ms,
+                          "note": "bulk: hga_build_summaries over the whole context of every "
+                                  "unit (rotated K and V pool rows, summaries of every chunk); "
+                                  "chunk: the summaries of one completed 64-token chunk of "
+                                  "every unit"},
         "gather_hbm": {"kernel": "hga_gather, HBM pool -> HBM working set (same lists)",
                        "launch_ms": gather_ms, "bytes_read_and_written": gather_bytes,
                        "achieved_GBps": gather_bytes / (gather_ms * 1e-3) / 1e9,
@@ -1035,9 +1129,20 @@ def run_host64k(args):
     print(json.dumps(out), flush=True)
 
 
-def time_graph(step, R, args):
-    """Mean step time (ms) over graph replays of R consecutive steps."""
+def time_graph_exact(step, R, args, min_replays=1000):
+    """Step time over exactly args.steps steps, and its distribution.
+
+    One HIP graph holds R consecutive steps (replicas 0..R-1), a second the
+    remaining args.steps % R.  The timed region (bracketed by device
+    synchronisation) replays the first args.steps // R times and the second
+    once: exactly args.steps steps; returns their mean (ms).  Then at least
+    min_replays replays of the first graph, each between two events on the
+    launch stream with the queue filled ahead (a spin kernel holds the GPU
+    while the host enqueues), give the per-step distribution (replay / R):
+    median, p10, p90 in microseconds."""
+    import numpy as np
     import torch
+    K = max(1, args.steps)
     for i in range(max(args.warmup, R)):
         step(i % R)
     torch.cuda.synchronize()
@@ -1045,18 +1150,50 @@ def time_graph(step, R, args):
     with torch.cuda.graph(g):
         for r in range(R):
             step(r)
+    g_tail = None
+    if K % R:
+        g_tail = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_tail):
+            for r in range(K % R):
+                step(r)
     for _ in range(max(1, args.warmup // R)):
         g.replay()
     torch.cuda.synchronize()
-    n_rep = max(1, args.steps // R)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(n_rep):
+    for _ in range(K // R):
         g.replay()
+    if g_tail is not None:
+        g_tail.replay()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / (n_rep * R), n_rep * R
+    ms_step = t0.elapsed_time(t1) / K
+    # distribution: per-replay events, queue filled ahead in batches
+    n = max(min_replays, (K + R - 1) // R)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    per = []
+    batch = 250
+    for b0 in range(0, n, batch):
+        b1 = min(n, b0 + batch)
+        torch.cuda._sleep(int(5e7))
+        ev[b0].record()
+        for i in range(b0, b1):
+            g.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per += [ev[i].elapsed_time(ev[i + 1]) * 1e3 / R for i in range(b0, b1)]
+    per = np.asarray(per)
+    dist = {"replays": int(n), "steps_per_replay": R, "steps": int(n * R),
+            "median_us": float(np.median(per)), "p10_us": float(np.percentile(per, 10)),
+            "p90_us": float(np.percentile(per, 90)), "mean_us": float(per.mean())}
+    return ms_step, K, dist
+
+
+def time_graph(step, R, args):
+    """Mean step time (ms) over exactly args.steps graph-replayed steps."""
+    ms_step, K, _ = time_graph_exact(step, R, args, min_replays=0)
+    return ms_step, K
 
 
 def time_launches(step, R, args):

@@ -51,12 +51,16 @@ struct RouteArgs {
 // Position and candidate range of a unit; false if the query position is
 // unusable (negative, query tokens spanning two chunks, a query chunk beyond
 // the summary table, or, in a fused step, tokens beyond the pool).
-__device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch& r, int max_cand,
-                                               int b, int* pos0, Windows* w) {
-  *pos0 = r.q_pos0[b];
+__device__ __forceinline__ bool route_geometry_at(const KCfg& c, const RouteLaunch& r,
+                                                  int max_cand, int p0, int* pos0, Windows* w) {
+  *pos0 = p0;
   *w = windows_of(*pos0 / kChunk, c.n_sink, c.n_local);
   return *pos0 >= 0 && (*pos0 % kChunk) + r.lq <= kChunk && *pos0 / kChunk < r.max_chunks &&
          w->cand_hi - w->cand_lo <= max_cand && (r.pool_cap <= 0 || *pos0 + r.lq <= r.pool_cap);
+}
+__device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch& r, int max_cand,
+                                               int b, int* pos0, Windows* w) {
+  return route_geometry_at(c, r, max_cand, r.q_pos0[b], pos0, w);
 }
 
 // MODE 0: pooled query of up to S tokens + scores (decode);
@@ -95,6 +99,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   const int qt0 = (b % r.nq) * r.lq;              // first query row of this chunk
   const int lq = r.lq;
   const int tile0 = blockIdx.x * kTile;
+  const int pos0_in = r.q_pos0[b];  // first: a scalar load ahead of everything
   constexpr bool multi = MODE == 1 || MODE == 2;
   constexpr bool pool_q = MODE != 3;    // this launch forms the pooled query
   constexpr bool score = MODE != 2;     // this launch scores its tile
@@ -145,6 +150,9 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   } else {
     load_batch(0);
   }
+  // the query loads go out ahead of the row loads (the rows are the bulk of
+  // the traffic; a query load queued behind them delays the pooled query)
+  __builtin_amdgcn_sched_barrier(0);
   const int sub = lane % kLanesPerRow, rin = lane / kLanesPerRow;
   float4 buf[ITER][NV];
 #pragma unroll
@@ -158,9 +166,21 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     for (int v = 0; v < NV; ++v) buf[it][v] = rowp[v * kLanesPerRow + sub];
   }
 
+  // ... and stay ahead of the exits below (the compiler would otherwise sink
+  // them past the exits, behind every row load): this waits for the query
+  // values only, the row loads issued after them stay in flight
+  if constexpr (pool_q && !multi) {
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) asm volatile("" ::"v"(xa[hh]), "v"(xb[hh]));
+  } else if constexpr (pool_q) {
+#pragma unroll
+    for (int u = 0; u < TB; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) asm volatile("" ::"v"(ya[u][hh]), "v"(yb[u][hh]));
+  }
   int pos0;
   Windows w;
-  if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) return;  // route_select reports it
+  if (!route_geometry_at(c, r, a.max_cand, pos0_in, &pos0, &w)) return;  // route_select reports it
   const int n_cand = w.cand_hi - w.cand_lo;
   if (tile0 >= n_cand && (blockIdx.x != 0 || !pool_q)) return;  // tile 0 stores qbar
 

@@ -106,6 +106,7 @@ def lib():
                                _dp, _dp, ctypes.c_long, _ip, _ip, ctypes.c_int, _dp]
         L.ora_step.restype = ctypes.c_int
         L.ora_max_threads.restype = ctypes.c_int
+        L.ora_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -356,3 +357,8 @@ def step(cfg, q, pos0, chunk_sum, group_sum, kpool, vpool, max_sel):
 
 def max_threads() -> int:
     return lib().ora_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of step()'s parallel loop (timing only)."""
+    lib().ora_set_threads(int(n))

@@ -556,3 +556,13 @@ int ora_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads of the batched driver's parallel loop (timing only; results do
+ * not depend on it: each unit is computed by one thread, in the same order). */
+void ora_set_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
