@@ -407,7 +407,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
 
     # hga_gather from the HBM pool into a working set (the same lists): its
     # own copy rate, read + write (the FP8 pool has no gather)
-    gather_ms, gather_bytes = float("nan"), 0
+    gather_ms, gather_bytes, copy_ms = float("nan"), 0, float("nan")
     if p.get("pool_dtype", 0) == 0:
         kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
                          dtype=reps[0]["k_pool"].dtype, device="cuda")
@@ -425,6 +425,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
         gather_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
         gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
         del kw, vw
+        copy_ms = copy_rate_ms(gather_bytes // 2)
 
     # summary build: the bulk build of the whole context (every unit's pool
     # and summaries) and the refresh of one completed chunk, event-timed
@@ -513,7 +514,12 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
         "gather_hbm": {"kernel": "hga_gather, HBM pool -> HBM working set (same lists)",
                        "launch_ms": gather_ms, "bytes_read_and_written": gather_bytes,
                        "achieved_GBps": gather_bytes / (gather_ms * 1e-3) / 1e9,
-                       "frac_of_8TBps": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                       "frac_of_8TBps": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "device_copy_GBps": gather_bytes / (copy_ms * 1e-3) / 1e9,
+                       "frac_of_device_copy": copy_ms / gather_ms,
+                       "device_copy_note": "a contiguous device-to-device copy of the same "
+                                           "bytes (torch copy_, event-timed): the rate a plain "
+                                           "read + write stream reaches on this device"},
     }
     del reps, st
     torch.cuda.synchronize()
@@ -1127,6 +1133,28 @@ def run_host64k(args):
                     "overlap_fraction_two_streams": overlap_of(t_tiered)},
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_rate_ms(n_bytes, reps=20):
+    """Median duration (ms) of a contiguous device copy of n_bytes (read
+    n_bytes, write n_bytes), event-timed."""
+    import numpy as np
+    import torch
+    src = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))
+    ev[0].record()
+    for i in range(reps):
+        dst.copy_(src)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+    del src, dst
+    return t
 
 
 def time_graph_exact(step, R, args, min_replays=1000):

@@ -218,7 +218,6 @@ hga_status hga_gather(const hga_config* cfg, int32_t B, const void* k_pool, cons
                       void* k_ws, void* v_ws, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 ||
       !sel_groups || !n_sel || max_sel <= 0 ||
       !k_ws || !v_ws || part < HGA_PART_ALL || part > HGA_PART_ROUTED ||
@@ -252,9 +251,8 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   // three-product split)
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
-  // the FP8 pool: decode shapes reading the pool itself
-  if (cfg->pool_dtype == 1 && (lq > kMaxLqDecode || src_layout != HGA_SRC_POOL))
-    return HGA_ERR_UNSUPPORTED;
+  // the FP8 pool: decode shapes (from the pool or a working set of it)
+  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
@@ -546,7 +544,7 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              void* ev_fork, void* ev_join) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
+  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;  // FP8: decode
   if (cfg->route_per_head) return HGA_ERR_UNSUPPORTED;
   if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
       hot_cap <= 0 || hot_cap % kGroupTokens != 0 || !k_cold || !v_cold || cold_cap <= 0 ||
@@ -602,8 +600,8 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
     // shapes), then the routed part and the merge follow in order
     hipError_t e;
     if (lq <= kMaxLqDecode) {
-      const GatherArgs g = make_gather_args(k, kc, vc, cold_cap, sel_groups, n_sel, max_sel, q_pos0,
-                                            HGA_PART_ROUTED, k_ws, v_ws);
+      const GatherArgs g = make_gather_args(k, B, kc, vc, cold_cap, sel_groups, n_sel, max_sel,
+                                            q_pos0, HGA_PART_ROUTED, k_ws, v_ws);
       e = launch_tiered_front(k, ah, g, max_sel * k.lists * B, sa);
     } else {
       e = launch_attend_split(k, ah, sa);

@@ -190,8 +190,10 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       v8[nb] = load_stream8(vc + vbase + (size_t)(16 * nb + rl) * kGroupTokens + 8 * (qg & 1));
-    // the scales follow the codes of every pool unit; row = group row * 16 + token
-    const size_t codes = (size_t)a.B * c.hkv * a.src_cap * D;
+    // the scales follow the codes of every pool (or working-set) unit; row =
+    // group row * 16 + token
+    const size_t codes =
+        (size_t)a.B * (a.src_layout == HGA_SRC_WORKING_SET ? c.lists : c.hkv) * a.src_cap * D;
     const size_t srow = ((qg >> 1) ? kb[1] : kb[0]) / D + 8 * (qg & 1);
     const float4* kq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(kc + codes) + srow);
     const float4* vq = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(vc + codes) + srow);
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(AttendArgs args) {
 // pool into the working set.  The copy workgroups wait on PCIe most of the
 // time, so the window attention runs beside the transfer instead of before
 // or after it.
-template <int D, int HG, bool BF16>
+template <int D, int HG, bool BF16, bool FP8 = false>
 __global__ __launch_bounds__(256) void tier_front_kernel(AttendArgs win, int win_x, int win_y, int n_win,
                                                          GatherArgs g, int n_items) {
   const int wg = blockIdx.x;
@@ -428,7 +430,7 @@ __global__ __launch_bounds__(256) void tier_front_kernel(AttendArgs win, int win
     gather_items(g, n_items, wg - n_win, gridDim.x - n_win);
     return;
   }
-  decode_split<D, HG, BF16>(win, wg % win_x, (wg / win_x) % win_y, wg / (win_x * win_y));
+  decode_split<D, HG, BF16, FP8>(win, wg % win_x, (wg / win_x) % win_y, wg / (win_x * win_y));
 }
 
 template <int D, int HG>
@@ -459,6 +461,13 @@ template <int D, int HG>
 static void launch_front_dh(const AttendArgs& x, int gx, int gy, int n_win, const GatherArgs& g,
                             int n_items, int n_gwg, hipStream_t st) {
   const dim3 grid(n_win + n_gwg);
+  if constexpr (D == 128) {
+    if (x.cfg.pool8) {
+      hipLaunchKernelGGL((tier_front_kernel<D, HG, true, true>), grid, dim3(256), 0, st, x, gx, gy,
+                         n_win, g, n_items);
+      return;
+    }
+  }
   if (x.cfg.dtype == HGA_BF16)
     hipLaunchKernelGGL((tier_front_kernel<D, HG, true>), grid, dim3(256), 0, st, x, gx, gy, n_win, g, n_items);
   else

@@ -13,8 +13,8 @@ hipError_t launch_gather(const KCfg& cfg, int B, const void* k_pool, const void*
                          int pool_cap, const int* sel, const int* n_sel, int max_sel,
                          const int* q_pos0, int part, void* k_ws, void* v_ws, bool from_host,
                          hipStream_t st) {
-  const GatherArgs a = make_gather_args(cfg, k_pool, v_pool, pool_cap, sel, n_sel, max_sel, q_pos0,
-                                        part, k_ws, v_ws);
+  const GatherArgs a = make_gather_args(cfg, B, k_pool, v_pool, pool_cap, sel, n_sel, max_sel,
+                                        q_pos0, part, k_ws, v_ws);
   const int n_items = max_sel * cfg.lists * B;
   // over PCIe a few hundred workgroups keep the link busy and leave CUs to
   // other work; from HBM every group gets its own workgroup so that all its

@@ -24,16 +24,23 @@ struct GatherArgs {
   const int* n_sel;
   const int* q_pos0;
   int lists, kvdiv, hkv, n_sink, n_local, pool_cap, max_sel, part, row_vecs;  // row_vecs: uint4 per token row
+  // FP8 pool: the row scales after the codes, of the pool and of the working
+  // set (null otherwise)
+  const float* k_sc;
+  const float* v_sc;
+  float* k_sc_ws;
+  float* v_sc_ws;
 };
 
 // A persistent grid of at most kGatherWgs workgroups walks the (slot, KV
 // head, sequence) items; each item copies one group of K and of V (4 KiB
-// each at d = 128, bf16), 16 bytes per lane.  Reading a pinned host pool,
+// each at d = 128, bf16; 2 KiB of codes and 64 bytes of row scales from the
+// FP8 pool), 16 bytes per lane.  Reading a pinned host pool,
 // the workgroups spend their time waiting on PCIe, so the grid is kept small
 // enough to leave CUs to other work.
 constexpr int kGatherWgs = 256;
 
-inline GatherArgs make_gather_args(const KCfg& cfg, const void* k_pool, const void* v_pool,
+inline GatherArgs make_gather_args(const KCfg& cfg, int B, const void* k_pool, const void* v_pool,
                                    int pool_cap, const int* sel, const int* n_sel, int max_sel,
                                    const int* q_pos0, int part, void* k_ws, void* v_ws) {
   GatherArgs a;
@@ -52,7 +59,17 @@ inline GatherArgs make_gather_args(const KCfg& cfg, const void* k_pool, const vo
   a.pool_cap = pool_cap;
   a.max_sel = max_sel;
   a.part = part;
-  a.row_vecs = cfg.d * (cfg.dtype == HGA_BF16 ? 2 : 4) / 16;
+  a.row_vecs = cfg.d * (cfg.pool8 ? 1 : (cfg.dtype == HGA_BF16 ? 2 : 4)) / 16;
+  a.k_sc = a.v_sc = nullptr;
+  a.k_sc_ws = a.v_sc_ws = nullptr;
+  if (cfg.pool8) {  // codes of every unit, then the row scales
+    const size_t pool_codes = (size_t)B * cfg.hkv * pool_cap * cfg.d;
+    const size_t ws_codes = (size_t)B * cfg.lists * max_sel * kGroupTokens * cfg.d;
+    a.k_sc = reinterpret_cast<const float*>(static_cast<const char*>(k_pool) + pool_codes);
+    a.v_sc = reinterpret_cast<const float*>(static_cast<const char*>(v_pool) + pool_codes);
+    a.k_sc_ws = reinterpret_cast<float*>(static_cast<char*>(k_ws) + ws_codes);
+    a.v_sc_ws = reinterpret_cast<float*>(static_cast<char*>(v_ws) + ws_codes);
+  }
   return a;
 }
 
@@ -87,6 +104,12 @@ __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, i
       const uint4 vv = a.v_pool[src + i];
       a.k_ws[dst + i] = kv;
       a.v_ws[dst + i] = vv;
+    }
+    if (a.k_sc && threadIdx.x < kGroupTokens) {  // FP8: the group's 16 row scales of K and V
+      const size_t ss = (size_t)unit_p * a.pool_cap + (size_t)gid * kGroupTokens + threadIdx.x;
+      const size_t sd = ((size_t)unit * a.max_sel + slot) * kGroupTokens + threadIdx.x;
+      a.k_sc_ws[sd] = a.k_sc[ss];
+      a.v_sc_ws[sd] = a.v_sc[ss];
     }
   }
 }

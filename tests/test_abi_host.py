@@ -207,22 +207,17 @@ def test_prefill_prompt_rejects():
 
 
 def test_fp8_pool_limits():
-    """The FP8 pool needs bf16 inputs and head_dim 128, and runs the decode
-    paths only."""
+    """The FP8 pool needs bf16 inputs and head_dim 128; its gather checks its
+    arguments like the bf16 one (no call here reaches a launch)."""
     assert hga.hga_validate(cfg(pool_dtype=1)) == hga.HGA_OK
     assert hga.hga_validate(cfg(pool_dtype=1, qkv_dtype=hga.HGA_F32)) == hga.HGA_ERR_UNSUPPORTED
     assert hga.hga_validate(cfg(pool_dtype=1, head_dim=64)) == hga.HGA_ERR_UNSUPPORTED
     c = ctypes.byref(cfg(pool_dtype=1))
-    f = hga.lib().hga_attend
-    args = [c, 8, FAKE, 1, FAKE, FAKE, FAKE, 0, 65536, FAKE, FAKE, 128, 0, FAKE, None, FAKE,
-            1 << 30, None]
-    a = list(args); a[3] = 32  # prefill shape
-    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
-    a = list(args); a[7] = hga.HGA_SRC_WORKING_SET
-    assert f(*a) == hga.HGA_ERR_UNSUPPORTED
     g = hga.lib().hga_gather
-    assert g(c, 8, FAKE, FAKE, 65536, 0, FAKE, FAKE, 128, None, 0, FAKE, FAKE, None) == \
-        hga.HGA_ERR_UNSUPPORTED
+    assert g(c, 8, FAKE, FAKE, 65536, 0, FAKE, FAKE, 128, None, 2, FAKE, FAKE, None) == \
+        hga.HGA_ERR_INVALID_ARGUMENT  # part needs positions
+    assert g(c, 8, FAKE, FAKE, 65535, 0, FAKE, FAKE, 128, None, 0, FAKE, FAKE, None) == \
+        hga.HGA_ERR_INVALID_ARGUMENT  # pool_cap not a multiple of 16
 
 
 def test_warm_gather_rejects():

@@ -219,3 +219,126 @@ def test_fp8_prefill_step_equals_separate_calls(pos, lq):
             _, vscales, _ = oracle.fp8_rows(inp.f64(inp.v[b, h, pos:pos + lq]))
             _, vs = pb.v_rows(b, h)
             np.testing.assert_array_equal(vs[pos:pos + lq], vscales)
+
+
+def fp8_ws(B, lists, max_sel, d=128):
+    """An FP8 working set: codes [B][lists][max_sel*16][d], then row scales."""
+    n = B * lists * max_sel * 16 * (d + 4)
+    return (torch.zeros(n, dtype=torch.uint8, device="cuda"),
+            torch.zeros(n, dtype=torch.uint8, device="cuda"))
+
+
+def split_ws(buf, B, lists, max_sel, d=128):
+    h = buf.cpu().numpy()
+    nc = B * lists * max_sel * 16 * d
+    return (h[:nc].reshape(B, lists, max_sel, 16 * d),
+            h[nc:].view(np.float32).reshape(B, lists, max_sel, 16))
+
+
+def pool_groups(buf, B, hkv, T, d=128):
+    h = buf.cpu().numpy()
+    nc = B * hkv * T * d
+    return (h[:nc].reshape(B, hkv, T // 16, 16 * d),
+            h[nc:].view(np.float32).reshape(B, hkv, T // 16, 16))
+
+
+def pinned(t):
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+@pytest.mark.parametrize("host", [False, True])
+def test_fp8_gather_copies_codes_and_scales(host):
+    """hga_gather from the FP8 pool (device memory, or pinned host memory over
+    PCIe) copies each listed group's 16 code rows and 16 row scales of K and
+    V into its working-set slot, bit for bit; HGA_PART_ROUTED copies the routed
+    slots only."""
+    inp, st, pool = fp8_state(batch=2, context=4096)
+    B, T, ms = st.B, st.T, st.max_sel
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    kp, vp = (pinned(pool.k), pinned(pool.v)) if host else (pool.k, pool.v)
+    kw, vw = fp8_ws(B, 4, ms)
+    hga.hga_gather(st.cfg, B, kp, vp, T, int(host), s.sel, s.n_sel, ms, st.pos0,
+                   hga.HGA_PART_ALL, kw, vw)
+    kr, vr = fp8_ws(B, 4, ms)
+    hga.hga_gather(st.cfg, B, kp, vp, T, int(host), s.sel, s.n_sel, ms, st.pos0,
+                   hga.HGA_PART_ROUTED, kr, vr)
+    torch.cuda.synchronize()
+    sel, nsel = s.sel.cpu().numpy(), s.n_sel.cpu().numpy()
+    for buf, wbuf, rbuf in ((pool.k, kw, kr), (pool.v, vw, vr)):
+        pc, psc = pool_groups(buf, B, 4, T)
+        wc, wsc = split_ws(wbuf, B, 4, ms)
+        rc, rsc = split_ws(rbuf, B, 4, ms)
+        for b in range(B):
+            for h in range(4):
+                n = nsel[b, h]
+                g = sel[b, h, :n]
+                np.testing.assert_array_equal(wc[b, h, :n], pc[b, h, g])
+                np.testing.assert_array_equal(wsc[b, h, :n], psc[b, h, g])
+                routed = slice(4, n - 4 * 4 - 4)  # sink | routed | local | current (pos 4095)
+                np.testing.assert_array_equal(rc[b, h, routed], pc[b, h, g[routed]])
+                np.testing.assert_array_equal(rsc[b, h, routed], psc[b, h, g[routed]])
+                assert not rc[b, h, :4].any() and not rc[b, h, n - 20:n].any()
+
+
+def test_fp8_attend_working_set_equals_pool():
+    """Decode attention over an FP8 working set gives the bits of the same
+    attention over the FP8 pool."""
+    inp, st, pool = fp8_state(batch=2, context=4096, max_lq=5)
+    B, T, ms = st.B, st.T, st.max_sel
+    for lq in (1, 5):
+        q = gh.query_slice(st, 0) if lq == 1 else st.q[:, :, :1].repeat(1, 1, lq, 1).contiguous()
+        pos_t = torch.full((B,), 3000, dtype=torch.int32, device="cuda")
+        s = gh.alloc_step(st, lq)
+        gh.route(st, q, lq, pos_t, s)
+        hga.hga_attend(st.cfg, B, q, lq, pos_t, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel,
+                       s.n_sel, ms, hga.HGA_PART_ALL, s.out, s.lse, st.ws)
+        kw, vw = fp8_ws(B, 4, ms)
+        hga.hga_gather(st.cfg, B, pool.k, pool.v, T, 0, s.sel, s.n_sel, ms, pos_t,
+                       hga.HGA_PART_ALL, kw, vw)
+        ow, lw = torch.empty_like(s.out), torch.empty_like(s.lse)
+        hga.hga_attend(st.cfg, B, q, lq, pos_t, kw, vw, hga.HGA_SRC_WORKING_SET, 0, s.sel,
+                       s.n_sel, ms, hga.HGA_PART_ALL, ow, lw, st.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ow, s.out) and torch.equal(lw, s.lse), lq
+
+
+@pytest.mark.parametrize("form", ["two streams", "one launch"])
+def test_fp8_tiered_against_device_path_and_oracle(form):
+    """The host tier on the FP8 pool: windows from the device pool, routed
+    groups copied from the pinned host pool (codes and scales) and attended
+    from the working set, merged exactly.  Equal to hga_attend over the whole
+    list within the merge's rounding, and to the oracle run on its own FP8
+    pool within the decode tolerance."""
+    inp, st, pool = fp8_state(batch=2, context=8192)
+    B, T, ms = st.B, st.T, st.max_sel
+    cfg = oracle.cfg_from(inp.params)
+    kc, vc = pinned(pool.k), pinned(pool.v)
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    hga.hga_attend(st.cfg, B, q, 1, st.pos0, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel, s.n_sel,
+                   ms, hga.HGA_PART_ALL, s.out, s.lse, st.ws)
+    kw, vw = fp8_ws(B, 4, ms)
+    out = torch.full_like(s.out, float("nan"))
+    lse = torch.full_like(s.lse, float("nan"))
+    side = torch.cuda.Stream() if form == "two streams" else None
+    hga.hga_attend_tiered(st.cfg, B, q, 1, st.pos0, pool.k, pool.v, T, kc, vc, T, s.sel, s.n_sel,
+                          ms, kw, vw, out, lse, torch.zeros_like(st.ws), stream_b=side,
+                          events=(torch.cuda.Event(), torch.cuda.Event()))
+    torch.cuda.synchronize()
+    assert (out - s.out).abs().max().item() <= 1e-5
+    assert (lse - s.lse).abs().max().item() <= 1e-5
+    pos = int(inp.pos0[0])
+    o = out.cpu().numpy()
+    qh = q.cpu().numpy().view(np.uint16)
+    for b in range(B):
+        for h in range(4):
+            kd = oracle.pool_fp8(cfg, inp.f64(inp.k[b, h]), 0)[2]
+            vd = oracle.fp8_rows(inp.f64(inp.v[b, h]))[2]
+            g = s.sel[b, h, :int(s.n_sel[b, h])].cpu().numpy()
+            o_ref, _ = oracle.attend(cfg, inp.f64(qh[b, h * 8:(h + 1) * 8]), pos, kd, vd, g)
+            assert max_abs(o[b, h * 8:(h + 1) * 8], o_ref) <= ATOL_OUT, (b, h)
