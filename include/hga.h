@@ -106,10 +106,12 @@ typedef struct {
                               the smallest power of two s with max|x| <= 448 s.  A pool
                               buffer then holds the codes, [B][Hkv][cap][d] bytes (V in
                               transposed group blocks), followed by the row scales,
-                              [B][Hkv][cap] fp32.  Supported by hga_build_summaries,
-                              hga_route, hga_attend (1..15 query tokens, HGA_SRC_POOL)
-                              and hga_decode_step; other entry points return
-                              HGA_ERR_UNSUPPORTED */
+                              [B][Hkv][cap] fp32.  Every entry point takes it; a
+                              working set (hga_gather, hga_warm_gather) then holds
+                              the codes [B][lists][max_sel*16][d] bytes followed by
+                              the row scales [B][lists][max_sel*16] fp32, and a
+                              warm cache the codes [B][lists][n_warm*16][d] bytes
+                              followed by [B][lists][n_warm*16] fp32 scales */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
@@ -429,7 +431,8 @@ hga_status hga_warm_workspace_bytes(const hga_config* cfg, int32_t B, int32_t ma
  *     k_ws / v_ws [B][lists][max_sel*16][d] -- what hga_gather with
  *     HGA_PART_ROUTED would write; window slots are not touched.
  *   k_cold, v_cold  the pool in pinned host memory, as hga_gather
- *   k_warm, v_warm  [B][lists][n_warm][16][d] qkv_dtype device memory: slot w
+ *   k_warm, v_warm  [B][lists][n_warm][16][d] qkv_dtype (FP8 pool: codes, then
+ *                   row scales, as cfg->pool_dtype describes) device memory: slot w
  *                   holds a group's K rows and its V^T block (the pool's
  *                   group layout)
  *   warm_tags [B][lists][n_warm] int32, warm_used [B][lists][n_warm] int32:

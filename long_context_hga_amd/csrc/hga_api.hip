@@ -251,8 +251,6 @@ hga_status hga_attend(const hga_config* cfg, int32_t B, const void* q_raw, int32
   // three-product split)
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
-  // the FP8 pool: decode shapes (from the pool or a working set of it)
-  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
     return HGA_ERR_UNSUPPORTED;
@@ -296,7 +294,6 @@ static hga_status fused_step(const hga_config* cfg, int32_t B, const void* q_raw
     return HGA_ERR_INVALID_ARGUMENT;
   if (lq > kMaxLqDecode && (cfg->qkv_dtype != HGA_BF16 || cfg->head_dim != 128))
     return HGA_ERR_UNSUPPORTED;
-  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode
   if (max_sel < max_selected(cfg)) return HGA_ERR_OUT_OF_RANGE;
   if (max_sel > kMaxListDecode) return HGA_ERR_UNSUPPORTED;
   if ((int64_t)B * lists_of(cfg) * lq > kMaxUnits || grid_z_of(cfg, B, lq) > kMaxGridZ)
@@ -462,7 +459,6 @@ hga_status hga_prefill_prompt(const hga_config* cfg, int32_t B, int32_t T, const
                               void* ws, size_t ws_bytes, void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || T <= 0 || T % kChunk != 0 || phases <= 0 || (phases & ~HGA_PROMPT_ALL) ||
       !k_pool || !v_pool || pool_cap <= 0 || pool_cap % kGroupTokens != 0 || !chunk_sum ||
       !group_sum || max_chunks <= 0 || !sel_groups || !n_sel || !ws)
@@ -544,7 +540,6 @@ hga_status hga_attend_tiered(const hga_config* cfg, int32_t B, const void* q_raw
                              void* ev_fork, void* ev_join) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (cfg->pool_dtype == 1 && lq > kMaxLqDecode) return HGA_ERR_UNSUPPORTED;  // FP8: decode
   if (cfg->route_per_head) return HGA_ERR_UNSUPPORTED;
   if (B <= 0 || !q_raw || lq <= 0 || lq > kChunk || !q_pos0 || !k_hot || !v_hot ||
       hot_cap <= 0 || hot_cap % kGroupTokens != 0 || !k_cold || !v_cold || cold_cap <= 0 ||
@@ -651,7 +646,6 @@ hga_status hga_warm_gather(const hga_config* cfg, int32_t B, const void* k_cold,
                            void* stream) {
   hga_status s = check_cfg(cfg);
   if (s != HGA_OK) return s;
-  if (cfg->pool_dtype == 1) return HGA_ERR_UNSUPPORTED;  // FP8 pool: decode paths only
   if (B <= 0 || !k_cold || !v_cold || cold_cap <= 0 || cold_cap % kGroupTokens != 0 ||
       !sel_groups || !n_sel || max_sel <= 0 || !q_pos0 || !k_warm || !v_warm || !warm_tags ||
       !warm_used || !k_ws || !v_ws || !ws || step <= 0)

@@ -13,6 +13,10 @@
 //                   hi + lo, two products)
 //   O^T += V^T P^T  A = 16 dims x 32 keys of V^T, B = the lane's own
 //                   probabilities (hi + lo) in the key order S^T left them.
+// FP8 pool (FP8 = true): the tile's E4M3FN codes are staged as bf16 (exact:
+// every E4M3FN value is a bf16 value) and its 128 K and 128 V row scales go
+// to LDS beside them; the K row scale multiplies the scores and the V row
+// scale the probabilities (powers of two: exact), as in the decode kernel.
 #pragma once
 
 #include "hga_attend_common.h"
@@ -129,46 +133,96 @@ struct TileStaging {
 //   K: group it, sub = (row sub/16, 16-byte chunk sub%16)
 //   V: group it's V^T block ([D][16], as the pool stores it), sub = (dim
 //      sub/2, tokens 8*(sub%2) .. +7)
-template <int D, int NTHR = 256>
-__device__ __forceinline__ void load_tile(const uint16_t* k, const uint16_t* v,
+// FP8: the same elements as codes (8 bytes per load, in .x and .y), and the
+// row scale of key tid (tid < 128: K) or key tid - 128 (tid < 256: V) of the
+// tile in sc; scales of the pool rows follow its codes (k_sc, v_sc).
+template <int D, int NTHR = 256, bool FP8 = false>
+__device__ __forceinline__ void load_tile(const void* k, const void* v,
                                           const size_t (&gbase)[kTileGroups], int tid,
                                           u32x4 (&kraw)[TileStaging<NTHR>::GPT],
-                                          u32x4 (&vraw)[TileStaging<NTHR>::GPT]) {
+                                          u32x4 (&vraw)[TileStaging<NTHR>::GPT],
+                                          const float* k_sc = nullptr, const float* v_sc = nullptr,
+                                          float* sc = nullptr) {
   using TS = TileStaging<NTHR>;
   constexpr int CH = D / 8;
   const int sub = tid % 256, half = tid / 256;
+  if constexpr (FP8) {
+    const uint8_t* kc = static_cast<const uint8_t*>(k);
+    const uint8_t* vc = static_cast<const uint8_t*>(v);
 #pragma unroll
-  for (int i = 0; i < TS::GPT; ++i)
-    kraw[i] = *reinterpret_cast<const u32x4*>(k + TS::pick(gbase, i, half) + (size_t)(sub / CH) * D + (sub % CH) * 8);
+    for (int i = 0; i < TS::GPT; ++i) {
+      const uint2 x = *reinterpret_cast<const uint2*>(kc + TS::pick(gbase, i, half) + (size_t)(sub / CH) * D + (sub % CH) * 8);
+      kraw[i] = u32x4{x.x, x.y, 0u, 0u};
+    }
 #pragma unroll
-  for (int i = 0; i < TS::GPT; ++i)
-    vraw[i] = *reinterpret_cast<const u32x4*>(v + TS::pick(gbase, i, half) + (size_t)(sub >> 1) * kGroupTokens + 8 * (sub & 1));
+    for (int i = 0; i < TS::GPT; ++i) {
+      const uint2 x = *reinterpret_cast<const uint2*>(vc + TS::pick(gbase, i, half) + (size_t)(sub >> 1) * kGroupTokens + 8 * (sub & 1));
+      vraw[i] = u32x4{x.x, x.y, 0u, 0u};
+    }
+    if (tid < 2 * kTileKeys) {  // key = tid % 128 of the tile: group key / 16, token key % 16
+      const int key = tid % kTileKeys;
+      const size_t row = gbase[key / kGroupTokens] / D + key % kGroupTokens;
+      *sc = tid < kTileKeys ? k_sc[row] : v_sc[row];
+    }
+  } else {
+    const uint16_t* kb = static_cast<const uint16_t*>(k);
+    const uint16_t* vb = static_cast<const uint16_t*>(v);
+#pragma unroll
+    for (int i = 0; i < TS::GPT; ++i)
+      kraw[i] = *reinterpret_cast<const u32x4*>(kb + TS::pick(gbase, i, half) + (size_t)(sub / CH) * D + (sub % CH) * 8);
+#pragma unroll
+    for (int i = 0; i < TS::GPT; ++i)
+      vraw[i] = *reinterpret_cast<const u32x4*>(vb + TS::pick(gbase, i, half) + (size_t)(sub >> 1) * kGroupTokens + 8 * (sub & 1));
+  }
+}
+
+// 8 E4M3FN codes (x.x, x.y) -> the same 8 values as bf16 (exact)
+__device__ __forceinline__ u32x4 fp8x8_bf16(u32x4 x) {
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.x, true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x.y, true);
+  return u32x4{pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f1[0], f1[1]), pack_bf16x2(f2[0], f2[1]),
+               pack_bf16x2(f3[0], f3[1])};
 }
 
 // The loaded tile into LDS.  V of a key that is missing (gpos < 0) or lies
 // after pos_last is stored as zero: an unwritten pool row may hold NaN, and
 // 0 x NaN would poison the product.  all_before (uniform): every group is
 // present and ends before the first query position, so nothing is masked.
-template <int D, int NTHR = 256>
+// FP8: codes become bf16 here, and the row scales (sc from load_tile) go to
+// sc_k / sc_v [128] (the V scale of a key that is masked as above is stored
+// as zero, so that it meets its zero probability as a zero).
+template <int D, int NTHR = 256, bool FP8 = false>
 __device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
                                            const u32x4 (&kraw)[TileStaging<NTHR>::GPT],
                                            const u32x4 (&vraw)[TileStaging<NTHR>::GPT],
                                            const int (&gpos)[kTileGroups], int pos_last, int tid,
-                                           bool all_before) {
+                                           bool all_before, float sc = 0.f, float* sc_k = nullptr,
+                                           float* sc_v = nullptr) {
   using TS = TileStaging<NTHR>;
   constexpr int CH = D / 8;
   const int sub = tid % 256, half = tid / 256;
+  if constexpr (FP8) {
+    if (tid < kTileKeys) {
+      sc_k[tid] = sc;
+    } else if (tid < 2 * kTileKeys) {
+      const int key = tid - kTileKeys, gp = gpos[key / kGroupTokens];
+      const bool keep = all_before || (gp >= 0 && gp + key % kGroupTokens <= pos_last);
+      sc_v[key] = keep ? sc : 0.f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TS::GPT; ++i) {
     const int it = TS::R * i + half;
     const int key = it * kGroupTokens + sub / CH, ch = sub % CH;
-    *reinterpret_cast<u32x4*>(ks + key * D + (ch ^ (key % CH)) * 8) = kraw[i];
+    *reinterpret_cast<u32x4*>(ks + key * D + (ch ^ (key % CH)) * 8) = FP8 ? fp8x8_bf16(kraw[i]) : kraw[i];
   }
   const int dim = sub >> 1, hf = sub & 1;
 #pragma unroll
   for (int i = 0; i < TS::GPT; ++i) {
     const int it = TS::R * i + half;
-    u32x4 x = vraw[i];
+    u32x4 x = FP8 ? fp8x8_bf16(vraw[i]) : vraw[i];
     if (!all_before) {  // uniform
       const int gp = TS::pick(gpos, i, half);
       uint32_t keep = 0u;
@@ -192,11 +246,12 @@ __device__ __forceinline__ void stage_tile(uint16_t* ks, uint16_t* vt,
 // reads of quarter t + 1 are issued before the products of quarter t
 // (scheduling barriers keep that order), so LDS latency hides under the
 // matrix-core work.
-template <int D>
+template <int D, bool FP8 = false>
 __device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&qop_hi)[D / 32],
                                              const bf16x8 (&qop_lo)[D / 32],
                                              const int (&gpos)[kTileGroups], int tau, int rl, int qg,
-                                             f32x4 (&s)[4][2], bool all_before) {
+                                             f32x4 (&s)[4][2], bool all_before,
+                                             const float* sc_k = nullptr) {
   constexpr int KS = D / 32;
   constexpr int NT = kTileGroups / 2;
   auto load_k = [&](int t, bf16x8 (&kop)[2][KS]) {
@@ -225,6 +280,18 @@ __device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (FP8) {  // the K row scale of key 32t + 16n + 4qg + i
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const float4 kq = *reinterpret_cast<const float4*>(sc_k + 32 * t + 16 * n + 4 * qg);
+        s[t][n][0] *= kq.x;
+        s[t][n][1] *= kq.y;
+        s[t][n][2] *= kq.z;
+        s[t][n][3] *= kq.w;
+      }
+  }
   float tmax = -INFINITY;
   if (!all_before) {  // uniform
 #pragma unroll
@@ -251,9 +318,10 @@ __device__ __forceinline__ float tile_scores(const uint16_t* ks, const bf16x8 (&
 // Probabilities p = 2^(s - mref) of the tile (added to the lane's l) and
 // O^T += V^T P^T.  The V^T operand reads of quarter t + 1 are issued with
 // the products of quarter t.
-template <int D>
+template <int D, bool FP8 = false>
 __device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][2], float mref, int rl,
-                                        int qg, float& l, f32x4 (&o)[D / 16]) {
+                                        int qg, float& l, f32x4 (&o)[D / 16],
+                                        const float* sc_v = nullptr) {
   constexpr int NB = D / 16;
   constexpr int NT = kTileGroups / 2;
   auto load_v = [&](int t, bf16x8 (&vop)[NB]) {
@@ -267,9 +335,14 @@ __device__ __forceinline__ void tile_pv(const uint16_t* vt, const f32x4 (&s)[4][
     uint32_t ph[4], pl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1)] - mref);
-      const float p1 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1) + 1] - mref);
+      float p0 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1)] - mref);
+      float p1 = __builtin_amdgcn_exp2f(s[t][k >> 1][2 * (k & 1) + 1] - mref);
       l += p0 + p1;
+      if constexpr (FP8) {  // the V row scale joins the probability
+        const int key = 32 * t + 16 * (k >> 1) + 4 * qg + 2 * (k & 1);
+        p0 *= sc_v[key];
+        p1 *= sc_v[key + 1];
+      }
       split_pair(p0, p1, ph[k], pl[k]);
     }
     hi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));

@@ -14,7 +14,8 @@
 // waves share the split's 128 keys, staged once in LDS.
 //
 // The split's 128 keys are one tile of hga_mfma_tile.h (LDS layouts, the
-// two contractions on the matrix cores).  The hi/lo split (x = hi + lo, both
+// two contractions on the matrix cores; the FP8 pool's codes and row
+// scales).  The hi/lo split (x = hi + lo, both
 // bf16) carries 16 significant bits of the query and of the probabilities;
 // K and V enter unrounded (they are bf16), so the products carry about
 // 2^-17 relative error before fp32 accumulation.
@@ -31,13 +32,15 @@
 
 namespace hga {
 
-template <int D, int HG>
+template <int D, int HG, bool FP8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attend_prefill_kernel(AttendArgs args) {
   static_assert(D == 128, "staging maps assume 16 chunks of 16 bytes per key row");
   constexpr int KS = D / 32;              // k-steps of the QK^T contraction
   constexpr int NB = D / 16;              // 16-dim blocks of the output
   __shared__ __align__(16) uint16_t ks[kTileKeys * D];   // [128 keys][D], swizzled
   __shared__ __align__(16) uint16_t vt[D * kTileKeys];   // [D][128 keys], swizzled
+  __shared__ __align__(16) float sc_k[FP8 ? kTileKeys : 1];  // FP8: row scales of the keys
+  __shared__ __align__(16) float sc_v[FP8 ? kTileKeys : 1];
 
   const KCfg& c = args.cfg;
   const AttendLaunch& a = args.a;
@@ -96,13 +99,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // ---- every K/V load of the split, issued before any is used; the query
   // is rotated while they are in flight
   u32x4 kraw[kSplitGroups], vraw[kSplitGroups];
-  load_tile<D>(static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), gbase, tid, kraw, vraw);
+  float sc = 0.f;
+  const float* k_sc = nullptr;
+  const float* v_sc = nullptr;
+  if constexpr (FP8) {  // the row scales follow the codes of every pool (or working-set) unit
+    const size_t codes =
+        (size_t)a.B * (a.src_layout == HGA_SRC_WORKING_SET ? c.lists : c.hkv) * a.src_cap * D;
+    k_sc = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.k) + codes);
+    v_sc = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v) + codes);
+  }
+  load_tile<D, 256, FP8>(a.k, a.v, gbase, tid, kraw, vraw, k_sc, v_sc, &sc);
   bf16x8 qop_hi[KS], qop_lo[KS];
   rotate_q<D>(c, qraw, pos0 + row, qg, qop_hi, qop_lo);
   bool all_before = true;  // every group present and before the query chunk (uniform)
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) all_before = all_before && gpos[g] >= 0 && gpos[g] + kGroupTokens <= pos0;
-  stage_tile<D>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before);
+  stage_tile<D, 256, FP8>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before, sc, sc_k, sc_v);
   __syncthreads();
   if (wave * 16 >= a.lq) return;  // no query rows in this wave
 
@@ -110,13 +122,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // split's 128 scores first, then the probabilities and O^T (no running
   // rescale inside a split)
   f32x4 s[4][2];
-  const float m = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gpos, pos0 + row, rl, qg, s, all_before));
+  const float m =
+      rows_max(tile_scores<D, FP8>(ks, qop_hi, qop_lo, gpos, pos0 + row, rl, qg, s, all_before, sc_k));
   const float mref = m == -INFINITY ? 0.f : m;  // a row with no visible key: p = 0
   float l = 0.f;
   f32x4 o[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tile_pv<D>(vt, s, mref, rl, qg, l, o);
+  tile_pv<D, FP8>(vt, s, mref, rl, qg, l, o, sc_v);
   l = rows_sum(l);
   const int ri = sp + record_base(a, lp);  // < n_splits for lists hga_route can write
   if (row < a.lq && ri < args.n_splits) {
@@ -134,6 +147,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 void launch_prefill(const AttendArgs& x, hipStream_t st) {
   const dim3 grid(x.grid_splits, x.cfg.hq, x.a.B);
+  if (x.cfg.pool8) {
+    switch (x.cfg.lhg) {
+      case 1: hipLaunchKernelGGL((attend_prefill_kernel<128, 1, true>), grid, dim3(256), 0, st, x); break;
+      case 2: hipLaunchKernelGGL((attend_prefill_kernel<128, 2, true>), grid, dim3(256), 0, st, x); break;
+      case 4: hipLaunchKernelGGL((attend_prefill_kernel<128, 4, true>), grid, dim3(256), 0, st, x); break;
+      default: hipLaunchKernelGGL((attend_prefill_kernel<128, 8, true>), grid, dim3(256), 0, st, x); break;
+    }
+    return;
+  }
   switch (x.cfg.lhg) {
     case 1: hipLaunchKernelGGL((attend_prefill_kernel<128, 1>), grid, dim3(256), 0, st, x); break;
     case 2: hipLaunchKernelGGL((attend_prefill_kernel<128, 2>), grid, dim3(256), 0, st, x); break;

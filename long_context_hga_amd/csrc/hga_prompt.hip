@@ -31,8 +31,9 @@ namespace hga {
 struct PromptArgs {
   KCfg cfg;
   const uint16_t* q;   // [Bp][Hq][T][d] bf16 raw queries
-  const uint16_t* k;   // pool [Bp][Hkv][cap][d]
-  const uint16_t* v;   // pool [Bp][Hkv][cap/16][d][16]
+  const void* k;       // pool [Bp][Hkv][cap][d] (FP8: codes, then row scales)
+  const void* v;       // pool [Bp][Hkv][cap/16][d][16]
+  int Bp;              // pool sequences
   const int* sel;      // [Bv][Hkv][max_sel], Bv = Bp * nq virtual sequences
   const int* n_sel;    // [Bv][Hkv]
   float* out;          // [Bp][Hq][T][d]
@@ -43,7 +44,7 @@ struct PromptArgs {
 constexpr int kXcds = 8;
 
 // HPW query heads per workgroup (2, or 1 when a KV head has one query head).
-template <int D, int HG, int HPW>
+template <int D, int HG, int HPW, bool FP8 = false>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) void attend_prompt_kernel(PromptArgs a) {
   static_assert(D == 128, "staging maps assume 16 chunks of 16 bytes per key row");
   static_assert(HG % HPW == 0, "head pairs");
@@ -53,6 +54,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
   constexpr int GPT = TileStaging<NTHR>::GPT;
   __shared__ __align__(16) uint16_t ks[kTileKeys * D];
   __shared__ __align__(16) uint16_t vt[D * kTileKeys];
+  __shared__ __align__(16) float sc_k[FP8 ? kTileKeys : 1];  // FP8: row scales of the keys
+  __shared__ __align__(16) float sc_v[FP8 ? kTileKeys : 1];
 
   const KCfg& c = a.cfg;
   const int per_xcd = (a.n_items + kXcds - 1) / kXcds;
@@ -82,6 +85,14 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   uint4 qraw[KS];
   load_q_raw<D>(a.q + tok * D, qg, qraw);
+  const float* k_sc = nullptr;
+  const float* v_sc = nullptr;
+  if constexpr (FP8) {  // the row scales follow the codes of every pool unit
+    const size_t codes = (size_t)a.Bp * c.hkv * a.cap * D;
+    k_sc = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.k) + codes);
+    v_sc = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v) + codes);
+  }
+  float sc = 0.f;
 
   if (n_sel < 0 || n_sel > a.max_sel) {  // uniform: no usable list
     const float nan = __builtin_nanf("");
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
   u32x4 kraw[GPT], vraw[GPT];
   if (n_tiles > 0) {
     tile_groups(0, gpos, gbase);
-    load_tile<D, NTHR>(a.k, a.v, gbase, tid, kraw, vraw);
+    load_tile<D, NTHR, FP8>(a.k, a.v, gbase, tid, kraw, vraw, k_sc, v_sc, &sc);
   }
   bf16x8 qop_hi[KS], qop_lo[KS];
   rotate_q<D>(c, qraw, tau, qg, qop_hi, qop_lo);
@@ -132,17 +143,18 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
     for (int it = 0; it < kTileGroups; ++it)
       all_before = all_before && gpos[it] >= 0 && gpos[it] + kGroupTokens <= pos0;
-    stage_tile<D, NTHR>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before);
+    stage_tile<D, NTHR, FP8>(ks, vt, kraw, vraw, gpos, pos_last, tid, all_before, sc, sc_k, sc_v);
     __syncthreads();
     int gcur[kTileGroups];
 #pragma unroll
     for (int it = 0; it < kTileGroups; ++it) gcur[it] = gpos[it];
     if (t + 1 < n_tiles) {  // the next tile's loads fly during this tile
       tile_groups(t + 1, gpos, gbase);
-      load_tile<D, NTHR>(a.k, a.v, gbase, tid, kraw, vraw);
+      load_tile<D, NTHR, FP8>(a.k, a.v, gbase, tid, kraw, vraw, k_sc, v_sc, &sc);
     }
     f32x4 s[4][2];
-    const float tmax = rows_max(tile_scores<D>(ks, qop_hi, qop_lo, gcur, tau, rl, qg, s, all_before));
+    const float tmax =
+        rows_max(tile_scores<D, FP8>(ks, qop_hi, qop_lo, gcur, tau, rl, qg, s, all_before, sc_k));
     const float mn = fmaxf(m, tmax);
     const float mref = mn == -INFINITY ? 0.f : mn;
     if (__ballot(mn != m)) {  // some row's maximum grew: rescale (by 1 where it did not)
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int n = 0; n < NB; ++n) o[n] *= al;
     }
     m = mn;
-    tile_pv<D>(vt, s, mref, rl, qg, l, o);
+    tile_pv<D, FP8>(vt, s, mref, rl, qg, l, o, sc_v);
   }
   l = rows_sum(l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -180,8 +192,9 @@ hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStrea
   PromptArgs a;
   a.cfg = cfg;
   a.q = static_cast<const uint16_t*>(p.q);
-  a.k = static_cast<const uint16_t*>(p.k);
-  a.v = static_cast<const uint16_t*>(p.v);
+  a.k = p.k;
+  a.v = p.v;
+  a.Bp = p.B;
   a.sel = p.sel;
   a.n_sel = p.n_sel;
   a.out = p.out;
@@ -193,6 +206,15 @@ hipError_t launch_prompt_attend(const KCfg& cfg, const PromptLaunch& p, hipStrea
   const int hpw = cfg.hg >= 2 ? 2 : 1;
   a.n_items = p.B * p.nq * cfg.hkv * (cfg.hg / hpw);
   const dim3 grid((unsigned)((a.n_items + kXcds - 1) / kXcds * kXcds));
+  if (cfg.pool8) {
+    switch (cfg.hg) {
+      case 1: hipLaunchKernelGGL((attend_prompt_kernel<128, 1, 1, true>), grid, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((attend_prompt_kernel<128, 2, 2, true>), grid, dim3(512), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((attend_prompt_kernel<128, 4, 2, true>), grid, dim3(512), 0, st, a); break;
+      default: hipLaunchKernelGGL((attend_prompt_kernel<128, 8, 2, true>), grid, dim3(512), 0, st, a); break;
+    }
+    return hipGetLastError();
+  }
   switch (cfg.hg) {
     case 1: hipLaunchKernelGGL((attend_prompt_kernel<128, 1, 1>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((attend_prompt_kernel<128, 2, 2>), grid, dim3(512), 0, st, a); break;

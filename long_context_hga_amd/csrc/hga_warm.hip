@@ -9,8 +9,9 @@
 // moves only the selected group across PCIe.
 //
 // Per (sequence, list) unit the cache has n_warm slots, each one group of K
-// (4 KiB at d = 128, bf16) and its V^T block, with a tag (group id, -1 =
-// empty) and the step that last used it.  One call:
+// (4 KiB at d = 128, bf16; with the FP8 pool its codes, the cache's row
+// scales following the codes of every slot) and its V^T block, with a tag
+// (group id, -1 = empty) and the step that last used it.  One call:
 //   warm_update_kernel (one workgroup per unit): the tags go into an LDS
 //     hash table; the routed groups of the unit's list found there are hits
 //     (their stamps renewed); the i-th miss in list order takes the i-th
@@ -43,6 +44,14 @@ struct WarmArgs {
   int* slot_of;        // workspace [units][max_sel]: cache slot of a routed list position, else -1
   int* src_of;         // workspace [units][max_sel]: group to fetch (miss), -1 for a hit
   int lists, hkv, kvdiv, n_sink, n_local, cap, max_sel, W, step, row_vecs;
+  // FP8 pool: the row scales after the codes of the host pool, the cache and
+  // the working set (null otherwise)
+  const float* k_sc_cold;
+  const float* v_sc_cold;
+  float* k_sc_warm;
+  float* v_sc_warm;
+  float* k_sc_ws;
+  float* v_sc_ws;
 };
 
 constexpr int kMaxWarm = 1024;  // slots per unit
@@ -186,6 +195,10 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(WarmArgs a, int n_items)
     const int src = a.src_of[(size_t)unit * a.max_sel + p];
     const size_t wdst = ((size_t)unit * a.W + slot) * n;
     const size_t dst = ((size_t)unit * a.max_sel + p) * n;
+    // FP8: the 16 row scales of K and V of the group (token rows of the slot)
+    const size_t wsd = ((size_t)unit * a.W + slot) * kGroupTokens + threadIdx.x;
+    const size_t sd = ((size_t)unit * a.max_sel + p) * kGroupTokens + threadIdx.x;
+    const bool scales = a.k_sc_cold && threadIdx.x < kGroupTokens;
     if (src >= 0) {  // miss: host pool -> cache slot and working set
       const int unit_p = (unit / a.lists) * a.hkv + (unit % a.lists) / a.kvdiv;
       const size_t from = ((size_t)unit_p * a.cap + (size_t)src * kGroupTokens) * a.row_vecs;
@@ -197,12 +210,24 @@ __global__ __launch_bounds__(256) void warm_fill_kernel(WarmArgs a, int n_items)
         a.k_ws[dst + i] = kv;
         a.v_ws[dst + i] = vv;
       }
+      if (scales) {
+        const size_t ss = (size_t)unit_p * a.cap + (size_t)src * kGroupTokens + threadIdx.x;
+        const float ks = a.k_sc_cold[ss], vs = a.v_sc_cold[ss];
+        a.k_sc_warm[wsd] = ks;
+        a.v_sc_warm[wsd] = vs;
+        a.k_sc_ws[sd] = ks;
+        a.v_sc_ws[sd] = vs;
+      }
     } else {  // hit: cache slot -> working set
       for (int i = threadIdx.x; i < n; i += 256) {
         const uint4 kv = a.k_warm[wdst + i];
         const uint4 vv = a.v_warm[wdst + i];
         a.k_ws[dst + i] = kv;
         a.v_ws[dst + i] = vv;
+      }
+      if (scales) {
+        a.k_sc_ws[sd] = a.k_sc_warm[wsd];
+        a.v_sc_ws[sd] = a.v_sc_warm[wsd];
       }
     }
   }
@@ -237,7 +262,23 @@ hipError_t launch_warm(const KCfg& cfg, int B, const void* k_cold, const void* v
   a.max_sel = max_sel;
   a.W = n_warm;
   a.step = step;
-  a.row_vecs = cfg.d * (cfg.dtype == HGA_BF16 ? 2 : 4) / 16;
+  a.row_vecs = cfg.d * (cfg.pool8 ? 1 : (cfg.dtype == HGA_BF16 ? 2 : 4)) / 16;
+  a.k_sc_cold = a.v_sc_cold = nullptr;
+  a.k_sc_warm = a.v_sc_warm = a.k_sc_ws = a.v_sc_ws = nullptr;
+  if (cfg.pool8) {  // codes of every unit, then the row scales
+    auto after = [&](const void* p, size_t codes) {
+      return reinterpret_cast<const float*>(static_cast<const char*>(p) + codes);
+    };
+    const size_t cold = (size_t)B * cfg.hkv * cap * cfg.d;
+    const size_t warm = (size_t)units * n_warm * kGroupTokens * cfg.d;
+    const size_t wset = (size_t)units * max_sel * kGroupTokens * cfg.d;
+    a.k_sc_cold = after(k_cold, cold);
+    a.v_sc_cold = after(v_cold, cold);
+    a.k_sc_warm = const_cast<float*>(after(k_warm, warm));
+    a.v_sc_warm = const_cast<float*>(after(v_warm, warm));
+    a.k_sc_ws = const_cast<float*>(after(k_ws, wset));
+    a.v_sc_ws = const_cast<float*>(after(v_ws, wset));
+  }
   hipLaunchKernelGGL(warm_update_kernel, dim3(units), dim3(256), 0, st, a);
   const int n_items = units * max_sel;
   const int n_wg = n_items < 256 ? n_items : 256;

@@ -5,9 +5,11 @@ power-of-two row scale.
 The append is compared with the oracle's quantiser (values exact: the same
 codes and scales; keys: the same scales and codes except where the two fp64
 rotations fall on either side of a rounding tie, which must stay rare and one
-code apart).  Decode attention on the FP8 pool is compared with the oracle
-run on the GPU's own dequantised pool (tests/oracle_ref.py tolerance), and
-the fused decode step with the separate calls (bit-identical)."""
+code apart).  Decode, chunked-prefill, whole-prompt and host-tier attention
+on the FP8 pool are compared with the oracle run on its own FP8 pool
+(tests/oracle_ref.py tolerance); the gather and the warm tier copy codes and
+row scales bit for bit; attention over an FP8 working set equals attention
+over the pool, and the fused steps equal the separate calls (bit-identical)."""
 import numpy as np
 import pytest
 
@@ -342,3 +344,198 @@ def test_fp8_tiered_against_device_path_and_oracle(form):
             g = s.sel[b, h, :int(s.n_sel[b, h])].cpu().numpy()
             o_ref, _ = oracle.attend(cfg, inp.f64(qh[b, h * 8:(h + 1) * 8]), pos, kd, vd, g)
             assert max_abs(o[b, h * 8:(h + 1) * 8], o_ref) <= ATOL_OUT, (b, h)
+
+
+def test_fp8_warm_tier_equals_gather():
+    """The warm tier on the FP8 pool: over drifting decode steps the working
+    set's routed slots (codes and row scales) equal what hga_gather copies
+    from the pinned host pool, and the attention through the cache equals the
+    device path within the merge's rounding."""
+    inp, st, pool = fp8_state(batch=2, context=8192)
+    B, T, ms, n_warm = st.B, st.T, st.max_sel, 208
+    kc, vc = pinned(pool.k), pinned(pool.v)
+    units = B * 4
+    k_warm = torch.zeros(units * n_warm * 16 * (128 + 4), dtype=torch.uint8, device="cuda")
+    v_warm = torch.zeros_like(k_warm)
+    tags = torch.full((B, 4, n_warm), -1, dtype=torch.int32, device="cuda")
+    used = torch.zeros((B, 4, n_warm), dtype=torch.int32, device="cuda")
+    hits = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+    wsw = torch.zeros(hga.hga_warm_workspace_bytes(st.cfg, B, ms), dtype=torch.uint8,
+                      device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    qf = gh.query_slice(st, 0).view(torch.bfloat16).float()
+    total_hits = 0
+    for step in range(1, 7):
+        q = qf.to(torch.bfloat16).view(torch.int16).contiguous()
+        s = gh.alloc_step(st, 1)
+        gh.route(st, q, 1, st.pos0, s)
+        kw, vw = fp8_ws(B, 4, ms)
+        hga.hga_warm_gather(st.cfg, B, kc, vc, T, s.sel, s.n_sel, ms, st.pos0, k_warm, v_warm,
+                            tags, used, n_warm, step, kw, vw, hits, wsw)
+        kr, vr = fp8_ws(B, 4, ms)
+        hga.hga_gather(st.cfg, B, kc, vc, T, 1, s.sel, s.n_sel, ms, st.pos0,
+                       hga.HGA_PART_ROUTED, kr, vr)
+        oa, la = torch.empty_like(s.out), torch.empty_like(s.lse)
+        ob, lb = torch.empty_like(s.out), torch.empty_like(s.lse)
+        hga.hga_attend(st.cfg, B, q, 1, st.pos0, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel,
+                       s.n_sel, ms, hga.HGA_PART_WINDOWS, oa, la, st.ws)
+        hga.hga_attend(st.cfg, B, q, 1, st.pos0, kw, vw, hga.HGA_SRC_WORKING_SET, 0, s.sel,
+                       s.n_sel, ms, hga.HGA_PART_ROUTED, ob, lb, torch.zeros_like(st.ws))
+        out, lse = torch.empty_like(s.out), torch.empty_like(s.lse)
+        hga.hga_merge_partials(st.cfg, B, 1, oa, la, ob, lb, out, lse)
+        hga.hga_attend(st.cfg, B, q, 1, st.pos0, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel,
+                       s.n_sel, ms, hga.HGA_PART_ALL, s.out, s.lse, st.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(kw, kr) and torch.equal(vw, vr), step
+        assert (out - s.out).abs().max().item() <= 1e-5, step
+        total_hits += int(hits.sum().item())
+        qf = (qf + 0.25 * torch.randn(qf.shape, generator=gen, device="cuda")) / (1 + 0.0625) ** 0.5
+    assert total_hits > 0  # the drifting queries reuse cached groups
+
+
+def fp8_oracle_pool(inp, cfg, b, h):
+    """The oracle's own FP8 pool of unit (b, h), dequantised: keys, values."""
+    return (oracle.pool_fp8(cfg, inp.f64(inp.k[b, h]), 0)[2],
+            oracle.fp8_rows(inp.f64(inp.v[b, h]))[2])
+
+
+def test_fp8_prefill_chunk_against_oracle_and_working_set():
+    """A 64-token query chunk (the MFMA prefill kernel) on the FP8 pool
+    against the oracle run on its own FP8 pool; the same attention over an
+    FP8 working set gives the same bits."""
+    inp = synth.generate("prefill32k", context=4096, overrides=dict(pool_dtype=1))
+    st = gh.build_state(inp)
+    B, T, ms = st.B, st.T, st.max_sel
+    pool = Fp8Pool(B, 4, T, 128)
+    hga.hga_build_summaries(st.cfg, B, st.k_raw, st.v_raw, 0, T, pool.k, pool.v, T, None, None,
+                            st.max_chunks)
+    cfg = oracle.cfg_from(inp.params)
+    pos = int(inp.pos0[0])
+    q = st.q.contiguous()
+    lq = q.shape[2]
+    s = gh.alloc_step(st, lq)
+    gh.route(st, q, lq, st.pos0, s)
+    hga.hga_attend(st.cfg, B, q, lq, st.pos0, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel, s.n_sel,
+                   ms, hga.HGA_PART_ALL, s.out, s.lse, st.ws)
+    kw, vw = fp8_ws(B, 4, ms)
+    hga.hga_gather(st.cfg, B, pool.k, pool.v, T, 0, s.sel, s.n_sel, ms, st.pos0, hga.HGA_PART_ALL,
+                   kw, vw)
+    ow, lw = torch.empty_like(s.out), torch.empty_like(s.lse)
+    hga.hga_attend(st.cfg, B, q, lq, st.pos0, kw, vw, hga.HGA_SRC_WORKING_SET, 0, s.sel, s.n_sel,
+                   ms, hga.HGA_PART_ALL, ow, lw, st.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ow, s.out) and torch.equal(lw, s.lse)
+    out, lse = s.out.cpu().numpy(), s.lse.cpu().numpy()
+    for b in range(B):
+        for h in range(4):
+            kd, vd = fp8_oracle_pool(inp, cfg, b, h)
+            g = s.sel[b, h, :int(s.n_sel[b, h])].cpu().numpy()
+            o_ref, l_ref = oracle.attend(cfg, q_unit(inp, cfg, b, h, 0, lq), pos, kd, vd, g)
+            assert max_abs(out[b, h * 8:(h + 1) * 8], o_ref) <= ATOL_OUT, (b, h)
+            assert max_abs(lse[b, h * 8:(h + 1) * 8], l_ref) <= 1e-3, (b, h)
+
+
+def test_fp8_prefill_step_64_tokens_equals_separate_calls():
+    """hga_prefill_step with a whole 64-token chunk on the FP8 pool: the
+    chunk's tokens appended, its summaries built, routed and attended by the
+    MFMA kernel; the bits of the separate calls."""
+    inp, st, _ = fp8_state(batch=2, context=4096, max_lq=64)
+    B, T, lq, pos = st.B, st.T, 64, 20 * 64
+    q = st.q[:, :, :1].repeat(1, 1, lq, 1).contiguous()
+    pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+    kn = st.k_raw[:, :, pos:pos + lq].contiguous()
+    vn = st.v_raw[:, :, pos:pos + lq].contiguous()
+
+    def fresh():
+        pool = Fp8Pool(B, 4, T, 128)
+        cs, gs = torch.zeros_like(st.chunk_sum), torch.zeros_like(st.group_sum)
+        hga.hga_build_summaries(st.cfg, B, st.k_raw[:, :, :pos].contiguous(),
+                                st.v_raw[:, :, :pos].contiguous(), 0, pos, pool.k, pool.v, T, cs,
+                                gs, st.max_chunks)
+        return pool, cs, gs
+
+    pa, csa, gsa = fresh()
+    sa = gh.alloc_step(st, lq)
+    hga.hga_build_summaries(st.cfg, B, kn, vn, pos, lq, pa.k, pa.v, T, csa, gsa, st.max_chunks)
+    hga.hga_route(st.cfg, B, q, lq, pos_t, csa, gsa, st.max_chunks, sa.sel, sa.n_sel, st.max_sel,
+                  None, st.ws)
+    hga.hga_attend(st.cfg, B, q, lq, pos_t, pa.k, pa.v, hga.HGA_SRC_POOL, T, sa.sel, sa.n_sel,
+                   st.max_sel, hga.HGA_PART_ALL, sa.out, sa.lse, st.ws)
+    pb, csb, gsb = fresh()
+    sb = gh.alloc_step(st, lq)
+    hga.hga_prefill_step(st.cfg, B, q, lq, kn, vn, pos_t, pb.k, pb.v, T,
+                         torch.zeros_like(st.k_raw[:, :, :64]), csb, gsb, st.max_chunks, sb.sel,
+                         sb.n_sel, st.max_sel, sb.out, sb.lse, torch.zeros_like(st.ws))
+    torch.cuda.synchronize()
+    assert torch.equal(sa.n_sel, sb.n_sel) and torch.equal(sa.sel, sb.sel)
+    assert torch.equal(sa.out, sb.out) and torch.equal(sa.lse, sb.lse)
+    assert torch.equal(pa.k, pb.k) and torch.equal(pa.v, pb.v)
+    assert torch.equal(csa, csb) and torch.equal(gsa, gsb)
+
+
+def test_fp8_tiered_prefill_chunk_equals_device_path():
+    """A 64-token query chunk through the host tier on the FP8 pool (both
+    parts on the MFMA prefill kernel) equals the device path within the
+    merge's rounding."""
+    inp = synth.generate("prefill32k", context=4096, overrides=dict(pool_dtype=1))
+    st = gh.build_state(inp)
+    B, T, ms = st.B, st.T, st.max_sel
+    pool = Fp8Pool(B, 4, T, 128)
+    hga.hga_build_summaries(st.cfg, B, st.k_raw, st.v_raw, 0, T, pool.k, pool.v, T, None, None,
+                            st.max_chunks)
+    kc, vc = pinned(pool.k), pinned(pool.v)
+    q = st.q.contiguous()
+    lq = q.shape[2]
+    s = gh.alloc_step(st, lq)
+    gh.route(st, q, lq, st.pos0, s)
+    hga.hga_attend(st.cfg, B, q, lq, st.pos0, pool.k, pool.v, hga.HGA_SRC_POOL, T, s.sel, s.n_sel,
+                   ms, hga.HGA_PART_ALL, s.out, s.lse, st.ws)
+    for side in (torch.cuda.Stream(), None):
+        kw, vw = fp8_ws(B, 4, ms)
+        out = torch.full_like(s.out, float("nan"))
+        lse = torch.full_like(s.lse, float("nan"))
+        hga.hga_attend_tiered(st.cfg, B, q, lq, st.pos0, pool.k, pool.v, T, kc, vc, T, s.sel,
+                              s.n_sel, ms, kw, vw, out, lse, torch.zeros_like(st.ws),
+                              stream_b=side, events=(torch.cuda.Event(), torch.cuda.Event()))
+        torch.cuda.synchronize()
+        assert (out - s.out).abs().max().item() <= 1e-5
+        assert (lse - s.lse).abs().max().item() <= 1e-5
+
+
+def test_fp8_prompt_against_oracle():
+    """The whole-prompt prefill on the FP8 pool (2K prompt): the append phase
+    writes the FP8 pool hga_build_summaries writes, and sampled query chunks
+    (windows only up to routed) match the oracle run on its own FP8 pool."""
+    inp = synth.generate("prompt32k", context=2048, overrides=dict(pool_dtype=1))
+    st = gh.build_state(inp, max_lq=64)
+    B, T, ms = st.B, st.T, st.max_sel
+    nq = T // 64
+    ref = Fp8Pool(B, 4, T, 128)
+    hga.hga_build_summaries(st.cfg, B, st.k_raw, st.v_raw, 0, T, ref.k, ref.v, T, None, None,
+                            st.max_chunks)
+    pool = Fp8Pool(B, 4, T, 128)
+    cs, gs = torch.zeros_like(st.chunk_sum), torch.zeros_like(st.group_sum)
+    sel = torch.full((B, nq, 4, ms), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((B, nq, 4), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, 32, T, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, 32, T), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(hga.hga_prompt_workspace_bytes(st.cfg, B, T, st.max_chunks),
+                     dtype=torch.uint8, device="cuda")
+    hga.hga_prefill_prompt(st.cfg, B, T, st.q, st.k_raw, st.v_raw, pool.k, pool.v, T, cs, gs,
+                           st.max_chunks, sel, n_sel, ms, out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k, ref.k) and torch.equal(pool.v, ref.v)
+    assert torch.equal(cs, st.chunk_sum) and torch.equal(gs, st.group_sum)
+    assert torch.isfinite(out).all()
+    cfg = oracle.cfg_from(inp.params)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    sl, ns = sel.cpu().numpy(), n_sel.cpu().numpy()
+    for b in range(B):
+        for h in range(4):
+            kd, vd = fp8_oracle_pool(inp, cfg, b, h)
+            for qc in (0, 3, 11, 31):
+                p0 = qc * 64
+                g = sl[b, qc, h, :ns[b, qc, h]]
+                o_ref, l_ref = oracle.attend(cfg, q_unit(inp, cfg, b, h, p0, 64), p0, kd, vd, g)
+                assert max_abs(o[b, h * 8:(h + 1) * 8, p0:p0 + 64], o_ref) <= ATOL_OUT, (b, h, qc)
+                assert max_abs(l[b, h * 8:(h + 1) * 8, p0:p0 + 64], l_ref) <= 1e-3, (b, h, qc)
