@@ -116,7 +116,7 @@ int main(void) {
   EXPECT(hga_prefill_step(&c, 8, FAKE, 65, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, FAKE,
                           1024, FAKE, FAKE, 128, FAKE, NULL, FAKE, 1u << 30, NULL),
          HGA_ERR_INVALID_ARGUMENT);
-  b = c; b.pool_dtype = 1;
+  b = c; b.pool_dtype = 1; b.qkv_dtype = HGA_F32;  /* the FP8 pool takes bf16 inputs */
   EXPECT(hga_prefill_step(&b, 8, FAKE, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, FAKE, FAKE, FAKE,
                           1024, FAKE, FAKE, 128, FAKE, NULL, FAKE, 1u << 30, NULL),
          HGA_ERR_UNSUPPORTED);
