@@ -257,6 +257,8 @@ def main():
                          "64-token query chunk at 32K context (MFMA attention); host64k: "
                          "batch-4 64K decode with the pool in pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="host64k: the K/V pool (host, windows, working sets, cache) in FP8")
     ap.add_argument("--sweep", action="store_true",
                     help="decode sweep over context 4K..64K and batch 8..32 (one JSON line "
                          "per point) instead of the benchmark line")
@@ -899,10 +901,18 @@ def run_host64k(args):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    inp = synth.generate("host64k")
+    fp8 = bool(args.fp8)
+    inp = synth.generate("host64k", overrides=dict(pool_dtype=1) if fp8 else None)
     p = inp.params
     B, T = p["batch"], p["context"]
     st = gh.build_state(inp)
+    if fp8:  # the FP8 pool: codes then row scales, built from the raw K/V
+        nbytes = B * p["n_kv_heads"] * T * (p["head_dim"] + 4)
+        st.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        st.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        hga.hga_build_summaries(st.cfg, B, st.k_raw, st.v_raw, 0, T, st.k_pool, st.v_pool, T, None,
+                                None, st.max_chunks)
+        torch.cuda.synchronize()
     k_cold = torch.empty(st.k_pool.shape, dtype=st.k_pool.dtype, pin_memory=True)
     v_cold = torch.empty(st.v_pool.shape, dtype=st.v_pool.dtype, pin_memory=True)
     k_cold.copy_(st.k_pool)
@@ -917,7 +927,10 @@ def run_host64k(args):
     del st.k_raw, st.v_raw
     cfg = st.cfg
     hkv, d = p["n_kv_heads"], p["head_dim"]
-    kw = torch.zeros((B, hkv, st.max_sel * 16, d), dtype=st.k_pool.dtype, device="cuda")
+    if fp8:  # working set: codes then row scales
+        kw = torch.zeros(B * hkv * st.max_sel * 16 * (d + 4), dtype=torch.uint8, device="cuda")
+    else:
+        kw = torch.zeros((B, hkv, st.max_sel * 16, d), dtype=st.k_pool.dtype, device="cuda")
     vw = torch.zeros_like(kw)
     s = gh.alloc_step(st, 1)
     side = torch.cuda.Stream()
@@ -984,7 +997,10 @@ def run_host64k(args):
     # sequence of queries that drift (q <- (q + eps z) / sqrt(1 + eps^2), z
     # ~ N(0, 1), seeded): consecutive steps route to overlapping groups
     n_warm, eps, n_warm_steps = 2 * p["topk_groups"], 0.25, max(32, n // 4)
-    k_warm = torch.zeros((B, hkv, n_warm, 16, d), dtype=st.k_pool.dtype, device="cuda")
+    if fp8:  # cache slots: codes then row scales
+        k_warm = torch.zeros(B * hkv * n_warm * 16 * (d + 4), dtype=torch.uint8, device="cuda")
+    else:
+        k_warm = torch.zeros((B, hkv, n_warm, 16, d), dtype=st.k_pool.dtype, device="cuda")
     v_warm = torch.zeros_like(k_warm)
     w_tags = torch.full((B, hkv, n_warm), -1, dtype=torch.int32, device="cuda")
     w_used = torch.zeros((B, hkv, n_warm), dtype=torch.int32, device="cuda")
@@ -1093,7 +1109,7 @@ def run_host64k(args):
     h2d_gbs = (256 << 20) / (t_h2d * 1e-3) / 1e9
     routed_groups = int((s.n_sel.cpu().numpy() - (p["n_sink_chunks"] + p["n_local_chunks"] + 1)
                          * p["groups_per_chunk"]).sum())
-    routed_bytes = routed_groups * 16 * d * 2 * 2
+    routed_bytes = routed_groups * 16 * ((d + 4) if fp8 else d * 2) * 2
     pcie_gbs = routed_bytes / (t_gather * 1e-3) / 1e9
     def overlap_of(t):
         return 1.0 - (t - max(t_routed, t_windows)) / min(t_routed, t_windows)
@@ -1113,7 +1129,10 @@ def run_host64k(args):
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, pre-RoPE)",
         "config": {"workload": "host64k: GQA 32q/4kv heads, d=128, bf16, ctx 65536, batch 4 decode "
                                "at t=65535, top-52 chunks, top-104 groups; full K/V pool in pinned "
-                               "host memory, windows and summaries in HBM",
+                               "host memory, windows and summaries in HBM"
+                               + ("; FP8 pool (E4M3FN codes + power-of-two row scales)" if fp8
+                                  else ""),
+                   "pool": "fp8" if fp8 else "bf16",
                    "batch": B, "context": T, "timing": "eager, events around each step",
                    "tier_form": "one launch" if ms_one <= ms_two else "two streams",
                    "ms_per_step_one_launch": ms_one, "ms_per_step_two_streams": ms_two},
