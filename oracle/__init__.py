@@ -44,6 +44,7 @@ class OraCfg(ctypes.Structure):
         ("pool_bf16", ctypes.c_int),
         ("rep_integer", ctypes.c_int),
         ("rope_interleaved", ctypes.c_int),
+        ("route_max", ctypes.c_int),
     ]
 
 
@@ -122,21 +123,23 @@ def _i(a):
 
 
 def make_cfg(d, hq, hkv, C, G, n_sink, n_local, topk_c, topk_g, theta, hf_wavelength,
-             pool_bf16=True, rep_integer=False, rope_interleaved=False) -> OraCfg:
+             pool_bf16=True, rep_integer=False, rope_interleaved=False,
+             route_max=False) -> OraCfg:
     return OraCfg(d, hq, hkv, C, G, n_sink, n_local, topk_c, topk_g, float(theta),
                   float(hf_wavelength), int(bool(pool_bf16)), int(bool(rep_integer)),
-                  int(bool(rope_interleaved)))
+                  int(bool(rope_interleaved)), int(bool(route_max)))
 
 
 def cfg_from(p: dict) -> OraCfg:
     """Build the oracle config from a plain dict (keys as in ``synth.CONFIGS``;
     ``rep_position`` 1 selects the representative position a + n/2,
-    ``rope_style`` 1 interleaved RoPE pairs)."""
+    ``rope_style`` 1 interleaved RoPE pairs, ``route_pool`` 1 the max-pooled
+    routing query)."""
     return make_cfg(p["head_dim"], p["n_q_heads"], p["n_kv_heads"], p["chunk_size"],
                     p["groups_per_chunk"], p["n_sink_chunks"], p["n_local_chunks"],
                     p["topk_chunks"], p["topk_groups"], p["rope_theta"], p["hf_wavelength"],
                     p["dtype"] == "bf16", p.get("rep_position", 0) == 1,
-                    p.get("rope_style", 0) == 1)
+                    p.get("rope_style", 0) == 1, p.get("route_pool", 0) == 1)
 
 
 def omega(cfg, j):

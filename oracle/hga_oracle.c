@@ -64,6 +64,9 @@ typedef struct {
   int pool_bf16;      /* 1: pool keys stored as bf16 (RNE); 0: as fp32 (RNE) */
   int rep_integer;    /* representative position of a span: 0: a + (n-1)/2; 1: a + n/2 */
   int rope_interleaved; /* RoPE pairs: 0: (x_j, x_{j+d/2}); 1: (x_{2j}, x_{2j+1}) */
+  int route_max;      /* routing query of a KV head's query heads: 0: their mean;
+                         1: each head's own (mean over the query tokens), a
+                         candidate scoring the largest of the heads' scores */
 } ora_cfg;
 
 /* ---------------------------------------------------------------- RoPE
@@ -311,17 +314,43 @@ void ora_pooled_query(const ora_cfg* c, const double* q, int hg, int lq, long po
   free(tmp);
 }
 
-/* Level-2 routing score of every group id g < n_groups:
- * qbar . group_sum[g] / sqrt(d), with qbar the pooled routing query that
- * ora_select forms from q [hg][lq][d] at positions pos0.. (the scores of the
- * groups of the chosen chunks are the ones level 2 ranks). */
+/* The routing queries of one KV head from q [hg][lq][d] at positions pos0..
+ * into qb: one (route_max = 0: the mean of every rotated query row of the
+ * head's query heads and tokens) or hg (route_max = 1: per query head, the
+ * mean of its rotated query tokens).  Returns their number. */
+static int ora_route_queries(const ora_cfg* c, const double* q, int hg, int lq, long pos0,
+                             double* qb) {
+  int d = c->d;
+  if (!c->route_max) {
+    ora_pooled_query(c, q, hg, lq, pos0, qb);
+    return 1;
+  }
+  for (int h = 0; h < hg; ++h) ora_pooled_query(c, q + (long)h * lq * d, 1, lq, pos0, qb + (long)h * d);
+  return hg;
+}
+
+/* Routing score of a summary row s: the largest of qb[i] . s / sqrt(d) over
+ * the nq routing queries (the only one with the mean query). */
+static double ora_route_score(const double* qb, int nq, const double* s, int d, double inv_sqrt_d) {
+  double best = -INFINITY;
+  for (int i = 0; i < nq; ++i) {
+    const double v = dot(qb + (long)i * d, s, d) * inv_sqrt_d;
+    if (v > best) best = v;
+  }
+  return best;
+}
+
+/* Level-2 routing score of every group id g < n_groups against the routing
+ * queries that ora_select forms from q [hg][lq][d] at positions pos0.. (the
+ * scores of the groups of the chosen chunks are the ones level 2 ranks). */
 void ora_group_scores(const ora_cfg* c, const double* q, int lq, long pos0,
                       const double* group_sum, long n_groups, double* out) {
   int d = c->d, hg = c->hq / c->hkv;
-  double* qbar = (double*)malloc(sizeof(double) * d);
-  ora_pooled_query(c, q, hg, lq, pos0, qbar);
-  for (long g = 0; g < n_groups; ++g) out[g] = dot(qbar, group_sum + g * d, d) / sqrt((double)d);
-  free(qbar);
+  double* qb = (double*)malloc(sizeof(double) * d * hg);
+  const int nq = ora_route_queries(c, q, hg, lq, pos0, qb);
+  for (long g = 0; g < n_groups; ++g)
+    out[g] = ora_route_score(qb, nq, group_sum + g * d, d, 1.0 / sqrt((double)d));
+  free(qb);
 }
 
 /* Two-level selection for one (sequence, KV head).
@@ -343,8 +372,8 @@ int ora_select(const ora_cfg* c, const double* q, int lq, long pos0, const doubl
   long last = pos0 + lq - 1;
   double inv_sqrt_d = 1.0 / sqrt((double)d);
 
-  double* qbar = (double*)malloc(sizeof(double) * d);
-  ora_pooled_query(c, q, hg, lq, pos0, qbar);
+  double* qb = (double*)malloc(sizeof(double) * d * hg);
+  const int nq = ora_route_queries(c, q, hg, lq, pos0, qb);
 
   long* win = (long*)malloc(sizeof(long) * (ct + 1));
   long lo, hi;
@@ -355,7 +384,7 @@ int ora_select(const ora_cfg* c, const double* q, int lq, long pos0, const doubl
   ora_item* l1 = (ora_item*)malloc(sizeof(ora_item) * (ncand > 0 ? ncand : 1));
   for (long i = 0; i < ncand; ++i) {
     l1[i].id = lo + i;
-    l1[i].s = dot(qbar, chunk_sum + (lo + i) * d, d) * inv_sqrt_d;
+    l1[i].s = ora_route_score(qb, nq, chunk_sum + (lo + i) * d, d, inv_sqrt_d);
     if (cand_scores) cand_scores[i] = l1[i].s;
   }
   qsort(l1, ncand, sizeof(ora_item), by_score_desc_id_asc);
@@ -370,7 +399,7 @@ int ora_select(const ora_cfg* c, const double* q, int lq, long pos0, const doubl
     for (int j = 0; j < G; ++j) {
       long gid = l1[i].id * G + j;
       l2[i * G + j].id = gid;
-      l2[i * G + j].s = dot(qbar, group_sum + gid * d, d) * inv_sqrt_d;
+      l2[i * G + j].s = ora_route_score(qb, nq, group_sum + gid * d, d, inv_sqrt_d);
     }
   qsort(l2, n2, sizeof(ora_item), by_score_desc_id_asc);
   long k2 = c->topk_g < n2 ? c->topk_g : n2;
@@ -395,7 +424,7 @@ int ora_select(const ora_cfg* c, const double* q, int lq, long pos0, const doubl
   free(l2);
   free(l1);
   free(win);
-  free(qbar);
+  free(qb);
   return ret;
 }
 

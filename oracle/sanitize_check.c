@@ -16,7 +16,7 @@
 typedef struct {
   int d, hq, hkv, C, G, n_sink, n_local, topk_c, topk_g;
   double theta, hf_wavelength;
-  int pool_bf16, rep_integer, rope_interleaved;
+  int pool_bf16, rep_integer, rope_interleaved, route_max;
 } ora_cfg;
 
 double ora_omega(const ora_cfg* c, int j);
@@ -69,7 +69,8 @@ int main(void) {
   const int d = 64, hq = 4, hkv = 2, hg = 2, T = 1024, C = 64, G = 4;
   const long nch = T / C;
   for (int variant = 0; variant < 4; ++variant) {
-    ora_cfg c = {d, hq, hkv, C, G, 1, 2, 3, 6, 1e4, 64.0, variant & 1, variant >> 1, variant & 1};
+    ora_cfg c = {d, hq, hkv, C, G, 1, 2, 3, 6, 1e4, 64.0, variant & 1, variant >> 1, variant & 1,
+                 variant >> 1};
     double* kraw = randv((long)T * d);
     double* v = randv((long)T * d);
     double* q = randv((long)hg * 3 * d);

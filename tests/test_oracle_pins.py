@@ -685,3 +685,50 @@ def test_warm_policy_invariants_over_many_steps():
         assert nh == len(seen & set(routed))
         seen |= set(routed)
         assert set(int(t) for t in tags if t >= 0) == seen
+
+
+# ------------------------------------------------ max-pooled routing query
+def test_max_pooled_routing_with_one_head_is_the_mean():
+    """One query head per KV head: the largest of one score is that score, so
+    the max-pooled routing query routes exactly as the mean query."""
+    _, k, cs, gs, r = tiny_state(T=2048, seed=21)
+    for t in (700, 1500, 2047):
+        q = r.standard_normal((1, 2, 64))
+        a = oracle.select(cfg(kc=5, kg=9), q, t - 1, cs, gs)
+        c_max = cfg(kc=5, kg=9)
+        c_max.route_max = 1
+        b = oracle.select(c_max, q, t - 1, cs, gs)
+        assert list(a[0]) == list(b[0])
+        np.testing.assert_array_equal(a[2], b[2])
+
+
+def test_max_pooled_scores_are_the_largest_head_score():
+    """Brute force: with 4 query heads and 3 query tokens, each candidate's
+    level-1 score is the largest over the heads of the head's token-mean
+    rotated query (transformers' RoPE) dotted with the chunk summary, and the
+    level-2 scores the same over the group summaries; every such score is at
+    least the mean query's score."""
+    d, hg, lq = 64, 4, 3
+    c = oracle.make_cfg(d, hg, 1, 64, 4, 1, 1, 3, 6, 1e4, 64.0, False, route_max=True)
+    c_mean = oracle.make_cfg(d, hg, 1, 64, 4, 1, 1, 3, 6, 1e4, 64.0, False)
+    k = RNG.standard_normal((64 * 24, d))
+    cs, gs = oracle.summaries(c, k)
+    q = RNG.standard_normal((hg, lq, d))
+    pos0 = 64 * 23 + 17
+    sel, _, scores = oracle.select(c, q, pos0, cs, gs)
+    _, _, mean_scores = oracle.select(c_mean, q, pos0, cs, gs)
+    qh = np.stack([lib_rope(q[h], np.arange(pos0, pos0 + lq), c).mean(axis=0) for h in range(hg)])
+    cand = np.arange(1, 23 - 1)
+    want = (cs[cand] @ qh.T / math.sqrt(d)).max(axis=1)
+    np.testing.assert_allclose(scores, want, rtol=1e-12, atol=1e-13)
+    assert np.all(scores >= mean_scores - 1e-12)
+    g_all = np.arange(gs.shape[0])
+    want_g = (gs[g_all] @ qh.T / math.sqrt(d)).max(axis=1)
+    got_g = oracle.group_scores(c, q, pos0, gs)  # the groups of the chunks before the query's
+    np.testing.assert_allclose(got_g, want_g[:len(got_g)], rtol=1e-12, atol=1e-13)
+    # the routed groups: top-6 of the groups of the top-3 chunks by these scores
+    top1 = cand[np.lexsort((cand, -want))[:3]]
+    groups = np.array([ch * 4 + j for ch in sorted(top1) for j in range(4)])
+    top2 = set(groups[np.lexsort((groups, -want_g[groups]))[:6]])
+    routed = {g for g in sel if 1 <= g // 4 < 22}
+    assert routed == top2
