@@ -112,12 +112,18 @@ typedef struct {
                               the row scales [B][lists][max_sel*16] fp32, and a
                               warm cache the codes [B][lists][n_warm*16][d] bytes
                               followed by [B][lists][n_warm*16] fp32 scales */
+  int32_t route_pool;      /* routing query of a list's query heads ("Kernmechanisme"
+                              items 2-3 leave the pooling open): 0 = their mean
+                              (over heads and query tokens); 1 = max pooling: each
+                              head's query is the mean over the query tokens, and a
+                              candidate chunk or group scores the largest of the
+                              heads' scores.  Equal to 0 with one head per list */
 } hga_config;
 
 /* Checks a configuration (host only).  HGA_OK, HGA_ERR_INVALID_ARGUMENT for
  * inconsistent values (d odd, Hq % Hkv != 0, C % G != 0, negative budgets,
- * theta <= 1, rep_position, route_per_head, rope_style or pool_dtype outside
- * {0, 1}),
+ * theta <= 1, rep_position, route_per_head, rope_style, pool_dtype or
+ * route_pool outside {0, 1}),
  * HGA_ERR_UNSUPPORTED for valid shapes this build does not implement. */
 hga_status hga_validate(const hga_config* cfg);
 

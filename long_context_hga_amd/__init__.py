@@ -65,13 +65,15 @@ class hga_config(ctypes.Structure):
         ("route_per_head", ctypes.c_int32),
         ("rope_style", ctypes.c_int32),
         ("pool_dtype", ctypes.c_int32),
+        ("route_pool", ctypes.c_int32),
     ]
 
 
 def config_from(p: dict, **over) -> hga_config:
     """hga_config from a plain dict with the field names above (``dtype`` may
     be given as "bf16"/"f32" instead of ``qkv_dtype``; ``rep_position``,
-    ``route_per_head``, ``rope_style`` and ``pool_dtype`` default to 0)."""
+    ``route_per_head``, ``rope_style``, ``pool_dtype`` and ``route_pool``
+    default to 0)."""
     q = dict(p)
     q.update(over)
     dt = q.get("qkv_dtype", HGA_BF16 if q.get("dtype") == "bf16" else HGA_F32)
@@ -80,7 +82,8 @@ def config_from(p: dict, **over) -> hga_config:
                       int(q["n_local_chunks"]), int(q["topk_chunks"]), int(q["topk_groups"]),
                       float(q["rope_theta"]), float(q["hf_wavelength"]), int(dt),
                       int(q.get("rep_position", 0)), int(q.get("route_per_head", 0)),
-                      int(q.get("rope_style", 0)), int(q.get("pool_dtype", 0)))
+                      int(q.get("rope_style", 0)), int(q.get("pool_dtype", 0)),
+                      int(q.get("route_pool", 0)))
 
 
 _lib = None

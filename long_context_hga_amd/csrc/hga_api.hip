@@ -39,7 +39,8 @@ hga_status check_cfg(const hga_config* c) {
       !(c->hf_wavelength >= 0.0) || (c->qkv_dtype != HGA_F32 && c->qkv_dtype != HGA_BF16) ||
       (c->rep_position != 0 && c->rep_position != 1) ||
       (c->route_per_head != 0 && c->route_per_head != 1) ||
-      (c->rope_style != 0 && c->rope_style != 1) || (c->pool_dtype != 0 && c->pool_dtype != 1))
+      (c->rope_style != 0 && c->rope_style != 1) || (c->pool_dtype != 0 && c->pool_dtype != 1) ||
+      (c->route_pool != 0 && c->route_pool != 1))
     return HGA_ERR_INVALID_ARGUMENT;
   const int hg = c->n_q_heads / c->n_kv_heads;
   if ((c->head_dim != 64 && c->head_dim != 128) || c->chunk_size != kChunk ||
@@ -68,6 +69,7 @@ KCfg make_kcfg(const hga_config* c) {
   k.qscale_log2 = (float)(1.4426950408889634 / sqrt((double)c->head_dim));
   k.rep_shift = c->rep_position == 1 ? 0.5 : 0.0;
   k.interleaved = c->rope_style == 1;
+  k.route_max = c->route_pool == 1 && k.lhg > 1;  // one head per list: the mean is the max
   k.pool8 = c->pool_dtype == 1;
   k.hf_mask = 0;
   for (int j = 0; j < c->head_dim / 2; ++j) {

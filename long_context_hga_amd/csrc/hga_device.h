@@ -23,6 +23,7 @@ struct KCfg {
   int lists, lhg, kvdiv;
   int interleaved;                 // RoPE pairs (2j, 2j+1) instead of (j, j + d/2)
   int pool8;                       // K/V pool of E4M3FN codes with per-row scales
+  int route_max;                   // routing score: the largest of the lhg heads' scores
   int n_sink, n_local, topk_c, topk_g;
   int dtype;                       // hga_dtype
   float qscale_log2;               // log2(e) / sqrt(d)

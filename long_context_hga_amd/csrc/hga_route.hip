@@ -36,6 +36,31 @@ namespace hga {
 
 constexpr int kTile = 64;       // candidate chunks per tile workgroup
 constexpr int kLanesPerRow = 8; // lanes per summary row
+constexpr int kMaxHg = 8;       // query heads per list (max pooling keeps one query each)
+
+// Max pooling: the largest over the nh routing queries q [nh][D] (fp64, LDS)
+// of their dot products with a summary row held by 8 lanes (NV float4 per
+// lane, this lane's sub-slice sub), before the 1/sqrt(d) factor.
+template <int NV>
+__device__ __forceinline__ double route_row_max(const float4 (&row)[NV], const double* q, int nh,
+                                                int sub) {
+  constexpr int D = NV * 32;
+  double best = -INFINITY;
+  for (int hh = 0; hh < nh; ++hh) {
+    const double* qq = q + (size_t)hh * D;
+    double d = 0.0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int i = 4 * (v * kLanesPerRow + sub);
+      d = fma((double)row[v].x, qq[i], d);
+      d = fma((double)row[v].y, qq[i + 1], d);
+      d = fma((double)row[v].z, qq[i + 2], d);
+      d = fma((double)row[v].w, qq[i + 3], d);
+    }
+    best = fmax(best, group8_sum_d(d));
+  }
+  return best;
+}
 
 struct RouteArgs {
   KCfg cfg;
@@ -71,7 +96,7 @@ __device__ __forceinline__ bool route_geometry(const KCfg& c, const RouteLaunch&
 // MODE 3: scores only, with the stored pooled query.  The whole-prompt
 //         prefill runs 2 then 3, so the query of a chunk is pooled once
 //         instead of once per tile.
-template <int D, bool BF16, int MODE>
+template <int D, bool BF16, int MODE, bool MAXQ = false>
 __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   constexpr int P = D / 2;
   constexpr int S = 256 / P;                 // query-token slices
@@ -88,6 +113,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   static_assert(TPT % TB == 0, "token batches");
   __shared__ double qpart[S2][P][2];
   __shared__ double qbar[D];
+  __shared__ double qh[MAXQ ? kMaxHg : 1][D];  // max pooling: each query head's routing query
 
   const KCfg& c = a.cfg;
   const RouteLaunch& r = a.r;
@@ -189,7 +215,105 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   // token's position once, and the rotated sums are added over tokens.  The
   // angle of a thread's next token follows by one fp64 rotation by the
   // token stride times omega_j (error ~1e-16 per step).
-  if constexpr (pool_q) {
+  // Max pooling: the same per query head (no sum over the heads), one head
+  // at a time through qpart; qh[h] = head h's mean over the query tokens.
+  auto reduce_head = [&](int hh) {
+    if (tid < P) {
+      const int ns = multi ? S2 : S;
+      double sa = 0.0, sb = 0.0;
+      for (int u = 0; u < ns; ++u) {
+        sa += qpart[u][tid][0];
+        sb += qpart[u][tid][1];
+      }
+      const double inv = 1.0 / (double)lq;
+      qh[hh][pair_a(c, tid)] = sa * inv;
+      qh[hh][pair_b(c, tid)] = sb * inv;
+      if (blockIdx.x == 0) {
+        r.qbar[((size_t)unit * c.lhg + hh) * D + pair_a(c, tid)] = sa * inv;
+        r.qbar[((size_t)unit * c.lhg + hh) * D + pair_b(c, tid)] = sb * inv;
+      }
+    }
+  };
+  if constexpr (pool_q && MAXQ) {
+    auto to_d = [](T x) -> double {
+      if constexpr (BF16) return bf16_to_f(x);
+      else return x;
+    };
+    if constexpr (!multi) {
+      double cs = 1.0, sn = 0.0;
+      if (sl < lq) rope_cs((double)(pos0 + sl), c.omega[j], &cs, &sn);
+#pragma unroll
+      for (int hh = 0; hh < kMaxHg; ++hh) {
+        if (hh >= c.lhg) break;  // uniform
+        const double x = sl < lq ? to_d(xa[hh]) : 0.0, y = sl < lq ? to_d(xb[hh]) : 0.0;
+        qpart[sl][j][0] = x * cs - y * sn;
+        qpart[sl][j][1] = x * sn + y * cs;
+        __syncthreads();
+        reduce_head(hh);
+        __syncthreads();
+      }
+    } else {
+      double qa[kMaxHg][2], qb[kMaxHg][2];
+#pragma unroll
+      for (int hh = 0; hh < kMaxHg; ++hh) qa[hh][0] = qa[hh][1] = qb[hh][0] = qb[hh][1] = 0.0;
+      double cs[2], sn[2], cd[2], sd[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const double wj = c.omega[2 * jp + e];
+        rope_cs((double)(pos0 + sl2), wj, &cs[e], &sn[e]);
+        sincos_rad((double)S2 * wj, &sd[e], &cd[e]);
+      }
+      for (int u0 = 0; u0 < TPT && sl2 + u0 * S2 < lq; u0 += TB) {
+        if (u0 > 0) load_batch(u0);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+          if (sl2 + (u0 + u) * S2 < lq) {
+#pragma unroll
+            for (int hh = 0; hh < kMaxHg; ++hh)
+              if (hh < c.lhg) {
+                double e0, e1, e2, e3;  // the four loaded elements in load order
+                if constexpr (BF16) {
+                  e0 = bf16_to_f((uint16_t)(ya[u][hh] & 0xFFFFu));
+                  e1 = bf16_to_f((uint16_t)(ya[u][hh] >> 16));
+                  e2 = bf16_to_f((uint16_t)(yb[u][hh] & 0xFFFFu));
+                  e3 = bf16_to_f((uint16_t)(yb[u][hh] >> 16));
+                } else {
+                  e0 = ya[u][hh].x;
+                  e1 = ya[u][hh].y;
+                  e2 = yb[u][hh].x;
+                  e3 = yb[u][hh].y;
+                }
+                const double x[2] = {e0, c.interleaved ? e2 : e1};
+                const double y[2] = {c.interleaved ? e1 : e2, e3};
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                  qa[hh][e] += x[e] * cs[e] - y[e] * sn[e];
+                  qb[hh][e] += x[e] * sn[e] + y[e] * cs[e];
+                }
+              }
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const double c2 = cs[e] * cd[e] - sn[e] * sd[e];
+            sn[e] = sn[e] * cd[e] + cs[e] * sd[e];
+            cs[e] = c2;
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < kMaxHg; ++hh) {
+        if (hh >= c.lhg) break;  // uniform
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          qpart[sl2][2 * jp + e][0] = qa[hh][e];
+          qpart[sl2][2 * jp + e][1] = qb[hh][e];
+        }
+        __syncthreads();
+        reduce_head(hh);
+        __syncthreads();
+      }
+    }
+  } else if constexpr (pool_q) {
     auto to_d = [](T x) -> double {
       if constexpr (BF16) return bf16_to_f(x);
       else return x;
@@ -291,28 +415,38 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   for (int it = 0; it < ITER; ++it)
 #pragma unroll
     for (int v = 0; v < NV; ++v) hold(buf[it][v]);
+  if constexpr (MAXQ && !pool_q) {  // the stored per-head routing queries
+    for (int i = tid; i < c.lhg * D; i += 256) qh[i / D][i % D] = r.qbar[(size_t)unit * c.lhg * D + i];
+    __syncthreads();
+  }
   double qv[NV][4];
+  if constexpr (!MAXQ) {
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * (v * kLanesPerRow + sub) + e;
-      qv[v][e] = pool_q ? qbar[i] : r.qbar[(size_t)unit * D + i];
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * (v * kLanesPerRow + sub) + e;
+        qv[v][e] = pool_q ? qbar[i] : r.qbar[(size_t)unit * D + i];
+      }
+  }
   double* scores = r.scores + (size_t)unit * a.score_ld;
   double rmn = INFINITY, rmx = -INFINITY;  // this wave's score range (its 16 rows)
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int idx = tile0 + wave * (kTile / 4) + it * RPI + rin;
     double d = 0.0;
+    if constexpr (MAXQ) {
+      d = route_row_max<NV>(buf[it], &qh[0][0], c.lhg, sub);
+    } else {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      d = fma((double)buf[it][v].x, qv[v][0], d);
-      d = fma((double)buf[it][v].y, qv[v][1], d);
-      d = fma((double)buf[it][v].z, qv[v][2], d);
-      d = fma((double)buf[it][v].w, qv[v][3], d);
+      for (int v = 0; v < NV; ++v) {
+        d = fma((double)buf[it][v].x, qv[v][0], d);
+        d = fma((double)buf[it][v].y, qv[v][1], d);
+        d = fma((double)buf[it][v].z, qv[v][2], d);
+        d = fma((double)buf[it][v].w, qv[v][3], d);
+      }
+      d = group8_sum_d(d);
     }
-    d = group8_sum_d(d);
     if (sub == 0 && idx < n_cand) {
       const double sc = d * c.inv_sqrt_d;
       scores[idx] = sc;
@@ -383,11 +517,12 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool MAXQ = false>
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int RPP = 256 / kLanesPerRow;  // rows per pass of the workgroup
   constexpr int U = 8;                     // passes in flight
+  __shared__ double s_qh[MAXQ ? kMaxHg : 1][D];  // max pooling: the heads' routing queries
   __shared__ int hist[256];
   __shared__ int kk[2];
   __shared__ double red[8];
@@ -410,11 +545,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   // table; entries past the candidates are dropped below)
   const int sub = lane % kLanesPerRow;
   double qv[NV][4];
+  if constexpr (MAXQ) {
+    for (int i = tid; i < c.lhg * D; i += 256)
+      s_qh[i / D][i % D] = r.qbar[(size_t)unit * c.lhg * D + i];
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+      for (int e = 0; e < 4; ++e)
+        qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+  }
   const double* scores = r.scores + (size_t)unit * a.score_ld;
   constexpr int SPT = 4;  // scores per thread in flight
   double v4[SPT];
@@ -490,14 +630,18 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
     for (int u = 0; u < U; ++u) {
       const int i = base + u * RPP + rsub;
       double d = 0.0;
+      if constexpr (MAXQ) {
+        d = route_row_max<NV>(gb[u], &s_qh[0][0], c.lhg, sub) * c.inv_sqrt_d;
+      } else {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        d = fma((double)gb[u][v].x, qv[v][0], d);
-        d = fma((double)gb[u][v].y, qv[v][1], d);
-        d = fma((double)gb[u][v].z, qv[v][2], d);
-        d = fma((double)gb[u][v].w, qv[v][3], d);
+        for (int v = 0; v < NV; ++v) {
+          d = fma((double)gb[u][v].x, qv[v][0], d);
+          d = fma((double)gb[u][v].y, qv[v][1], d);
+          d = fma((double)gb[u][v].z, qv[v][2], d);
+          d = fma((double)gb[u][v].w, qv[v][3], d);
+        }
+        d = group8_sum_d(d) * c.inv_sqrt_d;
       }
-      d = group8_sum_d(d) * c.inv_sqrt_d;
       if (sub == 0 && i < n2) {
         s_lds[i] = d;
         mn2 = fmin(mn2, d);
@@ -562,7 +706,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 constexpr int kFastMaxCand = 1024;
 constexpr int kFastMaxKept = 64;  // level-1 chunks kept: level 2 ranks <= 256 groups
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool MAXQ = false>
 __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
@@ -578,6 +722,7 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   __shared__ int s_k2[4];                  // level-2 groups kept by each wave
   __shared__ int s_nbl[2];                 // overflowed boundary members collected
   __shared__ int s_bl[kFastMaxCand];
+  __shared__ double s_qh[MAXQ ? kMaxHg : 1][D];  // max pooling: the heads' routing queries
 
   const KCfg& c = a.cfg;
   const RouteLaunch& r = a.r;
@@ -593,11 +738,16 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   // ---- 1. loads (clamped into the workspace rows; unused entries ignored)
   const int sub = lane % kLanesPerRow, g8 = lane / kLanesPerRow;
   double qv[NV][4];
+  if constexpr (MAXQ) {  // in LDS before the first barrier
+    for (int i = tid; i < c.lhg * D; i += 256)
+      s_qh[i / D][i % D] = r.qbar[(size_t)unit * c.lhg * D + i];
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+      for (int e = 0; e < 4; ++e)
+        qv[v][e] = r.qbar[(size_t)unit * D + 4 * (v * kLanesPerRow + sub) + e];
+  }
   const double* scores = r.scores + (size_t)unit * a.score_ld;
   double x[4];
   {
@@ -681,14 +831,18 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
     for (int u = 0; u < U; ++u) {
       const int i = base + 8 * u + g8;
       double d = 0.0;
+      if constexpr (MAXQ) {
+        d = route_row_max<NV>(gb[u], &s_qh[0][0], c.lhg, sub) * c.inv_sqrt_d;
+      } else {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        d = fma((double)gb[u][v].x, qv[v][0], d);
-        d = fma((double)gb[u][v].y, qv[v][1], d);
-        d = fma((double)gb[u][v].z, qv[v][2], d);
-        d = fma((double)gb[u][v].w, qv[v][3], d);
+        for (int v = 0; v < NV; ++v) {
+          d = fma((double)gb[u][v].x, qv[v][0], d);
+          d = fma((double)gb[u][v].y, qv[v][1], d);
+          d = fma((double)gb[u][v].z, qv[v][2], d);
+          d = fma((double)gb[u][v].w, qv[v][3], d);
+        }
+        d = group8_sum_d(d) * c.inv_sqrt_d;
       }
-      d = group8_sum_d(d) * c.inv_sqrt_d;
       if (sub == 0 && i < n2w) {
         s_l2[wave][i] = d;
         mn2 = fmin(mn2, d);
@@ -758,9 +912,13 @@ int route_score_ld(const KCfg& cfg, int max_chunks) {
   return score_ld_of(max_cand_of(cfg, max_chunks));
 }
 
+// Pooled-query rows per unit: one, or one per query head with max pooling.
+static int qbar_rows(const KCfg& cfg) { return cfg.route_max ? cfg.lhg : 1; }
+
 size_t route_ws_bytes(const KCfg& cfg, int B, int max_chunks) {
   const int mc = max_cand_of(cfg, max_chunks);
-  return (size_t)B * cfg.lists * (score_ld_of(mc) + cfg.d + 8 * n_tiles_of(mc)) * sizeof(double);
+  return (size_t)B * cfg.lists *
+         (score_ld_of(mc) + (size_t)qbar_rows(cfg) * cfg.d + 8 * n_tiles_of(mc)) * sizeof(double);
 }
 
 size_t route_select_lds(const KCfg& cfg, int max_chunks) {
@@ -771,17 +929,26 @@ size_t route_select_lds(const KCfg& cfg, int max_chunks) {
   return nmax * (sizeof(double) + 3 * sizeof(int)) + (size_t)n2 * sizeof(int);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool MAXQ>
 static void launch_tiles(bool multi, bool pooled_once, dim3 grid, hipStream_t st,
                          const RouteArgs& a) {
   if (pooled_once) {  // pooled query once per unit, then the tiles
-    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 2>), dim3(1, grid.y, grid.z), dim3(256), 0, st, a);
-    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 3>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 2, MAXQ>), dim3(1, grid.y, grid.z), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 3, MAXQ>), grid, dim3(256), 0, st, a);
   } else if (multi) {
-    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 1>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 1, MAXQ>), grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 0>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((route_tiles_kernel<D, BF16, 0, MAXQ>), grid, dim3(256), 0, st, a);
   }
+}
+
+// Tiles then selection for one (head dim, dtype, pooling).
+template <int D, bool BF16, bool MAXQ>
+static void launch_route_d(bool multi, bool pooled_once, bool fast, dim3 grid, dim3 sgrid,
+                           size_t lds, hipStream_t st, const RouteArgs& a) {
+  launch_tiles<D, BF16, MAXQ>(multi, pooled_once, grid, st, a);
+  if (fast) hipLaunchKernelGGL((route_select_fast_kernel<D, BF16, MAXQ>), sgrid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((route_select_kernel<D, BF16, MAXQ>), sgrid, dim3(256), lds, st, a);
 }
 
 hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
@@ -794,7 +961,7 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   a.n_tiles = n_tiles_of(a.max_cand);
   // the workspace holds the scores with stride score_ld, then qbar, then the
   // ranges (the callers place qbar at B * lists * score_ld)
-  a.ranges = r.qbar + (size_t)r.B * cfg.lists * cfg.d;
+  a.ranges = r.qbar + (size_t)r.B * cfg.lists * qbar_rows(cfg) * cfg.d;
   if (front) a.f = *front;
   const int n_tiles = a.n_tiles;
   size_t lds = route_select_lds(cfg, r.max_chunks);
@@ -805,25 +972,22 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   const bool bf = cfg.dtype == HGA_BF16;
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   const bool fast = fast_select(cfg, a.max_cand);
+  const bool mq = cfg.route_max != 0;
   if (cfg.d == 128) {
     if (bf) {
-      launch_tiles<128, true>(multi, r.pool_once, grid, st, a);
-      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<128, true>), sgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((route_select_kernel<128, true>), sgrid, dim3(256), lds, st, a);
+      if (mq) launch_route_d<128, true, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      else launch_route_d<128, true, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
     } else {
-      launch_tiles<128, false>(multi, r.pool_once, grid, st, a);
-      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<128, false>), sgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((route_select_kernel<128, false>), sgrid, dim3(256), lds, st, a);
+      if (mq) launch_route_d<128, false, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      else launch_route_d<128, false, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
     }
   } else {
     if (bf) {
-      launch_tiles<64, true>(multi, r.pool_once, grid, st, a);
-      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<64, true>), sgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((route_select_kernel<64, true>), sgrid, dim3(256), lds, st, a);
+      if (mq) launch_route_d<64, true, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      else launch_route_d<64, true, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
     } else {
-      launch_tiles<64, false>(multi, r.pool_once, grid, st, a);
-      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<64, false>), sgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((route_select_kernel<64, false>), sgrid, dim3(256), lds, st, a);
+      if (mq) launch_route_d<64, false, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      else launch_route_d<64, false, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
     }
   }
   return hipGetLastError();

@@ -54,12 +54,15 @@ int main(void) {
   EXPECT(hga_validate(&b), HGA_ERR_INVALID_ARGUMENT);
   b = c; b.pool_dtype = 1; b.qkv_dtype = HGA_F32;
   EXPECT(hga_validate(&b), HGA_ERR_UNSUPPORTED);
-  for (int v = 0; v < 16; ++v) {  /* every switch combination validates and sizes */
+  b = c; b.route_pool = 2;
+  EXPECT(hga_validate(&b), HGA_ERR_INVALID_ARGUMENT);
+  for (int v = 0; v < 32; ++v) {  /* every switch combination validates and sizes */
     b = c;
     b.rep_position = v & 1;
     b.route_per_head = (v >> 1) & 1;
     b.rope_style = (v >> 2) & 1;
     b.pool_dtype = (v >> 3) & 1;
+    b.route_pool = (v >> 4) & 1;
     EXPECT(hga_validate(&b), HGA_OK);
     size_t n = 0;
     EXPECT(hga_workspace_bytes(&b, 8, 65536, 1, &n), HGA_OK);

@@ -204,3 +204,118 @@ def test_interleaved_whole_prompt_and_fused_step():
                         dst.max_sel, s2.out, s2.lse, torch.zeros_like(dst.ws))
     torch.cuda.synchronize()
     assert torch.equal(s1.n_sel, s2.n_sel) and torch.equal(s1.out, s2.out)
+
+
+def _route_attend_check(inp, st, cfg, uc, pos, lq, units, q=None):
+    """Route + attend lq query tokens at pos; selections and outputs of the
+    given (b, h) units against the oracle run with cfg.  Returns the lists."""
+    B, hg = st.B, cfg.hq // cfg.hkv
+    q = st.q[:, :, :lq].contiguous() if q is None else q
+    pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+    s = gh.alloc_step(st, lq)
+    gh.route(st, q, lq, pos_t, s)
+    gh.attend(st, q, lq, pos_t, s)
+    torch.cuda.synchronize()
+    sel, nsel, out = s.sel.cpu().numpy(), s.n_sel.cpu().numpy(), s.out.cpu().numpy()
+    lists = {}
+    for b, h in units:
+        cs, gs, kp, v = uc.get(b, h)
+        qu = q_unit(inp, cfg, b, h, 0, lq)
+        g = sel[b, h, :nsel[b, h]]
+        osel, margins, oscores = oracle.select(cfg, qu, pos, cs, gs)
+        check_selection(cfg, g, osel, margins, oscores, pos, lq,
+                        oracle.group_scores(cfg, qu, pos, gs))
+        o_ref, _ = oracle.attend(cfg, qu, pos, kp, v, g)
+        assert max_abs(out[b, h * hg:(h + 1) * hg], o_ref) <= ATOL_OUT, (pos, lq, b, h)
+        lists[b, h] = g.copy()
+    return lists, s
+
+
+def test_max_pooled_routing_query():
+    """Max pooling of the routing query (route_pool = 1: each query head's
+    token-mean query, a candidate scoring the largest head score): decode (1
+    and 7 query tokens) and a 64-token prefill chunk at 4K against the oracle
+    run with max pooling; the lists differ from mean pooling; the fused
+    decode step gives the bits of the separate calls."""
+    import long_context_hga_amd as hga
+    inp = synth.generate("prefill32k", batch=2, context=4096, overrides=dict(route_pool=1, needles=0))
+    st = gh.build_state(inp)
+    cfg = oracle.cfg_from(inp.params)
+    assert cfg.route_max == 1
+    uc = UnitCache(inp, cfg)
+    units = [(b, h) for b in range(st.B) for h in range(4)]
+    differ = 0
+    for pos, lq in ((4095, 1), (3000, 7), (4032, 64)):
+        lists, _ = _route_attend_check(inp, st, cfg, uc, pos, lq, units)
+        mean_cfg = oracle.cfg_from(dict(inp.params, route_pool=0))
+        for (b, h), g in lists.items():
+            cs, gs, _, _ = uc.get(b, h, need_pool=False)
+            gm, _, _ = oracle.select(mean_cfg, q_unit(inp, mean_cfg, b, h, 0, lq), pos, cs, gs)
+            differ += int(len(gm) != len(g) or (gm != g).any())
+    assert differ > 0  # the switch reaches the kernels
+    # fused decode step == separate calls, with max pooling
+    B, T = st.B, st.T
+    pos = 4000
+    pos_t = torch.full((B,), pos, dtype=torch.int32, device="cuda")
+    q = gh.query_slice(st, 0)
+    c0 = pos // 64 * 64
+    kt = st.k_raw[:, :, pos:pos + 1].contiguous()
+    vt = st.v_raw[:, :, pos:pos + 1].contiguous()
+    sa = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, pos_t, sa)
+    gh.attend(st, q, 1, pos_t, sa)
+    sb = gh.alloc_step(st, 1)
+    stage = st.k_raw[:, :, c0:c0 + 64].contiguous()
+    hga.hga_decode_step(st.cfg, B, q, kt, vt, pos_t, st.k_pool.clone(), st.v_pool.clone(), T,
+                        stage, st.chunk_sum.clone(), st.group_sum.clone(), st.max_chunks, sb.sel,
+                        sb.n_sel, st.max_sel, sb.out, sb.lse, torch.zeros_like(st.ws))
+    torch.cuda.synchronize()
+    assert torch.equal(sa.sel, sb.sel) and torch.equal(sa.out, sb.out)
+
+
+@pytest.mark.parametrize("context", [65536, 131072])
+def test_max_pooled_routing_long_contexts(context):
+    """Max pooling at 64K (1018 candidates: the fast selection) and 128K
+    (2042: the streaming selection), one sequence, every KV head against the
+    oracle."""
+    inp = synth.generate("decode64k", batch=1, context=context, overrides=dict(route_pool=1))
+    st = gh.build_state(inp)
+    cfg = oracle.cfg_from(inp.params)
+    uc = UnitCache(inp, cfg)
+    print(f"[max pooling] context {context}", flush=True)
+    _route_attend_check(inp, st, cfg, uc, int(inp.pos0[0]), 1, [(0, h) for h in range(4)],
+                        q=gh.query_slice(st, 0))
+
+
+def test_max_pooled_routing_whole_prompt():
+    """The whole-prompt prefill with max pooling (the pooled query once per
+    query chunk and head): sampled chunks of a 2K prompt against the oracle."""
+    import long_context_hga_amd as hga
+    inp = synth.generate("prompt32k", context=2048, overrides=dict(route_pool=1))
+    st = gh.build_state(inp, max_lq=64)
+    cfg = oracle.cfg_from(inp.params)
+    uc = UnitCache(inp, cfg)
+    B, T, ms = st.B, st.T, st.max_sel
+    nq = T // 64
+    sel = torch.full((B, nq, 4, ms), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((B, nq, 4), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, 32, T, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(hga.hga_prompt_workspace_bytes(st.cfg, B, T, st.max_chunks),
+                     dtype=torch.uint8, device="cuda")
+    hga.hga_prefill_prompt(st.cfg, B, T, st.q, st.k_raw, st.v_raw, st.k_pool.clone(),
+                           st.v_pool.clone(), T, st.chunk_sum.clone(), st.group_sum.clone(),
+                           st.max_chunks, sel, n_sel, ms, out, None, ws)
+    torch.cuda.synchronize()
+    sl, ns, o = sel.cpu().numpy(), n_sel.cpu().numpy(), out.cpu().numpy()
+    for b in range(B):
+        for h in range(4):
+            cs, gs, kp, v = uc.get(b, h)
+            for qc in (6, 19, 31):
+                p0 = qc * 64
+                qu = q_unit(inp, cfg, b, h, p0, 64)
+                g = sl[b, qc, h, :ns[b, qc, h]]
+                osel, margins, oscores = oracle.select(cfg, qu, p0, cs, gs)
+                check_selection(cfg, g, osel, margins, oscores, p0, 64,
+                                oracle.group_scores(cfg, qu, p0, gs))
+                o_ref, _ = oracle.attend(cfg, qu, p0, kp, v, g)
+                assert max_abs(o[b, h * 8:(h + 1) * 8, p0:p0 + 64], o_ref) <= ATOL_OUT, (b, h, qc)
