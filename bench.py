@@ -147,23 +147,25 @@ def calibrate_copy(n_bytes=512 << 20, reps=4):
 
 
 def calibrate_mfma(rounds=2500):
-    """Dense bf16 rate that v_mfma_f32_16x16x32_bf16 reaches on this device
-    (all CUs, 1, 2 and 4 waves per SIMD), from the calibration library."""
+    """Dense bf16 rate that v_mfma_f32_16x16x32_bf16 and
+    v_mfma_f32_32x32x16_bf16 reach on this device (all CUs, 1, 2 and 4 waves
+    per SIMD), from the calibration library."""
     import ctypes
     import torch
     torch.cuda.init()
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     lib = ctypes.CDLL(os.path.join(ROOT, "long_context_hga_amd", "libhga_calib.so"))
-    f = lib.hga_calib_mfma_rate
-    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
-                  ctypes.POINTER(ctypes.c_double)]
-    for w in (1, 2, 4):
-        tf, ms = ctypes.c_double(), ctypes.c_double()
-        rc = f(n_cus, w, rounds, ctypes.byref(tf), ctypes.byref(ms))
-        assert rc == 0, rc
-        print(json.dumps({"calibration": "v_mfma_f32_16x16x32_bf16 issue rate", "cus": n_cus,
-                          "waves_per_simd": w, "tflops": tf.value, "ms": ms.value,
-                          "published_peak_tflops": 2500.0}), flush=True)
+    f = lib.hga_calib_mfma_rate_shape
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    for shape, name in ((0, "v_mfma_f32_16x16x32_bf16"), (1, "v_mfma_f32_32x32x16_bf16")):
+        for w in (1, 2, 4):
+            tf, ms = ctypes.c_double(), ctypes.c_double()
+            rc = f(n_cus, w, rounds, shape, ctypes.byref(tf), ctypes.byref(ms))
+            assert rc == 0, rc
+            print(json.dumps({"calibration": f"{name} issue rate", "cus": n_cus,
+                              "waves_per_simd": w, "tflops": tf.value, "ms": ms.value,
+                              "published_peak_tflops": 2500.0}), flush=True)
 
 
 def cpu_baseline(inp, cfg_params, min_seconds=10.0):

@@ -42,13 +42,16 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, OUT)
-    # the benchmark's calibration kernels (not part of the HGA path)
+    # the benchmark's calibration kernels (not part of the HGA path: a
+    # failure here is reported and leaves the library build standing)
     tmp = CALIB_OUT + ".tmp"
     r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, *sorted(glob.glob(os.path.join(CALIB, "*.hip")))],
                        capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for the calibration kernels:\n{r.stderr}")
-    os.replace(tmp, CALIB_OUT)
+        print(f"warning: hipcc failed for the calibration kernels (bench.py --calibrate-mfma "
+              f"unavailable):\n{r.stderr}", file=sys.stderr)
+    else:
+        os.replace(tmp, CALIB_OUT)
     return OUT
 
 

@@ -1,5 +1,6 @@
-// Calibration kernel for the benchmark (not part of the HGA path): the issue
-// rate of v_mfma_f32_16x16x32_bf16 on this device.  Each wave runs n rounds
+// Calibration kernels for the benchmark (not part of the HGA path): the issue
+// rates of v_mfma_f32_16x16x32_bf16 and v_mfma_f32_32x32x16_bf16 on this
+// device.  Each wave runs n rounds
 // of K independent products on K accumulators and folds the accumulators
 // into one store, so nothing is optimised away.  Reported as dense bf16
 // TFLOP/s, next to the published peak, to read the matrix-core utilisation
@@ -10,6 +11,29 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 32x32x16: 16 accumulator registers per product, 32768 flops per instruction
+template <int K>
+__global__ __launch_bounds__(256) void mfma32_rate_kernel(float* out, int n) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (lane + i));
+    b[i] = (__bf16)(0.002f * (lane - i));
+  }
+  f32x16 c[K];
+  for (int k = 0; k < K; ++k)
+    for (int e = 0; e < 16; ++e) c[k][e] = 0.f;
+  for (int r = 0; r < n; ++r) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int k = 0; k < K; ++k)
+    for (int e = 0; e < 16; ++e) s += c[k][e];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
 
 template <int K>
 __global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int n) {
@@ -33,11 +57,19 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, int n) {
 }  // namespace
 
 // waves_per_simd in 1..4: 256 CUs x 4 SIMDs are filled with that many waves
-// each (256-thread workgroups).  Returns 0 on success; *tflops = dense bf16
-// rate of the timed launch, *ms its duration.
+// each (256-thread workgroups).  shape 0: v_mfma_f32_16x16x32_bf16 (8
+// independent accumulators), 1: v_mfma_f32_32x32x16_bf16 (4).  Returns 0 on
+// success; *tflops = dense bf16 rate of the timed launch, *ms its duration.
+extern "C" int hga_calib_mfma_rate_shape(int n_cus, int waves_per_simd, int rounds, int shape,
+                                         double* tflops, double* ms);
 extern "C" int hga_calib_mfma_rate(int n_cus, int waves_per_simd, int rounds, double* tflops,
                                    double* ms) {
-  if (n_cus <= 0 || waves_per_simd < 1 || waves_per_simd > 4 || rounds <= 0 || !tflops || !ms)
+  return hga_calib_mfma_rate_shape(n_cus, waves_per_simd, rounds, 0, tflops, ms);
+}
+extern "C" int hga_calib_mfma_rate_shape(int n_cus, int waves_per_simd, int rounds, int shape,
+                                         double* tflops, double* ms) {
+  if (n_cus <= 0 || waves_per_simd < 1 || waves_per_simd > 4 || rounds <= 0 || !tflops || !ms ||
+      shape < 0 || shape > 1)
     return 1;
   const int blocks = n_cus * waves_per_simd;
   float* out = nullptr;
@@ -46,16 +78,21 @@ extern "C" int hga_calib_mfma_rate(int n_cus, int waves_per_simd, int rounds, do
   int rc = 0;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) rc = 3;
   if (!rc) {
-    hipLaunchKernelGGL(mfma_rate_kernel<8>, dim3(blocks), dim3(256), 0, 0, out, rounds);  // warm
+    auto launch = [&]() {
+      if (shape == 0) hipLaunchKernelGGL(mfma_rate_kernel<8>, dim3(blocks), dim3(256), 0, 0, out, rounds);
+      else hipLaunchKernelGGL(mfma32_rate_kernel<4>, dim3(blocks), dim3(256), 0, 0, out, rounds);
+    };
+    launch();  // warm
     hipEventRecord(e0, 0);
-    hipLaunchKernelGGL(mfma_rate_kernel<8>, dim3(blocks), dim3(256), 0, 0, out, rounds);
+    launch();
     hipEventRecord(e1, 0);
     if (hipEventSynchronize(e1) != hipSuccess) rc = 4;
   }
   if (!rc) {
     float t = 0.f;
     if (hipEventElapsedTime(&t, e0, e1) != hipSuccess) rc = 5;
-    const double flops = (double)blocks * 4 /* waves */ * rounds * 8 /* K */ * 16384.0;
+    // per wave and round: 8 products of 16384 flops, or 4 of 32768
+    const double flops = (double)blocks * 4 /* waves */ * rounds * (shape == 0 ? 8 * 16384.0 : 4 * 32768.0);
     *ms = t;
     *tflops = flops / (t * 1e-3) / 1e12;
   }
