@@ -66,13 +66,15 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="aa6b2e1bf9bbb64260006c959078abb4a19bde55e1c7282259fffb75e0835519",
-    fetch_kib=16745.93 + 1469.92, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="e599596f8353e6b4e1fd858f7fa384a7e7731e7b3d455f342d4647012e27883b",
+    fetch_kib=16750.46 + 1469.90, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 # The same for the routing entry point (its tile kernel plus its selection
-# kernel), or None when not taken on the current routing sources.
-ROUTE_TRAFFIC = None
+# kernel), valid for the routing sources it was taken on.
+ROUTE_TRAFFIC = dict(
+    source_sha256="42e4d7bba0b2a0b5e36a542bd5de42ccdff459eb1062f1caa4db4a6ef04ed7f8",
+    fetch_kib=8487.16 + 1948.14, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):
@@ -259,6 +261,12 @@ def main():
                          "64-token query chunk at 32K context (MFMA attention); host64k: "
                          "batch-4 64K decode with the pool in pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replays", type=int, default=1000,
+                    help="graph replays of the per-step timing distribution (at least)")
+    ap.add_argument("--profile-calls", type=int, default=0, metavar="N",
+                    help="decode64k: only run N steps through the separate entry points "
+                         "(append, hga_route, hga_attend, chunk refresh, hga_gather), no "
+                         "graphs and no spin kernels, for hardware-counter runs")
     ap.add_argument("--fp8", action="store_true",
                     help="host64k: the K/V pool (host, windows, working sets, cache) in FP8")
     ap.add_argument("--sweep", action="store_true",
@@ -295,6 +303,8 @@ def main():
 
 def run_decode64k(args):
     out, inp = measure_decode(args, "decode64k")
+    if out is None:  # --profile-calls
+        return
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, inp.params)
@@ -304,7 +314,8 @@ def run_decode64k(args):
 def measure_decode(args, name, batch=None, context=None, overrides=None, replicas=None):
     """Time the fused decode step of workload ``name`` (optionally resized)
     as a replayed HIP graph, and the attend / route calls with events.
-    Returns the result line (without cpu_baseline) and the inputs."""
+    Returns the result line (without cpu_baseline, None with
+    --profile-calls) and the inputs."""
     import numpy as np
     import torch
 
@@ -372,15 +383,33 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
         s = x["s"]
         hga.hga_build_summaries(cfg, B, x["kt"], x["vt"], pos, 1, x["k_pool"], x["v_pool"], T,
                                 None, None, st.max_chunks)
-        ev[0].record()
+        if ev:
+            ev[0].record()
         hga.hga_route(cfg, B, x["q"], 1, st.pos0, x["chunk_sum"], x["group_sum"], st.max_chunks,
                       s.sel, s.n_sel, st.max_sel, None, x["ws"])
-        ev[1].record()
+        if ev:
+            ev[1].record()
         hga.hga_attend(cfg, B, x["q"], 1, st.pos0, x["k_pool"], x["v_pool"], hga.HGA_SRC_POOL, T,
                        s.sel, s.n_sel, st.max_sel, hga.HGA_PART_ALL, s.out, s.lse, x["ws"])
-        ev[2].record()
+        if ev:
+            ev[2].record()
         hga.hga_build_summaries(cfg, B, x["kc"], None, c0, 64, None, None, T, x["chunk_sum"],
                                 x["group_sum"], st.max_chunks)
+
+    if args.profile_calls:
+        # counter runs: only the separate-entry calls, synchronised once
+        kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
+                         dtype=reps[0]["k_pool"].dtype, device="cuda")
+        vw = torch.empty_like(kw)
+        for i in range(args.profile_calls):
+            x = reps[i % R]
+            step_parts(i % R, None)
+            hga.hga_gather(cfg, B, x["k_pool"], x["v_pool"], T, 0, x["s"].sel, x["s"].n_sel,
+                           st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
+        torch.cuda.synchronize()
+        print(f"[bench] {args.profile_calls} separate-entry steps + gathers done", file=sys.stderr,
+              flush=True)
+        return None, inp
 
     for i in range(max(args.warmup, R)):
         step(i % R)
@@ -390,7 +419,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     # whole-step throughput: HIP graphs of consecutive steps (one per
     # replica); the timed region replays them for exactly --steps steps, then
     # the per-step distribution over many more replays
-    ms_step, steps_timed, dist = time_graph_exact(step, R, args)
+    ms_step, steps_timed, dist = time_graph_exact(step, R, args, min_replays=args.replays)
     for r, x in enumerate(reps):  # graph replays reproduce the eager results
         assert torch.equal(x["s"].out, eager_out[r]), "graph replay differs from eager run"
 
@@ -410,7 +439,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     assert (s0.n_sel == st.max_sel).all().item() and torch.isfinite(s0.out).all().item()
 
     # hga_gather from the HBM pool into a working set (the same lists): its
-    # own copy rate, read + write (the FP8 pool has no gather)
+    # own copy rate, read + write (bf16 pool)
     gather_ms, gather_bytes, copy_ms = float("nan"), 0, float("nan")
     if p.get("pool_dtype", 0) == 0:
         kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
@@ -418,6 +447,10 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
         vw = torch.empty_like(kw)
         gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(20)]
+        for x in reps:  # first launches (code load, caches) stay out of the timing
+            hga.hga_gather(cfg, B, x["k_pool"], x["v_pool"], T, 0, x["s"].sel, x["s"].n_sel,
+                           st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
+        torch.cuda.synchronize()
         torch.cuda._sleep(int(1e8))
         for i, (e0, e1) in enumerate(gev):
             x = reps[i % R]
@@ -426,7 +459,7 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
                            st.max_sel, st.pos0, hga.HGA_PART_ALL, kw, vw)
             e1.record()
         torch.cuda.synchronize()
-        gather_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in gev]))
+        gather_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in gev]))
         gather_bytes = 2 * int(reps[0]["s"].n_sel.sum().item()) * 16 * p["head_dim"] * 2 * 2
         del kw, vw
         copy_ms = copy_rate_ms(gather_bytes // 2)

@@ -3,7 +3,7 @@
 //
 // HGA technical summary (gist.science), "Geheugenarchitectuur": summaries and
 // the always-visible windows are hot in accelerator memory, a bounded LRU
-// cache in accelerator memory holds recently routed chunks (warm), and the
+// cache in accelerator memory keeps the chunks routing picked lately (warm), and the
 // full token K/V history stays in host RAM (cold).  The cache holds the unit
 // the routing delivers and the attention reads, the 16-token group, so a miss
 // moves only the selected group across PCIe.
