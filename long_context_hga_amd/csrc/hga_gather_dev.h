@@ -81,10 +81,12 @@ __device__ __forceinline__ void gather_items(const GatherArgs& a, int n_items, i
     const int b = unit / a.lists;
     const int unit_p = b * a.hkv + (unit % a.lists) / a.kvdiv;  // pool rows of its KV head
     // the list length and the slot's group id are read together (the slot
-    // index is always inside the list buffer); the id is used only if the
-    // slot is listed
-    const int n_sel = a.n_sel[unit];
-    const int gid = a.sel[(size_t)unit * a.max_sel + slot];
+    // index is always inside the list buffer; the empty asm keeps the
+    // compiler from issuing the second load after the first has returned);
+    // the id is used only if the slot is listed
+    int n_sel = a.n_sel[unit];
+    int gid = a.sel[(size_t)unit * a.max_sel + slot];
+    asm volatile("" : "+v"(n_sel), "+v"(gid));
     if (n_sel < 0 || slot >= n_sel) continue;  // uniform over the workgroup
     if (a.part != HGA_PART_ALL) {
       const int pos0 = a.q_pos0[b];

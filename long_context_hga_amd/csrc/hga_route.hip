@@ -710,7 +710,10 @@ template <int D, bool BF16, bool MAXQ = false>
 __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
-  constexpr int U = 8;                     // level-2 row passes in flight per wave
+  // level-2 row passes in flight per wave: 12 x 8 rows covers 24 kept chunks, so a
+  // wave rarely needs a second round trip (52 kept chunks over 4 waves give
+  // ~13 +- 3 per wave); 252 VGPRs, one workgroup per CU anyway
+  constexpr int U = 12;
   __shared__ int s_fine[kSelBins], s_fine2[kSelBins];
   __shared__ int s_coarse[kSelCoarse], s_coarse2[kSelCoarse];
   __shared__ int s_slot[kSelBins * kSelSlots];  // both levels (level 2 starts after a barrier)
