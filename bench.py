@@ -148,6 +148,49 @@ def calibrate_copy(n_bytes=512 << 20, reps=4):
                       "bytes_written_per_dispatch": n_bytes, "dispatches": reps}), flush=True)
 
 
+def calibrate_copy_rate(reps=50):
+    """Read + write rate of plain device-to-device copies (calibration
+    library kernels in five shapes, and torch's copy_) at the gather's size
+    (the decode64k lists: 33.5 MB each way) and at 512 MiB: the ceiling a
+    copy reaches on this device, next to the published 8 TB/s."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_hga_amd", "libhga_calib.so"))
+    f = lib.hga_calib_copy_rate
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    names = ["1 uint4 per thread", "4 uint4 per thread, loads first",
+             "4 uint4 per thread, non-temporal", "8 uint4 per thread, loads first",
+             "grid-stride, 8 workgroups per CU"]
+    for n_bytes in (33554432, 512 << 20):
+        src = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for v, name in enumerate(names):
+            gb, ms = ctypes.c_double(), ctypes.c_double()
+            rc = f(src.data_ptr(), dst.data_ptr(), n_bytes, v, reps, n_cus, ctypes.byref(gb),
+                   ctypes.byref(ms))
+            assert rc == 0, rc
+            print(json.dumps({"calibration": "device copy rate", "kernel": name, "bytes": n_bytes,
+                              "ms": ms.value, "GBps_read_plus_write": gb.value,
+                              "frac_of_8TBps": gb.value / HBM_PEAK_GBS}), flush=True)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        dst.copy_(src)
+        ev[0].record()
+        for _ in range(reps):
+            dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        print(json.dumps({"calibration": "device copy rate", "kernel": "torch copy_", "bytes": n_bytes,
+                          "ms": ms, "GBps_read_plus_write": 2 * n_bytes / (ms * 1e-3) / 1e9,
+                          "frac_of_8TBps": 2 * n_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}),
+              flush=True)
+        del src, dst
+
+
 def calibrate_mfma(rounds=2500):
     """Dense bf16 rate that v_mfma_f32_16x16x32_bf16 and
     v_mfma_f32_32x32x16_bf16 reach on this device (all CUs, 1, 2 and 4 waves
@@ -277,6 +320,8 @@ def main():
                          "waves per SIMD")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--calibrate-copy-rate", action="store_true",
+                    help="only measure plain device copies (the copy ceiling of the gather)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
@@ -284,6 +329,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_copy_rate:
+        calibrate_copy_rate()
         return
     if args.calibrate_mfma:
         calibrate_mfma()
