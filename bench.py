@@ -66,15 +66,15 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="e599596f8353e6b4e1fd858f7fa384a7e7731e7b3d455f342d4647012e27883b",
-    fetch_kib=16750.46 + 1469.90, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="09b5e9664aee9abfedac94e222b509fa14338f373a029d6c2432048b0c4cf98f",
+    fetch_kib=16744.96 + 1446.12, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="42e4d7bba0b2a0b5e36a542bd5de42ccdff459eb1062f1caa4db4a6ef04ed7f8",
-    fetch_kib=8487.16 + 1948.14, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="a61274dc0c13b3644513f2a2efb816eddf73fe66930df296e2132252ef027a59",
+    fetch_kib=8491.62 + 1955.06, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):

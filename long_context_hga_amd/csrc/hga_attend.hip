@@ -25,6 +25,10 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
   using OV = typename std::conditional<EPL == 2, float2, float>::type;
   const KCfg& c = args.cfg;
   const AttendLaunch& a = args.a;
+  // every kernel argument used below, read at once (one scalar round trip)
+  asm volatile("" ::"s"(c.lists), "s"(c.hq), "s"(c.n_sink), "s"(c.n_local), "s"(a.lq),
+               "s"(a.max_sel), "s"(a.part_sel), "s"(a.two_part), "s"(args.n_splits), "s"(a.part),
+               "s"(a.out), "s"(a.lse), "s"(a.q_pos0), "s"(a.n_sel));
   const int lane = threadIdx.x;
   const int hh = blockIdx.x % HG, ut = blockIdx.x / HG;  // ut = unit * lq + tq
   const int unit = ut / a.lq, tq = ut % a.lq;

@@ -104,6 +104,13 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
 
   const KCfg& c = args.cfg;
   const AttendLaunch& a = args.a;
+  // every kernel argument used below, read from the argument segment at once
+  // (one scalar round trip, instead of one at each first use)
+  asm volatile("" ::"s"(c.lists), "s"(c.kvdiv), "s"(c.hq), "s"(c.hkv), "s"(c.n_sink),
+               "s"(c.n_local), "s"(c.interleaved), "s"(c.qscale_log2), "s"(a.lq), "s"(a.max_sel),
+               "s"(a.src_layout), "s"(a.src_cap), "s"(a.part_sel), "s"(a.two_part),
+               "s"(args.n_splits), "s"(a.B), "s"(a.q), "s"(a.q_pos0), "s"(a.k), "s"(a.v),
+               "s"(a.sel), "s"(a.n_sel), "s"(a.part));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = lane & 15, qg = lane >> 4;
   const int n_rows = HG * a.lq;
