@@ -203,7 +203,9 @@ def calibrate_mfma(rounds=2500):
     f = lib.hga_calib_mfma_rate_shape
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
-    for shape, name in ((0, "v_mfma_f32_16x16x32_bf16"), (1, "v_mfma_f32_32x32x16_bf16")):
+    for shape, name in ((0, "v_mfma_f32_16x16x32_bf16"), (1, "v_mfma_f32_32x32x16_bf16"),
+                        (2, "v_mfma_f32_16x16x32_bf16, distinct operands, 8 accumulators"),
+                        (3, "v_mfma_f32_16x16x32_bf16, distinct operands, 16 accumulators")):
         for w in (1, 2, 4):
             tf, ms = ctypes.c_double(), ctypes.c_double()
             rc = f(n_cus, w, rounds, shape, ctypes.byref(tf), ctypes.byref(ms))
