@@ -234,11 +234,14 @@ def cpu_baseline(inp, cfg_params, min_seconds=10.0):
     kp = np.zeros((U, T, d))
     vp = np.zeros((U, T, d))
     kraw = []
+    t_sum = 0.0  # the summary builds of the completed chunks, timed (one thread each)
     for b in range(B):
         for h in range(hkv):
             u = b * hkv + h
             kr = inp.f64(inp.k[b, h])
+            t0 = time.perf_counter()
             a, g = oracle.summaries(cfg, kr[:c0])
+            t_sum += time.perf_counter() - t0
             cs[u, :a.shape[0]] = a
             gs[u, :g.shape[0]] = g
             kp[u] = oracle.pool(cfg, kr, 0)
@@ -281,7 +284,11 @@ def cpu_baseline(inp, cfg_params, min_seconds=10.0):
             "single_thread": {"value": B / med1, "unit": "tokens/s", "cores": 1,
                               "sample": f"route + attend of the same {U} units on one thread "
                                         f"(no append or refresh); median of {len(t1s)} runs "
-                                        f"({med1 * 1e3:.1f} ms each)"}}
+                                        f"({med1 * 1e3:.1f} ms each)"},
+            "summary_build": {"value": U * c0 / t_sum / 1e6, "unit": "M token rows/s", "cores": 1,
+                              "sample": f"chunk and group summaries of the {c0} completed tokens "
+                                        f"of each of the {U} units, one thread ({t_sum:.2f} s in "
+                                        f"all)"}}
 
 
 def host_cpu_model():
