@@ -189,6 +189,29 @@ def calibrate_copy_rate(reps=50):
                           "frac_of_8TBps": 2 * n_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}),
               flush=True)
         del src, dst
+    # what one CU pulls from HBM: few workgroups, each reading its own 1 MiB,
+    # a fresh slice of a 2 GiB buffer per launch (no cache reuse)
+    import numpy as np
+    g = lib.hga_calib_cu_read_rate
+    g.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    per = 1 << 20
+    src = torch.ones(2048 * per, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256 * 1024, dtype=torch.int32, device="cuda")
+    for n_wg, thr in ((32, 1024), (32, 256), (64, 1024), (256, 256)):
+        ts = []
+        for r in range(1, 2048 // n_wg):
+            gb, ms = ctypes.c_double(), ctypes.c_double()
+            rc = g(src.data_ptr() + r * n_wg * per, per, n_wg, thr, out.data_ptr(), 1,
+                   ctypes.byref(gb), ctypes.byref(ms))
+            assert rc == 0, rc
+            ts.append(ms.value)
+        t = float(np.median(ts))
+        print(json.dumps({"calibration": "per-workgroup HBM read rate", "workgroups": n_wg,
+                          "threads": thr, "bytes_per_workgroup": per, "launches": len(ts),
+                          "us_median": t * 1e3, "GBps_per_workgroup": per / (t * 1e-3) / 1e9,
+                          "GBps_total": n_wg * per / (t * 1e-3) / 1e9}), flush=True)
+    del src, out
 
 
 def calibrate_mfma(rounds=2500):

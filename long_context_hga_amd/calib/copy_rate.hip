@@ -39,7 +39,67 @@ __global__ __launch_bounds__(256) void copy_stride_kernel(const u32x4* __restric
     dst[i] = src[i];
 }
 
+// Per-workgroup read rate: workgroup w reads its own `per_wg` bytes (16
+// uint4 per thread in flight), folding them into one word per thread so the
+// loads stay.  With few workgroups this is the rate one CU pulls on its own.
+template <int NT>
+__global__ __launch_bounds__(NT) void cu_read_kernel(const u32x4* __restrict__ src, size_t per_wg,
+                                                     uint32_t* __restrict__ out) {
+  const u32x4* base = src + (size_t)blockIdx.x * (per_wg / 16);
+  const size_t n = per_wg / 16;
+  uint32_t acc = 0;
+  for (size_t i0 = 0; i0 < n; i0 += (size_t)16 * NT) {
+    u32x4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const size_t i = i0 + (size_t)u * NT + threadIdx.x;
+      v[u] = i < n ? base[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  out[(size_t)blockIdx.x * NT + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+// Read rate of n_wg workgroups of `threads` (256 or 1024) threads, each
+// reading its own per_wg bytes of src (a multiple of 16); out holds n_wg *
+// threads words.  *gbps: total bytes read / time, *ms: one launch (mean of
+// reps back to back).
+extern "C" int hga_calib_cu_read_rate(const void* src, size_t per_wg, int n_wg, int threads,
+                                      void* out, int reps, double* gbps, double* ms) {
+  if (!src || !out || per_wg == 0 || per_wg % 16 || n_wg <= 0 || (threads != 256 && threads != 1024) ||
+      reps <= 0 || !gbps || !ms)
+    return 1;
+  const u32x4* s = static_cast<const u32x4*>(src);
+  uint32_t* o = static_cast<uint32_t*>(out);
+  auto launch = [&]() {
+    if (threads == 256) hipLaunchKernelGGL(cu_read_kernel<256>, dim3(n_wg), dim3(256), 0, 0, s, per_wg, o);
+    else hipLaunchKernelGGL(cu_read_kernel<1024>, dim3(n_wg), dim3(1024), 0, 0, s, per_wg, o);
+  };
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return 2;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    hipEventDestroy(e0);
+    return 2;
+  }
+  int rc = 0;
+  launch();
+  (void)hipEventRecord(e0, 0);
+  for (int r = 0; r < reps; ++r) launch();
+  (void)hipEventRecord(e1, 0);
+  if (hipEventSynchronize(e1) != hipSuccess) rc = 3;
+  float t = 0.f;
+  if (!rc && hipEventElapsedTime(&t, e0, e1) != hipSuccess) rc = 4;
+  if (!rc) {
+    *ms = t / reps;
+    *gbps = (double)per_wg * n_wg / (*ms * 1e-3) / 1e9;
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return rc;
+}
 
 // variant 0: one uint4 per thread; 1: 4 per thread; 2: 4 per thread,
 // non-temporal; 3: 8 per thread; 4: grid-stride over 8 workgroups per CU
