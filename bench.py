@@ -415,6 +415,9 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
 
     pos = int(inp.pos0[0])
     c0 = (pos // 64) * 64
+    # selected lists per sequence: one per query head when routing per head;
+    # a working set holds max_sel groups of every list
+    lists = p["n_q_heads"] if p.get("route_per_head") else p["n_kv_heads"]
     q = gh.query_slice(st, 0)
     # raw K/V of the new token; raw keys of the chunk it completes (the
     # staging rows of the fused step, and the chunk input of the separate
@@ -478,9 +481,10 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
 
     if args.profile_calls:
         # counter runs: only the separate-entry calls, synchronised once
-        kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
+        kw = torch.empty((B, lists, st.max_sel * 16, p["head_dim"]),
                          dtype=reps[0]["k_pool"].dtype, device="cuda")
         vw = torch.empty_like(kw)
+        assert kw.numel() == B * reps[0]["s"].sel.shape[1] * st.max_sel * 16 * p["head_dim"]
         for i in range(args.profile_calls):
             x = reps[i % R]
             step_parts(i % R, None)
@@ -522,9 +526,11 @@ def measure_decode(args, name, batch=None, context=None, overrides=None, replica
     # own copy rate, read + write (bf16 pool)
     gather_ms, gather_bytes, copy_ms = float("nan"), 0, float("nan")
     if p.get("pool_dtype", 0) == 0:
-        kw = torch.empty((B, p["n_kv_heads"], st.max_sel * 16, p["head_dim"]),
+        kw = torch.empty((B, lists, st.max_sel * 16, p["head_dim"]),
                          dtype=reps[0]["k_pool"].dtype, device="cuda")
         vw = torch.empty_like(kw)
+        # the gather writes max_sel groups of every list of every sequence
+        assert kw.numel() == B * reps[0]["s"].sel.shape[1] * st.max_sel * 16 * p["head_dim"]
         gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(20)]
         for x in reps:  # first launches (code load, caches) stay out of the timing
@@ -674,14 +680,18 @@ def run_sweep(args):
               file=sys.stderr, flush=True)
         out, _ = measure_decode(args, name, batch=batch, context=context, overrides=over,
                                 replicas=R)
-        c, r = out["config"], out["roofline"]
+        c = out["config"]
+        calls = (out["roofline"], out["roofline_other_call"])
+        r = [x for x in calls if x["kernel"].startswith("hga_attend")][0]
+        rr = [x for x in calls if x["kernel"].startswith("hga_route")][0]
         print(json.dumps({"sweep": "decode", "workload": c["workload"], "context": c["context"],
                           "batch": c["batch"], "tokens_per_s": out["value"],
                           "ms_per_step": out["ms_per_step"],
+                          "median_us": out["timing_distribution"]["median_us"],
                           "step_GBps_algorithmic": c["step_GBps_algorithmic"],
                           "attend_ms": r["launch_ms"], "attend_bytes": r["bytes_per_launch"],
                           "attend_GBps": r["achieved"], "attend_frac_of_8TBps": r["frac"],
-                          "route_ms": r["route_launch_ms"]}), flush=True)
+                          "route_ms": rr["launch_ms"]}), flush=True)
 
 
 def prefill_algorithmic(p):
@@ -1035,6 +1045,9 @@ def run_host64k(args):
     torch.cuda.synchronize()
     pos = int(inp.pos0[0])
     c0 = (pos // 64) * 64
+    # selected lists per sequence: one per query head when routing per head;
+    # a working set holds max_sel groups of every list
+    lists = p["n_q_heads"] if p.get("route_per_head") else p["n_kv_heads"]
     q = gh.query_slice(st, 0)
     kt = st.k_raw[:, :, pos:pos + 1].contiguous()
     vt = st.v_raw[:, :, pos:pos + 1].contiguous()
