@@ -206,9 +206,11 @@ hga_status hga_route(const hga_config* cfg, int32_t B, const void* q_raw, int32_
  *   k_pool, v_pool as written by hga_build_summaries (pool_cap a multiple of
  *           16): device memory, or pinned host memory (pool_is_host = 1, read
  *           directly over PCIe).
- *   k_ws, v_ws [B][Hkv][max_sel*16][d] elements: list slot s of unit (b, h)
- *           receives the 16*d block of group sel_groups[b][h][s] (K rows;
- *           V in the pool's transposed group layout).  Bit-exact copy.
+ *   k_ws, v_ws [B][lists][max_sel*16][d] elements (lists = Hkv, or Hq with
+ *           route_per_head = 1; caller-owned, and the library cannot check
+ *           its size): list slot s of list (b, h) receives the 16*d block of
+ *           group sel_groups[b][h][s] (K rows; V in the pool's transposed
+ *           group layout).  Bit-exact copy.
  *   part    HGA_PART_ALL copies every slot; HGA_PART_ROUTED only the routed
  *           slots; HGA_PART_WINDOWS only the window slots (q_pos0 tells them
  *           apart; it may be NULL for HGA_PART_ALL).
