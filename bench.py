@@ -66,15 +66,15 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="09b5e9664aee9abfedac94e222b509fa14338f373a029d6c2432048b0c4cf98f",
-    fetch_kib=16744.96 + 1446.12, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="e64a94b2114a33bc277413cb49fcd818bdea454fe687d060a6d0e23070657190",
+    fetch_kib=16750.51 + 1446.12, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="a61274dc0c13b3644513f2a2efb816eddf73fe66930df296e2132252ef027a59",
-    fetch_kib=8491.62 + 1955.06, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="9b5d12fd1798d536545e26689732d2038902207a4dd097c0d2f65037f776f347",
+    fetch_kib=8484.17 + 1946.71, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):

@@ -142,6 +142,10 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
       qy[i] = __float_as_uint(static_cast<const float*>(a.q)[row + pair_b(c, jr)]);
     }
   }
+  // the RoPE frequency of pair jr (a kernel argument indexed by lane, so a
+  // vector load): issued with the query loads, ahead of the K/V loads, so
+  // that the rotation below does not wait for them
+  const double nu = c.omega[jr] * 0.15915494309189533577;  // turns per position
 
   bool bad = n_sel < 0 || n_sel > a.max_sel || pos0 < 0 || (pos0 % kChunk) + a.lq > kChunk;
   ListParts lp{0, 0, 0};
@@ -238,7 +242,6 @@ __device__ __forceinline__ void decode_split(const AttendArgs& args, int split, 
   // ---- rotated, pre-scaled query rows of this column block -> LDS (bf16
   // hi, lo); rows past the last (head, token) are zero
   {
-    const double nu = c.omega[jr] * 0.15915494309189533577;  // turns per position
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rg + NRG * i;

@@ -49,14 +49,28 @@ __device__ __forceinline__ void load_q_raw(const uint16_t* qrow, int qg, uint4 (
   for (int k = 0; k < D / 32; ++k) qraw[k] = *reinterpret_cast<const uint4*>(qrow + 32 * k + 8 * qg);
 }
 
+// The RoPE frequencies of the lane's 16 query pairs, in the order rotate_q
+// takes them: interleaved pairs, i = 4k + w is pair 16k + 4qg + w; half-split
+// pairs, i = 8 half + 2w + e is pair 32 half + 8qg + 2w + e.  These are kernel
+// arguments indexed by lane (vector loads): the caller issues them with the
+// query loads so that the rotation, which runs while the K/V loads are in
+// flight, does not wait for those.
+template <int D>
+__device__ __forceinline__ void load_q_omega(const KCfg& c, int qg, double (&om)[16]) {
+  static_assert(D == 128, "16 RoPE pairs per lane");
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    om[i] = c.omega[c.interleaved ? 16 * (i >> 2) + 4 * qg + (i & 3) : 32 * (i >> 3) + 8 * qg + (i & 7)];
+}
+
 // Rotated, pre-scaled query of the lane's row at position tau: the angle
 // tau * omega_j is formed in fp64 as a fraction of a turn and reduced exactly
 // to [-1/2, 1/2]; sin and cos of the reduced turn run in fp32 (v_sin_f32 /
 // v_cos_f32 take turns), within ~1e-6 rad.  The result is split into bf16
 // hi + lo operands.
 template <int D>
-__device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 32], int tau, int qg,
-                                         bf16x8 (&qop_hi)[D / 32], bf16x8 (&qop_lo)[D / 32]) {
+__device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 32], const double (&om)[16],
+                                         int tau, bf16x8 (&qop_hi)[D / 32], bf16x8 (&qop_lo)[D / 32]) {
   constexpr int KS = D / 32;
   const double tau_d = (double)tau;
   uint32_t hi[KS][4], lo[KS][4];
@@ -68,8 +82,7 @@ __device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 
       const uint32_t wv[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const int j = 16 * k + 4 * qg + w;
-        const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
+        const double turns = tau_d * (om[4 * k + w] * 0.15915494309189533577);
         const float fr = (float)(turns - rint(turns));
         const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
         const float x = __uint_as_float(wv[w] << 16);
@@ -93,8 +106,7 @@ __device__ __forceinline__ void rotate_q(const KCfg& c, const uint4 (&qraw)[D / 
       float rx[2], ry[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int j = 32 * half + 8 * qg + 2 * w + e;
-        const double turns = tau_d * (c.omega[j] * 0.15915494309189533577);
+        const double turns = tau_d * (om[8 * half + 2 * w + e] * 0.15915494309189533577);
         const float fr = (float)(turns - rint(turns));
         const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
         const float x = __uint_as_float(e ? (wx[w] & 0xFFFF0000u) : (wx[w] << 16));

@@ -69,9 +69,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     sel_spec[g] = sel[v < a.max_sel ? v : a.max_sel - 1];
   }
   uint4 qraw[KS];
+  double om[16];
   {
     const int tq = row < a.lq ? row : a.lq - 1;
     load_q_raw<D>(static_cast<const uint16_t*>(a.q) + ((size_t)(b * c.hq + qh) * a.lq + tq) * D, qg, qraw);
+    load_q_omega<D>(c, qg, om);
   }
 
   bool bad = n_sel < 0 || n_sel > a.max_sel || pos0 < 0 || (pos0 % kChunk) + a.lq > kChunk;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   load_tile<D, 256, FP8>(a.k, a.v, gbase, tid, kraw, vraw, k_sc, v_sc, &sc);
   bf16x8 qop_hi[KS], qop_lo[KS];
-  rotate_q<D>(c, qraw, pos0 + row, qg, qop_hi, qop_lo);
+  rotate_q<D>(c, qraw, om, pos0 + row, qop_hi, qop_lo);
   bool all_before = true;  // every group present and before the query chunk (uniform)
 #pragma unroll
   for (int g = 0; g < kSplitGroups; ++g) all_before = all_before && gpos[g] >= 0 && gpos[g] + kGroupTokens <= pos0;

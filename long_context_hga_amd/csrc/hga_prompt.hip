@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
     }
   }
   uint4 qraw[KS];
+  double om[16];
   load_q_raw<D>(a.q + tok * D, qg, qraw);
+  load_q_omega<D>(c, qg, om);
   const float* k_sc = nullptr;
   const float* v_sc = nullptr;
   if constexpr (FP8) {  // the row scales follow the codes of every pool unit
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2))) 
     load_tile<D, NTHR, FP8>(a.k, a.v, gbase, tid, kraw, vraw, k_sc, v_sc, &sc);
   }
   bf16x8 qop_hi[KS], qop_lo[KS];
-  rotate_q<D>(c, qraw, tau, qg, qop_hi, qop_lo);
+  rotate_q<D>(c, qraw, om, tau, qop_hi, qop_lo);
 
   f32x4 o[NB];
 #pragma unroll

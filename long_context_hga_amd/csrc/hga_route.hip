@@ -20,9 +20,9 @@
 // position arrives, and also store the score range of every 16 rows, so the
 // selection can bin its scores without a reduction of its own.
 // Selection (route_select_fast_kernel, up to 1024 candidates and 64 kept
-// chunks): histogram selection with member slots (hga_topk.h), two workgroup
-// barriers, each wave loading the group rows of its own kept chunks as soon as
-// its cut is known, and the level-2 choice on one wave.  Longer candidate
+// chunks): histogram selection with member slots (hga_topk.h) at both
+// levels; between them one barrier publishes every wave's kept chunks and the
+// group rows of all kept chunks are dealt evenly over the four waves.  Longer candidate
 // lists run route_select_kernel: a 256-bin histogram between the min and max
 // score finds the bin holding the k-th largest score, every score in a
 // higher bin is kept, and the boundary bin is resolved exactly by rank
@@ -163,6 +163,15 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       }
     }
   };
+  // this thread's RoPE frequencies (kernel arguments indexed by lane: a
+  // vector load, issued here so that it is not queued behind the row loads)
+  double om[2] = {0.0, 0.0};
+  if constexpr (pool_q && !multi) {
+    om[0] = c.omega[j];
+  } else if constexpr (pool_q) {
+    om[0] = c.omega[2 * jp];
+    om[1] = c.omega[2 * jp + 1];
+  }
   if constexpr (!pool_q) {
   } else if constexpr (!multi) {
     const int t0 = sl < lq ? sl : lq - 1;
@@ -198,7 +207,9 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   if constexpr (pool_q && !multi) {
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) asm volatile("" ::"v"(xa[hh]), "v"(xb[hh]));
+    asm volatile("" ::"v"(om[0]));
   } else if constexpr (pool_q) {
+    asm volatile("" ::"v"(om[0]), "v"(om[1]));
 #pragma unroll
     for (int u = 0; u < TB; ++u)
 #pragma unroll
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     };
     if constexpr (!multi) {
       double cs = 1.0, sn = 0.0;
-      if (sl < lq) rope_cs((double)(pos0 + sl), c.omega[j], &cs, &sn);
+      if (sl < lq) rope_cs((double)(pos0 + sl), om[0], &cs, &sn);
 #pragma unroll
       for (int hh = 0; hh < kMaxHg; ++hh) {
         if (hh >= c.lhg) break;  // uniform
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       double cs[2], sn[2], cd[2], sd[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const double wj = c.omega[2 * jp + e];
+        const double wj = om[e];
         rope_cs((double)(pos0 + sl2), wj, &cs[e], &sn[e]);
         sincos_rad((double)S2 * wj, &sd[e], &cd[e]);
       }
@@ -328,7 +339,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
             y += to_d(xb[hh]);
           }
         double cs, sn;
-        rope_cs((double)(pos0 + sl), c.omega[j], &cs, &sn);
+        rope_cs((double)(pos0 + sl), om[0], &cs, &sn);
         qpart[sl][j][0] = x * cs - y * sn;
         qpart[sl][j][1] = x * sn + y * cs;
       } else {
@@ -340,7 +351,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
       double cs[2], sn[2], cd[2], sd[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const double wj = c.omega[2 * jp + e];
+        const double wj = om[e];
         rope_cs((double)(pos0 + sl2), wj, &cs[e], &sn[e]);
         sincos_rad((double)S2 * wj, &sd[e], &cd[e]);
       }
@@ -697,12 +708,15 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 //  2. Level 1 (sel_level, all threads): bins between the min and max of the
 //     ranges, counts and member slots, a barrier, then in every wave the cut
 //     and the boundary ranking.
-//  3. Each wave lists its kept chunks in order (ballot) and at once loads and
-//     scores the G group rows of its own kept chunks into its own region, with
-//     the range of those scores; barrier.
-//  4. Level 2 (sel_level again): thread t takes element t of the regions
-//     concatenated (ascending group order); the kept groups are written in
-//     that order after one more barrier for the per-wave counts.
+//  3. Each wave lists its kept chunks in order (scan of the keep bits) with
+//     their count; barrier.  The k1 * G group rows of the kept chunks, in
+//     ascending group order, are dealt over the waves 8 rows at a time (row i
+//     to wave (i / 8) % 4), every row load of a wave in flight at once; each
+//     wave scores its rows into the level-2 arrays at their element index and
+//     keeps the range of its scores; barrier.
+//  4. Level 2 (sel_level again): thread t takes element t; the kept groups
+//     are written in element order (= ascending group id) after one more
+//     barrier for the per-wave counts.
 constexpr int kFastMaxCand = 1024;
 constexpr int kFastMaxKept = 64;  // level-1 chunks kept: level 2 ranks <= 256 groups
 
@@ -710,17 +724,17 @@ template <int D, bool BF16, bool MAXQ = false>
 __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
-  // level-2 row passes in flight per wave: 12 x 8 rows covers 24 kept chunks, so a
-  // wave rarely needs a second round trip (52 kept chunks over 4 waves give
-  // ~13 +- 3 per wave); 252 VGPRs, one workgroup per CU anyway
-  constexpr int U = 12;
+  // level-2 row passes per wave: 8 x 8 rows, a quarter of the kFastMaxKept * G rows
+  constexpr int U = 8;
+  static_assert(4 * 8 * U >= kGroups * KPW, "one pass of loads covers every level-2 row");
   __shared__ int s_fine[kSelBins], s_fine2[kSelBins];
   __shared__ int s_coarse[kSelCoarse], s_coarse2[kSelCoarse];
-  __shared__ int s_slot[kSelBins * kSelSlots];  // both levels (level 2 starts after a barrier)
+  __shared__ __align__(16) int s_slot[kSelBins * kSelSlots];  // both levels (level 2 starts after a barrier)
   __shared__ __align__(16) double s_vals[kFastMaxCand];  // scores by element; token-plane scratch
   __shared__ int s_kl[4][KPW];             // kept candidate indices of each wave, ascending
-  __shared__ double s_l2[4][kGroups * KPW];  // level-2 scores of each wave's rows
-  __shared__ int s_n2[4];
+  __shared__ double s_l2[kGroups * KPW];  // level-2 scores, ascending group order
+  __shared__ int s_g2[kGroups * KPW];     // their group ids
+  __shared__ int s_n2[4];                 // chunks kept by each wave
   __shared__ double s_r2[8];               // level-2 score range of each wave (min, max)
   __shared__ int s_k2[4];                  // level-2 groups kept by each wave
   __shared__ int s_nbl[2];                 // overflowed boundary members collected
@@ -762,6 +776,7 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   const int n_rng = a.n_tiles * 4;
   const double2 rng = reinterpret_cast<const double2*>(a.ranges)[(size_t)unit * n_rng +
                                                                  (lane < n_rng ? lane : n_rng - 1)];
+  const int p0 = r.q_pos0[b];  // in flight across the barrier with the other loads
   const SelHist h1{s_fine, s_coarse, s_slot}, h2{s_fine2, s_coarse2, s_slot};
   sel_clear(h1, tid, 256);
   sel_clear(h2, tid, 256);
@@ -770,7 +785,7 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
 
   int pos0;
   Windows w;
-  if (!route_geometry(c, r, a.max_cand, b, &pos0, &w)) {
+  if (!route_geometry_at(c, r, a.max_cand, p0, &pos0, &w)) {
     if (tid == 0) r.n_sel[unit] = -1;
     return;
   }
@@ -804,35 +819,42 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
                      s_coarse, s_slot, s_vals, s_bl, &s_nbl[0]);
   }
 
-  // ---- 3. this wave's kept chunks in candidate order, their group rows
+  // ---- 3. each wave's kept chunks in candidate order; one barrier; then the
+  // group rows of all kept chunks in ascending group order, dealt evenly over
+  // the waves (row i goes to wave (i / 8) % 4, pass i / 32)
   const int kc = __popc(keep);
   const int kincl = wave_incl_scan(kc);
-  const int kw = __builtin_amdgcn_readlane(kincl, 63);  // kept by this wave (<= k1 <= KPW)
   {
     int o = kincl - kc;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if ((keep >> e) & 1u) s_kl[wave][o++] = 4 * tid + e;
   }
-  __builtin_amdgcn_wave_barrier();
-  // group rows: 8 lanes per 512-byte row, 8 rows per pass, U passes in flight
-  const int n2w = kw * kGroups;
+  if (lane == 63) s_n2[wave] = kincl;  // chunks kept by this wave
+  __syncthreads();
+  const int c0 = s_n2[0], c01 = c0 + s_n2[1], c012 = c01 + s_n2[2];
+  const int n2 = (c012 + s_n2[3]) * kGroups;  // = k1 * G <= 256
   double mn2 = INFINITY, mx2 = -INFINITY;
-  for (int base = 0; base < n2w; base += 8 * U) {
+  if (n2 > 0) {  // uniform
     float4 gb[U][NV];
+    int gids[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int i = base + 8 * u + g8;
-      i = i < n2w ? i : n2w - 1;  // clamped: every load issues, extras ignored
-      const int gid = (w.cand_lo + s_kl[wave][i / kGroups]) * kGroups + i % kGroups;
+      int i = 32 * u + 8 * wave + g8;
+      i = i < n2 ? i : n2 - 1;  // clamped: every load issues, extras ignored
+      const int j = i / kGroups;  // kept chunk rank, ascending candidate order
+      const int rg = (j >= c0) + (j >= c01) + (j >= c012);
+      const int e = j - (rg == 0 ? 0 : rg == 1 ? c0 : rg == 2 ? c01 : c012);
+      gids[u] = (w.cand_lo + s_kl[rg][e]) * kGroups + i % kGroups;
       const float4* rowp = reinterpret_cast<const float4*>(
-          r.group_sum + ((size_t)unit_p * r.max_chunks * kGroups + gid) * D);
+          r.group_sum + ((size_t)unit_p * r.max_chunks * kGroups + gids[u]) * D);
 #pragma unroll
       for (int v = 0; v < NV; ++v) gb[u][v] = rowp[v * kLanesPerRow + sub];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = base + 8 * u + g8;
+      if (32 * u + 8 * wave >= n2) break;  // uniform: no row of this pass is in the list
+      const int i = 32 * u + 8 * wave + g8;
       double d = 0.0;
       if constexpr (MAXQ) {
         d = route_row_max<NV>(gb[u], &s_qh[0][0], c.lhg, sub) * c.inv_sqrt_d;
@@ -846,8 +868,9 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
         }
         d = group8_sum_d(d) * c.inv_sqrt_d;
       }
-      if (sub == 0 && i < n2w) {
-        s_l2[wave][i] = d;
+      if (sub == 0 && i < n2) {
+        s_l2[i] = d;
+        s_g2[i] = gids[u];
         mn2 = fmin(mn2, d);
         mx2 = fmax(mx2, d);
       }
@@ -856,24 +879,17 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   mn2 = wave_ext_d<false>(mn2);
   mx2 = wave_ext_d<true>(mx2);
   if (lane == 0) {
-    s_n2[wave] = n2w;
     s_r2[wave] = mn2;
     s_r2[4 + wave] = mx2;
   }
   __syncthreads();
 
-  // ---- 4. level 2: thread t takes element t of the concatenated regions
-  const int c0n = s_n2[0], c1n = s_n2[1], c2n = s_n2[2];
-  const int n2 = c0n + c1n + c2n + s_n2[3];  // = k1 * G <= 256
+  // ---- 4. level 2: thread t takes element t (ascending group order)
   double y = 0.0;
   int gid = 0;
   if (tid < n2) {
-    int e = tid, rg = 0;
-    if (e >= c0n) { e -= c0n; rg = 1;
-      if (e >= c1n) { e -= c1n; rg = 2;
-        if (e >= c2n) { e -= c2n; rg = 3; } } }
-    y = s_l2[rg][e];
-    gid = (w.cand_lo + s_kl[rg][e / kGroups]) * kGroups + e % kGroups;
+    y = s_l2[tid];
+    gid = s_g2[tid];
   }
   bool kept2 = tid < n2;
   if (k2 < n2 && k2 > 0) {  // uniform

@@ -303,13 +303,6 @@ __device__ __forceinline__ void sel_clear(const SelHist& h, int t, int step) {
   for (int i = t; i < kSelCoarse; i += step) h.coarse[i] = 0;
 }
 
-// Counts element idx in bin b and records it while the bin has free slots.
-__device__ __forceinline__ void sel_add(const SelHist& h, int b, int idx) {
-  const int at = atomicAdd(&h.fine[b], 1);
-  atomicAdd(&h.coarse[b >> 4], 1);
-  if (at < kSelSlots) h.slot[b * kSelSlots + at] = idx;
-}
-
 // The bin bs of the k-th best (count(bins > bs) < k <= count(bins >= bs)),
 // need = k - count(bins > bs) and nb = count(bs), from complete counts; run
 // by a whole wave (every lane gets the result).  1 <= k <= total.
@@ -339,22 +332,35 @@ __device__ __forceinline__ void sel_cut(const SelHist& h, int k, int* bs, int* n
   *nb = cL;
 }
 
-// Rank of element (i, x) of the boundary bin bs among its slot-listed
-// members (valid when nb <= kSelSlots): the members scoring higher, or equal
-// with a lower index.  vals: the scores by element index (LDS).
-__device__ __forceinline__ int sel_rank_slots(const SelHist& h, int bs, int nb, int i, double x,
-                                              const double* vals) {
+// The slot-listed members of the boundary bin bs (nb <= kSelSlots of them,
+// nb >= 1) and their scores, read once for all of a thread's elements: one
+// 16-byte slot read, then the nb score reads together (absent slots repeat
+// member 0).  slot must be 16-byte aligned.  vals: scores by element (LDS).
+struct SlotMembers {
   int m[kSelSlots];
+  double v[kSelSlots];
+};
+__device__ __forceinline__ SlotMembers sel_slot_members(const SelHist& h, int bs, int nb,
+                                                        const double* vals) {
+  static_assert(kSelSlots == 4, "one 16-byte slot read");
+  const int4 ms = *reinterpret_cast<const int4*>(h.slot + bs * kSelSlots);
+  SlotMembers r;
+  r.m[0] = ms.x;
+  r.m[1] = nb > 1 ? ms.y : ms.x;
+  r.m[2] = nb > 2 ? ms.z : ms.x;
+  r.m[3] = nb > 3 ? ms.w : ms.x;
 #pragma unroll
-  for (int u = 0; u < kSelSlots; ++u) m[u] = h.slot[bs * kSelSlots + u];
+  for (int u = 0; u < kSelSlots; ++u) r.v[u] = vals[r.m[u]];
+  return r;
+}
+
+// Rank of element (i, x) of the boundary bin among those members: the
+// members scoring higher, or equal with a lower index.
+__device__ __forceinline__ int sel_rank_slots(const SlotMembers& sm, int nb, int i, double x) {
   int r = 0;
 #pragma unroll
-  for (int u = 0; u < kSelSlots; ++u) {
-    if (u < nb) {
-      const double v = vals[m[u]];
-      r += (v > x) || (v == x && m[u] < i);
-    }
-  }
+  for (int u = 0; u < kSelSlots; ++u)
+    r += (u < nb) && ((sm.v[u] > x) || (sm.v[u] == x && sm.m[u] < i));
   return r;
 }
 
@@ -376,13 +382,20 @@ __device__ __noinline__ uint32_t sel_level(double x0, double x1, double x2, doub
   const int id[4] = {i0, i1, i2, i3};
   // a monotone map to bins (the scale needs no more than fp32)
   const double scale = mx > mn ? (double)((float)kSelBins / (float)(mx - mn)) : 0.0;
-  int bin[4];
+  // the four fine counts go out before any of their results is waited for;
+  // an absent element adds 0 to a count of its own (no value changes)
+  int bin[4], at[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    bin[e] = -1;
-    if (id[e] >= 0) {
-      bin[e] = topk_bin_n<kSelBins>(x[e], mn, scale);
-      sel_add(h, bin[e], id[e]);
+    bin[e] = id[e] >= 0 ? topk_bin_n<kSelBins>(x[e], mn, scale) : -1;
+    at[e] = atomicAdd(&h.fine[bin[e] >= 0 ? bin[e] : (4 * threadIdx.x + e) % kSelBins],
+                      id[e] >= 0 ? 1 : 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (id[e] >= 0) {  // counted; recorded while the bin has free slots
+      atomicAdd(&h.coarse[bin[e] >> 4], 1);
+      if (at[e] < kSelSlots) h.slot[bin[e] * kSelSlots + at[e]] = id[e];
       vals[id[e]] = x[e];
     }
   }
@@ -394,9 +407,10 @@ __device__ __noinline__ uint32_t sel_level(double x0, double x1, double x2, doub
   for (int e = 0; e < 4; ++e) keep |= (bin[e] > bs || (bin[e] == bs && nb == need) ? 1u : 0u) << e;
   if (nb == need) return keep;  // uniform
   if (nb <= kSelSlots) {
+    const SlotMembers sm = sel_slot_members(h, bs, nb, vals);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (bin[e] == bs && sel_rank_slots(h, bs, nb, id[e], x[e], vals) < need) keep |= 1u << e;
+      if (bin[e] == bs && sel_rank_slots(sm, nb, id[e], x[e]) < need) keep |= 1u << e;
     return keep;
   }
   // more members than slots (uniform): collect them all, then rank
