@@ -727,8 +727,8 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   // level-2 row passes per wave: 8 x 8 rows, a quarter of the kFastMaxKept * G rows
   constexpr int U = 8;
   static_assert(4 * 8 * U >= kGroups * KPW, "one pass of loads covers every level-2 row");
-  __shared__ int s_fine[kSelBins], s_fine2[kSelBins];
-  __shared__ int s_coarse[kSelCoarse], s_coarse2[kSelCoarse];
+  __shared__ __align__(16) int s_fine[kSelBins];
+  __shared__ __align__(16) int s_fine2[kSelBins];
   __shared__ __align__(16) int s_slot[kSelBins * kSelSlots];  // both levels (level 2 starts after a barrier)
   __shared__ __align__(16) double s_vals[kFastMaxCand];  // scores by element; token-plane scratch
   __shared__ int s_kl[4][KPW];             // kept candidate indices of each wave, ascending
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   const double2 rng = reinterpret_cast<const double2*>(a.ranges)[(size_t)unit * n_rng +
                                                                  (lane < n_rng ? lane : n_rng - 1)];
   const int p0 = r.q_pos0[b];  // in flight across the barrier with the other loads
-  const SelHist h1{s_fine, s_coarse, s_slot}, h2{s_fine2, s_coarse2, s_slot};
+  const SelHist h1{s_fine, s_slot}, h2{s_fine2, s_slot};
   sel_clear(h1, tid, 256);
   sel_clear(h2, tid, 256);
   if (tid < 2) s_nbl[tid] = 0;
@@ -815,8 +815,12 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
     const double mn = wave_ext_d<false>(rv ? rng.x : INFINITY);
     const double mx = wave_ext_d<true>(rv ? rng.y : -INFINITY);
     auto idx = [&](int e) { return 4 * tid + e < n_cand ? 4 * tid + e : -1; };
-    keep = sel_level(x[0], x[1], x[2], x[3], idx(0), idx(1), idx(2), idx(3), k1, mn, mx, s_fine,
-                     s_coarse, s_slot, s_vals, s_bl, &s_nbl[0]);
+    // the scores by element for the boundary ranking (two 16-byte stores;
+    // published by the routine's barrier)
+    reinterpret_cast<double2*>(s_vals)[2 * tid] = make_double2(x[0], x[1]);
+    reinterpret_cast<double2*>(s_vals)[2 * tid + 1] = make_double2(x[2], x[3]);
+    keep = sel_level(x[0], x[1], x[2], x[3], idx(0), idx(1), idx(2), idx(3), 4, k1, mn, mx, s_fine,
+                     s_slot, s_vals, s_bl, &s_nbl[0]);
   }
 
   // ---- 3. each wave's kept chunks in candidate order; one barrier; then the
@@ -895,8 +899,8 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   if (k2 < n2 && k2 > 0) {  // uniform
     const double mn = fmin(fmin(s_r2[0], s_r2[1]), fmin(s_r2[2], s_r2[3]));
     const double mx = fmax(fmax(s_r2[4], s_r2[5]), fmax(s_r2[6], s_r2[7]));
-    kept2 = sel_level(y, 0.0, 0.0, 0.0, tid < n2 ? tid : -1, -1, -1, -1, k2, mn, mx, s_fine2,
-                      s_coarse2, s_slot, s_vals, s_bl, &s_nbl[1]) & 1u;
+    kept2 = sel_level(y, 0.0, 0.0, 0.0, tid < n2 ? tid : -1, -1, -1, -1, 1, k2, mn, mx, s_fine2,
+                      s_slot, s_l2, s_bl, &s_nbl[1]) & 1u;
   } else if (k2 <= 0) {
     kept2 = false;
   }

@@ -273,21 +273,22 @@ __device__ int block_topk(const double* s, int n, int k, int* out, const BlockTo
 // ---------------------------------------------------------------------------
 // Histogram selection with member slots (the routing's fast selection).
 // Scores are binned into kSelBins fine bins between their min and max (a
-// monotone map), counted in LDS together with kSelBins / 16 coarse bins, and
-// each fine bin records the indices of its first kSelSlots members.  The bin
-// bs of the k-th best is found by one wave in two short scans (the coarse bin
-// holding it, then its 16 fine bins); every element in a higher bin is kept,
-// and when bs holds more members than the `need` it contributes, they are
-// ranked exactly (score descending, index ascending) among the members its
-// slots list (or, when the bin overflowed its slots, among all members).
+// monotone map), counted in LDS, and each fine bin records the indices of
+// its first kSelSlots members.  The bin bs of the k-th best is found by one
+// wave in two short scans (the group of 16 bins holding it, from the lane
+// sums of 16 counts each, then its 16 bins); every element in a higher bin is
+// kept, and when bs holds more members than the `need` it contributes, they
+// are ranked exactly (score descending, index ascending) among the members
+// its slots list (or, when the bin overflowed its slots, among all members).
+// LDS atomics are the costly step here (they run at a fraction of the LDS
+// rate), so each element takes exactly one: its fine count, whose return
+// value is its slot.
 constexpr int kSelBins = 1024;
-constexpr int kSelCoarse = kSelBins / 16;
 constexpr int kSelSlots = 4;
 
 struct SelHist {
-  int* fine;    // kSelBins counts
-  int* coarse;  // kSelCoarse counts
-  int* slot;    // kSelBins * kSelSlots member indices
+  int* fine;  // kSelBins counts, 16-byte aligned
+  int* slot;  // kSelBins * kSelSlots member indices, 16-byte aligned
 };
 
 template <int NB>
@@ -300,23 +301,29 @@ __device__ __forceinline__ int topk_bin_n(double x, double mn, double scale) {
 // Zeroes the counts; threads t = 0, step, 2 step, ... of the caller share it.
 __device__ __forceinline__ void sel_clear(const SelHist& h, int t, int step) {
   for (int i = t; i < kSelBins; i += step) h.fine[i] = 0;
-  for (int i = t; i < kSelCoarse; i += step) h.coarse[i] = 0;
 }
 
 // The bin bs of the k-th best (count(bins > bs) < k <= count(bins >= bs)),
 // need = k - count(bins > bs) and nb = count(bs), from complete counts; run
 // by a whole wave (every lane gets the result).  1 <= k <= total.
 __device__ __forceinline__ void sel_cut(const SelHist& h, int k, int* bs, int* need, int* nb) {
-  static_assert(kSelCoarse == 64, "one coarse bin per lane");
+  static_assert(kSelBins == 64 * 16, "16 bins per lane");
   const int lane = threadIdx.x & 63;
-  const int cc = h.coarse[lane];
+  // lane l sums bins 16 l .. 16 l + 15 (four 16-byte reads)
+  const int4* f4 = reinterpret_cast<const int4*>(h.fine + 16 * lane);
+  int cc = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int4 v = f4[u];
+    cc += (v.x + v.y) + (v.z + v.w);
+  }
   const int pre = wave_incl_scan(cc);
   const int total = __builtin_amdgcn_readlane(pre, 63);
-  const int suf = total - pre + cc;  // count in coarse bins >= lane
-  const int above = suf - cc;        // count in coarse bins > lane
+  const int suf = total - pre + cc;  // count in bins >= 16 lane
+  const int above = suf - cc;        // count in bins >= 16 (lane + 1)
   const int C = __ffsll((long long)__ballot(above < k && k <= suf)) - 1;
   const int above_c = __builtin_amdgcn_readlane(above, C);
-  // the 16 fine bins of C, highest first: lane l of each 16-lane row holds
+  // the 16 bins of C, highest first: lane l of each 16-lane row holds
   // bin 16 C + 15 - l; a row-local inclusive scan counts bins >= it in C
   const int fl = lane & 15;
   const int fc = h.fine[16 * C + 15 - fl];
@@ -335,7 +342,7 @@ __device__ __forceinline__ void sel_cut(const SelHist& h, int k, int* bs, int* n
 // The slot-listed members of the boundary bin bs (nb <= kSelSlots of them,
 // nb >= 1) and their scores, read once for all of a thread's elements: one
 // 16-byte slot read, then the nb score reads together (absent slots repeat
-// member 0).  slot must be 16-byte aligned.  vals: scores by element (LDS).
+// member 0).  vals: scores by element (LDS).
 struct SlotMembers {
   int m[kSelSlots];
   double v[kSelSlots];
@@ -366,39 +373,37 @@ __device__ __forceinline__ int sel_rank_slots(const SlotMembers& sm, int nb, int
 
 // One level of the selection, run by all 256 threads of the workgroup (the
 // routing calls it for both levels, so the second call runs from a warm
-// instruction cache).  Thread t holds up to 4 elements: x[e] with element
-// index id[e] (< 0: no element).  Of the n elements the k best are kept
-// (1 <= k < n); mn / mx bound the scores.  The counts (fine, coarse) are zero
-// on entry (the caller clears them a barrier earlier); slot receives the
-// member slots, vals (indexed by element) the scores for the boundary
-// ranking; bl / nbl (nbl zero on entry) collect the members of a boundary
-// bin that overflowed its slots.  Returns bit e set iff element e is kept.
+// instruction cache).  Thread t holds up to ne (1..4, uniform) elements: x[e]
+// with element index id[e] (< 0: no element; elements ne..3 must be absent).  Of the n elements the k best
+// are kept (1 <= k < n); mn / mx bound the scores.  The counts (fine) are
+// zero on entry (the caller clears them a barrier earlier); slot receives
+// the member slots; vals must already hold every element's score at its
+// index (the boundary ranking reads it after this routine's barrier); bl /
+// nbl (nbl zero on entry) collect the members of a boundary bin that
+// overflowed its slots.  Returns bit e set iff element e is kept.
 __device__ __noinline__ uint32_t sel_level(double x0, double x1, double x2, double x3, int i0,
-                                           int i1, int i2, int i3, int k, double mn, double mx,
-                                           int* fine, int* coarse, int* slot, double* vals,
+                                           int i1, int i2, int i3, int ne, int k, double mn,
+                                           double mx, int* fine, int* slot, const double* vals,
                                            int* bl, int* nbl) {
-  const SelHist h{fine, coarse, slot};  // by pointer: a struct argument would go through scratch
+  const SelHist h{fine, slot};  // by pointer: a struct argument would go through scratch
   const double x[4] = {x0, x1, x2, x3};
   const int id[4] = {i0, i1, i2, i3};
   // a monotone map to bins (the scale needs no more than fp32)
   const double scale = mx > mn ? (double)((float)kSelBins / (float)(mx - mn)) : 0.0;
-  // the four fine counts go out before any of their results is waited for;
-  // an absent element adds 0 to a count of its own (no value changes)
+  // the counts of the ne elements go out before any of their results is
+  // waited for; an absent element among them adds 0 to a count of its own
   int bin[4], at[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     bin[e] = id[e] >= 0 ? topk_bin_n<kSelBins>(x[e], mn, scale) : -1;
-    at[e] = atomicAdd(&h.fine[bin[e] >= 0 ? bin[e] : (4 * threadIdx.x + e) % kSelBins],
-                      id[e] >= 0 ? 1 : 0);
+    at[e] = kSelSlots;
+    if (e < ne)  // uniform
+      at[e] = atomicAdd(&h.fine[bin[e] >= 0 ? bin[e] : (4 * threadIdx.x + e) % kSelBins],
+                        id[e] >= 0 ? 1 : 0);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (id[e] >= 0) {  // counted; recorded while the bin has free slots
-      atomicAdd(&h.coarse[bin[e] >> 4], 1);
-      if (at[e] < kSelSlots) h.slot[bin[e] * kSelSlots + at[e]] = id[e];
-      vals[id[e]] = x[e];
-    }
-  }
+  for (int e = 0; e < 4; ++e)
+    if (id[e] >= 0 && at[e] < kSelSlots) h.slot[bin[e] * kSelSlots + at[e]] = id[e];
   __syncthreads();
   int bs, need, nb;
   sel_cut(h, k, &bs, &need, &nb);
