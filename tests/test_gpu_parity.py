@@ -172,6 +172,46 @@ def test_decode64k_reduced_batch2():
     assert pinned == units  # the oracle's smallest gap at the cut here is 1.5e-5
 
 
+@pytest.mark.parametrize("context", [16384, 65536])
+def test_exact_ties_keep_lowest_ids(context):
+    """All-zero keys: every chunk and group summary is zero, so every level-1
+    and level-2 score ties at exactly 0.0 on both sides.  The order (score
+    descending, id ascending) then fixes the lists: the k_c lowest candidate
+    chunks, and of their groups the k_g lowest.  Every score falls in one
+    histogram bin, so both levels take the boundary path whose bin holds more
+    members than its slots (250 and 1018 level-1 members here); the attention
+    is a uniform softmax over the visible selected keys."""
+    inp = synth.generate("decode64k", batch=1, context=context)
+    inp.k[...] = 0
+    st = gh.build_state(inp)
+    cfg = ora_cfg(inp)
+    pos = context - 1
+    q = gh.query_slice(st, 0)
+    pos_t = torch.full((1,), pos, dtype=torch.int32, device="cuda")
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, pos_t, s)
+    gh.attend(st, q, 1, pos_t, s)
+    torch.cuda.synchronize()
+    sel, nsel, out = s.sel.cpu().numpy(), s.n_sel.cpu().numpy(), s.out.cpu().numpy()
+    uc = UnitCache(inp, cfg)
+    G, ns, nl = 4, cfg.n_sink, cfg.n_local
+    ct = pos // 64
+    expect = np.concatenate([np.arange(ns * G), np.arange(ns * G, ns * G + cfg.topk_g),
+                             np.arange((ct - nl) * G, pos // 16 + 1)]).astype(np.int32)
+    hg = cfg.hq // cfg.hkv
+    for h in range(inp.k.shape[1]):
+        cs, gs, kp, v = uc.get(0, h)
+        assert not cs.any() and not gs.any()
+        qu = q_unit(inp, cfg, 0, h, 0, 1)
+        osel, _, _ = oracle.select(cfg, qu, pos, cs, gs)
+        g = sel[0, h, :nsel[0, h]]
+        np.testing.assert_array_equal(np.asarray(osel, dtype=np.int32), expect)
+        np.testing.assert_array_equal(g, expect)
+        o_ref, _ = oracle.attend(cfg, qu, pos, kp, v, g)
+        assert max_abs(out[0, h * hg:(h + 1) * hg, 0], o_ref[:, 0]) <= ATOL_OUT
+    say(f"[ties {context}] {expect.size} groups per list, lowest ids at both levels")
+
+
 def test_select_all_equals_dense():
     """Budgets above the candidate counts: the output is dense causal attention."""
     # t = 2047: candidates are chunks 1..26, so 26 chunks / 104 groups is all of them
