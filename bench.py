@@ -66,8 +66,8 @@ HBM_PEAK_GBS = 8000.0
 # on: if hga_attend.hip or hga_decode.hip has changed since, traffic is
 # reported as null.
 ATTEND_TRAFFIC = dict(
-    source_sha256="e64a94b2114a33bc277413cb49fcd818bdea454fe687d060a6d0e23070657190",
-    fetch_kib=16750.51 + 1446.12, write_kib=2080.00 + 136.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="cc38ba742d4ea0f51728196b44e428741e9ca90e81376bd039f78dec69db21e8",
+    fetch_kib=16752.70 + 1448.19, write_kib=2080.02 + 136.00, fetch_scale=2.0, write_scale=1.0)
 
 
 # The same for the routing entry point (its tile kernel plus its selection

@@ -25,10 +25,13 @@ __global__ __launch_bounds__(64) void attend_combine_kernel(AttendArgs args) {
   using OV = typename std::conditional<EPL == 2, float2, float>::type;
   const KCfg& c = args.cfg;
   const AttendLaunch& a = args.a;
-  // every kernel argument used below, read at once (one scalar round trip)
+  // every kernel argument used below, read at once (one scalar round trip;
+  // rec_splits, not used here, keeps whole the 16-byte argument load it shares
+  // with max_sel: left dead, its register was reused by a later load, which
+  // then had to wait for the first)
   asm volatile("" ::"s"(c.lists), "s"(c.hq), "s"(c.n_sink), "s"(c.n_local), "s"(a.lq),
                "s"(a.max_sel), "s"(a.part_sel), "s"(a.two_part), "s"(args.n_splits), "s"(a.part),
-               "s"(a.out), "s"(a.lse), "s"(a.q_pos0), "s"(a.n_sel));
+               "s"(a.out), "s"(a.lse), "s"(a.q_pos0), "s"(a.n_sel), "s"(a.rec_splits));
   const int lane = threadIdx.x;
   const int hh = blockIdx.x % HG, ut = blockIdx.x / HG;  // ut = unit * lq + tq
   const int unit = ut / a.lq, tq = ut % a.lq;
