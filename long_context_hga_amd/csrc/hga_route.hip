@@ -70,7 +70,7 @@ struct RouteArgs {
   int n_tiles;      // tile workgroups per unit
   double* ranges;   // workspace [units][n_tiles * 4] of (min, max): the level-1 scores of
                     // rows 16 l .. 16 l + 15 of the candidates (wave l % 4 of tile l / 4)
-  StepFront f;      // used by the workgroups with blockIdx.z == 1 of route_select
+  StepFront f;      // used by the workgroups with blockIdx.z >= 1 of route_select
 };
 
 // Position and candidate range of a unit; false if the query position is
@@ -480,9 +480,19 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 // summaries are built from the staging rows of the earlier positions plus
 // the new keys.  Neither is read by this step's routing: the current chunk
 // is never a candidate.  An unusable position (as route_geometry) writes
-// nothing.
+// nothing.  part < 0: all of it; with a step of many tokens the work is
+// spread over kFrontParts workgroups: part 0 builds the summaries (no
+// stores of rows), part 1 + g appends the step's tokens of group g of the
+// chunk.  Every token row and summary is computed as in the one-workgroup
+// form (build_span steps the angles of a 16-token group from the group's
+// first position either way), so the results are the same bits; what is
+// spread is the rows' stores, which the one workgroup issued through a
+// single CU.
+constexpr int kFrontParts = 1 + kGroups;
+constexpr int kFrontSplitLq = kGroupTokens;  // steps of at least a group of tokens split their work
+
 template <int D, bool BF16>
-__device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
+__device__ void step_front(const RouteArgs& a, int h, int b, double* lds, int part) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   const KCfg& c = a.cfg;
   const StepFront& f = a.f;
@@ -500,10 +510,16 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   // tokens, appended one row at a time by a small routine of its own)
   T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
   T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
+  // the step's tokens this workgroup appends: all, none (part 0: the
+  // summaries only) or those of group part - 1
+  const int g0 = c0 + (part - 1) * kGroupTokens;
+  const int lo = part <= 0 ? pos : (pos > g0 ? pos : g0);
+  const int hi = part < 0 ? pos + lq
+                          : (part == 0 ? pos : (pos + lq < g0 + kGroupTokens ? pos + lq : g0 + kGroupTokens));
   if constexpr (D == 128 && BF16) {
-    if (c.pool8) {  // lq <= 15 (checked on the host)
+    if (c.pool8) {
       const Fp8Rows f8 = fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit);
-      for (int p = pos; p < pos + lq; ++p)
+      for (int p = lo; p < hi; ++p)
         fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + ((size_t)unit * lq + (p - pos)) * D,
                        static_cast<const uint16_t*>(f.v_new) + ((size_t)unit * lq + (p - pos)) * D,
                        c0, p, f8);
@@ -515,11 +531,23 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
   float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
   const bool ends = pos + lq - c0 == kChunk;  // uniform
-  if (ends && pos == c0) {  // the whole chunk in this step: one pass
-    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
+  if (part > 0) {  // this group's tokens: rows only
+    if (lo < hi) build_span<D, BF16>(c, c0, lo, hi, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
     return;
   }
-  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
+  if (part == 0) {  // the summaries only
+    if (!ends) return;
+    if (pos == c0) {
+      build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, static_cast<T*>(nullptr),
+                          static_cast<T*>(nullptr), cs, gs, lds);
+      return;
+    }
+  } else if (ends && pos == c0) {  // the whole chunk in this step: one pass
+    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
+    return;
+  } else {
+    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
+  }
   if (ends) {
     build_span<D, BF16>(
         c, c0, c0, c0 + kChunk,
@@ -544,8 +572,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  if (blockIdx.z == 1) {  // a fused step's token work, once per KV head
-    if (h % c.kvdiv == 0) step_front<D, BF16>(a, h / c.kvdiv, b, dyn);
+  if (blockIdx.z >= 1) {  // a fused step's token work, once per KV head
+    if (h % c.kvdiv == 0)
+      step_front<D, BF16>(a, h / c.kvdiv, b, dyn, gridDim.z > 2 ? (int)blockIdx.z - 1 : -1);
     return;
   }
   const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
@@ -745,8 +774,9 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  if (blockIdx.z == 1) {  // a fused step's token work, once per KV head
-    if (h % c.kvdiv == 0) step_front<D, BF16>(a, h / c.kvdiv, b, s_vals);
+  if (blockIdx.z >= 1) {  // a fused step's token work, once per KV head
+    if (h % c.kvdiv == 0)
+      step_front<D, BF16>(a, h / c.kvdiv, b, s_vals, gridDim.z > 2 ? (int)blockIdx.z - 1 : -1);
     return;
   }
   const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
@@ -991,7 +1021,9 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   const size_t front_lds = (size_t)256 * 2 * sizeof(double);  // build_span scratch: S*P*2 doubles
   if (front && lds < front_lds) lds = front_lds;
   dim3 grid(n_tiles, cfg.lists, r.B);
-  dim3 sgrid(cfg.lists, r.B, front ? 2 : 1);
+  // the token work: one workgroup per unit, or kFrontParts for a step of
+  // many tokens
+  dim3 sgrid(cfg.lists, r.B, front ? (r.lq >= kFrontSplitLq ? 1 + kFrontParts : 2) : 1);
   const bool bf = cfg.dtype == HGA_BF16;
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   const bool fast = fast_select(cfg, a.max_cand);
