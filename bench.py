@@ -73,8 +73,8 @@ ATTEND_TRAFFIC = dict(
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="926855cee77975a685f24b882686b1ce68b5ced1b6af7012090d4adc43dd7c4f",
-    fetch_kib=8488.12 + 1950.62, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="629d76ac79c18924fbe1bd417da50c30e06c70326b66b42a9cc740965a7a3001",
+    fetch_kib=8490.54 + 1957.72, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):

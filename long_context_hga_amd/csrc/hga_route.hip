@@ -480,19 +480,9 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
 // summaries are built from the staging rows of the earlier positions plus
 // the new keys.  Neither is read by this step's routing: the current chunk
 // is never a candidate.  An unusable position (as route_geometry) writes
-// nothing.  part < 0: all of it; with a step of many tokens the work is
-// spread over kFrontParts workgroups: part 0 builds the summaries (no
-// stores of rows), part 1 + g appends the step's tokens of group g of the
-// chunk.  Every token row and summary is computed as in the one-workgroup
-// form (build_span steps the angles of a 16-token group from the group's
-// first position either way), so the results are the same bits; what is
-// spread is the rows' stores, which the one workgroup issued through a
-// single CU.
-constexpr int kFrontParts = 1 + kGroups;
-constexpr int kFrontSplitLq = kGroupTokens;  // steps of at least a group of tokens split their work
-
+// nothing.
 template <int D, bool BF16>
-__device__ void step_front(const RouteArgs& a, int h, int b, double* lds, int part) {
+__device__ void step_front(const RouteArgs& a, int h, int b, double* lds) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   const KCfg& c = a.cfg;
   const StepFront& f = a.f;
@@ -510,16 +500,10 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds, int pa
   // tokens, appended one row at a time by a small routine of its own)
   T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
   T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
-  // the step's tokens this workgroup appends: all, none (part 0: the
-  // summaries only) or those of group part - 1
-  const int g0 = c0 + (part - 1) * kGroupTokens;
-  const int lo = part <= 0 ? pos : (pos > g0 ? pos : g0);
-  const int hi = part < 0 ? pos + lq
-                          : (part == 0 ? pos : (pos + lq < g0 + kGroupTokens ? pos + lq : g0 + kGroupTokens));
   if constexpr (D == 128 && BF16) {
-    if (c.pool8) {
+    if (c.pool8) {  // lq <= 15 (checked on the host)
       const Fp8Rows f8 = fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit);
-      for (int p = lo; p < hi; ++p)
+      for (int p = pos; p < pos + lq; ++p)
         fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + ((size_t)unit * lq + (p - pos)) * D,
                        static_cast<const uint16_t*>(f.v_new) + ((size_t)unit * lq + (p - pos)) * D,
                        c0, p, f8);
@@ -531,23 +515,11 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds, int pa
   float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
   float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
   const bool ends = pos + lq - c0 == kChunk;  // uniform
-  if (part > 0) {  // this group's tokens: rows only
-    if (lo < hi) build_span<D, BF16>(c, c0, lo, hi, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
-    return;
-  }
-  if (part == 0) {  // the summaries only
-    if (!ends) return;
-    if (pos == c0) {
-      build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, static_cast<T*>(nullptr),
-                          static_cast<T*>(nullptr), cs, gs, lds);
-      return;
-    }
-  } else if (ends && pos == c0) {  // the whole chunk in this step: one pass
+  if (ends && pos == c0) {  // the whole chunk in this step: one pass
     build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, cs, gs, lds, stage);
     return;
-  } else {
-    build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
   }
+  build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
   if (ends) {
     build_span<D, BF16>(
         c, c0, c0, c0 + kChunk,
@@ -556,7 +528,71 @@ __device__ void step_front(const RouteArgs& a, int h, int b, double* lds, int pa
   }
 }
 
-template <int D, bool BF16, bool MAXQ = false>
+// The token work of a step of many tokens spread over kFrontParts
+// workgroups per unit: part 0 builds the chunk's summaries (no row stores),
+// part 1 + g appends the step's tokens of group g of the chunk (rows and
+// staging rows, no summaries).  Every row and sum is computed as step_front
+// computes it (build_span steps the angles of a 16-token group from the
+// group's first position either way), so the results are the same bits;
+// what is spread is the row stores, which one workgroup would issue through
+// a single CU.
+constexpr int kFrontParts = 1 + kGroups;
+constexpr int kFrontSplitLq = kGroupTokens;  // steps of at least a group of tokens split their work
+
+template <int D, bool BF16>
+__device__ void step_front_part(const RouteArgs& a, int h, int b, double* lds, int part) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  const KCfg& c = a.cfg;
+  const StepFront& f = a.f;
+  const int unit = b * c.hkv + h;
+  const int pos = a.r.q_pos0[b];
+  const int lq = a.r.lq;
+  if (pos < 0 || (pos % kChunk) + lq > kChunk || pos / kChunk >= a.r.max_chunks ||
+      pos + lq > f.pool_cap)
+    return;  // route_select reports the position
+  const int c0 = pos / kChunk * kChunk;
+  const T* kn = static_cast<const T*>(f.k_new) + (size_t)unit * lq * D;
+  const T* vn = static_cast<const T*>(f.v_new) + (size_t)unit * lq * D;
+  auto knew = [&](int p) { return kn + (size_t)(p - pos) * D; };
+  auto vnew = [&](int p) { return vn + (size_t)(p - pos) * D; };
+  if (part == 0) {  // the summaries, when the step ends the chunk
+    if (pos + lq - c0 != kChunk) return;
+    T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
+    const int chunk = pos / kChunk;
+    float* cs = f.chunk_sum + ((size_t)unit * a.r.max_chunks + chunk) * D;
+    float* gs = f.group_sum + ((size_t)unit * a.r.max_chunks + chunk) * kGroups * D;
+    if (pos == c0) {
+      build_span<D, BF16>(c, c0, pos, pos + lq, knew, vnew, static_cast<T*>(nullptr),
+                          static_cast<T*>(nullptr), cs, gs, lds);
+    } else {  // earlier positions from their staging rows (written by earlier steps)
+      build_span<D, BF16>(
+          c, c0, c0, c0 + kChunk,
+          [&](int p) { return p >= pos ? knew(p) : stage + (size_t)(p - c0) * D; },
+          [&](int) { return kn; }, static_cast<T*>(nullptr), static_cast<T*>(nullptr), cs, gs, lds);
+    }
+    return;
+  }
+  // the step's tokens of group part - 1
+  const int g0 = c0 + (part - 1) * kGroupTokens;
+  const int lo = pos > g0 ? pos : g0;
+  const int hi = pos + lq < g0 + kGroupTokens ? pos + lq : g0 + kGroupTokens;
+  if (lo >= hi) return;
+  T* stage = static_cast<T*>(f.k_stage) + (size_t)unit * kChunk * D;
+  T* kp = c.pool8 ? nullptr : static_cast<T*>(f.k_pool) + (size_t)unit * f.pool_cap * D;
+  T* vp = c.pool8 ? nullptr : static_cast<T*>(f.v_pool) + (size_t)unit * f.pool_cap * D;
+  if constexpr (D == 128 && BF16) {
+    if (c.pool8) {
+      const Fp8Rows f8 = fp8_rows_of(f.k_pool, f.v_pool, a.r.B * c.hkv, f.pool_cap, D, unit);
+      for (int p = lo; p < hi; ++p)
+        fp8_append_row(c, static_cast<const uint16_t*>(f.k_new) + ((size_t)unit * lq + (p - pos)) * D,
+                       static_cast<const uint16_t*>(f.v_new) + ((size_t)unit * lq + (p - pos)) * D,
+                       c0, p, f8);
+    }
+  }
+  build_span<D, BF16>(c, c0, lo, hi, knew, vnew, kp, vp, nullptr, nullptr, lds, stage);
+}
+
+template <int D, bool BF16, bool MAXQ = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int RPP = 256 / kLanesPerRow;  // rows per pass of the workgroup
@@ -572,9 +608,11 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  if (blockIdx.z >= 1) {  // a fused step's token work, once per KV head
-    if (h % c.kvdiv == 0)
-      step_front<D, BF16>(a, h / c.kvdiv, b, dyn, gridDim.z > 2 ? (int)blockIdx.z - 1 : -1);
+  if (SPLIT ? blockIdx.z >= 1 : blockIdx.z == 1) {  // a fused step's token work, per KV head
+    if (h % c.kvdiv == 0) {
+      if constexpr (SPLIT) step_front_part<D, BF16>(a, h / c.kvdiv, b, dyn, (int)blockIdx.z - 1);
+      else step_front<D, BF16>(a, h / c.kvdiv, b, dyn);
+    }
     return;
   }
   const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
@@ -749,7 +787,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs a) {
 constexpr int kFastMaxCand = 1024;
 constexpr int kFastMaxKept = 64;  // level-1 chunks kept: level 2 ranks <= 256 groups
 
-template <int D, bool BF16, bool MAXQ = false>
+template <int D, bool BF16, bool MAXQ = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   constexpr int NV = D / 32;
   constexpr int KPW = kFastMaxKept;       // kept chunks a wave can list
@@ -774,9 +812,11 @@ __global__ __launch_bounds__(256) void route_select_fast_kernel(RouteArgs a) {
   const RouteLaunch& r = a.r;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  if (blockIdx.z >= 1) {  // a fused step's token work, once per KV head
-    if (h % c.kvdiv == 0)
-      step_front<D, BF16>(a, h / c.kvdiv, b, s_vals, gridDim.z > 2 ? (int)blockIdx.z - 1 : -1);
+  if (SPLIT ? blockIdx.z >= 1 : blockIdx.z == 1) {  // a fused step's token work, per KV head
+    if (h % c.kvdiv == 0) {
+      if constexpr (SPLIT) step_front_part<D, BF16>(a, h / c.kvdiv, b, s_vals, (int)blockIdx.z - 1);
+      else step_front<D, BF16>(a, h / c.kvdiv, b, s_vals);
+    }
     return;
   }
   const int unit = b * c.lists + h;                     // lists and workspace: virtual sequence
@@ -995,11 +1035,20 @@ static void launch_tiles(bool multi, bool pooled_once, dim3 grid, hipStream_t st
   }
 }
 
-// Tiles then selection for one (head dim, dtype, pooling).
+// Tiles then selection for one (head dim, dtype, pooling); split: the token
+// work of a step of many tokens on kFrontParts workgroups per unit (such
+// steps run at head_dim 128 in bf16 only).
 template <int D, bool BF16, bool MAXQ>
-static void launch_route_d(bool multi, bool pooled_once, bool fast, dim3 grid, dim3 sgrid,
-                           size_t lds, hipStream_t st, const RouteArgs& a) {
+static void launch_route_d(bool multi, bool pooled_once, bool fast, bool split, dim3 grid,
+                           dim3 sgrid, size_t lds, hipStream_t st, const RouteArgs& a) {
   launch_tiles<D, BF16, MAXQ>(multi, pooled_once, grid, st, a);
+  if constexpr (D == 128 && BF16) {
+    if (split) {
+      if (fast) hipLaunchKernelGGL((route_select_fast_kernel<D, BF16, MAXQ, true>), sgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((route_select_kernel<D, BF16, MAXQ, true>), sgrid, dim3(256), lds, st, a);
+      return;
+    }
+  }
   if (fast) hipLaunchKernelGGL((route_select_fast_kernel<D, BF16, MAXQ>), sgrid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((route_select_kernel<D, BF16, MAXQ>), sgrid, dim3(256), lds, st, a);
 }
@@ -1023,26 +1072,27 @@ hipError_t launch_route(const KCfg& cfg, const RouteLaunch& r, hipStream_t st,
   dim3 grid(n_tiles, cfg.lists, r.B);
   // the token work: one workgroup per unit, or kFrontParts for a step of
   // many tokens
-  dim3 sgrid(cfg.lists, r.B, front ? (r.lq >= kFrontSplitLq ? 1 + kFrontParts : 2) : 1);
+  const bool split = front && r.lq >= kFrontSplitLq && cfg.d == 128 && cfg.dtype == HGA_BF16;
+  dim3 sgrid(cfg.lists, r.B, front ? (split ? 1 + kFrontParts : 2) : 1);
   const bool bf = cfg.dtype == HGA_BF16;
   const bool multi = r.lq > 256 / (cfg.d / 2);  // more tokens than slices
   const bool fast = fast_select(cfg, a.max_cand);
   const bool mq = cfg.route_max != 0;
   if (cfg.d == 128) {
     if (bf) {
-      if (mq) launch_route_d<128, true, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
-      else launch_route_d<128, true, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      if (mq) launch_route_d<128, true, true>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
+      else launch_route_d<128, true, false>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
     } else {
-      if (mq) launch_route_d<128, false, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
-      else launch_route_d<128, false, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      if (mq) launch_route_d<128, false, true>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
+      else launch_route_d<128, false, false>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
     }
   } else {
     if (bf) {
-      if (mq) launch_route_d<64, true, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
-      else launch_route_d<64, true, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      if (mq) launch_route_d<64, true, true>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
+      else launch_route_d<64, true, false>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
     } else {
-      if (mq) launch_route_d<64, false, true>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
-      else launch_route_d<64, false, false>(multi, r.pool_once, fast, grid, sgrid, lds, st, a);
+      if (mq) launch_route_d<64, false, true>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
+      else launch_route_d<64, false, false>(multi, r.pool_once, fast, split, grid, sgrid, lds, st, a);
     }
   }
   return hipGetLastError();
