@@ -73,8 +73,8 @@ ATTEND_TRAFFIC = dict(
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="629d76ac79c18924fbe1bd417da50c30e06c70326b66b42a9cc740965a7a3001",
-    fetch_kib=8490.54 + 1957.72, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
+    source_sha256="7736b2184a8502923fb133ea23fe8cb499ea13ad508d388b93694ee940b0a2dc",
+    fetch_kib=8490.04 + 1957.72, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
 def algorithmic_bytes(p, B):

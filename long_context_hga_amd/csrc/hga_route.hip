@@ -34,6 +34,15 @@
 
 namespace hga {
 
+// A 16-byte summary-row load that is read once per step: non-temporal, so
+// that the streamed rows do not displace cached lines (the scores, lists
+// and code the next kernels of the step read)
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_row_nt(const float4* p) {
+  const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kTile = 64;       // candidate chunks per tile workgroup
 constexpr int kLanesPerRow = 8; // lanes per summary row
 constexpr int kMaxHg = 8;       // query heads per list (max pooling keeps one query each)
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
     const float4* rowp =
         reinterpret_cast<const float4*>(r.chunk_sum + ((size_t)unit_p * r.max_chunks + row) * D);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) buf[it][v] = rowp[v * kLanesPerRow + sub];
+    for (int v = 0; v < NV; ++v) buf[it][v] = load_row_nt(rowp + v * kLanesPerRow + sub);
   }
 
   // ... and stay ahead of the exits below (the compiler would otherwise sink
