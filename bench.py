@@ -238,6 +238,78 @@ def calibrate_mfma(rounds=2500):
                               "published_peak_tflops": 2500.0}), flush=True)
 
 
+def calibrate_valu_decode(reps=200):
+    """The decode attention split on the vector ALUs (a calibration kernel of
+    libhga_calib.so, not part of the library) against the library's
+    matrix-core split, on the same decode64k lists: the two outputs compared,
+    both calls (split + merge) event-timed with the queue filled ahead.  The
+    calls alternate on one state, so each reads the selected K/V under the
+    same cache conditions as the other."""
+    import ctypes
+    import math
+    import numpy as np
+    import torch
+    import gpu_harness as gh
+    import synth
+    torch.cuda.init()
+    inp = synth.generate("decode64k")
+    st = gh.build_state(inp)
+    p = inp.params
+    B, T, d, hkv, hq = st.B, st.T, p["head_dim"], p["n_kv_heads"], p["n_q_heads"]
+    q = gh.query_slice(st, 0)
+    s = gh.alloc_step(st, 1)
+    gh.route(st, q, 1, st.pos0, s)
+    gh.attend(st, q, 1, st.pos0, s)
+    torch.cuda.synchronize()
+    vrows = gh.v_token_view(st.v_pool).contiguous()  # token rows [B][Hkv][T/16][16][d]
+    assert vrows.numel() == B * hkv * T * d
+    omega = (ctypes.c_double * (d // 2))(*[p["rope_theta"] ** (-2.0 * j / d) for j in range(d // 2)])
+    splits = (st.max_sel + 7) // 8
+    part = torch.empty(B * hkv * splits * (16 + 8 * d), dtype=torch.float32, device="cuda")
+    out = torch.full((B, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_hga_amd", "libhga_calib.so"))
+    f = lib.hga_calib_valu_decode
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_float, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    qscale = math.log2(math.e) / math.sqrt(d)
+
+    def valu():
+        rc = f(q.data_ptr(), st.pos0.data_ptr(), st.k_pool.data_ptr(), vrows.data_ptr(), T,
+               s.sel.data_ptr(), s.n_sel.data_ptr(), st.max_sel, B, hq, hkv, omega, qscale,
+               part.data_ptr(), out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, rc
+
+    def mfma():
+        gh.attend(st, q, 1, st.pos0, s)
+
+    valu()
+    torch.cuda.synchronize()
+    ref = s.out[:, :, 0, :]
+    assert torch.isfinite(out).all().item()
+    diff = (out - ref).abs().max().item()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda._sleep(int(2e8))
+    for e in ev:
+        e[0].record()
+        mfma()
+        e[1].record()
+        valu()
+        e[2].record()
+    torch.cuda.synchronize()
+    t_mfma = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    t_valu = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    kv_bytes = int(s.n_sel.sum().item()) * 16 * d * 2 * 2
+    print(json.dumps({"calibration": "decode attention split + merge: vector ALUs vs matrix cores",
+                      "workload": "decode64k lists (batch 8, 2048 selected keys per sequence and KV head)",
+                      "max_abs_diff_vs_library": diff, "selected_kv_bytes": kv_bytes,
+                      "mfma_call_ms": t_mfma, "valu_call_ms": t_valu,
+                      "mfma_GBps": kv_bytes / (t_mfma * 1e-3) / 1e9,
+                      "valu_GBps": kv_bytes / (t_valu * 1e-3) / 1e9, "reps": reps}), flush=True)
+    assert diff < 1e-4, diff
+
+
 def cpu_baseline(inp, cfg_params, min_seconds=10.0):
     """The fp64 C oracle doing the same step (append + chunk refresh + route +
     attend for every sequence of the batch), repeated for about min_seconds."""
@@ -354,6 +426,9 @@ def main():
                     help="only run a plain 512 MiB device copy (counter calibration)")
     ap.add_argument("--calibrate-copy-rate", action="store_true",
                     help="only measure plain device copies (the copy ceiling of the gather)")
+    ap.add_argument("--calibrate-valu-decode", action="store_true",
+                    help="only compare the decode attention on the vector ALUs (calibration "
+                         "kernel) with the library's matrix-core decode on the decode64k lists")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
@@ -367,6 +442,9 @@ def main():
         return
     if args.calibrate_mfma:
         calibrate_mfma()
+        return
+    if args.calibrate_valu_decode:
+        calibrate_valu_decode()
         return
     if args.sweep:
         run_sweep(args)
