@@ -73,7 +73,7 @@ ATTEND_TRAFFIC = dict(
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="7736b2184a8502923fb133ea23fe8cb499ea13ad508d388b93694ee940b0a2dc",
+    source_sha256="5c1281228bb81c921cb5082e87876fa398cc627f653fd0f2371286d04b301db0",
     fetch_kib=8490.04 + 1957.72, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 
