@@ -73,7 +73,7 @@ ATTEND_TRAFFIC = dict(
 # The same for the routing entry point (its tile kernel plus its selection
 # kernel), valid for the routing sources it was taken on.
 ROUTE_TRAFFIC = dict(
-    source_sha256="5c1281228bb81c921cb5082e87876fa398cc627f653fd0f2371286d04b301db0",
+    source_sha256="9e3ab9994fd6827c5c8a7759439521fe496c7511c2222ed124de0c7042b058c1",
     fetch_kib=8490.04 + 1957.72, write_kib=319.00 + 17.00, fetch_scale=2.0, write_scale=1.0)
 
 

@@ -118,9 +118,8 @@ __global__ __launch_bounds__(256) void route_tiles_kernel(RouteArgs a) {
   constexpr int S2 = 256 / JP;               // multi-token path: query-token slices
   constexpr int TPT = kChunk / S2;           // multi-token path: tokens per thread (max)
   using QT = typename std::conditional<BF16, uint32_t, float2>::type;  // two adjacent dims
-  // multi-token path: tokens per load batch (64 VGPRs; a chunked-prefill step's tile
-  // launch, a few workgroups per unit, loads all its tokens at once)
-  constexpr int TB = BF16 ? (MODE == 1 ? TPT : 4) : 2;
+  // multi-token path: tokens per load batch (bf16: every token of the thread at once)
+  constexpr int TB = BF16 ? TPT : 2;
   static_assert(TPT % TB == 0, "token batches");
   __shared__ double qpart[S2][P][2];
   __shared__ double qbar[D];
